@@ -1,0 +1,189 @@
+"""fp64 CPU oracle of the MSA layer hot path — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (``learned_kv_block_amd``)
+never imports it, and the oracle shares no code with the HIP kernels.
+
+The arithmetic lives in ``msa_oracle.c`` (plain double-precision loops, one
+query row at a time); this module only builds it with gcc and marshals numpy
+arrays through ctypes. ``diagnostics.py`` holds the selector metrics (set
+recall, teacher-mass coverage, relative output error).
+
+Every oracle function here is pinned by CPU tests against values fixed by the
+pages or by mathematics (worked examples, closed forms, library special
+cases, brute force, finite differences); see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "libmsa_ref.so")
+
+
+class RefShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seqlen_kv", "seqlen_q", "q_start", "num_q_heads", "num_kv_heads",
+        "head_dim", "idx_dim", "block_size", "topk", "dtype")]
+
+
+def build(force: bool = False) -> None:
+    """Compile the oracle with gcc (-O2, OpenMP over query rows)."""
+    if force or not os.path.exists(_SO):
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-o", _SO + ".tmp",
+                               os.path.join(_HERE, "msa_oracle.c"), "-lm"])
+        os.replace(_SO + ".tmp", _SO)
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        sp = ctypes.POINTER(RefShape)
+        lib.msa_ref_topk_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+        lib.msa_ref_select.argtypes = [sp, P, P, P, I64, P, P, P, P, ctypes.c_int]
+        lib.msa_ref_attn.argtypes = [sp, P, P, P, P, P, I64, P, P, ctypes.c_int]
+        lib.msa_ref_kl_row.argtypes = [ctypes.c_int, I64, P, P, P, P, P, P, P]
+        lib.msa_ref_kl.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, P, ctypes.c_int]
+        for f in ("msa_ref_topk_row", "msa_ref_select", "msa_ref_attn", "msa_ref_kl_row",
+                  "msa_ref_kl"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def shape_of(cfg) -> RefShape:
+    """RefShape from any object with the MSA shape attributes (e.g. seeded_inputs.MsaConfig)."""
+    return RefShape(cfg.batch, cfg.seqlen_kv, cfg.seqlen_q, cfg.q_start, cfg.num_q_heads,
+                    cfg.num_kv_heads, cfg.head_dim, cfg.idx_dim, cfg.block_size, cfg.topk,
+                    cfg.dtype)
+
+
+def _raw(a: np.ndarray, dtype: int) -> np.ndarray:
+    """Inputs are fp32 arrays (dtype 0) or uint16 bf16 bit patterns (dtype 1)."""
+    want = np.float32 if dtype == 0 else np.uint16
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError(f"oracle input must be {want.__name__} for dtype {dtype}, got {a.dtype}")
+    return a
+
+
+def _rows(shape: RefShape, rows):
+    if rows is None:
+        n = shape.batch * shape.seqlen_q
+        return None, n
+    r = _c(rows, np.int64)
+    return r, r.shape[0]
+
+
+def topk_row(M: Sequence[float], L: int, k: int):
+    """Selection of one row of block scores M[0..L] (L = local block). Returns (ids, margin)."""
+    M = _c(M, np.float64)
+    ids = np.empty(k, dtype=np.int32)
+    mg = np.zeros(1, dtype=np.float64)
+    rc = _L().msa_ref_topk_row(_p(M), int(L), int(k), _p(ids), _p(mg))
+    assert rc == 0
+    return ids, float(mg[0])
+
+
+def select(shape: RefShape, q_idx, k_idx, rows=None, want_scores=False, want_lse=False,
+           want_margin=False):
+    """ids [n, Hkv, k] (+ optional block scores / block LSE [n, Hkv, nb], margin [n, Hkv])."""
+    q_idx = _raw(q_idx, shape.dtype)
+    k_idx = _raw(k_idx, shape.dtype)
+    r, n = _rows(shape, rows)
+    nb = (shape.seqlen_kv + shape.block_size - 1) // shape.block_size
+    H = shape.num_kv_heads
+    ids = np.empty((n, H, shape.topk), dtype=np.int32)
+    sc = np.empty((n, H, nb), dtype=np.float64) if want_scores else None
+    bl = np.empty((n, H, nb), dtype=np.float64) if want_lse else None
+    mg = np.empty((n, H), dtype=np.float64) if want_margin else None
+    rc = _L().msa_ref_select(ctypes.byref(shape), _p(q_idx), _p(k_idx), _p(r), n, _p(ids),
+                             _p(sc), _p(bl), _p(mg), threads())
+    assert rc == 0, rc
+    out = {"ids": ids}
+    if want_scores:
+        out["block_scores"] = sc
+    if want_lse:
+        out["block_lse"] = bl
+    if want_margin:
+        out["margin"] = mg
+    return out
+
+
+def attn(shape: RefShape, q, k, v, ids, rows=None):
+    """(O [n, Hq, d], LSE [n, Hq]) in float64 on the support given by ids [n, Hkv, k]."""
+    q = _raw(q, shape.dtype)
+    k = _raw(k, shape.dtype)
+    v = _raw(v, shape.dtype)
+    ids = _c(ids, np.int32)
+    r, n = _rows(shape, rows)
+    out = np.empty((n, shape.num_q_heads, shape.head_dim), dtype=np.float64)
+    lse = np.empty((n, shape.num_q_heads), dtype=np.float64)
+    rc = _L().msa_ref_attn(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(ids), _p(r), n, _p(out),
+                           _p(lse), threads())
+    assert rc == 0, rc
+    return out, lse
+
+
+def kl_row(s_main, s_idx):
+    """KL alignment of one row from explicit logits: s_main [G, n], s_idx [n].
+
+    Returns dict(kl, dS, P, P_idx, lse_idx)."""
+    s_main = _c(s_main, np.float64)
+    s_idx = _c(s_idx, np.float64)
+    G, n = s_main.shape
+    kl = np.zeros(1)
+    dS = np.empty(n)
+    P = np.empty(n)
+    Pi = np.empty(n)
+    li = np.zeros(1)
+    rc = _L().msa_ref_kl_row(G, n, _p(s_main), _p(s_idx), _p(kl), _p(dS), _p(P), _p(Pi), _p(li))
+    assert rc == 0
+    return {"kl": float(kl[0]), "dS": dS, "P": P, "P_idx": Pi, "lse_idx": float(li[0])}
+
+
+def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True):
+    """KL alignment: dict(kl_rows [n, Hkv], kl_mean, lse_idx [n, Hkv], dlogits [n, Hkv, k, Bk])."""
+    q = _raw(q, shape.dtype)
+    k = _raw(k, shape.dtype)
+    q_idx = _raw(q_idx, shape.dtype)
+    k_idx = _raw(k_idx, shape.dtype)
+    ids = _c(ids, np.int32)
+    r, n = _rows(shape, rows)
+    H = shape.num_kv_heads
+    klr = np.empty((n, H), dtype=np.float64)
+    li = np.empty((n, H), dtype=np.float64)
+    dl = np.empty((n, H, shape.topk, shape.block_size), dtype=np.float64) if want_dlogits else None
+    mean = np.zeros(1)
+    rc = _L().msa_ref_kl(ctypes.byref(shape), _p(q), _p(k), _p(q_idx), _p(k_idx), _p(ids), _p(r),
+                         n, _p(klr), _p(dl), _p(li), _p(mean), threads())
+    assert rc == 0, rc
+    out = {"kl_rows": klr, "kl_mean": float(mean[0]), "lse_idx": li}
+    if want_dlogits:
+        out["dlogits"] = dl
+    return out

@@ -1,0 +1,434 @@
+/*
+ * msa_oracle.c — plain, slow, fp64 CPU oracle of the MSA layer hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing here is part of the product path: only the
+ * test suite, the smoke check and the CPU-baseline leg of the benchmark load
+ * this library. It shares no code with the HIP kernels (only the seeded input
+ * generator feeds both sides).
+ *
+ * Every quantity is the plain definition from the pages, evaluated in double
+ * precision from the exact input values (fp32 or bf16 bit patterns), one query
+ * row at a time, with per-row scratch only (never an N x N buffer). Rows are
+ * independent, so any subset of rows can be evaluated on its own.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [Indexer]  "MSA Indexer 与 DSA Lightning Indexer 的差别" (MSA vs DSA indexer note)
+ *  [KL]       "MSA 中的 KL 对齐与局部知识蒸馏" (MSA KL alignment note)
+ *  [Blog]     "MiniMax Sparse Attention：教长上下文模型使用索引" (MSA blog post)
+ *  [Native]   "2.4 · 训练原生稀疏" (training-native sparse attention)
+ *  [Superv]   "4.1.1 · 监督与联合训练" (selector supervision and joint training)
+ *
+ * Readings where the pages leave a step open (each also listed in the design notes):
+ *  - the forced local block counts inside k; the other k-1 slots take the best
+ *    earlier blocks;
+ *  - equal block scores rank the lower block index first;
+ *  - with fewer than k visible blocks, all visible blocks are selected and the
+ *    rest of the list is -1;
+ *  - the selected ids are written in ascending order;
+ *  - the main-branch softmax scale is 1/sqrt(head_dim);
+ *  - query head h belongs to GQA group floor(h / G);
+ *  - the teacher is normalised over the selected support J (sparse stage);
+ *  - the KL mean is taken over all (batch, query, group) rows.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t batch, seqlen_kv, seqlen_q, q_start, num_q_heads, num_kv_heads;
+  int32_t head_dim, idx_dim, block_size, topk, dtype; /* dtype: 0 fp32, 1 bf16 bits */
+} msa_ref_shape;
+
+enum { REF_OK = 0, REF_ERR_ARG = 1 };
+
+/* Exact value of element idx of an fp32 or bf16 array, as a double. */
+static double ld(const void* p, int dtype, int64_t idx) {
+  if (dtype == 0) return (double)((const float*)p)[idx];
+  uint32_t u = ((uint32_t)((const uint16_t*)p)[idx]) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static int shape_ok(const msa_ref_shape* s) {
+  if (!s) return 0;
+  if (s->batch < 0 || s->seqlen_kv < 0 || s->seqlen_q < 0 || s->q_start < 0) return 0;
+  if (s->num_kv_heads < 1 || s->num_q_heads < 1 || s->num_q_heads % s->num_kv_heads) return 0;
+  if (s->head_dim < 1 || s->idx_dim < 1 || s->block_size < 1 || s->topk < 1) return 0;
+  if ((int64_t)s->q_start + s->seqlen_q > s->seqlen_kv) return 0;
+  if (s->dtype != 0 && s->dtype != 1) return 0;
+  return 1;
+}
+
+static int num_blocks(const msa_ref_shape* s) {
+  return (s->seqlen_kv + s->block_size - 1) / s->block_size;
+}
+
+/* ------------------------------------------------------------------------ selection */
+
+/* Ranking of [Indexer] §2.2 with the tie rule: block a outranks block b when its
+ * score is larger, or the scores are equal and a has the lower index. */
+static int outranks(const double* M, int a, int b) {
+  return M[a] > M[b] || (M[a] == M[b] && a < b);
+}
+
+/*
+ * Block selection for one (query, group) row. M[0..L] are the block scores,
+ * L = the query's own (local) block.
+ *  - [Indexer] §2.2: take the top-k blocks by block score; the final recipe
+ *    always includes the query's local incomplete block.
+ *  - [Blog] "索引分支如何选择区块": the most recent local block is always
+ *    included, even when its learned score is low.
+ *  - [Blog] "系统教训": softmax preserves order, so the top-k is taken on raw
+ *    scores.
+ * Writes ids[0..k-1] ascending, -1 padded. *margin (optional) is the cutoff
+ * margin of [Superv] eq. (9) over the non-local candidates: score of the last
+ * block taken minus score of the best block left out, +inf when nothing is left
+ * out.
+ */
+int msa_ref_topk_row(const double* M, int L, int k, int32_t* ids, double* margin) {
+  if (!M || !ids || L < 0 || k < 1) return REF_ERR_ARG;
+  for (int s = 0; s < k; ++s) ids[s] = -1;
+  if (L + 1 <= k) {
+    for (int b = 0; b <= L; ++b) ids[b] = b;
+    if (margin) *margin = INFINITY;
+    return REF_OK;
+  }
+  /* k-1 rounds of "take the best block not yet taken" among blocks 0..L-1 */
+  unsigned char* taken = (unsigned char*)calloc((size_t)L, 1);
+  if (!taken) return REF_ERR_ARG;
+  int last = -1;
+  for (int round = 0; round < k - 1; ++round) {
+    int best = -1;
+    for (int b = 0; b < L; ++b)
+      if (!taken[b] && (best < 0 || outranks(M, b, best))) best = b;
+    taken[best] = 1;
+    last = best;
+  }
+  if (margin) {
+    int next = -1;
+    for (int b = 0; b < L; ++b)
+      if (!taken[b] && (next < 0 || outranks(M, b, next))) next = b;
+    *margin = (last >= 0 && next >= 0) ? M[last] - M[next] : INFINITY;
+  }
+  int n = 0;
+  for (int b = 0; b < L; ++b)
+    if (taken[b]) ids[n++] = b;
+  ids[n++] = L; /* the forced local block is the largest index */
+  free(taken);
+  return REF_OK;
+}
+
+/*
+ * Index logits, block scores and selection for the listed query rows.
+ *  - [Indexer] §2.1: S_idx[i,j] = Q_idx[i,r] . K_idx[j] / sqrt(d_idx), with Hkv
+ *    index-query heads (one per GQA group) and one shared index-key head.
+ *  - [Indexer] §2.2: M[i,b] = max over tokens j of block b with j <= i.
+ *  - [KL] §6: the index forward can keep a per-block log-sum-exp; block_lse
+ *    (optional) is logsumexp over the same causally visible tokens of block b.
+ * q_idx is compact: [nrows, Hkv, d_idx] for the listed rows; k_idx is the full
+ * [B, N, d_idx]. rows[q] = b*Nq + t (NULL = all rows in order).
+ * Outputs per listed row: ids [nrows, Hkv, k]; block_scores / block_lse
+ * [nrows, Hkv, nb] (entries after the local block are -inf); margin [nrows, Hkv].
+ */
+int msa_ref_select(const msa_ref_shape* s, const void* q_idx, const void* k_idx,
+                   const int64_t* rows, int64_t nrows, int32_t* ids, double* block_scores,
+                   double* block_lse, double* margin, int nthreads) {
+  if (!shape_ok(s) || !q_idx || !k_idx || !ids || nrows < 0) return REF_ERR_ARG;
+  const int Hkv = s->num_kv_heads, di = s->idx_dim, Bk = s->block_size, k = s->topk;
+  const int nb = num_blocks(s);
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const double inv_sqrt_di = 1.0 / sqrt((double)di);
+  if (nthreads < 1) nthreads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* M = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+    double* ql = (double*)malloc(sizeof(double) * (size_t)di);
+    if (!sc || !M || !ql) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nrows; ++q) {
+      if (err) continue;
+      const int64_t row = rows ? rows[q] : q;
+      const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+      const int64_t i = s->q_start + t;
+      const int L = (int)(i / Bk);
+      for (int r = 0; r < Hkv; ++r) {
+        for (int c = 0; c < di; ++c) ql[c] = ld(q_idx, s->dtype, (q * Hkv + r) * di + c);
+        for (int64_t j = 0; j <= i; ++j) {
+          double acc = 0.0;
+          for (int c = 0; c < di; ++c) acc += ql[c] * ld(k_idx, s->dtype, (b * N + j) * di + c);
+          sc[j] = acc * inv_sqrt_di;
+        }
+        for (int blk = 0; blk <= L; ++blk) {
+          const int64_t j0 = (int64_t)blk * Bk;
+          int64_t j1 = j0 + Bk - 1;
+          if (j1 > i) j1 = i;
+          double m = -INFINITY;
+          for (int64_t j = j0; j <= j1; ++j) m = sc[j] > m ? sc[j] : m;
+          M[blk] = m;
+          if (block_lse) {
+            double z = 0.0;
+            for (int64_t j = j0; j <= j1; ++j) z += exp(sc[j] - m);
+            block_lse[(q * Hkv + r) * nb + blk] = m + log(z);
+          }
+        }
+        if (block_scores)
+          for (int blk = 0; blk < nb; ++blk)
+            block_scores[(q * Hkv + r) * nb + blk] = blk <= L ? M[blk] : -INFINITY;
+        if (block_lse)
+          for (int blk = L + 1; blk < nb; ++blk) block_lse[(q * Hkv + r) * nb + blk] = -INFINITY;
+        double mg;
+        msa_ref_topk_row(M, L, k, ids + (q * Hkv + r) * k, &mg);
+        if (margin) margin[q * Hkv + r] = mg;
+      }
+    }
+    free(sc);
+    free(M);
+    free(ql);
+  }
+  return err ? REF_ERR_ARG : REF_OK;
+}
+
+/* ------------------------------------------------------------------------ support */
+
+/* Support J of one (query, group) row ([KL] §2): causally visible tokens
+ * (j <= i) of the selected blocks, in ascending block order. Returns |J|;
+ * slot[] and off[] give each token's list position and offset in its block. */
+static int64_t support(const int32_t* ids, int k, int Bk, int64_t i, int64_t N, int64_t* J,
+                       int* slot, int* off) {
+  int64_t n = 0;
+  for (int sl = 0; sl < k; ++sl) {
+    const int32_t blk = ids[sl];
+    if (blk < 0) continue;
+    for (int o = 0; o < Bk; ++o) {
+      const int64_t j = (int64_t)blk * Bk + o;
+      if (j > i || j >= N) break;
+      J[n] = j;
+      if (slot) slot[n] = sl;
+      if (off) off[n] = o;
+      ++n;
+    }
+  }
+  return n;
+}
+
+/* ------------------------------------------------------------------------ attention */
+
+/*
+ * Exact softmax attention of each query head over the selected support.
+ *  - [Native] eq. (2): softmax with the denominator restricted to the selected
+ *    set, output = sum of weights times values.
+ *  - [Blog] "核心思想": the main branch runs standard scaled dot-product
+ *    softmax attention on the tokens of the selected blocks; scale 1/sqrt(d).
+ *  - [Indexer] §2.3: the G query heads of GQA group r share the group's block
+ *    list and KV head r; each head keeps its own query.
+ *  - [KL] §6: the forward also reports LSE_main per (query, head).
+ * q is compact [nrows, Hq, d]; k, v are [B, N, Hkv, d]; ids [nrows, Hkv, k].
+ * out [nrows, Hq, d], lse [nrows, Hq] (double).
+ */
+int msa_ref_attn(const msa_ref_shape* s, const void* q, const void* kk, const void* v,
+                 const int32_t* ids, const int64_t* rows, int64_t nrows, double* out,
+                 double* lse, int nthreads) {
+  if (!shape_ok(s) || !q || !kk || !v || !ids || !out || nrows < 0) return REF_ERR_ARG;
+  const int Hq = s->num_q_heads, Hkv = s->num_kv_heads, G = Hq / Hkv, d = s->head_dim;
+  const int Bk = s->block_size, k = s->topk;
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  if (nthreads < 1) nthreads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    const int64_t cap = (int64_t)k * Bk;
+    int64_t* J = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!J || !sc || !o) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t qq = 0; qq < nrows; ++qq) {
+      if (err) continue;
+      const int64_t row = rows ? rows[qq] : qq;
+      const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+      const int64_t i = s->q_start + t;
+      for (int r = 0; r < Hkv; ++r) {
+        const int64_t n = support(ids + (qq * Hkv + r) * k, k, Bk, i, N, J, NULL, NULL);
+        for (int h = r * G; h < (r + 1) * G; ++h) {
+          double m = -INFINITY;
+          for (int64_t a = 0; a < n; ++a) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+              acc += ld(q, s->dtype, (qq * Hq + h) * d + c) *
+                     ld(kk, s->dtype, ((b * N + J[a]) * Hkv + r) * d + c);
+            sc[a] = acc * inv_sqrt_d;
+            m = sc[a] > m ? sc[a] : m;
+          }
+          double z = 0.0;
+          for (int64_t a = 0; a < n; ++a) z += exp(sc[a] - m);
+          const double LSE = m + log(z);
+          for (int c = 0; c < d; ++c) o[c] = 0.0;
+          for (int64_t a = 0; a < n; ++a) {
+            const double w = exp(sc[a] - LSE);
+            for (int c = 0; c < d; ++c) o[c] += w * ld(v, s->dtype, ((b * N + J[a]) * Hkv + r) * d + c);
+          }
+          for (int c = 0; c < d; ++c) out[(qq * Hq + h) * d + c] = n > 0 ? o[c] : 0.0;
+          if (lse) lse[qq * Hq + h] = n > 0 ? LSE : -INFINITY;
+        }
+      }
+    }
+    free(J);
+    free(sc);
+    free(o);
+  }
+  return err ? REF_ERR_ARG : REF_OK;
+}
+
+/* ------------------------------------------------------------------------ KL alignment */
+
+/*
+ * KL alignment of one (query, group) row on a support of n tokens.
+ *  s_main [G][n]: main-branch logits of the group's G heads on the support.
+ *  s_idx  [n]   : index-branch logits z_j on the support.
+ *  - [KL] §2.1: student P_idx = softmax of the index logits over J.
+ *  - [KL] §2.2: teacher P = (1/G) sum over the group's heads of each head's
+ *    own softmax over J (probabilities are averaged, not logits).
+ *  - [KL] §3: D_KL(P || P_idx) = sum_j P_j log(P_j / P_idx_j); its gradient
+ *    with respect to z_j is P_idx_j - P_j.
+ *  - [Superv] eq. (15): p = exp(s - LSE).
+ * Terms with P_j = 0 contribute 0. Writes *kl and, when dS != NULL,
+ * dS[j] = P_idx_j - P_j. Optional outputs: P[n], P_idx[n], lse_idx.
+ */
+int msa_ref_kl_row(int G, int64_t n, const double* s_main, const double* s_idx, double* kl,
+                   double* dS, double* P_out, double* Pidx_out, double* lse_idx_out) {
+  if (G < 1 || n < 0 || (n > 0 && (!s_main || !s_idx)) || !kl) return REF_ERR_ARG;
+  if (n == 0) {
+    *kl = 0.0;
+    if (lse_idx_out) *lse_idx_out = -INFINITY;
+    return REF_OK;
+  }
+  double* P = (double*)calloc((size_t)n, sizeof(double));
+  if (!P) return REF_ERR_ARG;
+  for (int h = 0; h < G; ++h) {
+    const double* sh = s_main + (int64_t)h * n;
+    double m = -INFINITY;
+    for (int64_t a = 0; a < n; ++a) m = sh[a] > m ? sh[a] : m;
+    double z = 0.0;
+    for (int64_t a = 0; a < n; ++a) z += exp(sh[a] - m);
+    const double lse_h = m + log(z);
+    for (int64_t a = 0; a < n; ++a) P[a] += exp(sh[a] - lse_h) / (double)G;
+  }
+  double m = -INFINITY;
+  for (int64_t a = 0; a < n; ++a) m = s_idx[a] > m ? s_idx[a] : m;
+  double z = 0.0;
+  for (int64_t a = 0; a < n; ++a) z += exp(s_idx[a] - m);
+  const double lse_idx = m + log(z);
+  double acc = 0.0;
+  for (int64_t a = 0; a < n; ++a) {
+    const double pidx = exp(s_idx[a] - lse_idx);
+    if (P[a] > 0.0) acc += P[a] * (log(P[a]) - (s_idx[a] - lse_idx));
+    if (dS) dS[a] = pidx - P[a];
+    if (P_out) P_out[a] = P[a];
+    if (Pidx_out) Pidx_out[a] = pidx;
+  }
+  *kl = acc;
+  if (lse_idx_out) *lse_idx_out = lse_idx;
+  free(P);
+  return REF_OK;
+}
+
+/*
+ * KL alignment for the listed query rows ([KL] §2-§3, §6).
+ * Recomputes the main logits S^(h) = q_h . k_j / sqrt(d) of the group's heads
+ * and the index logits S_idx = q_idx . k_idx_j / sqrt(d_idx) on the support J
+ * given by ids, then applies msa_ref_kl_row.
+ * q, q_idx compact ([nrows, Hq, d], [nrows, Hkv, d_idx]); k [B,N,Hkv,d];
+ * k_idx [B,N,d_idx]; ids [nrows, Hkv, k].
+ * kl_rows [nrows, Hkv]; dlogits (optional) [nrows, Hkv, k, Bk] holds
+ * P_idx - P at (slot, offset in block), 0 at masked or unused positions;
+ * lse_idx (optional) [nrows, Hkv]; kl_mean (optional) = mean of kl_rows over
+ * the listed rows and all groups ([KL] §3 averages over N*Hkv).
+ */
+int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void* q_idx,
+               const void* k_idx, const int32_t* ids, const int64_t* rows, int64_t nrows,
+               double* kl_rows, double* dlogits, double* lse_idx, double* kl_mean,
+               int nthreads) {
+  if (!shape_ok(s) || !q || !kk || !q_idx || !k_idx || !ids || !kl_rows || nrows < 0)
+    return REF_ERR_ARG;
+  const int Hq = s->num_q_heads, Hkv = s->num_kv_heads, G = Hq / Hkv, d = s->head_dim;
+  const int di = s->idx_dim, Bk = s->block_size, k = s->topk;
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d), inv_sqrt_di = 1.0 / sqrt((double)di);
+  if (nthreads < 1) nthreads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    const int64_t cap = (int64_t)k * Bk;
+    int64_t* J = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    int* slot = (int*)malloc(sizeof(int) * (size_t)cap);
+    int* off = (int*)malloc(sizeof(int) * (size_t)cap);
+    double* sm = (double*)malloc(sizeof(double) * (size_t)(cap * G));
+    double* si = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* dS = (double*)malloc(sizeof(double) * (size_t)cap);
+    if (!J || !slot || !off || !sm || !si || !dS) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t qq = 0; qq < nrows; ++qq) {
+      if (err) continue;
+      const int64_t row = rows ? rows[qq] : qq;
+      const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+      const int64_t i = s->q_start + t;
+      for (int r = 0; r < Hkv; ++r) {
+        const int64_t n = support(ids + (qq * Hkv + r) * k, k, Bk, i, N, J, slot, off);
+        for (int h = 0; h < G; ++h) {
+          const int hq = r * G + h;
+          for (int64_t a = 0; a < n; ++a) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+              acc += ld(q, s->dtype, (qq * Hq + hq) * d + c) *
+                     ld(kk, s->dtype, ((b * N + J[a]) * Hkv + r) * d + c);
+            sm[(int64_t)h * n + a] = acc * inv_sqrt_d;
+          }
+        }
+        for (int64_t a = 0; a < n; ++a) {
+          double acc = 0.0;
+          for (int c = 0; c < di; ++c)
+            acc += ld(q_idx, s->dtype, (qq * Hkv + r) * di + c) *
+                   ld(k_idx, s->dtype, (b * N + J[a]) * di + c);
+          si[a] = acc * inv_sqrt_di;
+        }
+        double kl, li;
+        msa_ref_kl_row(G, n, sm, si, &kl, dS, NULL, NULL, &li);
+        kl_rows[qq * Hkv + r] = kl;
+        if (lse_idx) lse_idx[qq * Hkv + r] = li;
+        if (dlogits) {
+          double* drow = dlogits + (qq * Hkv + r) * (int64_t)k * Bk;
+          for (int64_t a = 0; a < (int64_t)k * Bk; ++a) drow[a] = 0.0;
+          for (int64_t a = 0; a < n; ++a) drow[(int64_t)slot[a] * Bk + off[a]] = dS[a];
+        }
+      }
+    }
+    free(J);
+    free(slot);
+    free(off);
+    free(sm);
+    free(si);
+    free(dS);
+  }
+  if (err) return REF_ERR_ARG;
+  if (kl_mean) {
+    double acc = 0.0;
+    for (int64_t a = 0; a < nrows * Hkv; ++a) acc += kl_rows[a];
+    *kl_mean = nrows > 0 ? acc / (double)(nrows * Hkv) : 0.0;
+  }
+  return REF_OK;
+}
