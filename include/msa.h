@@ -1,0 +1,195 @@
+/*
+ * msa.h — C ABI of the MSA (MiniMax Sparse Attention) layer hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path, per query position i and GQA group r:
+ *   index logits  S_idx[i,j] = Q_idx[i,r] . K_idx[j] / sqrt(d_idx), one shared
+ *                 K_idx head ("MSA Indexer 与 DSA Lightning Indexer 的差别"
+ *                 (MSA vs DSA indexer note) §2.1);
+ *   block scores  M[i,b] = max over tokens j of 128-token block b with j <= i
+ *                 (same note, §2.2);
+ *   selection     the query's own (local) block plus the k-1 best earlier
+ *                 blocks by raw score, no softmax (same note §2.2; "MiniMax
+ *                 Sparse Attention：教长上下文模型使用索引" (MSA blog), sections
+ *                 on block selection and on kernel design);
+ *   attention     exact causal softmax attention of the group's G query heads
+ *                 over the selected blocks only ("2.4 · 训练原生稀疏"
+ *                 (training-native sparse attention) eq. 2), also reporting the
+ *                 log-sum-exp per (query, head) ("MSA 中的 KL 对齐与局部知识蒸馏"
+ *                 (MSA KL alignment note) §6);
+ *   KL alignment  teacher = per-head softmax on the selected support averaged
+ *                 over the group, student = index softmax on the same support,
+ *                 KL(teacher || student) and its gradient P_idx - P in the
+ *                 index logits (KL alignment note §2-§3, §6).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensor pointers are DEVICE pointers to dense row-major arrays:
+ *      q      [batch, seqlen_q, num_q_heads, head_dim]
+ *      k, v   [batch, seqlen_kv, num_kv_heads, head_dim]
+ *      q_idx  [batch, seqlen_q, num_kv_heads, idx_dim]
+ *      k_idx  [batch, seqlen_kv, idx_dim]
+ *    element type fp32 (MSA_F32) or bf16 (MSA_BF16), all of the same type.
+ *  - Query row t of a sequence sits at key position i = q_start + t (prefill:
+ *    q_start = 0, seqlen_q = seqlen_kv; one decode step: q_start =
+ *    seqlen_kv - 1, seqlen_q = 1). Keys j <= i are visible to it.
+ *  - GQA: G = num_q_heads / num_kv_heads; query head h belongs to group h / G.
+ *  - Scales: 1/sqrt(idx_dim) for index logits, 1/sqrt(head_dim) for the main
+ *    attention. Logarithms are natural.
+ *  - The caller owns every buffer, including the workspace (size from
+ *    msa_workspace_size). The library allocates no memory, keeps no pointer
+ *    past a call and does not synchronise: all work is enqueued on `stream`,
+ *    and buffers must stay valid until that work has run. Calls on different
+ *    streams with different workspaces may run concurrently.
+ *  - Every argument is validated on the host before anything is launched; a
+ *    call that returns an error has enqueued nothing. Faults inside kernels
+ *    surface asynchronously on the stream.
+ *  - Supported in this version: block_size 128; head_dim 64 or 128; idx_dim
+ *    32 or 64; num_kv_heads 1, 2, 4 or 8; G 1, 2, 4, 8 or 16; 1 <= topk <= 32;
+ *    seqlen_kv <= 262144 (at most 2048 blocks). seqlen_kv need not be a
+ *    multiple of 128 (the last block may be short). Other values return
+ *    MSA_ERR_UNSUPPORTED. The device must be gfx950.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MSA_ERR_SHAPE = 2,       /* inconsistent shape (e.g. Hq % Hkv != 0, q_start+seqlen_q > seqlen_kv) */
+  MSA_ERR_UNSUPPORTED = 3, /* valid but not supported by this build (see list above) */
+  MSA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than msa_workspace_size */
+  MSA_ERR_DEVICE = 5       /* HIP error at launch, or the current device is not gfx950 */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+typedef struct {
+  int32_t batch;        /* sequences; 0 is allowed (nothing to do) */
+  int32_t seqlen_kv;    /* N: keys per sequence */
+  int32_t seqlen_q;     /* query rows per sequence; 0 is allowed */
+  int32_t q_start;      /* key position of query row 0 */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv: GQA groups, index-query heads */
+  int32_t head_dim;     /* d */
+  int32_t idx_dim;      /* d_idx */
+  int32_t block_size;   /* Bk, must be 128 */
+  int32_t topk;         /* k: blocks per (query, group), counting the forced local block */
+  int32_t dtype;        /* msa_dtype of every floating-point input and of `out` */
+} msa_shape;
+
+enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2 };
+
+/*
+ * Bytes of workspace the call `op` (MSA_OP_*) needs for `shape`; 0 for an
+ * invalid shape or op. For MSA_OP_SELECT it assumes block_scores == NULL
+ * (with block_scores given, the call needs no workspace).
+ */
+size_t msa_workspace_size(const msa_shape* shape, int op);
+
+/*
+ * msa_select — index scoring, causal block max and block selection
+ * (MSA vs DSA indexer note §2.1-§2.2; MSA blog, block selection and the
+ * softmax-free Top-k of its kernel section; "4.1.1 · 监督与联合训练"
+ * (selector supervision) §1.2 on a fixed secondary key for ties).
+ *
+ *  in   q_idx, k_idx        device, layouts above
+ *  out  block_ids           device int32 [batch, seqlen_q, num_kv_heads, topk]:
+ *                           the local block floor(i/128) plus the topk-1
+ *                           earlier blocks of largest block score; equal scores
+ *                           rank the lower block index first; ascending order;
+ *                           -1 in unused slots when fewer than topk blocks are
+ *                           visible (all visible blocks are then selected).
+ *  out  block_scores (opt)  device fp32 [batch, seqlen_q, num_kv_heads, nb],
+ *                           nb = ceil(seqlen_kv/128): M[i,b] for b <= i/128;
+ *                           entries past the local block are not written.
+ *                           When NULL, the scores live in the workspace.
+ *  out  cutoff_margin (opt) device fp32 [batch, seqlen_q, num_kv_heads]:
+ *                           score of the worst selected non-local block minus
+ *                           the best unselected one ("4.1.1" eq. 9); +inf when
+ *                           every visible block is selected.
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_SELECT) bytes (may be
+ *       NULL / 0 when block_scores is given).
+ */
+msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                      int32_t* block_ids, float* block_scores, float* cutoff_margin,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_attn_fwd — exact softmax attention over the selected blocks ("2.4"
+ * eq. 2 restricted to the support; MSA vs DSA indexer note §2.3: the group's
+ * heads share the block list and their KV head, each keeps its own query;
+ * MSA blog kernel section: KV-outer execution that loads each selected block
+ * once for every query that chose it).
+ *
+ *  in   q, k, v             device, layouts above
+ *  in   block_ids           device int32 [batch, seqlen_q, num_kv_heads, topk]
+ *                           as written by msa_select (ids >= 0 must be
+ *                           distinct, <= i/128, and include i/128; -1 unused)
+ *  out  out                 device [batch, seqlen_q, num_q_heads, head_dim], dtype
+ *  out  lse                 device fp32 [batch, seqlen_q, num_q_heads]: natural
+ *                           log-sum-exp of the scaled logits over the support
+ *                           (LSE_main of the KL alignment note §6)
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_ATTN) bytes
+ */
+msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* block_ids, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_kl_align — KL alignment of the index branch on the selected support
+ * (KL alignment note §2.1 student, §2.2 teacher as the group mean of the
+ * heads' probabilities, §3 loss 1/(N*Hkv) sum KL(stopgrad(P) || P_idx) and
+ * gradient P_idx - P, §6 probabilities rebuilt from logits and LSEs).
+ *
+ *  in   q, k, q_idx, k_idx  device, layouts above
+ *  in   block_ids           as for msa_attn_fwd
+ *  in   lse_main            device fp32 [batch, seqlen_q, num_q_heads] from
+ *                           msa_attn_fwd on the same ids
+ *  out  kl_rows             device fp32 [batch, seqlen_q, num_kv_heads]:
+ *                           KL(P || P_idx) of each (query, group)
+ *  out  kl_mean             device fp32 [1]: mean of kl_rows over every row
+ *  out  dlogits_idx (opt)   device fp32 [batch, seqlen_q, num_kv_heads, topk, 128]:
+ *                           P_idx - P at (slot, offset in the slot's block); 0 at
+ *                           positions j > i and in unused slots. Unscaled: the
+ *                           caller applies lambda, 1/(N*Hkv) and the
+ *                           1/sqrt(idx_dim) of the index logits when chaining.
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_KL) bytes
+ */
+msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, const void* q_idx,
+                        const void* k_idx, const int32_t* block_ids, const float* lse_main,
+                        float* kl_rows, float* kl_mean, float* dlogits_idx, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* msa_status_string(msa_status status);
+
+/*
+ * Kernel timing for measurement tools. msa_prof_begin(kernel, n) makes the
+ * library record a HIP event pair on the launch stream around each of the
+ * next n launches of kernel `kernel` (MSA_K_*); msa_prof_end waits for them
+ * and returns the summed duration in milliseconds and the number of launches
+ * timed. The hook is process-wide and not meant for concurrent callers.
+ */
+enum {
+  MSA_K_INDEX_BLOCKMAX = 0, MSA_K_TOPK = 1, MSA_K_BUCKET_HIST = 2, MSA_K_BUCKET_SCAN = 3,
+  MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
+  MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
+  MSA_K_COUNT = 12
+};
+msa_status msa_prof_begin(int kernel, int max_launches);
+msa_status msa_prof_end(float* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

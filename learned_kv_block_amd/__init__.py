@@ -1,0 +1,239 @@
+"""MSA (MiniMax Sparse Attention) layer hot path on MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/msa.h (libmsa.so, hand-written HIP
+kernels). This module only marshals arguments: it checks tensor shapes, sizes
+the workspace, allocates outputs with torch and passes raw device pointers and
+the current HIP stream. Every step of the path runs in the library's kernels;
+there is no fallback. If libmsa.so is missing the calls raise.
+
+Functions (same names as the C entry points):
+  msa_select(q_idx, k_idx, topk, q_start=0, ...)     -> block ids (+ scores, margin)
+  msa_attn_fwd(q, k, v, block_ids, q_start=0, ...)   -> (out, lse)
+  msa_kl_align(q, k, q_idx, k_idx, block_ids, lse_main, q_start=0, ...)
+                                                     -> kl_rows, kl_mean, dlogits
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # noqa: F401  (loads the HIP runtime that libmsa.so binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmsa.so")
+
+MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
+MSA_F32, MSA_BF16 = 0, 1
+MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL = 0, 1, 2
+KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
+           "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
+           "kl_reduce"]
+EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align",
+           "msa_status_string", "msa_prof_begin", "msa_prof_end"]
+
+
+class MsaShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seqlen_kv", "seqlen_q", "q_start", "num_q_heads", "num_kv_heads", "head_dim",
+        "idx_dim", "block_size", "topk", "dtype")]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python learned_kv_block_amd/build.py` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.POINTER(MsaShape)
+        L.msa_workspace_size.argtypes = [S, ctypes.c_int]
+        L.msa_workspace_size.restype = ctypes.c_size_t
+        L.msa_select.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_attn_fwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_kl_align.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_prof_begin", "msa_prof_end"):
+            getattr(L, f).restype = ctypes.c_int
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_prof_begin.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.msa_prof_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().msa_status_string(int(status)).decode()
+
+
+def make_shape(batch, seqlen_kv, seqlen_q, q_start, num_q_heads, num_kv_heads, head_dim,
+               idx_dim, topk, dtype, block_size=128) -> MsaShape:
+    return MsaShape(batch, seqlen_kv, seqlen_q, q_start, num_q_heads, num_kv_heads, head_dim,
+                    idx_dim, block_size, topk, dtype)
+
+
+def workspace_size(shape: MsaShape, op: int) -> int:
+    return int(lib().msa_workspace_size(ctypes.byref(shape), op))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    if t.dtype == torch.float32:
+        return MSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: torch.Tensor, name: str, ndim: int):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _workspace(shape: MsaShape, op: int, device, workspace: Optional[torch.Tensor]):
+    n = workspace_size(shape, op)
+    if n == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < n:
+            raise ValueError(f"workspace of {workspace.numel()} bytes < {n} required")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(n, dtype=torch.uint8, device=device), n
+
+
+def shape_for(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_start: int = 0,
+              num_q_heads: Optional[int] = None, head_dim: int = 128) -> MsaShape:
+    B, Nq, Hkv, DI = q_idx.shape
+    N = k_idx.shape[1]
+    Hq = num_q_heads if num_q_heads is not None else Hkv
+    return make_shape(B, N, Nq, q_start, Hq, Hkv, head_dim, DI, topk, _dtype_code(q_idx))
+
+
+def msa_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_start: int = 0,
+               want_scores: bool = False, want_margin: bool = False,
+               num_q_heads: Optional[int] = None, head_dim: int = 128,
+               workspace: Optional[torch.Tensor] = None):
+    """Block selection. q_idx [B, Nq, Hkv, d_idx], k_idx [B, N, d_idx] (bf16/fp32, device).
+
+    Returns dict(ids [B, Nq, Hkv, topk] int32, block_scores [B, Nq, Hkv, nb] fp32 (opt),
+    margin [B, Nq, Hkv] fp32 (opt)). num_q_heads / head_dim only enter the shape check."""
+    _check(q_idx, "q_idx", 4)
+    _check(k_idx, "k_idx", 3)
+    sh = shape_for(q_idx, k_idx, topk, q_start, num_q_heads, head_dim)
+    B, Nq, Hkv, _ = q_idx.shape
+    nb = (k_idx.shape[1] + 127) // 128
+    dev = q_idx.device
+    ids = torch.empty((B, Nq, Hkv, topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev) if want_scores else None
+    margin = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev) if want_margin else None
+    ws, nws = (None, 0) if want_scores else _workspace(sh, MSA_OP_SELECT, dev, workspace)
+    st = lib().msa_select(ctypes.byref(sh), _ptr(q_idx), _ptr(k_idx), _ptr(ids), _ptr(scores),
+                          _ptr(margin), _ptr(ws), nws, _stream(q_idx))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_select")
+    out = {"ids": ids}
+    if want_scores:
+        out["block_scores"] = scores
+    if want_margin:
+        out["margin"] = margin
+    return out
+
+
+def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: torch.Tensor,
+                 q_start: int = 0, idx_dim: int = 64, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Sparse attention over the selected blocks. q [B, Nq, Hq, d], k/v [B, N, Hkv, d],
+    block_ids [B, Nq, Hkv, topk]. Returns (out [B, Nq, Hq, d], lse [B, Nq, Hq] fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (block_ids, "block_ids")):
+        _check(t, n, 4)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, block_ids.shape[3], _dtype_code(q))
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    ws, nws = _workspace(sh, MSA_OP_ATTN, q.device, workspace)
+    st = lib().msa_attn_fwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(block_ids),
+                            _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_attn_fwd")
+    return out, lse
+
+
+def msa_kl_align(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                 block_ids: torch.Tensor, lse_main: torch.Tensor, q_start: int = 0,
+                 want_dlogits: bool = True, workspace: Optional[torch.Tensor] = None):
+    """KL alignment on the selected support. Returns dict(kl_rows [B, Nq, Hkv],
+    kl_mean [1], dlogits [B, Nq, Hkv, topk, 128] (opt)), all fp32."""
+    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx"), (block_ids, "block_ids")):
+        _check(t, n, 4)
+    _check(k_idx, "k_idx", 3)
+    _check(lse_main, "lse_main", 3)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    K = block_ids.shape[3]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], K, _dtype_code(q))
+    dev = q.device
+    kl_rows = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+    kl_mean = torch.empty((1,), dtype=torch.float32, device=dev)
+    dl = torch.empty((B, Nq, Hkv, K, 128), dtype=torch.float32, device=dev) if want_dlogits else None
+    ws, nws = _workspace(sh, MSA_OP_KL, dev, workspace)
+    st = lib().msa_kl_align(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
+                            _ptr(block_ids), _ptr(lse_main), _ptr(kl_rows), _ptr(kl_mean),
+                            _ptr(dl), _ptr(ws), nws, _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_kl_align")
+    out = {"kl_rows": kl_rows, "kl_mean": kl_mean}
+    if want_dlogits:
+        out["dlogits"] = dl
+    return out
+
+
+class KernelTimer:
+    """Sum of the durations of one kernel's launches (HIP events recorded by the library)."""
+
+    def __init__(self, kernel: str, max_launches: int = 1000):
+        self.kid = KERNELS.index(kernel)
+        self.max = max_launches
+        self.total_ms = 0.0
+        self.launches = 0
+
+    def __enter__(self):
+        st = lib().msa_prof_begin(self.kid, self.max)
+        if st != MSA_OK:
+            raise MsaError(st, "msa_prof_begin")
+        return self
+
+    def __exit__(self, *exc):
+        ms = ctypes.c_float(0.0)
+        n = ctypes.c_int(0)
+        st = lib().msa_prof_end(ctypes.byref(ms), ctypes.byref(n))
+        if st != MSA_OK:
+            raise MsaError(st, "msa_prof_end")
+        self.total_ms = ms.value
+        self.launches = n.value
+        return False
+
+    @property
+    def avg_ms(self) -> float:
+        return self.total_ms / max(1, self.launches)

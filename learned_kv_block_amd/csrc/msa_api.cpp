@@ -1,0 +1,321 @@
+// msa_api.cpp — the C ABI of include/msa.h: host-side validation, workspace
+// layout and the launch sequence of each call. Every check runs before the
+// first launch, so an error return leaves the stream untouched.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "msa_internal.hpp"
+
+using namespace msa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape validation shared by all calls. Fills d on success.
+msa_status make_dims(const msa_shape* s, Dims* d) {
+  if (!s) return MSA_ERR_NULL;
+  if (s->batch < 0 || s->seqlen_kv < 0 || s->seqlen_q < 0 || s->q_start < 0) return MSA_ERR_SHAPE;
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1 || s->num_q_heads % s->num_kv_heads != 0)
+    return MSA_ERR_SHAPE;
+  if (s->head_dim < 1 || s->idx_dim < 1 || s->block_size < 1 || s->topk < 1) return MSA_ERR_SHAPE;
+  if ((int64_t)s->q_start + s->seqlen_q > s->seqlen_kv) return MSA_ERR_SHAPE;
+  if (s->dtype != MSA_F32 && s->dtype != MSA_BF16) return MSA_ERR_SHAPE;
+  const int G = s->num_q_heads / s->num_kv_heads;
+  if (s->block_size != 128) return MSA_ERR_UNSUPPORTED;
+  if (s->head_dim != 64 && s->head_dim != 128) return MSA_ERR_UNSUPPORTED;
+  if (s->idx_dim != 32 && s->idx_dim != 64) return MSA_ERR_UNSUPPORTED;
+  if (s->num_kv_heads != 1 && s->num_kv_heads != 2 && s->num_kv_heads != 4 && s->num_kv_heads != 8)
+    return MSA_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return MSA_ERR_UNSUPPORTED;
+  if (s->topk > 32) return MSA_ERR_UNSUPPORTED;
+  const int nb = (s->seqlen_kv + 127) / 128;
+  if (nb > 2048) return MSA_ERR_UNSUPPORTED;
+  d->B = s->batch;
+  d->N = s->seqlen_kv;
+  d->Nq = s->seqlen_q;
+  d->q_start = s->q_start;
+  d->Hq = s->num_q_heads;
+  d->Hkv = s->num_kv_heads;
+  d->G = G;
+  d->D = s->head_dim;
+  d->DI = s->idx_dim;
+  d->Bk = s->block_size;
+  d->K = s->topk;
+  d->nb = nb;
+  d->dtype = s->dtype;
+  d->rows = (int64_t)s->batch * s->seqlen_q;
+  d->slots = d->rows * d->Hkv * d->K;
+  d->buckets = (int64_t)s->batch * d->Hkv * nb;
+  d->entries_max = d->rows * d->Hkv * (int64_t)(d->K < nb ? d->K : nb);
+  d->qt = 128 / G;
+  const int64_t per_item = d->entries_max / d->qt + (d->buckets < d->entries_max ? d->buckets
+                                                                                 : d->entries_max);
+  d->items_max = per_item < d->entries_max ? per_item : d->entries_max;
+  // index ranges the kernels keep in 32-bit integers
+  if (d->entries_max >= (int64_t)1 << 31 || d->buckets >= (int64_t)1 << 30 ||
+      d->items_max >= (int64_t)1 << 30 || s->seqlen_q >= (1 << 25) ||
+      (int64_t)s->batch * s->seqlen_q >= (int64_t)1 << 31)
+    return MSA_ERR_UNSUPPORTED;
+  if (((d->Nq + 127) / 128 > 65535) || s->batch > 65535) return MSA_ERR_UNSUPPORTED;
+  return MSA_OK;
+}
+
+size_t elem_size(const Dims& d) { return d.dtype == MSA_BF16 ? 2 : 4; }
+
+struct Layout {
+  size_t counts, offsets, cursor, item_off, totals, items, entries;  // bucketing
+  size_t opart, lpart;                                               // attention
+  size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
+  size_t total;
+};
+
+Layout layout(const Dims& d, int op) {
+  Layout L;
+  std::memset(&L, 0, sizeof(L));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  if (op == MSA_OP_SELECT) {
+    L.total = (size_t)d.rows * d.Hkv * d.nb * sizeof(float);
+    return L;
+  }
+  L.counts = take(d.buckets * 4);
+  L.offsets = take((d.buckets + 1) * 4);
+  L.cursor = take(d.buckets * 4);
+  L.item_off = take((d.buckets + 1) * 4);
+  L.totals = take(16);
+  L.items = take(d.items_max * 16);
+  L.entries = take(d.entries_max * 4);
+  if (op == MSA_OP_ATTN) {
+    L.opart = take((size_t)d.slots * d.G * d.D * elem_size(d));
+    L.lpart = take((size_t)d.slots * d.G * 4);
+  } else {
+    L.slot_lse = take((size_t)d.slots * 4);
+    L.lse_idx = take((size_t)d.rows * d.Hkv * 4);
+    L.kl_part = take((size_t)d.slots * 4);
+    L.block_sums = take((size_t)((d.rows * d.Hkv + 255) / 256 + 1) * 4);
+  }
+  L.total = o;
+  return L;
+}
+
+AttnWs carve(const Layout& L, void* ws) {
+  char* p = static_cast<char*>(ws);
+  AttnWs w;
+  w.counts = reinterpret_cast<int32_t*>(p + L.counts);
+  w.offsets = reinterpret_cast<int32_t*>(p + L.offsets);
+  w.cursor = reinterpret_cast<int32_t*>(p + L.cursor);
+  w.item_off = reinterpret_cast<int32_t*>(p + L.item_off);
+  w.totals = reinterpret_cast<int32_t*>(p + L.totals);
+  w.items = reinterpret_cast<int4*>(p + L.items);
+  w.entries = reinterpret_cast<int32_t*>(p + L.entries);
+  return w;
+}
+
+msa_status check_ws(const Layout& L, void* ws, size_t bytes) {
+  if (L.total == 0) return MSA_OK;
+  if (!ws || bytes < L.total) return MSA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return MSA_ERR_WORKSPACE;
+  return MSA_OK;
+}
+
+// The current device must be gfx950 (checked once per device).
+msa_status check_device() {
+  static std::atomic<int> cache[64];  // 0 unknown, 1 ok, 2 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return MSA_ERR_DEVICE;
+  int c = cache[dev].load();
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MSA_ERR_DEVICE;
+    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(c);
+  }
+  return c == 1 ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+inline bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// ------------------------------------------------------------------ timing hook
+struct Prof {
+  std::mutex mu;
+  std::atomic<int> kernel{-1};
+  int max = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 2 per launch
+} g_prof;
+
+}  // namespace
+
+namespace msa {
+void prof_before(int kernel, hipStream_t s) {
+  if (g_prof.kernel != kernel) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
+  hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+}
+void prof_after(int kernel, hipStream_t s) {
+  if (g_prof.kernel != kernel) return;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
+  hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+  ++g_prof.used;
+}
+}  // namespace msa
+
+extern "C" {
+
+const char* msa_status_string(msa_status st) {
+  switch (st) {
+    case MSA_OK: return "ok";
+    case MSA_ERR_NULL: return "a required pointer is NULL";
+    case MSA_ERR_SHAPE: return "inconsistent shape";
+    case MSA_ERR_UNSUPPORTED: return "shape or type not supported by this build";
+    case MSA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MSA_ERR_DEVICE: return "HIP launch error or device is not gfx950";
+  }
+  return "unknown status";
+}
+
+size_t msa_workspace_size(const msa_shape* shape, int op) {
+  Dims d;
+  if (make_dims(shape, &d) != MSA_OK) return 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL) return 0;
+  return layout(d, op).total;
+}
+
+msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                      int32_t* block_ids, float* block_scores, float* cutoff_margin,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.rows == 0) return MSA_OK;
+  if (!q_idx || !k_idx || !block_ids) return MSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return MSA_ERR_SHAPE;
+  float* M = block_scores;
+  if (!M) {
+    const Layout L = layout(d, MSA_OP_SELECT);
+    if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+    M = static_cast<float*>(workspace);
+  }
+  if ((st = check_device()) != MSA_OK) return st;
+  prof_before(MSA_K_INDEX_BLOCKMAX, stream);
+  hipError_t e = launch_index_blockmax(d, q_idx, k_idx, M, nullptr, stream);
+  prof_after(MSA_K_INDEX_BLOCKMAX, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  prof_before(MSA_K_TOPK, stream);
+  e = launch_topk(d, M, block_ids, cutoff_margin, stream);
+  prof_after(MSA_K_TOPK, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* block_ids, void* out, float* lse, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.rows == 0) return MSA_OK;
+  if (!q || !k || !v || !block_ids || !out || !lse) return MSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MSA_ERR_SHAPE;
+  const Layout L = layout(d, MSA_OP_ATTN);
+  if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+  if ((st = check_device()) != MSA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const AttnWs w = carve(L, workspace);
+  if (launch_bucketing(d, block_ids, w, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  prof_before(MSA_K_SPARSE_ATTN, stream);
+  hipError_t e = launch_sparse_attn(d, q, k, v, w, ws + L.opart,
+                                    reinterpret_cast<float*>(ws + L.lpart), stream);
+  prof_after(MSA_K_SPARSE_ATTN, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  prof_before(MSA_K_COMBINE, stream);
+  e = launch_combine(d, ws + L.opart, reinterpret_cast<const float*>(ws + L.lpart), block_ids,
+                     out, lse, stream);
+  prof_after(MSA_K_COMBINE, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, const void* q_idx,
+                        const void* k_idx, const int32_t* block_ids, const float* lse_main,
+                        float* kl_rows, float* kl_mean, float* dlogits_idx, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (!kl_mean) return MSA_ERR_NULL;
+  if (d.rows > 0) {
+    if (!q || !k || !q_idx || !k_idx || !block_ids || !lse_main || !kl_rows) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx) ||
+        (dlogits_idx && !aligned16(dlogits_idx)))
+      return MSA_ERR_SHAPE;
+  }
+  const Layout L = layout(d, MSA_OP_KL);
+  if (d.rows > 0 && (st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+  if ((st = check_device()) != MSA_OK) return st;
+  if (d.rows == 0)
+    return launch_fill_f32(kl_mean, 1, 0.0f, stream) == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+  char* ws = static_cast<char*>(workspace);
+  const AttnWs w = carve(L, workspace);
+  if (launch_bucketing(d, block_ids, w, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  hipError_t e = launch_kl(d, q, k, q_idx, k_idx, block_ids, lse_main, w,
+                           reinterpret_cast<float*>(ws + L.slot_lse),
+                           reinterpret_cast<float*>(ws + L.lse_idx),
+                           reinterpret_cast<float*>(ws + L.kl_part), kl_rows,
+                           reinterpret_cast<float*>(ws + L.block_sums), kl_mean, dlogits_idx,
+                           stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_prof_begin(int kernel, int max_launches) {
+  if (kernel < 0 || kernel >= MSA_K_COUNT || max_launches < 1 || max_launches > 100000)
+    return MSA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      g_prof.kernel = -1;
+      return MSA_ERR_DEVICE;
+    }
+  g_prof.max = max_launches;
+  g_prof.used = 0;
+  g_prof.kernel = kernel;
+  return MSA_OK;
+}
+
+msa_status msa_prof_end(float* total_ms, int* launches) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  float sum = 0.0f;
+  msa_status st = MSA_OK;
+  for (int x = 0; x < g_prof.used; ++x) {
+    if (hipEventSynchronize(g_prof.ev[2 * x + 1]) != hipSuccess) { st = MSA_ERR_DEVICE; break; }
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, g_prof.ev[2 * x], g_prof.ev[2 * x + 1]) != hipSuccess) {
+      st = MSA_ERR_DEVICE;
+      break;
+    }
+    sum += ms;
+  }
+  if (total_ms) *total_ms = sum;
+  if (launches) *launches = g_prof.used;
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kernel = -1;
+  g_prof.max = g_prof.used = 0;
+  return st;
+}
+
+}  // extern "C"

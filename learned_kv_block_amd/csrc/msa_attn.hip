@@ -1,0 +1,491 @@
+// msa_attn.hip — KV-outer sparse attention over the selected blocks.
+//
+// Exact softmax attention restricted to the selected support ("2.4 · 训练原生
+// 稀疏" (training-native sparse attention) eq. 2), per GQA group: the group's G
+// query heads share the block list and KV head r, each keeps its own query
+// ("MSA Indexer 与 DSA Lightning Indexer 的差别" §2.3). Execution is KV-outer
+// ("MiniMax Sparse Attention：教长上下文模型使用索引", kernel section): the
+// selections are inverted into per-(batch, group, block) buckets of the query
+// rows that chose the block, each block is loaded once into LDS for a chunk of
+// those rows, and buckets that many rows chose (block 0, local blocks, hot
+// blocks) are cut into fixed-size work items so no block becomes a straggler.
+// Each (query, head, slot) gets a normalised partial output and its
+// log-sum-exp; the combine merges the <= k partials of a (query, head) with
+// the partition rule of "2.4" eq. (18) / "4.1.1 · 监督与联合训练" eq. (16):
+// LSE = logsumexp_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s.
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// ============================================================== bucketing (counting sort)
+//
+// bucket(b, r, blk) = (b*Hkv + r)*nb + blk; entry = (t << 6) | slot.
+
+constexpr int kBucketRows = 256;  // query rows per histogram workgroup
+
+template <bool LDSH>
+__global__ void __launch_bounds__(256)
+bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb,
+                   int32_t* __restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  const int HB = Hkv * nb;
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kBucketRows;
+  const int t1 = min(Nq, t0 + kBucketRows);
+  if (LDSH) {
+    for (int x = threadIdx.x; x < HB; x += 256) hist[x] = 0;
+    __syncthreads();
+  }
+  const int n = (t1 - t0) * Hkv * K;
+  const int32_t* base = ids + ((size_t)(b * (size_t)Nq + t0) * Hkv) * K;
+  int32_t* cb = counts + (size_t)b * HB;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int id = base[e];
+    if (id >= 0 && id < nb) {
+      const int r = (e / K) % Hkv;
+      if (LDSH) atomicAdd(&hist[r * nb + id], 1);
+      else atomicAdd(&cb[r * nb + id], 1);
+    }
+  }
+  if (LDSH) {
+    __syncthreads();
+    for (int x = threadIdx.x; x < HB; x += 256)
+      if (hist[x]) atomicAdd(&cb[x], hist[x]);
+  }
+}
+
+// Single workgroup: exclusive scans of entry counts and of item counts
+// (ceil(count / qt)) over all buckets.
+__global__ void __launch_bounds__(1024)
+bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
+                   int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
+                   int32_t* __restrict__ item_off, int32_t* __restrict__ totals,
+                   int entries_max, int items_max) {
+  __shared__ int32_t se[1024], si[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = (nbk + 1023) / 1024;
+  const int64_t lo = min(nbk, (int64_t)tid * per), hi = min(nbk, lo + per);
+  int32_t ce = 0, ci = 0;
+  for (int64_t x = lo; x < hi; ++x) {
+    const int32_t c = counts[x];
+    ce += c;
+    ci += (c + qt - 1) / qt;
+  }
+  se[tid] = ce;
+  si[tid] = ci;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t ae = tid >= off ? se[tid - off] : 0;
+    const int32_t ai = tid >= off ? si[tid - off] : 0;
+    __syncthreads();
+    se[tid] += ae;
+    si[tid] += ai;
+    __syncthreads();
+  }
+  int32_t re = se[tid] - ce, ri = si[tid] - ci;  // exclusive
+  for (int64_t x = lo; x < hi; ++x) {
+    const int32_t c = counts[x];
+    offsets[x] = re;
+    cursor[x] = re;
+    item_off[x] = ri;
+    re += c;
+    ri += (c + qt - 1) / qt;
+  }
+  if (tid == 1023) {
+    offsets[nbk] = se[1023];
+    item_off[nbk] = si[1023];
+    // both bounds hold for valid ids; clamping keeps malformed ids from
+    // indexing past the work arrays
+    totals[0] = min(se[1023], entries_max);
+    totals[1] = min(si[1023], items_max);
+  }
+}
+
+template <bool LDSH>
+__global__ void __launch_bounds__(256)
+bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb,
+                      int32_t* __restrict__ cursor, int32_t* __restrict__ entries,
+                      int entries_max) {
+  extern __shared__ int32_t sh[];
+  const int HB = Hkv * nb;
+  int32_t* hist = sh;
+  int32_t* base = sh + (LDSH ? HB : 0);
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kBucketRows;
+  const int t1 = min(Nq, t0 + kBucketRows);
+  const int n = (t1 - t0) * Hkv * K;
+  const int32_t* idp = ids + ((size_t)(b * (size_t)Nq + t0) * Hkv) * K;
+  int32_t* cb = cursor + (size_t)b * HB;
+  if (LDSH) {
+    for (int x = threadIdx.x; x < HB; x += 256) hist[x] = 0;
+    __syncthreads();
+    for (int e = threadIdx.x; e < n; e += 256) {
+      const int id = idp[e];
+      if (id >= 0 && id < nb) atomicAdd(&hist[((e / K) % Hkv) * nb + id], 1);
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < HB; x += 256) {
+      const int c = hist[x];
+      base[x] = c ? atomicAdd(&cb[x], c) : 0;
+      hist[x] = 0;
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int id = idp[e];
+    if (id >= 0 && id < nb) {
+      const int bin = ((e / K) % Hkv) * nb + id;
+      const int p = LDSH ? base[bin] + atomicAdd(&hist[bin], 1) : atomicAdd(&cb[bin], 1);
+      const int t = t0 + e / (Hkv * K);
+      if (p < entries_max) entries[p] = (t << 6) | (e % K);  // bound holds for valid ids
+    }
+  }
+}
+
+// One thread per work item: item = (bucket, first entry, count <= qt).
+__global__ void __launch_bounds__(256)
+work_items_kernel(const int32_t* __restrict__ item_off, const int32_t* __restrict__ offsets,
+                  const int32_t* __restrict__ totals, int64_t nbk, int qt,
+                  int4* __restrict__ items) {
+  const int it = blockIdx.x * 256 + threadIdx.x;
+  if (it >= totals[1]) return;
+  int64_t lo = 0, hi = nbk - 1;  // largest bkt with item_off[bkt] <= it
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (item_off[mid] <= it) lo = mid;
+    else hi = mid - 1;
+  }
+  const int64_t bkt = lo;
+  const int local = it - item_off[bkt];
+  const int start = offsets[bkt] + local * qt;
+  const int cnt = max(0, min(min(qt, offsets[bkt + 1] - start), totals[0] - start));
+  items[it] = make_int4((int)bkt, start, cnt, 0);
+}
+
+static size_t bucket_lds_bytes(const Dims& d, int arrays) {
+  return (size_t)arrays * d.Hkv * d.nb * sizeof(int32_t);
+}
+static bool bucket_use_lds(const Dims& d) { return bucket_lds_bytes(d, 2) <= 64 * 1024; }
+
+hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, hipStream_t s) {
+  hipError_t e;
+  if ((e = launch_fill_i32(w.counts, d.buckets, 0, s)) != hipSuccess) return e;
+  if (d.rows == 0) {
+    bucket_scan_kernel<<<1, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.offsets, w.cursor,
+                                          w.item_off, w.totals, 0, 0);
+    return hipGetLastError();
+  }
+  const dim3 grid((d.Nq + kBucketRows - 1) / kBucketRows, d.B);
+  const bool lds = bucket_use_lds(d);
+  prof_before(MSA_K_BUCKET_HIST, s);
+  if (lds)
+    bucket_hist_kernel<true><<<grid, 256, bucket_lds_bytes(d, 1), s>>>(ids, d.Nq, d.Hkv, d.K,
+                                                                      d.nb, w.counts);
+  else
+    bucket_hist_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, w.counts);
+  prof_after(MSA_K_BUCKET_HIST, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_before(MSA_K_BUCKET_SCAN, s);
+  bucket_scan_kernel<<<1, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.offsets, w.cursor,
+                                        w.item_off, w.totals, (int)d.entries_max,
+                                        (int)d.items_max);
+  prof_after(MSA_K_BUCKET_SCAN, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prof_before(MSA_K_BUCKET_SCATTER, s);
+  if (lds)
+    bucket_scatter_kernel<true><<<grid, 256, bucket_lds_bytes(d, 2), s>>>(
+        ids, d.Nq, d.Hkv, d.K, d.nb, w.cursor, w.entries, (int)d.entries_max);
+  else
+    bucket_scatter_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, w.cursor,
+                                                     w.entries, (int)d.entries_max);
+  prof_after(MSA_K_BUCKET_SCATTER, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (d.items_max > 0) {
+    prof_before(MSA_K_WORK_ITEMS, s);
+    work_items_kernel<<<(unsigned)((d.items_max + 255) / 256), 256, 0, s>>>(
+        w.item_off, w.offsets, w.totals, d.buckets, d.qt, w.items);
+    prof_after(MSA_K_WORK_ITEMS, s);
+  }
+  return hipGetLastError();
+}
+
+// ============================================================== sparse attention (KV-outer)
+//
+// One workgroup (4 waves) per work item: a 128-token K/V block of group r and
+// up to QT = 128/G query rows that selected it, i.e. 128 (query, head) rows,
+// 32 per wave. K is staged in LDS row-major and V transposed (V^T[d][key]).
+//   S^T = K Q^T   A = K rows from LDS, B = the wave's Q rows (registers);
+//                 each lane then holds 64 keys of one (query, head) row, so
+//                 the row max / sum are in-lane plus one exchange.
+//   O^T = V^T P^T B = P^T straight from the S^T accumulator (the key set a
+//                 lane holds is the k-set it supplies), A = V^T from LDS.
+// Blocks past a query's position are masked (j > i) only where needed.
+// The item -> workgroup mapping keeps consecutive items (same K/V block) on
+// the same XCD: workgroup id g runs on XCD g % 8.
+
+template <typename T> struct AttnPad;
+template <> struct AttnPad<bf16> { static constexpr int K = 8, V = 4; };
+template <> struct AttnPad<float> { static constexpr int K = 4, V = 2; };
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256, 2)
+sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                   const int4* __restrict__ items, const int32_t* __restrict__ entries,
+                   const int32_t* __restrict__ totals, T* __restrict__ opart,
+                   float* __restrict__ lpart, int N, int Nq, int q_start, int Hkv, int nb,
+                   int topk, float scale_log2) {
+  constexpr int QT = 128 / G;
+  constexpr int KSD = D / 16;  // k-steps over the head dim
+  constexpr int DT = D / 32;   // 32-wide output d tiles
+  constexpr int PK = AttnPad<T>::K, PV = AttnPad<T>::V;
+  __shared__ T Ks[128][D + PK];
+  __shared__ T Vt[D][128 + PV];
+  __shared__ int s_t[QT], s_s[QT];
+
+  // XCD-aware item order: XCD x = g % 8 takes a contiguous range of items.
+  const int total = totals[1];
+  const int per = (total + 7) / 8;
+  const int g = blockIdx.x;
+  const int it = (g & 7) * per + (g >> 3);
+  if ((g >> 3) >= per || it >= total) return;
+
+  const int4 item = items[it];
+  const int bkt = item.x, start = item.y, cnt = item.z;
+  const int blk = bkt % nb;
+  const int br = bkt / nb;
+  const int r = br % Hkv;
+  const int b = br / Hkv;
+  const int tid = threadIdx.x;
+  if (tid < QT) {
+    const int e = tid < cnt ? entries[start + tid] : 0;
+    s_t[tid] = e >> 6;
+    s_s[tid] = e & 63;
+  }
+  // stage K (row-major) and V (transposed)
+  const size_t kvrow = (size_t)Hkv * D;
+  const T* kb = k + ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
+  const T* vb = v + ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
+  const int nvalid = min(128, N - blk * 128);
+  constexpr int CH = D / 8;  // 8-element chunks per row
+  for (int c = tid; c < 128 * CH; c += 256) {
+    const int kr = c / CH, dc = c % CH;
+    st8<T>(&Ks[kr][dc * 8], kr < nvalid ? ld8<T>(kb + kr * kvrow + dc * 8) : zero8<T>());
+  }
+  for (int c = tid; c < 128 * CH; c += 256) {
+    const int kr = c % 128, dc = c / 128;
+    const vec8<T> x = kr < nvalid ? ld8<T>(vb + kr * kvrow + dc * 8) : zero8<T>();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Vt[dc * 8 + e][kr] = x[e];
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int row = 32 * wave + l32;  // (query, head) row of the item
+  const int qi = row / G;
+  const int hg = row % G;
+  const bool rv = qi < cnt;
+  const int t = rv ? s_t[qi] : 0;
+  const int i_row = q_start + t;
+  const int Hq = Hkv * G;
+  vec8<T> qf[KSD];
+  {
+    const T* qp = q + ((size_t)(b * (size_t)Nq + t) * Hq + r * G + hg) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = rv ? ld8<T>(qp + 16 * ks) : zero8<T>();
+  }
+  f32x16 sacc[4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+      mma(sacc[kt], ld8<T>(&Ks[kt * 32 + l32][16 * ks + 8 * h]), qf[ks]);
+  }
+  // softmax over the 128 keys of this block, in the log2 domain
+  const bool need_mask = blk * 128 + 127 > i_row;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = sacc[kt][e] * scale_log2;
+      if (need_mask && blk * 128 + kt * 32 + drow(e, h) > i_row) x = -INFINITY;
+      sacc[kt][e] = x;
+      mx = fmaxf(mx, x);
+    }
+  }
+  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  float ls = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2f(sacc[kt][e] - mx);
+      sacc[kt][e] = p;
+      ls += p;
+    }
+  }
+  ls += shfl_xor_f(ls, 32);
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {  // 16 keys per step: elements 8*(st%2).. of tile st/2
+    vec8<T> pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(sacc[st >> 1][8 * (st & 1) + e]);
+    const int key0 = 16 * st + 4 * h;  // keys key0..key0+3 and key0+8..key0+11
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const T* vp = &Vt[dt * 32 + l32][key0];
+      const vec4<T> lo = ld4<T>(vp), hi = ld4<T>(vp + 8);
+      vec8<T> vf;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[e] = lo[e];
+        vf[4 + e] = hi[e];
+      }
+      mma(oacc[dt], vf, pf);
+    }
+  }
+  if (rv) {
+    const float inv = 1.0f / ls;
+    const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + s_s[qi];
+    T* op = opart + (entry * G + hg) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        vec4<T> o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = cvt<T>(oacc[dt][4 * jg + e] * inv);
+        st4<T>(op + dt * 32 + 8 * jg + 4 * h, o);
+      }
+    }
+    if (h == 0) lpart[entry * G + hg] = (mx + __log2f(ls)) * kLn2;
+  }
+}
+
+template <typename T, int D>
+static hipError_t attn_dispatch_g(const Dims& d, const void* q, const void* k, const void* v,
+                                  const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
+  const unsigned grid = (unsigned)(d.items_max + 8);
+  const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+#define MSA_ATTN_CASE(GG)                                                                     \
+  case GG:                                                                                    \
+    sparse_attn_kernel<T, D, GG><<<grid, 256, 0, s>>>(                                        \
+        (const T*)q, (const T*)k, (const T*)v, w.items, w.entries, w.totals, (T*)opart, lpart, \
+        d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K, scale_log2);                                  \
+    break;
+  switch (d.G) {
+    MSA_ATTN_CASE(1)
+    MSA_ATTN_CASE(2)
+    MSA_ATTN_CASE(4)
+    MSA_ATTN_CASE(8)
+    MSA_ATTN_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MSA_ATTN_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const void* v,
+                              const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
+  if (d.items_max == 0) return hipSuccess;
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128) return attn_dispatch_g<bf16, 128>(d, q, k, v, w, opart, lpart, s);
+    if (d.D == 64) return attn_dispatch_g<bf16, 64>(d, q, k, v, w, opart, lpart, s);
+  } else {
+    if (d.D == 128) return attn_dispatch_g<float, 128>(d, q, k, v, w, opart, lpart, s);
+    if (d.D == 64) return attn_dispatch_g<float, 64>(d, q, k, v, w, opart, lpart, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ============================================================== LSE combine
+//
+// One thread per (query row, head, 8-wide d chunk). Partials of a (query,
+// group) are contiguous: [slot][head in group][d].
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
+               const int32_t* __restrict__ ids, T* __restrict__ out, float* __restrict__ lse,
+               int64_t rows, int Hkv, int topk) {
+  constexpr int C = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = rows * Hkv * G * C;
+  if (idx >= total) return;
+  const int c = (int)(idx % C);
+  int64_t rest = idx / C;
+  const int hg = (int)(rest % G);
+  rest /= G;
+  const int r = (int)(rest % Hkv);
+  const int64_t row = rest / Hkv;
+  const size_t e0 = (size_t)(row * Hkv + r) * topk;
+  const int32_t* id = ids + e0;
+  float m = -INFINITY;
+  for (int s = 0; s < topk; ++s)
+    if (id[s] >= 0) m = fmaxf(m, lpart[(e0 + s) * G + hg]);
+  float z = 0.0f;
+  for (int s = 0; s < topk; ++s)
+    if (id[s] >= 0) z += __expf(lpart[(e0 + s) * G + hg] - m);
+  const float L = m + __logf(z);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int s = 0; s < topk; ++s) {
+    if (id[s] < 0) continue;
+    const float wgt = __expf(lpart[(e0 + s) * G + hg] - L);
+    const vec8<T> o = ld8<T>(opart + ((e0 + s) * G + hg) * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[e];
+  }
+  vec8<T> res;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) res[e] = cvt<T>(acc[e]);
+  const int64_t hq = (int64_t)r * G + hg;
+  st8<T>(out + ((size_t)row * Hkv * G + hq) * D + c * 8, res);
+  if (c == 0) lse[row * Hkv * G + hq] = L;
+}
+
+template <typename T, int D>
+static hipError_t combine_dispatch_g(const Dims& d, const void* opart, const float* lpart,
+                                     const int32_t* ids, void* out, float* lse, hipStream_t s) {
+  const int64_t total = d.rows * d.Hq * (D / 8);
+  const unsigned grid = (unsigned)((total + 255) / 256);
+#define MSA_COMB_CASE(GG)                                                                   \
+  case GG:                                                                                  \
+    combine_kernel<T, D, GG><<<grid, 256, 0, s>>>((const T*)opart, lpart, ids, (T*)out, lse, \
+                                                  d.rows, d.Hkv, d.K);                      \
+    break;
+  switch (d.G) {
+    MSA_COMB_CASE(1)
+    MSA_COMB_CASE(2)
+    MSA_COMB_CASE(4)
+    MSA_COMB_CASE(8)
+    MSA_COMB_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MSA_COMB_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims& d, const void* opart, const float* lpart,
+                          const int32_t* ids, void* out, float* lse, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128) return combine_dispatch_g<bf16, 128>(d, opart, lpart, ids, out, lse, s);
+    if (d.D == 64) return combine_dispatch_g<bf16, 64>(d, opart, lpart, ids, out, lse, s);
+  } else {
+    if (d.D == 128) return combine_dispatch_g<float, 128>(d, opart, lpart, ids, out, lse, s);
+    if (d.D == 64) return combine_dispatch_g<float, 64>(d, opart, lpart, ids, out, lse, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -1,0 +1,123 @@
+// msa_internal.hpp — shared definitions of the MSA HIP kernels (gfx950).
+//
+// Matrix-core conventions used by every kernel
+// --------------------------------------------
+// All dense contractions use the 32x32 MFMA tile: D(32x32, fp32) += A(32x16) * B(16x32).
+//   bf16 inputs: one v_mfma_f32_32x32x16_bf16.
+//   fp32 inputs: eight v_mfma_f32_32x32x2_f32 over the same 16-wide k range.
+// Lane l (0..63), half h = l/32, l32 = l%32:
+//   A fragment: A[row = l32][k in K(h)]   (8 values, contiguous in memory)
+//   B fragment: B[k in K(h)][col = l32]   (8 values)
+//   D element e (0..15): row = 8*(e/4) + 4*h + (e%4), col = l32.
+// K(h) is the set of 8 k-indices a lane supplies. A and B use the same set,
+// so any fixed assignment of k-indices to (h, element) gives the same sum;
+// the kernels use that freedom to feed a D tile straight back as a B operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "msa.h"
+
+namespace msa {
+
+typedef __bf16 bf16;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct V8;
+template <> struct V8<bf16> { typedef bf16x8 type; };
+template <> struct V8<float> { typedef f32x8 type; };
+template <typename T> struct V4;
+template <> struct V4<bf16> { typedef bf16x4 type; };
+template <> struct V4<float> { typedef f32x4 type; };
+template <typename T> using vec8 = typename V8<T>::type;
+template <typename T> using vec4 = typename V4<T>::type;
+
+__device__ __forceinline__ void mma(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ vec8<T> zero8() {
+  vec8<T> z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (T)0.0f;
+  return z;
+}
+template <typename T> __device__ __forceinline__ vec8<T> ld8(const T* p) {
+  return *reinterpret_cast<const vec8<T>*>(p);
+}
+template <typename T> __device__ __forceinline__ void st8(T* p, const vec8<T>& v) {
+  *reinterpret_cast<vec8<T>*>(p) = v;
+}
+template <typename T> __device__ __forceinline__ vec4<T> ld4(const T* p) {
+  return *reinterpret_cast<const vec4<T>*>(p);
+}
+template <typename T> __device__ __forceinline__ void st4(T* p, const vec4<T>& v) {
+  *reinterpret_cast<vec4<T>*>(p) = v;
+}
+template <typename T> __device__ __forceinline__ T cvt(float x) { return (T)x; }
+
+// D-tile row of element e for lane half h.
+__device__ __forceinline__ constexpr int drow(int e, int h) { return 8 * (e / 4) + 4 * h + (e % 4); }
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------- host side
+
+struct Dims {
+  int B, N, Nq, q_start, Hq, Hkv, G, D, DI, Bk, K, nb, dtype;
+  int64_t rows;     // B * Nq query rows
+  int64_t slots;    // B * Nq * Hkv * K (selection slots)
+  int64_t buckets;  // B * Hkv * nb
+  int64_t entries_max;  // upper bound of used slots
+  int64_t items_max;    // upper bound of attention work items
+  int qt;               // queries per attention work item (128 / G)
+};
+
+// Workspace of the attention and KL calls (bucketing + partials).
+struct AttnWs {
+  int32_t* counts;    // [buckets]
+  int32_t* offsets;   // [buckets + 1]
+  int32_t* cursor;    // [buckets]
+  int32_t* item_off;  // [buckets + 1]
+  int32_t* totals;    // [4]: entries, items
+  int4* items;        // [items_max]: bucket, first entry, count, 0
+  int32_t* entries;   // [entries_max]: (t << 6) | slot
+};
+
+// Process-wide kernel timing hook (msa_prof_begin / msa_prof_end).
+void prof_before(int kernel, hipStream_t s);
+void prof_after(int kernel, hipStream_t s);
+
+// ---------------------------------------------------------------- launchers (return hipError_t)
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
+                                 float* block_lse, hipStream_t s);
+hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s);
+
+hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, hipStream_t s);
+hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const void* v,
+                              const AttnWs& w, void* opart, float* lpart, hipStream_t s);
+hipError_t launch_combine(const Dims& d, const void* opart, const float* lpart,
+                          const int32_t* ids, void* out, float* lse, hipStream_t s);
+
+hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
+                     const void* k_idx, const int32_t* ids, const float* lse_main,
+                     const AttnWs& w, float* idx_stats, float* lse_idx, float* kl_part,
+                     float* kl_rows, float* kl_block_sums, float* kl_mean, float* dlogits,
+                     hipStream_t s);
+
+}  // namespace msa

@@ -1,0 +1,390 @@
+// msa_kl.hip — KL alignment of the index branch on the selected support.
+//
+// "MSA 中的 KL 对齐与局部知识蒸馏" (MSA KL alignment note):
+//   §2.1 student P_idx = softmax of the index logits over the support J;
+//   §2.2 teacher P = (1/G) sum over the group's heads of each head's softmax
+//        over J (probabilities averaged, not logits);
+//   §3   KL(P || P_idx) per (query, group), loss = mean over N*Hkv rows,
+//        gradient in the index logits = P_idx - P;
+//   §6   probabilities are rebuilt from logits and the two LSEs
+//        (p = exp(s - LSE), also "4.1.1 · 监督与联合训练" eq. 15), LSE_main
+//        coming from the sparse forward; the work per KV tile is uneven, which
+//        the shared KV-outer work list (fixed-size items of hot buckets) absorbs.
+// Passes, all over the attention work items (one 128-token block of group r,
+// up to 128/G query rows):
+//   A  index logits on the block -> per-(query, slot) log-sum-exp;
+//   B  logsumexp over slots -> LSE_idx per (query, group); zero dS rows of
+//      unused slots;
+//   C  main logits of the G heads (MFMA) -> teacher P; index logits -> P_idx;
+//      dS = P_idx - P per token, KL partial per (query, slot);
+//   D  KL per row (fixed slot order) and the mean (fixed-order tree).
+#include "msa_internal.hpp"
+
+namespace msa {
+
+template <typename T> struct KlPad;
+template <> struct KlPad<bf16> { static constexpr int K = 8; };
+template <> struct KlPad<float> { static constexpr int K = 4; };
+
+// Index logits S_idx^T = K_idx_blk Q_idx^T for the item's queries. Wave w
+// owns keys [32w, 32w+32); column tile ct holds queries 32ct..32ct+31.
+// Writes z = S_idx (natural scale, fp32) to zs[q][key] in LDS.
+template <typename T, int DI, int QT>
+__device__ __forceinline__ void item_index_logits(const T* __restrict__ q_idx,
+                                                  const T* __restrict__ k_idx, int b, int r,
+                                                  int blk, int N, int Nq, int Hkv, int cnt,
+                                                  const int* s_t, float (*zs)[128 + 4],
+                                                  float scale) {
+  constexpr int KS = DI / 16;
+  constexpr int CT = (QT + 31) / 32;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int j = blk * 128 + 32 * wave + l32;
+  vec8<T> af[KS];
+  const T* kp = k_idx + ((size_t)b * N + j) * DI + 8 * h;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) af[ks] = j < N ? ld8<T>(kp + 16 * ks) : zero8<T>();
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int qi = ct * 32 + l32;
+    const bool qv = qi < cnt;
+    const int t = qv ? s_t[qi] : 0;
+    const T* qp = q_idx + ((size_t)(b * (size_t)Nq + t) * Hkv + r) * DI + 8 * h;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mma(acc, af[ks], qv ? ld8<T>(qp + 16 * ks) : zero8<T>());
+    if (qi < QT) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zs[qi][32 * wave + drow(e, h)] = acc[e] * scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass A
+template <typename T, int DI, int G>
+__global__ void __launch_bounds__(256)
+kl_idx_stats_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+                    const int4* __restrict__ items, const int32_t* __restrict__ entries,
+                    const int32_t* __restrict__ totals, float* __restrict__ slot_lse, int N,
+                    int Nq, int q_start, int Hkv, int nb, int topk) {
+  constexpr int QT = 128 / G;
+  __shared__ float zs[QT][128 + 4];
+  __shared__ int s_t[QT], s_s[QT];
+  const int total = totals[1];
+  const int per = (total + 7) / 8;
+  const int g = blockIdx.x;
+  const int it = (g & 7) * per + (g >> 3);
+  if ((g >> 3) >= per || it >= total) return;
+  const int4 item = items[it];
+  const int bkt = item.x, start = item.y, cnt = item.z;
+  const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+  const int tid = threadIdx.x;
+  if (tid < QT) {
+    const int e = tid < cnt ? entries[start + tid] : 0;
+    s_t[tid] = e >> 6;
+    s_s[tid] = e & 63;
+  }
+  __syncthreads();
+  item_index_logits<T, DI, QT>(q_idx, k_idx, b, r, blk, N, Nq, Hkv, cnt, s_t, zs,
+                               1.0f / sqrtf((float)DI));
+  __syncthreads();
+  // one thread per query: logsumexp over the visible tokens of the block
+  if (tid < cnt) {
+    const int i = q_start + s_t[tid];
+    const int last = min(127, i - blk * 128);
+    float m = -INFINITY;
+    for (int key = 0; key <= last; ++key) m = fmaxf(m, zs[tid][key]);
+    float z = 0.0f;
+    for (int key = 0; key <= last; ++key) z += __expf(zs[tid][key] - m);
+    const size_t entry = ((size_t)(b * (size_t)Nq + s_t[tid]) * Hkv + r) * topk + s_s[tid];
+    slot_lse[entry] = m + __logf(z);
+  }
+}
+
+// ---------------------------------------------------------------- pass B
+__global__ void __launch_bounds__(256)
+kl_idx_lse_kernel(const int32_t* __restrict__ ids, const float* __restrict__ slot_lse,
+                  float* __restrict__ lse_idx, float* __restrict__ dlogits, int64_t nrows,
+                  int topk) {
+  const int64_t rr = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, group)
+  if (rr >= nrows) return;
+  const int32_t* id = ids + rr * topk;
+  float m = -INFINITY;
+  for (int s = 0; s < topk; ++s)
+    if (id[s] >= 0) m = fmaxf(m, slot_lse[rr * topk + s]);
+  float z = 0.0f;
+  for (int s = 0; s < topk; ++s)
+    if (id[s] >= 0) z += __expf(slot_lse[rr * topk + s] - m);
+  lse_idx[rr] = m + __logf(z);
+  if (dlogits) {
+    for (int s = 0; s < topk; ++s) {
+      if (id[s] >= 0) continue;
+      float4* p = reinterpret_cast<float4*>(dlogits + (rr * topk + s) * 128);
+      for (int x = 0; x < 32; ++x) p[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass C
+//
+// S = Q K^T with the wave's 32 (query, head) rows as GEMM rows: A = Q
+// fragments (registers), B = K block from LDS. Lane element e holds row
+// drow(e, h), key column l32 of tile kt. The G heads of one query sit in RPQ
+// consecutive elements of a lane (plus the other lane half when G >= 8), so
+// the teacher's head average is an in-lane sum (+ one exchange).
+template <typename T, int D, int DI, int G>
+__global__ void __launch_bounds__(256, 2)
+kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx,
+               const T* __restrict__ k_idx, const float* __restrict__ lse_main,
+               const float* __restrict__ lse_idx, const int4* __restrict__ items,
+               const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
+               float* __restrict__ kl_part, float* __restrict__ dlogits, int N, int Nq,
+               int q_start, int Hkv, int nb, int topk, float scale_log2) {
+  constexpr int QT = 128 / G;
+  constexpr int KSD = D / 16;
+  constexpr int PK = KlPad<T>::K;
+  constexpr bool PARTNER = G >= 8;
+  constexpr int RPQ = PARTNER ? G / 2 : G;  // rows of one query per lane
+  constexpr int NLQ = 16 / RPQ;             // queries per lane
+  __shared__ T Ks[128][D + PK];
+  __shared__ float zs[QT][128 + 4];
+  __shared__ int s_t[QT], s_s[QT];
+  __shared__ float s_li[QT];
+
+  const int total = totals[1];
+  const int per = (total + 7) / 8;
+  const int g = blockIdx.x;
+  const int it = (g & 7) * per + (g >> 3);
+  if ((g >> 3) >= per || it >= total) return;
+  const int4 item = items[it];
+  const int bkt = item.x, start = item.y, cnt = item.z;
+  const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+  const int tid = threadIdx.x;
+  if (tid < QT) {
+    const int e = tid < cnt ? entries[start + tid] : 0;
+    const int t = e >> 6;
+    s_t[tid] = t;
+    s_s[tid] = e & 63;
+    s_li[tid] = tid < cnt ? lse_idx[(size_t)(b * (size_t)Nq + t) * Hkv + r] : 0.0f;
+  }
+  const size_t kvrow = (size_t)Hkv * D;
+  const T* kb = k + ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
+  const int nvalid = min(128, N - blk * 128);
+  constexpr int CH = D / 8;
+  for (int c = tid; c < 128 * CH; c += 256) {
+    const int kr = c / CH, dc = c % CH;
+    st8<T>(&Ks[kr][dc * 8], kr < nvalid ? ld8<T>(kb + kr * kvrow + dc * 8) : zero8<T>());
+  }
+  __syncthreads();
+  item_index_logits<T, DI, QT>(q_idx, k_idx, b, r, blk, N, Nq, Hkv, cnt, s_t, zs,
+                               1.0f / sqrtf((float)DI));
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int Hq = Hkv * G;
+  // A operand: this lane's Q row (wave row l32) for the MFMA rows
+  const int arow = 32 * wave + l32;
+  const int aqi = arow / G;
+  const bool av = aqi < cnt;
+  const int at = av ? s_t[aqi] : 0;
+  vec8<T> qf[KSD];
+  {
+    const T* qp = q + ((size_t)(b * (size_t)Nq + at) * Hq + r * G + arow % G) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = av ? ld8<T>(qp + 16 * ks) : zero8<T>();
+  }
+  // per-element (row) data: LSE_main of the row's head in the log2 domain
+  float lm2[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 32 * wave + drow(e, h);
+    const int qi = row / G;
+    lm2[e] = qi < cnt
+                 ? lse_main[(size_t)(b * (size_t)Nq + s_t[qi]) * Hq + r * G + row % G] * kLog2e
+                 : 0.0f;
+  }
+  float klacc[NLQ];
+#pragma unroll
+  for (int lq = 0; lq < NLQ; ++lq) klacc[lq] = 0.0f;
+  const float inv_g = 1.0f / (float)G;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks)
+      mma(acc, qf[ks], ld8<T>(&Ks[kt * 32 + l32][16 * ks + 8 * h]));
+    const int key = kt * 32 + l32;
+    const int tok = blk * 128 + key;
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) {
+      float P = 0.0f;
+#pragma unroll
+      for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e) P += exp2f(acc[e] * scale_log2 - lm2[e]);
+      if (PARTNER) P += shfl_xor_f(P, 32);
+      P *= inv_g;
+      const int row = 32 * wave + drow(lq * RPQ, h);
+      const int qi = row / G;
+      const bool owner = !PARTNER || h == 0;
+      if (qi < cnt && owner) {
+        const int t = s_t[qi];
+        const bool vis = tok <= q_start + t;
+        const float lpi = zs[qi][key] - s_li[qi];  // log P_idx
+        float dS = 0.0f;
+        if (vis) {
+          dS = __expf(lpi) - P;
+          if (P > 0.0f) klacc[lq] += P * (__logf(P) - lpi);
+        }
+        if (dlogits) {
+          const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + s_s[qi];
+          dlogits[entry * 128 + key] = dS;
+        }
+      }
+    }
+  }
+  // reduce the KL partial of each query over the 32 key columns of a lane half
+#pragma unroll
+  for (int lq = 0; lq < NLQ; ++lq) {
+    float v = klacc[lq];
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+    const int row = 32 * wave + drow(lq * RPQ, h);
+    const int qi = row / G;
+    const bool owner = !PARTNER || h == 0;
+    if (l32 == 0 && owner && qi < cnt) {
+      const size_t entry = ((size_t)(b * (size_t)Nq + s_t[qi]) * Hkv + r) * topk + s_s[qi];
+      kl_part[entry] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass D
+__global__ void __launch_bounds__(256)
+kl_reduce_kernel(const int32_t* __restrict__ ids, const float* __restrict__ kl_part,
+                 float* __restrict__ kl_rows, float* __restrict__ block_sums, int64_t nrows,
+                 int topk) {
+  __shared__ float red[256];
+  const int64_t rr = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float v = 0.0f;
+  if (rr < nrows) {
+    const int32_t* id = ids + rr * topk;
+    for (int s = 0; s < topk; ++s)
+      if (id[s] >= 0) v += kl_part[rr * topk + s];
+    kl_rows[rr] = v;
+  }
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
+}
+
+__global__ void __launch_bounds__(256)
+kl_mean_kernel(const float* __restrict__ block_sums, int64_t nblocks, int64_t nrows,
+               float* __restrict__ kl_mean) {
+  __shared__ double red[256];
+  double v = 0.0;
+  for (int64_t x = threadIdx.x; x < nblocks; x += 256) v += (double)block_sums[x];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *kl_mean = nrows > 0 ? (float)(red[0] / (double)nrows) : 0.0f;
+}
+
+// ---------------------------------------------------------------- launch
+
+template <typename T, int D, int DI, int G>
+static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void* q_idx,
+                         const void* k_idx, const int32_t* ids, const float* lse_main,
+                         const AttnWs& w, float* slot_lse, float* lse_idx, float* kl_part,
+                         float* kl_rows, float* block_sums, float* kl_mean, float* dlogits,
+                         hipStream_t s) {
+  const unsigned grid = (unsigned)(d.items_max + 8);
+  const int64_t nrows = d.rows * d.Hkv;
+  if (d.items_max > 0) {
+    prof_before(MSA_K_KL_IDX_STATS, s);
+    kl_idx_stats_kernel<T, DI, G><<<grid, 256, 0, s>>>(
+        (const T*)q_idx, (const T*)k_idx, w.items, w.entries, w.totals, slot_lse, d.N, d.Nq,
+        d.q_start, d.Hkv, d.nb, d.K);
+    prof_after(MSA_K_KL_IDX_STATS, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned rgrid = (unsigned)((nrows + 255) / 256);
+  if (nrows > 0) {
+    prof_before(MSA_K_KL_IDX_LSE, s);
+    kl_idx_lse_kernel<<<rgrid, 256, 0, s>>>(ids, slot_lse, lse_idx, dlogits, nrows, d.K);
+    prof_after(MSA_K_KL_IDX_LSE, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (d.items_max > 0) {
+    const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+    prof_before(MSA_K_KL_MAIN, s);
+    kl_main_kernel<T, D, DI, G><<<grid, 256, 0, s>>>(
+        (const T*)q, (const T*)k, (const T*)q_idx, (const T*)k_idx, lse_main, lse_idx, w.items,
+        w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K,
+        scale_log2);
+    prof_after(MSA_K_KL_MAIN, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nrows > 0) {
+    prof_before(MSA_K_KL_REDUCE, s);
+    kl_reduce_kernel<<<rgrid, 256, 0, s>>>(ids, kl_part, kl_rows, block_sums, nrows, d.K);
+    prof_after(MSA_K_KL_REDUCE, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  kl_mean_kernel<<<1, 256, 0, s>>>(block_sums, nrows > 0 ? (int64_t)rgrid : 0, nrows, kl_mean);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DI>
+static hipError_t kl_dispatch_g(const Dims& d, const void* q, const void* k, const void* qi,
+                                const void* ki, const int32_t* ids, const float* lm,
+                                const AttnWs& w, float* sl, float* li, float* kp, float* kr,
+                                float* bs, float* km, float* dl, hipStream_t s) {
+  switch (d.G) {
+    case 1: return kl_run<T, D, DI, 1>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+    case 2: return kl_run<T, D, DI, 2>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+    case 4: return kl_run<T, D, DI, 4>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+    case 8: return kl_run<T, D, DI, 8>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+    case 16: return kl_run<T, D, DI, 16>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t kl_dispatch_di(const Dims& d, const void* q, const void* k, const void* qi,
+                                 const void* ki, const int32_t* ids, const float* lm,
+                                 const AttnWs& w, float* sl, float* li, float* kp, float* kr,
+                                 float* bs, float* km, float* dl, hipStream_t s) {
+  if (d.DI == 64) return kl_dispatch_g<T, D, 64>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+  if (d.DI == 32) return kl_dispatch_g<T, D, 32>(d, q, k, qi, ki, ids, lm, w, sl, li, kp, kr, bs, km, dl, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
+                     const void* k_idx, const int32_t* ids, const float* lse_main,
+                     const AttnWs& w, float* slot_lse, float* lse_idx, float* kl_part,
+                     float* kl_rows, float* block_sums, float* kl_mean, float* dlogits,
+                     hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128) return kl_dispatch_di<bf16, 128>(d, q, k, q_idx, k_idx, ids, lse_main, w, slot_lse, lse_idx, kl_part, kl_rows, block_sums, kl_mean, dlogits, s);
+    if (d.D == 64) return kl_dispatch_di<bf16, 64>(d, q, k, q_idx, k_idx, ids, lse_main, w, slot_lse, lse_idx, kl_part, kl_rows, block_sums, kl_mean, dlogits, s);
+  } else {
+    if (d.D == 128) return kl_dispatch_di<float, 128>(d, q, k, q_idx, k_idx, ids, lse_main, w, slot_lse, lse_idx, kl_part, kl_rows, block_sums, kl_mean, dlogits, s);
+    if (d.D == 64) return kl_dispatch_di<float, 64>(d, q, k, q_idx, k_idx, ids, lse_main, w, slot_lse, lse_idx, kl_part, kl_rows, block_sums, kl_mean, dlogits, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

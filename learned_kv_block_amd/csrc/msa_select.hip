@@ -1,0 +1,408 @@
+// msa_select.hip — index scoring with fused causal block max, and block Top-k.
+//
+// Index branch of "MSA Indexer 与 DSA Lightning Indexer 的差别" (MSA vs DSA
+// indexer note): §2.1 scores S_idx = Q_idx . K_idx^T / sqrt(d_idx) with one
+// shared K_idx head; §2.2 block score M[i,b] = max of S_idx over the tokens
+// j <= i of 128-token block b, then Top-k blocks with the query's local block
+// always included. "MiniMax Sparse Attention：教长上下文模型使用索引" (MSA blog),
+// kernel section: the Top-k runs on raw scores (softmax keeps the order).
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// ============================================================== fill kernels
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * blockDim.x)
+    p[x] = v;
+}
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * blockDim.x)
+    p[x] = v;
+}
+static unsigned fill_grid(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  return (unsigned)(g < 1 ? 1 : (g > 4096 ? 4096 : g));
+}
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<fill_grid(n), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_f32_kernel<<<fill_grid(n), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// ============================================================== index GEMM + block max
+//
+// Workgroup = one tile of QT = 128/HKV consecutive query rows (all HKV groups:
+// 128 GEMM rows, contiguous in Q_idx) x a chunk of kIdxChunk key blocks.
+// Wave w owns keys [32w, 32w+32) of each 128-key block. The product is formed
+// transposed, D = K_idx_tile (keys as rows) * Q_idx_tile^T, so each lane holds
+// 16 keys of one GEMM row and the block max is an in-lane reduction plus one
+// exchange with the other lane half, then a 4-wave reduction through LDS.
+// The N x N score matrix never leaves registers; only one fp32 per
+// (row, block) is written, 8 contiguous blocks per row per workgroup.
+
+constexpr int kIdxChunk = 8;
+
+template <typename T, int DI, int HKV, bool LSE>
+__global__ void __launch_bounds__(256, 2)
+index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+                      float* __restrict__ M, float* __restrict__ blse, int N, int Nq,
+                      int q_start, int nb, int ntiles, float scale, float scale_log2) {
+  constexpr int QT = 128 / HKV;
+  constexpr int KS = DI / 16;
+  constexpr int CB = kIdxChunk;
+  __shared__ float red_m[2][4][128];
+  __shared__ float red_l[2][4][LSE ? 128 : 1];
+  __shared__ float out_m[128][CB + 1];
+  __shared__ float out_l[LSE ? 128 : 1][CB + 1];
+
+  const int tile = ntiles - 1 - (int)blockIdx.y;  // longest rows first
+  const int b = blockIdx.z;
+  const int t0 = tile * QT;
+  const int t_last = min(Nq, t0 + QT) - 1;
+  const int i_first = q_start + t0;
+  const int i_last = q_start + t_last;
+  const int kb0 = (int)blockIdx.x * CB;
+  if (kb0 * 128 > i_last) return;  // whole workgroup: chunk is after every row's window
+  const int kb1 = min(kb0 + CB - 1, i_last / 128);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+
+  // B operand: Q_idx^T fragments of the 128 rows, kept in registers.
+  vec8<T> qf[4][KS];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int row = 32 * ct + l32;
+    const int tq = t0 + row / HKV;
+    const int r = row % HKV;
+    const T* qp = q_idx + ((size_t)(b * (size_t)Nq + tq) * HKV + r) * DI + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = (tq < Nq) ? ld8<T>(qp + 16 * ks) : zero8<T>();
+  }
+
+  const T* kbase = k_idx + (size_t)b * N * DI + 8 * h;
+  int buf = 0;
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    const int j = kb * 128 + 32 * wave + l32;
+    vec8<T> af[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      af[ks] = (j < N) ? ld8<T>(kbase + (size_t)j * DI + 16 * ks) : zero8<T>();
+    f32x16 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma(acc[ct], af[ks], qf[ct][ks]);
+    }
+    const bool need_mask = (kb * 128 + 127 > i_first);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int row = 32 * ct + l32;
+      const int i_row = q_start + t0 + row / HKV;
+      float m = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb * 128 + 32 * wave + drow(e, h);
+        float x = acc[ct][e];
+        if (need_mask && key > i_row) x = -INFINITY;
+        acc[ct][e] = x;
+        m = fmaxf(m, x);
+      }
+      m = fmaxf(m, shfl_xor_f(m, 32));
+      float z = 0.0f;
+      if (LSE) {
+        if (m != -INFINITY) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) z += exp2f((acc[ct][e] - m) * scale_log2);
+        }
+        z += shfl_xor_f(z, 32);
+      }
+      if (h == 0) {
+        red_m[buf][wave][row] = m;
+        if (LSE) red_l[buf][wave][row] = z;
+      }
+    }
+    __syncthreads();
+    if (tid < 128) {
+      float m = fmaxf(fmaxf(red_m[buf][0][tid], red_m[buf][1][tid]),
+                      fmaxf(red_m[buf][2][tid], red_m[buf][3][tid]));
+      out_m[tid][kb - kb0] = m * scale;  // scale > 0 commutes with max
+      if (LSE) {
+        float z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mw = red_m[buf][w][tid];
+          if (mw != -INFINITY) z += red_l[buf][w][tid] * exp2f((mw - m) * scale_log2);
+        }
+        out_l[tid][kb - kb0] = m * scale + logf(z);
+      }
+    }
+    buf ^= 1;  // the next block writes the other buffer; one barrier per block suffices
+  }
+  __syncthreads();
+  if (tid < 128) {
+    const int row = tid;
+    const int tq = t0 + row / HKV;
+    const int r = row % HKV;
+    if (tq < Nq) {
+      const int L_row = (q_start + tq) / 128;
+      const size_t base = ((size_t)(b * (size_t)Nq + tq) * HKV + r) * nb;
+      const int kend = min(kb1, L_row);
+      for (int kb = kb0; kb <= kend; ++kb) {
+        M[base + kb] = out_m[row][kb - kb0];
+        if (LSE) blse[base + kb] = out_l[row][kb - kb0];
+      }
+    }
+  }
+}
+
+template <typename T, int DI, int HKV>
+static hipError_t index_dispatch_lse(const Dims& d, const void* qi, const void* ki, float* M,
+                                     float* bl, hipStream_t s) {
+  constexpr int QT = 128 / HKV;
+  const int ntiles = (d.Nq + QT - 1) / QT;
+  const int nchunks = (d.nb + kIdxChunk - 1) / kIdxChunk;
+  if (ntiles == 0 || d.B == 0) return hipSuccess;
+  dim3 grid(nchunks, ntiles, d.B);
+  const float scale = 1.0f / sqrtf((float)DI);
+  const float scale_log2 = scale * kLog2e;
+  if (bl)
+    index_blockmax_kernel<T, DI, HKV, true><<<grid, 256, 0, s>>>(
+        (const T*)qi, (const T*)ki, M, bl, d.N, d.Nq, d.q_start, d.nb, ntiles, scale, scale_log2);
+  else
+    index_blockmax_kernel<T, DI, HKV, false><<<grid, 256, 0, s>>>(
+        (const T*)qi, (const T*)ki, M, bl, d.N, d.Nq, d.q_start, d.nb, ntiles, scale, scale_log2);
+  return hipGetLastError();
+}
+
+template <typename T, int DI>
+static hipError_t index_dispatch_hkv(const Dims& d, const void* qi, const void* ki, float* M,
+                                     float* bl, hipStream_t s) {
+  switch (d.Hkv) {
+    case 1: return index_dispatch_lse<T, DI, 1>(d, qi, ki, M, bl, s);
+    case 2: return index_dispatch_lse<T, DI, 2>(d, qi, ki, M, bl, s);
+    case 4: return index_dispatch_lse<T, DI, 4>(d, qi, ki, M, bl, s);
+    case 8: return index_dispatch_lse<T, DI, 8>(d, qi, ki, M, bl, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
+                                 float* block_lse, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.DI == 64) return index_dispatch_hkv<bf16, 64>(d, q_idx, k_idx, M, block_lse, s);
+    if (d.DI == 32) return index_dispatch_hkv<bf16, 32>(d, q_idx, k_idx, M, block_lse, s);
+  } else {
+    if (d.DI == 64) return index_dispatch_hkv<float, 64>(d, q_idx, k_idx, M, block_lse, s);
+    if (d.DI == 32) return index_dispatch_hkv<float, 32>(d, q_idx, k_idx, M, block_lse, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ============================================================== block Top-k
+//
+// One wavefront per (b, t, r) row of block scores M[0..L], L = local block.
+// Keys are 64-bit: (order-preserving bits of the score) << 32 | ~block, so a
+// larger key means a higher score, or an equal score and a lower block index;
+// every key is distinct. Lane l owns blocks v*64 + l (coalesced loads).
+//  1. T = the (k-1)-th largest per-lane maximum score (bitonic sort of the 64
+//     lane maxima). Every block of the true top-(k-1) scores >= T, and at
+//     least k-1 blocks do, so the blocks with score >= T are the candidates.
+//  2. Candidates are compacted into LDS in (v, lane) order = ascending block.
+//  3. Each candidate's exact rank among candidates gives the selection; the
+//     selected ones keep their ascending order; the local block L (the
+//     largest visible index) goes last.
+// If ties make the candidate list overflow LDS, a k-1 round wave-argmax
+// fallback gives the same (exact) result.
+
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_of_ord(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ uint64_t make_key(float score, int blk) {
+  return ((uint64_t)ord_f32(score) << 32) | (uint64_t)(uint32_t)(~(uint32_t)blk);
+}
+__device__ __forceinline__ int key_blk(uint64_t key) { return (int)(~(uint32_t)(key & 0xffffffffull)); }
+__device__ __forceinline__ float key_score(uint64_t key) { return f32_of_ord((uint32_t)(key >> 32)); }
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, m, 64), hi = __shfl_xor((uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t y = shfl_xor_u64(x, m);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kTopkMax = 32;
+
+template <int V>
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int Hkv, int nb,
+            int k, int32_t* __restrict__ ids, float* __restrict__ margin) {
+  constexpr int CMAX = (kTopkMax - 1) * V;
+  __shared__ uint64_t cand[4][CMAX];
+  __shared__ uint64_t msel[4][2];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= nrows) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int t = (int)((row / Hkv) % Nq);
+  const int i = q_start + t;
+  const int L = i / 128;
+  int32_t* out = ids + row * k;
+  if (L + 1 <= k) {  // every visible block is selected
+    for (int s = lane; s < k; s += 64) out[s] = s <= L ? s : -1;
+    if (margin && lane == 0) margin[row] = INFINITY;
+    return;
+  }
+  const float* mr = M + row * (int64_t)nb;
+  uint64_t key[V];
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int blk = v * 64 + lane;
+    if (blk < L) {
+      const float sc = mr[blk];
+      key[v] = make_key(sc, blk);
+      lmax = max(lmax, ord_f32(sc));
+    } else {
+      key[v] = 0;  // not a candidate (every real key is > 0)
+    }
+  }
+  // 1. threshold from the lane maxima: bitonic sort, descending
+  uint32_t x = lmax;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t y = __shfl_xor(x, stride, 64);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0;
+      const uint32_t hi = max(x, y), lo = min(x, y);
+      x = (lower == desc) ? hi : lo;
+    }
+  }
+  const uint32_t T = __shfl(x, k - 2, 64);
+
+  // 2. count candidates
+  int C = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
+    C += __popcll(__ballot(c));
+  }
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t worst_sel = 0, best_unsel = 0;
+  if (C <= CMAX) {
+    int base = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
+      const uint64_t bal = __ballot(c);
+      if (c) cand[wave][base + __popcll(bal & lt_mask)] = key[v];
+      base += __popcll(bal);
+    }
+    if (margin && lane < 2) msel[wave][lane] = 0;
+    wave_sync();
+    // 3. exact ranks among candidates
+    int pos_base = 0;
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      const int c = c0 + lane;
+      const bool have = c < C;
+      const uint64_t kc = have ? cand[wave][c] : 0;
+      int rank = 0;
+      for (int c2 = 0; c2 < C; ++c2) rank += cand[wave][c2] > kc;
+      const bool sel = have && rank < k - 1;
+      const uint64_t bal = __ballot(sel);
+      if (sel) out[pos_base + __popcll(bal & lt_mask)] = key_blk(kc);
+      pos_base += __popcll(bal);
+      if (margin && have) {
+        if (rank == k - 2) msel[wave][0] = kc;
+        if (rank == k - 1) msel[wave][1] = kc;
+      }
+    }
+    if (margin) {
+      wave_sync();
+      worst_sel = msel[wave][0];
+      best_unsel = msel[wave][1];
+      uint64_t nc = 0;  // best non-candidate
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
+        if (!c && key[v] > nc) nc = key[v];
+      }
+      nc = wave_max_u64(nc);
+      best_unsel = nc > best_unsel ? nc : best_unsel;
+    }
+  } else {
+    // fallback: k-1 rounds of wave argmax over all blocks
+    uint32_t taken = 0;
+    for (int round = 0; round < k - 1; ++round) {
+      uint64_t bestl = 0;
+      int bestv = -1;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (!((taken >> v) & 1u) && key[v] > bestl) { bestl = key[v]; bestv = v; }
+      const uint64_t best = wave_max_u64(bestl);
+      if (bestv >= 0 && bestl == best) taken |= 1u << bestv;
+      if (round == k - 2) worst_sel = best;
+    }
+    int base = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const bool sel = (taken >> v) & 1u;
+      const uint64_t bal = __ballot(sel);
+      if (sel) out[base + __popcll(bal & lt_mask)] = v * 64 + lane;
+      base += __popcll(bal);
+    }
+    uint64_t nc = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (!((taken >> v) & 1u) && key[v] > nc) nc = key[v];
+    best_unsel = wave_max_u64(nc);
+  }
+  if (lane == 0) {
+    out[k - 1] = L;
+    if (margin)
+      margin[row] = best_unsel ? key_score(worst_sel) - key_score(best_unsel) : INFINITY;
+  }
+}
+
+hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s) {
+  const int64_t nrows = d.rows * d.Hkv;
+  if (nrows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((nrows + 3) / 4);
+  const int vneed = (d.nb + 63) / 64;
+  if (vneed <= 4)
+    topk_kernel<4><<<grid, 256, 0, s>>>(M, nrows, d.Nq, d.q_start, d.Hkv, d.nb, d.K, ids, margin);
+  else if (vneed <= 16)
+    topk_kernel<16><<<grid, 256, 0, s>>>(M, nrows, d.Nq, d.q_start, d.Hkv, d.nb, d.K, ids, margin);
+  else if (vneed <= 32)
+    topk_kernel<32><<<grid, 256, 0, s>>>(M, nrows, d.Nq, d.q_start, d.Hkv, d.nb, d.K, ids, margin);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace msa

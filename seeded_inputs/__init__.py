@@ -318,6 +318,8 @@ def device_tensor(cfg: MsaConfig, name: str, device="cuda"):
     total, ncols = cfg.view(name)
     tdtype = torch.float32 if cfg.dtype == F32 else torch.bfloat16
     out = torch.empty(cfg.shape(name), dtype=tdtype, device=device)
+    if total == 0:
+        return out
     flags_t = shift_t = None
     if cfg.skew and name in ("q_idx", "k_idx"):
         flags = _flags_for(cfg, name, np.arange(total, dtype=np.int64))
