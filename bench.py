@@ -1,0 +1,219 @@
+"""Benchmark of the MSA layer hot path on one MI355X.
+
+One step = msa_select (index GEMM + causal block max + Top-k) followed by
+msa_attn_fwd (bucketing, KV-outer sparse attention, LSE combine) over one
+batch of the skewed long-context workload: batch 1, N = 131072, Hq = 64,
+Hkv = 4, d = 128, d_idx = 64, 128-token blocks, k = 16, bf16 inputs with
+seeded synthetic values (inputs resident in HBM before timing).
+
+Prints one JSON line: query-tokens/s, ms per step, the effective-FLOP MFMA
+fraction of the whole layer, the roofline of the dominant kernel (sparse
+attention, timed live with HIP events over the timed steps) and the fp64
+oracle timed on the host on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15  # dense bf16 MFMA, MI355X
+PEAK_HBM = 8.0e12   # bytes/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_skewed_n131072_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "learned_kv_block_amd", "csrc", f)
+                  for f in ("msa_attn.hip", "msa_internal.hpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def effective_flops(cfg, ids):
+    """Index GEMM over the causal triangle + attention on the causally visible tokens of the
+    blocks actually selected (from the GPU's ids)."""
+    import torch
+    B, Nq, Hkv, G = cfg.batch, cfg.seqlen_q, cfg.num_kv_heads, cfg.group_size
+    i = torch.arange(Nq, device=ids.device, dtype=torch.int64) + cfg.q_start
+    f_idx = 2.0 * cfg.idx_dim * Hkv * B * float((i + 1).sum().item())
+    L = (i // 128).view(1, -1, 1, 1)
+    idsl = ids.long()
+    full = (idsl >= 0) & (idsl < L)
+    loc = idsl == L
+    tok = full.sum(-1) * 128 + loc.sum(-1) * ((i % 128) + 1).view(1, -1, 1)
+    f_attn = 4.0 * cfg.head_dim * G * float(tok.sum().item())
+    return f_idx, f_attn
+
+
+def cpu_baseline(cfg, seconds_target=15.0):
+    """fp64 oracle (select + attention) on a seeded sample of query rows, timed on the host."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+
+    threads = oracle.threads()
+    k = si.host_tensor(cfg, "k")
+    v = si.host_tensor(cfg, "v")
+    k_idx = si.host_tensor(cfg, "k_idx")
+    shp = oracle.shape_of(cfg)
+    rng = np.random.default_rng(1234)
+
+    def run(rows):
+        q = si.host_query_rows(cfg, "q", rows)
+        qi = si.host_query_rows(cfg, "q_idx", rows)
+        t0 = time.perf_counter()
+        ids = oracle.select(shp, qi, k_idx, rows=rows)["ids"]
+        oracle.attn(shp, q, k, v, ids, rows=rows)
+        return time.perf_counter() - t0
+
+    # calibrate on a small sample, then size the sample to ~seconds_target
+    probe = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=2 * threads))
+    dt = run(probe)
+    n = int(max(2 * threads, min(4096, len(probe) * seconds_target / max(dt, 1e-3))))
+    rows = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=n))
+    dt = run(rows)
+    return {"value": n / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} seeded uniformly random query rows of the same workload "
+                      f"(rows are independent; fp64 select + attention in {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="skewed_n131072")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the MSA layer on a single "
+              "MI355X; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import learned_kv_block_amd as msa
+    import seeded_inputs as si
+
+    cfg = si.CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    x = {n: si.device_tensor(cfg, n, dev) for n in ("q", "k", "v", "q_idx", "k_idx")}
+    sh_sel = msa.shape_for(x["q_idx"], x["k_idx"], cfg.topk, cfg.q_start, cfg.num_q_heads,
+                           cfg.head_dim)
+    ws_sel = torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_SELECT), dtype=torch.uint8,
+                         device=dev)
+    ws_attn = torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_ATTN), dtype=torch.uint8,
+                          device=dev)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                             num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim,
+                             workspace=ws_sel)
+        msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], q_start=cfg.q_start,
+                         idx_dim=cfg.idx_dim, workspace=ws_attn, out=out, lse=lse)
+        return sel["ids"]
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    ids = None
+    for _ in range(args.warmup):
+        ids = step()
+    torch.cuda.synchronize()
+    if ids is None:
+        ids = step()
+        torch.cuda.synchronize()
+    f_idx, f_attn = effective_flops(cfg, ids)
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    with msa.KernelTimer("sparse_attn", max_launches=args.steps) as kt:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / max(1, args.steps)
+    tokens = cfg.batch * cfg.seqlen_q
+    value = tokens * args.steps / elapsed
+
+    kernels = {}
+    if args.breakdown:
+        for name in ("index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
+                     "work_items", "sparse_attn", "combine"):
+            with msa.KernelTimer(name, max_launches=2) as t:
+                step()
+                step()
+                torch.cuda.synchronize()
+            kernels[name] = round(t.avg_ms, 4)
+        print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
+
+    attn_ms = kt.avg_ms
+    achieved = f_attn / (attn_ms * 1e-3)
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "kernel": "sparse_attn", "achieved": achieved / 1e12,
+                "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16,
+                "traffic": traffic, "avg_ms": attn_ms, "launches": kt.launches,
+                "flops_per_launch": f_attn}
+    line = {
+        "metric": "MSA-layer prefill query-tokens/s at N=128K (1 GPU) + % bf16 MFMA peak",
+        "value": value,
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen_kv,
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "idx_dim": cfg.idx_dim,
+                   "block_size": cfg.block_size, "topk": cfg.topk, "parallelism": "none"},
+        "effective_flops_per_step": f_idx + f_attn,
+        "index_flops_per_step": f_idx,
+        "attn_flops_per_step": f_attn,
+        "mfma_frac_effective": (f_idx + f_attn) / (ms_per_step * 1e-3) / PEAK_BF16,
+        "roofline": roofline,
+    }
+    if kernels:
+        line["kernel_ms"] = kernels
+    del x, ws_sel, ws_attn, out, lse
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
