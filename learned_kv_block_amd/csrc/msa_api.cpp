@@ -18,6 +18,22 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Work items hold up to qt query rows; items_max bounds sum over buckets of
+// ceil(count / qt) <= entries / qt + (non-empty buckets).
+void set_item_size(Dims* d, int qt) {
+  d->qt = qt;
+  const int64_t per_item =
+      d->entries_max / qt + (d->buckets < d->entries_max ? d->buckets : d->entries_max);
+  d->items_max = per_item < d->entries_max ? per_item : d->entries_max;
+}
+
+// The bf16 attention kernel runs 256 (query, head) rows per work item; the
+// fp32 attention and the KL passes run 128.
+Dims for_op(Dims d, int op) {
+  if (op == MSA_OP_ATTN && d.dtype == MSA_BF16) set_item_size(&d, 256 / d.G);
+  return d;
+}
+
 // Shape validation shared by all calls. Fills d on success.
 msa_status make_dims(const msa_shape* s, Dims* d) {
   if (!s) return MSA_ERR_NULL;
@@ -54,10 +70,8 @@ msa_status make_dims(const msa_shape* s, Dims* d) {
   d->slots = d->rows * d->Hkv * d->K;
   d->buckets = (int64_t)s->batch * d->Hkv * nb;
   d->entries_max = d->rows * d->Hkv * (int64_t)(d->K < nb ? d->K : nb);
-  d->qt = 128 / G;
-  const int64_t per_item = d->entries_max / d->qt + (d->buckets < d->entries_max ? d->buckets
-                                                                                 : d->entries_max);
-  d->items_max = per_item < d->entries_max ? per_item : d->entries_max;
+  d->num_cus = 0;
+  set_item_size(d, 128 / G);
   // index ranges the kernels keep in 32-bit integers
   if (d->entries_max >= (int64_t)1 << 31 || d->buckets >= (int64_t)1 << 30 ||
       d->items_max >= (int64_t)1 << 30 || s->seqlen_q >= (1 << 25) ||
@@ -129,9 +143,10 @@ msa_status check_ws(const Layout& L, void* ws, size_t bytes) {
   return MSA_OK;
 }
 
-// The current device must be gfx950 (checked once per device).
-msa_status check_device() {
-  static std::atomic<int> cache[64];  // 0 unknown, 1 ok, 2 not gfx950
+// The current device must be gfx950 (checked once per device); also reports
+// its compute-unit count.
+msa_status check_device(int* num_cus) {
+  static std::atomic<int> cache[64];  // 0 unknown, -1 not gfx950, else the CU count
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MSA_ERR_DEVICE;
   if (dev < 0 || dev >= 64) return MSA_ERR_DEVICE;
@@ -139,10 +154,15 @@ msa_status check_device() {
   if (c == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MSA_ERR_DEVICE;
-    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? (prop.multiProcessorCount > 0
+                                                                ? prop.multiProcessorCount
+                                                                : 1)
+                                                          : -1;
     cache[dev].store(c);
   }
-  return c == 1 ? MSA_OK : MSA_ERR_DEVICE;
+  if (c < 0) return MSA_ERR_DEVICE;
+  if (num_cus) *num_cus = c;
+  return MSA_OK;
 }
 
 inline bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
@@ -163,13 +183,13 @@ void prof_before(int kernel, hipStream_t s) {
   if (g_prof.kernel != kernel) return;
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
-  hipEventRecord(g_prof.ev[2 * g_prof.used], s);
+  (void)hipEventRecord(g_prof.ev[2 * g_prof.used], s);
 }
 void prof_after(int kernel, hipStream_t s) {
   if (g_prof.kernel != kernel) return;
   std::lock_guard<std::mutex> lk(g_prof.mu);
   if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
-  hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
+  (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
   ++g_prof.used;
 }
 }  // namespace msa
@@ -192,7 +212,7 @@ size_t msa_workspace_size(const msa_shape* shape, int op) {
   Dims d;
   if (make_dims(shape, &d) != MSA_OK) return 0;
   if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL) return 0;
-  return layout(d, op).total;
+  return layout(for_op(d, op), op).total;
 }
 
 msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_idx,
@@ -210,9 +230,9 @@ msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_i
     if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
     M = static_cast<float*>(workspace);
   }
-  if ((st = check_device()) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
   prof_before(MSA_K_INDEX_BLOCKMAX, stream);
-  hipError_t e = launch_index_blockmax(d, q_idx, k_idx, M, nullptr, stream);
+  hipError_t e = launch_index_blockmax(d, q_idx, k_idx, M, stream);
   prof_after(MSA_K_INDEX_BLOCKMAX, stream);
   if (e != hipSuccess) return MSA_ERR_DEVICE;
   prof_before(MSA_K_TOPK, stream);
@@ -227,12 +247,13 @@ msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, co
   Dims d;
   msa_status st = make_dims(shape, &d);
   if (st != MSA_OK) return st;
+  d = for_op(d, MSA_OP_ATTN);
   if (d.rows == 0) return MSA_OK;
   if (!q || !k || !v || !block_ids || !out || !lse) return MSA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MSA_ERR_SHAPE;
   const Layout L = layout(d, MSA_OP_ATTN);
   if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
-  if ((st = check_device()) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const AttnWs w = carve(L, workspace);
   if (launch_bucketing(d, block_ids, w, stream) != hipSuccess) return MSA_ERR_DEVICE;
@@ -264,7 +285,7 @@ msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, co
   }
   const Layout L = layout(d, MSA_OP_KL);
   if (d.rows > 0 && (st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
-  if ((st = check_device()) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
   if (d.rows == 0)
     return launch_fill_f32(kl_mean, 1, 0.0f, stream) == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
   char* ws = static_cast<char*>(workspace);

@@ -213,19 +213,47 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
 //
 // One workgroup (4 waves) per work item: a 128-token K/V block of group r and
 // up to QT = 128/G query rows that selected it, i.e. 128 (query, head) rows,
-// 32 per wave. K is staged in LDS row-major and V transposed (V^T[d][key]).
+// 32 per wave. K and V are staged in LDS row-major.
 //   S^T = K Q^T   A = K rows from LDS, B = the wave's Q rows (registers);
 //                 each lane then holds 64 keys of one (query, head) row, so
 //                 the row max / sum are in-lane plus one exchange.
 //   O^T = V^T P^T B = P^T straight from the S^T accumulator (the key set a
-//                 lane holds is the k-set it supplies), A = V^T from LDS.
+//                 lane holds is the k-set it supplies); A = V^T, read from the
+//                 row-major V tile with gfx950's transposing LDS read
+//                 (ds_read_b64_tr_b16: each 16-lane group reads a 4-key x
+//                 16-d tile and lane j receives the 4 keys of column j).
+//                 fp32 inputs have no transposing read and stage V^T instead.
 // Blocks past a query's position are masked (j > i) only where needed.
 // The item -> workgroup mapping keeps consecutive items (same K/V block) on
 // the same XCD: workgroup id g runs on XCD g % 8.
 
 template <typename T> struct AttnPad;
-template <> struct AttnPad<bf16> { static constexpr int K = 8, V = 4; };
+template <> struct AttnPad<bf16> { static constexpr int K = 8, V = 8; };
 template <> struct AttnPad<float> { static constexpr int K = 4, V = 2; };
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// A operand of O^T = V^T P^T for k-step st and d tile dt from row-major V:
+// elements 0..3 = V[16st + 4h + 0..3][d], 4..7 = V[16st + 4h + 8..11][d],
+// d = 32dt + l32.
+template <int LDV>
+__device__ __forceinline__ bf16x8 v_frag_tr(const bf16* Vs, int st, int dt, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int krow = 16 * st + 4 * (g >> 1) + (s >> 2);
+  const int dcol = dt * 32 + 16 * (g & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + krow * LDV + dcol));
+  const short4v hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(Vs + (krow + 8) * LDV + dcol));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = l4[e];
+    r[4 + e] = h4[e];
+  }
+  return r;
+}
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256, 2)
@@ -234,13 +262,13 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                    const int32_t* __restrict__ totals, T* __restrict__ opart,
                    float* __restrict__ lpart, int N, int Nq, int q_start, int Hkv, int nb,
                    int topk, float scale_log2) {
-  constexpr int QT = 128 / G;
-  constexpr int KSD = D / 16;  // k-steps over the head dim
-  constexpr int DT = D / 32;   // 32-wide output d tiles
+  constexpr bool TR = sizeof(T) == 2;  // bf16: row-major V + transposing reads
+  constexpr int KSD = D / 16;          // k-steps over the head dim
+  constexpr int DT = D / 32;           // 32-wide output d tiles
   constexpr int PK = AttnPad<T>::K, PV = AttnPad<T>::V;
+  constexpr int LDV = TR ? D + PV : 128 + PV;
   __shared__ T Ks[128][D + PK];
-  __shared__ T Vt[D][128 + PV];
-  __shared__ int s_t[QT], s_s[QT];
+  __shared__ T Vs[(TR ? 128 : D) * LDV];
 
   // XCD-aware item order: XCD x = g % 8 takes a contiguous range of items.
   const int total = totals[1];
@@ -256,12 +284,23 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   const int r = br % Hkv;
   const int b = br / Hkv;
   const int tid = threadIdx.x;
-  if (tid < QT) {
-    const int e = tid < cnt ? entries[start + tid] : 0;
-    s_t[tid] = e >> 6;
-    s_s[tid] = e & 63;
+  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int row = 32 * wave + l32;  // (query, head) row of the item
+  const int qi = row / G;
+  const int hg = row % G;
+  const bool rv = qi < cnt;
+  const int ent = rv ? entries[start + qi] : 0;
+  const int t = ent >> 6, slot = ent & 63;
+  const int i_row = q_start + t;
+  const int Hq = Hkv * G;
+  // this lane's Q fragments are requested before the K/V staging
+  vec8<T> qf[KSD];
+  {
+    const T* qp = q + ((size_t)(b * (size_t)Nq + t) * Hq + r * G + hg) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = rv ? ld8<T>(qp + 16 * ks) : zero8<T>();
   }
-  // stage K (row-major) and V (transposed)
+  // stage K and V
   const size_t kvrow = (size_t)Hkv * D;
   const T* kb = k + ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
   const T* vb = v + ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
@@ -270,29 +309,19 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   for (int c = tid; c < 128 * CH; c += 256) {
     const int kr = c / CH, dc = c % CH;
     st8<T>(&Ks[kr][dc * 8], kr < nvalid ? ld8<T>(kb + kr * kvrow + dc * 8) : zero8<T>());
+    if (TR) st8<T>(&Vs[kr * LDV + dc * 8], kr < nvalid ? ld8<T>(vb + kr * kvrow + dc * 8)
+                                                     : zero8<T>());
   }
-  for (int c = tid; c < 128 * CH; c += 256) {
-    const int kr = c % 128, dc = c / 128;
-    const vec8<T> x = kr < nvalid ? ld8<T>(vb + kr * kvrow + dc * 8) : zero8<T>();
+  if (!TR) {
+    for (int c = tid; c < 128 * CH; c += 256) {
+      const int kr = c % 128, dc = c / 128;
+      const vec8<T> x = kr < nvalid ? ld8<T>(vb + kr * kvrow + dc * 8) : zero8<T>();
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Vt[dc * 8 + e][kr] = x[e];
+      for (int e = 0; e < 8; ++e) Vs[(dc * 8 + e) * LDV + kr] = x[e];
+    }
   }
   __syncthreads();
 
-  const int wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-  const int row = 32 * wave + l32;  // (query, head) row of the item
-  const int qi = row / G;
-  const int hg = row % G;
-  const bool rv = qi < cnt;
-  const int t = rv ? s_t[qi] : 0;
-  const int i_row = q_start + t;
-  const int Hq = Hkv * G;
-  vec8<T> qf[KSD];
-  {
-    const T* qp = q + ((size_t)(b * (size_t)Nq + t) * Hq + r * G + hg) * D + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) qf[ks] = rv ? ld8<T>(qp + 16 * ks) : zero8<T>();
-  }
   f32x16 sacc[4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
@@ -338,23 +367,27 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     vec8<T> pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = cvt<T>(sacc[st >> 1][8 * (st & 1) + e]);
-    const int key0 = 16 * st + 4 * h;  // keys key0..key0+3 and key0+8..key0+11
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const T* vp = &Vt[dt * 32 + l32][key0];
-      const vec4<T> lo = ld4<T>(vp), hi = ld4<T>(vp + 8);
       vec8<T> vf;
+      if constexpr (TR) {
+        vf = v_frag_tr<LDV>(reinterpret_cast<const bf16*>(Vs), st, dt, lane);
+      } else {
+        const int key0 = 16 * st + 4 * h;  // keys key0..key0+3 and key0+8..key0+11
+        const T* vp = &Vs[(dt * 32 + l32) * LDV + key0];
+        const vec4<T> lo = ld4<T>(vp), hi = ld4<T>(vp + 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[e] = lo[e];
-        vf[4 + e] = hi[e];
+        for (int e = 0; e < 4; ++e) {
+          vf[e] = lo[e];
+          vf[4 + e] = hi[e];
+        }
       }
       mma(oacc[dt], vf, pf);
     }
   }
   if (rv) {
     const float inv = 1.0f / ls;
-    const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + s_s[qi];
+    const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + slot;
     T* op = opart + (entry * G + hg) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -367,6 +400,224 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       }
     }
     if (h == 0) lpart[entry * G + hg] = (mx + __log2f(ls)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------ bf16: persistent, pipelined
+//
+// One workgroup of 8 waves per CU, looping over a contiguous range of work
+// items of its XCD (consecutive items mostly share one K/V block). A work item
+// is 256 (query, head) rows, 32 per wave. K and V of the next item are copied
+// HBM/L2 -> LDS asynchronously (global_load_lds, 16 B per lane) into the
+// second of two LDS buffers while the current item computes, and are not
+// reloaded at all when the next item uses the same block. The next item's row
+// entries and Q fragments are also requested one item ahead.
+// LDS tiles are row-major without padding; the 16-byte chunk c of row rho is
+// stored at chunk c ^ swz(rho) so that both the K fragment reads (8 rows, one
+// chunk) and the transposing V reads (4 rows, two chunks) hit distinct banks.
+
+constexpr int kPipeWaves = 8;
+
+template <int D>
+__device__ __forceinline__ int swz(int rho) {
+  return D == 128 ? 2 * (rho & 7) : 2 * (rho & 3);
+}
+// element offset of (row, col) in a swizzled [128][D] tile
+template <int D>
+__device__ __forceinline__ int tile_off(int rho, int col) {
+  return rho * D + 8 * ((col >> 3) ^ swz<D>(rho)) + (col & 7);
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(512, 1)
+sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                        const bf16* __restrict__ v, const int4* __restrict__ items,
+                        const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
+                        bf16* __restrict__ opart, float* __restrict__ lpart, int N, int Nq,
+                        int q_start, int Hkv, int nb, int topk, float scale_log2) {
+  constexpr int KSD = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  constexpr int TILE = 128 * D;                   // elements per K or V tile
+  constexpr int LOADS = 128 * CPR / (64 * kPipeWaves);  // global_load_lds per wave per tile
+  __shared__ bf16 Kb[2][TILE];
+  __shared__ bf16 Vb[2][TILE];
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const int total = totals[1];
+  const int nwg_x = gridDim.x / 8;  // workgroups per XCD (gridDim.x is a multiple of 8)
+  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
+  const int per_x = (total + 7) / 8;
+  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
+  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  if (i0 >= i1) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int row = 32 * wave + l32;
+  const int qi = row / G, hg = row % G;
+  const int Hq = Hkv * G;
+  const size_t kvrow = (size_t)Hkv * D;
+
+  // async copy of the K and V tiles of bucket `bkt` into buffer `buf`
+  auto stage = [&](int bkt, int buf) {
+    const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+    const int nvalid = min(128, N - blk * 128);
+    const size_t base = ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int p = (wave * LOADS + j) * 64 + lane;  // 16-byte LDS position in the tile
+      const int rho = p / CPR, cs = p % CPR;
+      const int c = cs ^ swz<D>(rho);                // source chunk stored at cs
+      const size_t src = base + (size_t)min(rho, nvalid - 1) * kvrow + 8 * c;
+      lds_void* kd = (lds_void*)(&Kb[buf][(wave * LOADS + j) * 512]);
+      lds_void* vd = (lds_void*)(&Vb[buf][(wave * LOADS + j) * 512]);
+      __builtin_amdgcn_global_load_lds((const void*)(k + src), kd, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(v + src), vd, 16, 0, 0);
+    }
+  };
+  auto load_q = [&](int b, int r, int t, bool ok, vec8<bf16>* qf) {
+    const bf16* qp = q + ((size_t)(b * (size_t)Nq + t) * Hq + r * G + hg) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ok ? ld8<bf16>(qp + 16 * ks) : zero8<bf16>();
+  };
+
+  // prologue: item i0 staged and its Q loaded
+  int4 cur = items[i0];
+  int buf = 0;
+  stage(cur.x, buf);
+  int ent = qi < cur.z ? entries[cur.y + qi] : 0;
+  vec8<bf16> qf[KSD];
+  {
+    const int br = (cur.x / nb);
+    load_q(br / Hkv, br % Hkv, ent >> 6, qi < cur.z, qf);
+  }
+  int4 nxt = i0 + 1 < i1 ? items[i0 + 1] : make_int4(-1, 0, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int it = i0; it < i1; ++it) {
+    const int bkt = cur.x, cnt = cur.z;
+    const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+    const bool have_next = it + 1 < i1;
+    // ---- requests for the next item
+    int nbuf = buf;
+    int ent_n = 0;
+    if (have_next) {
+      if (nxt.x != bkt) {
+        nbuf = buf ^ 1;
+        stage(nxt.x, nbuf);
+      }
+      ent_n = qi < nxt.z ? entries[nxt.y + qi] : 0;
+    }
+    const int4 nxt2 = it + 2 < i1 ? items[it + 2] : make_int4(-1, 0, 0, 0);
+
+    // ---- S^T = K Q^T for the current item
+    const bool rv = qi < cnt;
+    const int t = ent >> 6, slot = ent & 63;
+    const int i_row = q_start + t;
+    const bf16* Kt = Kb[buf];
+    const bf16* Vt = Vb[buf];
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.0f;
+      const int rho = kt * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+        mma(sacc[kt], ld8<bf16>(Kt + tile_off<D>(rho, 16 * ks + 8 * h)), qf[ks]);
+    }
+    // Q of the next item (its entry has arrived by now)
+    vec8<bf16> qn[KSD];
+    {
+      const int nbr = have_next ? nxt.x / nb : 0;
+      load_q(nbr / Hkv, nbr % Hkv, ent_n >> 6, have_next && qi < nxt.z, qn);
+    }
+    // ---- softmax over the block's 128 keys (log2 domain)
+    float mx = -INFINITY;
+    const bool need_mask = blk * 128 + 127 > i_row;
+    if (__any(need_mask)) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (blk * 128 + kt * 32 + drow(e, h) > i_row) sacc[kt][e] = -INFINITY;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mxs = mx * scale_log2;
+    float ls = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], scale_log2, -mxs));
+        sacc[kt][e] = p;
+        ls += p;
+      }
+    }
+    ls += shfl_xor_f(ls, 32);
+    // ---- O^T = V^T P^T
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.0f;
+    typedef __attribute__((address_space(3))) short4v lds_short4;
+    const int g16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      vec8<bf16> pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = cvt<bf16>(sacc[st >> 1][8 * (st & 1) + e]);
+      const int krow = 16 * st + 4 * (g16 >> 1) + (s16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(Vt + tile_off<D>(krow, dcol)));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(Vt + tile_off<D>(krow + 8, dcol)));
+        const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+        bf16x8 vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[e] = l4[e];
+          vf[4 + e] = h4[e];
+        }
+        mma(oacc[dt], vf, pf);
+      }
+    }
+    // ---- partial output and its log-sum-exp
+    if (rv) {
+      const float inv = 1.0f / ls;
+      const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + slot;
+      bf16* op = opart + (entry * G + hg) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          vec4<bf16> o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = cvt<bf16>(oacc[dt][4 * jg + e] * inv);
+          st4<bf16>(op + dt * 32 + 8 * jg + 4 * h, o);
+        }
+      }
+      if (h == 0) lpart[entry * G + hg] = (mxs + __log2f(ls)) * kLn2;
+    }
+    // ---- advance: next item's tiles, entry and Q become current
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    cur = nxt;
+    nxt = nxt2;
+    buf = nbuf;
+    ent = ent_n;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = qn[ks];
   }
 }
 
@@ -393,12 +644,36 @@ static hipError_t attn_dispatch_g(const Dims& d, const void* q, const void* k, c
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t attn_pipe_dispatch_g(const Dims& d, const void* q, const void* k, const void* v,
+                                       const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
+  // one workgroup per CU, a multiple of 8 (one share per XCD)
+  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+#define MSA_PIPE_CASE(GG)                                                                       \
+  case GG:                                                                                      \
+    sparse_attn_pipe_kernel<D, GG><<<grid, 64 * kPipeWaves, 0, s>>>(                           \
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, w.items, w.entries, w.totals,          \
+        (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K, scale_log2);              \
+    break;
+  switch (d.G) {
+    MSA_PIPE_CASE(1)
+    MSA_PIPE_CASE(2)
+    MSA_PIPE_CASE(4)
+    MSA_PIPE_CASE(8)
+    MSA_PIPE_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MSA_PIPE_CASE
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const void* v,
                               const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
   if (d.items_max == 0) return hipSuccess;
   if (d.dtype == MSA_BF16) {
-    if (d.D == 128) return attn_dispatch_g<bf16, 128>(d, q, k, v, w, opart, lpart, s);
-    if (d.D == 64) return attn_dispatch_g<bf16, 64>(d, q, k, v, w, opart, lpart, s);
+    if (d.D == 128) return attn_pipe_dispatch_g<128>(d, q, k, v, w, opart, lpart, s);
+    if (d.D == 64) return attn_pipe_dispatch_g<64>(d, q, k, v, w, opart, lpart, s);
   } else {
     if (d.D == 128) return attn_dispatch_g<float, 128>(d, q, k, v, w, opart, lpart, s);
     if (d.D == 64) return attn_dispatch_g<float, 64>(d, q, k, v, w, opart, lpart, s);
@@ -417,6 +692,7 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
                const int32_t* __restrict__ ids, T* __restrict__ out, float* __restrict__ lse,
                int64_t rows, int Hkv, int topk) {
   constexpr int C = D / 8;
+  constexpr int SMAX = 32;  // largest supported topk
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = rows * Hkv * G * C;
   if (idx >= total) return;
@@ -428,22 +704,39 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
   const int64_t row = rest / Hkv;
   const size_t e0 = (size_t)(row * Hkv + r) * topk;
   const int32_t* id = ids + e0;
+  float lsv[SMAX];
   float m = -INFINITY;
-  for (int s = 0; s < topk; ++s)
-    if (id[s] >= 0) m = fmaxf(m, lpart[(e0 + s) * G + hg]);
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    if (s < topk) {
+      lsv[s] = id[s] >= 0 ? lpart[(e0 + s) * G + hg] : -INFINITY;
+      m = fmaxf(m, lsv[s]);
+    }
+  }
   float z = 0.0f;
-  for (int s = 0; s < topk; ++s)
-    if (id[s] >= 0) z += __expf(lpart[(e0 + s) * G + hg] - m);
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s)
+    if (s < topk) z += __expf(lsv[s] - m);
   const float L = m + __logf(z);
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  for (int s = 0; s < topk; ++s) {
-    if (id[s] < 0) continue;
-    const float wgt = __expf(lpart[(e0 + s) * G + hg] - L);
-    const vec8<T> o = ld8<T>(opart + ((e0 + s) * G + hg) * D + c * 8);
+  const T* op = opart + (e0 * G + hg) * D + c * 8;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)o[e];
+  for (int s0 = 0; s0 < SMAX; s0 += 8) {
+    if (s0 >= topk) break;
+    vec8<T> o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)  // every slot of the row is in bounds; unused ones get weight 0
+      if (s0 + u < topk) o[u] = ld8<T>(op + (size_t)(s0 + u) * G * D);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < topk) {
+        const float wgt = __expf(lsv[s0 + u] - L);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wgt > 0.0f ? wgt * (float)o[u][e] : 0.0f;
+      }
+    }
   }
   vec8<T> res;
 #pragma unroll

@@ -82,7 +82,8 @@ struct Dims {
   int64_t buckets;  // B * Hkv * nb
   int64_t entries_max;  // upper bound of used slots
   int64_t items_max;    // upper bound of attention work items
-  int qt;               // queries per attention work item (128 / G)
+  int qt;               // queries per work item: 256/G (bf16 attention), else 128/G
+  int num_cus;          // compute units of the device (persistent grids)
 };
 
 // Workspace of the attention and KL calls (bucketing + partials).
@@ -105,7 +106,7 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
-                                 float* block_lse, hipStream_t s);
+                                 hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s);
 
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, hipStream_t s);

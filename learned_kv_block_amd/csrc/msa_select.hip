@@ -43,25 +43,24 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // 128 GEMM rows, contiguous in Q_idx) x a chunk of kIdxChunk key blocks.
 // Wave w owns keys [32w, 32w+32) of each 128-key block. The product is formed
 // transposed, D = K_idx_tile (keys as rows) * Q_idx_tile^T, so each lane holds
-// 16 keys of one GEMM row and the block max is an in-lane reduction plus one
-// exchange with the other lane half, then a 4-wave reduction through LDS.
-// The N x N score matrix never leaves registers; only one fp32 per
-// (row, block) is written, 8 contiguous blocks per row per workgroup.
+// 16 keys of one GEMM row and a wave's part of the block max is an in-lane
+// reduction plus one exchange with the other lane half. The four waves' parts
+// of every block of the chunk meet in LDS after a single barrier per chunk.
+// K_idx fragments of the next block are requested before the current block's
+// MFMAs. The N x N score matrix never leaves registers; one fp32 per
+// (row, block) is written.
 
 constexpr int kIdxChunk = 8;
 
-template <typename T, int DI, int HKV, bool LSE>
+template <typename T, int DI, int HKV>
 __global__ void __launch_bounds__(256, 2)
 index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
-                      float* __restrict__ M, float* __restrict__ blse, int N, int Nq,
-                      int q_start, int nb, int ntiles, float scale, float scale_log2) {
+                      float* __restrict__ M, int N, int Nq, int q_start, int nb, int ntiles,
+                      float scale) {
   constexpr int QT = 128 / HKV;
   constexpr int KS = DI / 16;
   constexpr int CB = kIdxChunk;
-  __shared__ float red_m[2][4][128];
-  __shared__ float red_l[2][4][LSE ? 128 : 1];
-  __shared__ float out_m[128][CB + 1];
-  __shared__ float out_l[LSE ? 128 : 1][CB + 1];
+  __shared__ float red_m[CB][4][128];
 
   const int tile = ntiles - 1 - (int)blockIdx.y;  // longest rows first
   const int b = blockIdx.z;
@@ -88,13 +87,22 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   }
 
   const T* kbase = k_idx + (size_t)b * N * DI + 8 * h;
-  int buf = 0;
-  for (int kb = kb0; kb <= kb1; ++kb) {
-    const int j = kb * 128 + 32 * wave + l32;
-    vec8<T> af[KS];
+  vec8<T> af[KS];
+  {
+    const int j = kb0 * 128 + 32 * wave + l32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       af[ks] = (j < N) ? ld8<T>(kbase + (size_t)j * DI + 16 * ks) : zero8<T>();
+  }
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    vec8<T> an[KS];
+    {
+      const int j = (kb + 1) * 128 + 32 * wave + l32;
+      const bool ok = kb < kb1 && j < N;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        an[ks] = ok ? ld8<T>(kbase + (size_t)j * DI + 16 * ks) : zero8<T>();
+    }
     f32x16 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -108,102 +116,69 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     for (int ct = 0; ct < 4; ++ct) {
       const int row = 32 * ct + l32;
       const int i_row = q_start + t0 + row / HKV;
-      float m = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb * 128 + 32 * wave + drow(e, h);
-        float x = acc[ct][e];
-        if (need_mask && key > i_row) x = -INFINITY;
-        acc[ct][e] = x;
-        m = fmaxf(m, x);
+        for (int e = 0; e < 16; ++e)
+          if (kb * 128 + 32 * wave + drow(e, h) > i_row) acc[ct][e] = -INFINITY;
       }
+      float m = acc[ct][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) m = fmaxf(m, acc[ct][e]);
       m = fmaxf(m, shfl_xor_f(m, 32));
-      float z = 0.0f;
-      if (LSE) {
-        if (m != -INFINITY) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) z += exp2f((acc[ct][e] - m) * scale_log2);
-        }
-        z += shfl_xor_f(z, 32);
-      }
-      if (h == 0) {
-        red_m[buf][wave][row] = m;
-        if (LSE) red_l[buf][wave][row] = z;
-      }
+      if (h == 0) red_m[kb - kb0][wave][row] = m;
     }
-    __syncthreads();
-    if (tid < 128) {
-      float m = fmaxf(fmaxf(red_m[buf][0][tid], red_m[buf][1][tid]),
-                      fmaxf(red_m[buf][2][tid], red_m[buf][3][tid]));
-      out_m[tid][kb - kb0] = m * scale;  // scale > 0 commutes with max
-      if (LSE) {
-        float z = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float mw = red_m[buf][w][tid];
-          if (mw != -INFINITY) z += red_l[buf][w][tid] * exp2f((mw - m) * scale_log2);
-        }
-        out_l[tid][kb - kb0] = m * scale + logf(z);
-      }
-    }
-    buf ^= 1;  // the next block writes the other buffer; one barrier per block suffices
+    for (int ks = 0; ks < KS; ++ks) af[ks] = an[ks];
   }
   __syncthreads();
-  if (tid < 128) {
-    const int row = tid;
+  // combine the four waves: thread = (row, block of the chunk)
+  const int nblk = kb1 - kb0 + 1;
+  for (int x = tid; x < 128 * nblk; x += 256) {
+    const int row = x % 128, kk = x / 128;
     const int tq = t0 + row / HKV;
     const int r = row % HKV;
-    if (tq < Nq) {
-      const int L_row = (q_start + tq) / 128;
-      const size_t base = ((size_t)(b * (size_t)Nq + tq) * HKV + r) * nb;
-      const int kend = min(kb1, L_row);
-      for (int kb = kb0; kb <= kend; ++kb) {
-        M[base + kb] = out_m[row][kb - kb0];
-        if (LSE) blse[base + kb] = out_l[row][kb - kb0];
-      }
-    }
+    if (tq >= Nq || kb0 + kk > (q_start + tq) / 128) continue;
+    const float m = fmaxf(fmaxf(red_m[kk][0][row], red_m[kk][1][row]),
+                          fmaxf(red_m[kk][2][row], red_m[kk][3][row]));
+    const size_t o = ((size_t)(b * (size_t)Nq + tq) * HKV + r) * nb + kb0 + kk;
+    M[o] = m * scale;  // scale > 0 commutes with max
   }
 }
 
 template <typename T, int DI, int HKV>
-static hipError_t index_dispatch_lse(const Dims& d, const void* qi, const void* ki, float* M,
-                                     float* bl, hipStream_t s) {
+static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, float* M,
+                                 hipStream_t s) {
   constexpr int QT = 128 / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
   const int nchunks = (d.nb + kIdxChunk - 1) / kIdxChunk;
   if (ntiles == 0 || d.B == 0) return hipSuccess;
   dim3 grid(nchunks, ntiles, d.B);
   const float scale = 1.0f / sqrtf((float)DI);
-  const float scale_log2 = scale * kLog2e;
-  if (bl)
-    index_blockmax_kernel<T, DI, HKV, true><<<grid, 256, 0, s>>>(
-        (const T*)qi, (const T*)ki, M, bl, d.N, d.Nq, d.q_start, d.nb, ntiles, scale, scale_log2);
-  else
-    index_blockmax_kernel<T, DI, HKV, false><<<grid, 256, 0, s>>>(
-        (const T*)qi, (const T*)ki, M, bl, d.N, d.Nq, d.q_start, d.nb, ntiles, scale, scale_log2);
+  index_blockmax_kernel<T, DI, HKV><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, M, d.N, d.Nq,
+                                                         d.q_start, d.nb, ntiles, scale);
   return hipGetLastError();
 }
 
 template <typename T, int DI>
 static hipError_t index_dispatch_hkv(const Dims& d, const void* qi, const void* ki, float* M,
-                                     float* bl, hipStream_t s) {
+                                     hipStream_t s) {
   switch (d.Hkv) {
-    case 1: return index_dispatch_lse<T, DI, 1>(d, qi, ki, M, bl, s);
-    case 2: return index_dispatch_lse<T, DI, 2>(d, qi, ki, M, bl, s);
-    case 4: return index_dispatch_lse<T, DI, 4>(d, qi, ki, M, bl, s);
-    case 8: return index_dispatch_lse<T, DI, 8>(d, qi, ki, M, bl, s);
+    case 1: return index_dispatch<T, DI, 1>(d, qi, ki, M, s);
+    case 2: return index_dispatch<T, DI, 2>(d, qi, ki, M, s);
+    case 4: return index_dispatch<T, DI, 4>(d, qi, ki, M, s);
+    case 8: return index_dispatch<T, DI, 8>(d, qi, ki, M, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
-                                 float* block_lse, hipStream_t s) {
+                                 hipStream_t s) {
   if (d.dtype == MSA_BF16) {
-    if (d.DI == 64) return index_dispatch_hkv<bf16, 64>(d, q_idx, k_idx, M, block_lse, s);
-    if (d.DI == 32) return index_dispatch_hkv<bf16, 32>(d, q_idx, k_idx, M, block_lse, s);
+    if (d.DI == 64) return index_dispatch_hkv<bf16, 64>(d, q_idx, k_idx, M, s);
+    if (d.DI == 32) return index_dispatch_hkv<bf16, 32>(d, q_idx, k_idx, M, s);
   } else {
-    if (d.DI == 64) return index_dispatch_hkv<float, 64>(d, q_idx, k_idx, M, block_lse, s);
-    if (d.DI == 32) return index_dispatch_hkv<float, 32>(d, q_idx, k_idx, M, block_lse, s);
+    if (d.DI == 64) return index_dispatch_hkv<float, 64>(d, q_idx, k_idx, M, s);
+    if (d.DI == 32) return index_dispatch_hkv<float, 32>(d, q_idx, k_idx, M, s);
   }
   return hipErrorInvalidValue;
 }
