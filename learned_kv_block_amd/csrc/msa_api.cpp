@@ -68,7 +68,8 @@ msa_status make_dims(const msa_shape* s, Dims* d) {
   d->dtype = s->dtype;
   d->rows = (int64_t)s->batch * s->seqlen_q;
   d->slots = d->rows * d->Hkv * d->K;
-  d->buckets = (int64_t)s->batch * d->Hkv * nb;
+  d->nwin = (s->seqlen_q + kQueryWindow - 1) / kQueryWindow;
+  d->buckets = (int64_t)s->batch * d->Hkv * d->nwin * nb;
   d->entries_max = d->rows * d->Hkv * (int64_t)(d->K < nb ? d->K : nb);
   d->num_cus = 0;
   set_item_size(d, 128 / G);
@@ -111,8 +112,9 @@ Layout layout(const Dims& d, int op) {
   L.items = take(d.items_max * 16);
   L.entries = take(d.entries_max * 4);
   if (op == MSA_OP_ATTN) {
-    L.opart = take((size_t)d.slots * d.G * d.D * elem_size(d));
-    L.lpart = take((size_t)d.slots * d.G * 4);
+    // one extra slot: scratch target of the attention kernel's unused rows
+    L.opart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
+    L.lpart = take((size_t)(d.slots + 1) * d.G * 4);
   } else {
     L.slot_lse = take((size_t)d.slots * 4);
     L.lse_idx = take((size_t)d.rows * d.Hkv * 4);

@@ -19,13 +19,14 @@ namespace msa {
 
 // ============================================================== bucketing (counting sort)
 //
-// bucket(b, r, blk) = (b*Hkv + r)*nb + blk; entry = (t << 6) | slot.
+// bucket(b, r, w, blk) = ((b*Hkv + r)*nwin + w)*nb + blk with w = t / kQueryWindow;
+// entry = (t << 6) | slot. A histogram workgroup's rows lie in one window.
 
 constexpr int kBucketRows = 256;  // query rows per histogram workgroup
 
 template <bool LDSH>
 __global__ void __launch_bounds__(256)
-bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb,
+bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb, int nwin,
                    int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int HB = Hkv * nb;
@@ -38,19 +39,23 @@ bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int 
   }
   const int n = (t1 - t0) * Hkv * K;
   const int32_t* base = ids + ((size_t)(b * (size_t)Nq + t0) * Hkv) * K;
-  int32_t* cb = counts + (size_t)b * HB;
+  const int w = t0 / kQueryWindow;
+  // bucket of local bin x = r*nb + blk
+  auto gbin = [&](int x) {
+    return (((size_t)b * Hkv + x / nb) * nwin + w) * nb + x % nb;
+  };
   for (int e = threadIdx.x; e < n; e += 256) {
     const int id = base[e];
     if (id >= 0 && id < nb) {
       const int r = (e / K) % Hkv;
       if (LDSH) atomicAdd(&hist[r * nb + id], 1);
-      else atomicAdd(&cb[r * nb + id], 1);
+      else atomicAdd(&counts[gbin(r * nb + id)], 1);
     }
   }
   if (LDSH) {
     __syncthreads();
     for (int x = threadIdx.x; x < HB; x += 256)
-      if (hist[x]) atomicAdd(&cb[x], hist[x]);
+      if (hist[x]) atomicAdd(&counts[gbin(x)], hist[x]);
   }
 }
 
@@ -104,7 +109,7 @@ bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
 template <bool LDSH>
 __global__ void __launch_bounds__(256)
 bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb,
-                      int32_t* __restrict__ cursor, int32_t* __restrict__ entries,
+                      int nwin, int32_t* __restrict__ cursor, int32_t* __restrict__ entries,
                       int entries_max) {
   extern __shared__ int32_t sh[];
   const int HB = Hkv * nb;
@@ -115,7 +120,10 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, i
   const int t1 = min(Nq, t0 + kBucketRows);
   const int n = (t1 - t0) * Hkv * K;
   const int32_t* idp = ids + ((size_t)(b * (size_t)Nq + t0) * Hkv) * K;
-  int32_t* cb = cursor + (size_t)b * HB;
+  const int w = t0 / kQueryWindow;
+  auto gbin = [&](int x) {
+    return (((size_t)b * Hkv + x / nb) * nwin + w) * nb + x % nb;
+  };
   if (LDSH) {
     for (int x = threadIdx.x; x < HB; x += 256) hist[x] = 0;
     __syncthreads();
@@ -126,7 +134,7 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, i
     __syncthreads();
     for (int x = threadIdx.x; x < HB; x += 256) {
       const int c = hist[x];
-      base[x] = c ? atomicAdd(&cb[x], c) : 0;
+      base[x] = c ? atomicAdd(&cursor[gbin(x)], c) : 0;
       hist[x] = 0;
     }
     __syncthreads();
@@ -135,7 +143,7 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, i
     const int id = idp[e];
     if (id >= 0 && id < nb) {
       const int bin = ((e / K) % Hkv) * nb + id;
-      const int p = LDSH ? base[bin] + atomicAdd(&hist[bin], 1) : atomicAdd(&cb[bin], 1);
+      const int p = LDSH ? base[bin] + atomicAdd(&hist[bin], 1) : atomicAdd(&cursor[gbin(bin)], 1);
       const int t = t0 + e / (Hkv * K);
       if (p < entries_max) entries[p] = (t << 6) | (e % K);  // bound holds for valid ids
     }
@@ -180,9 +188,10 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   prof_before(MSA_K_BUCKET_HIST, s);
   if (lds)
     bucket_hist_kernel<true><<<grid, 256, bucket_lds_bytes(d, 1), s>>>(ids, d.Nq, d.Hkv, d.K,
-                                                                      d.nb, w.counts);
+                                                                      d.nb, d.nwin, w.counts);
   else
-    bucket_hist_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, w.counts);
+    bucket_hist_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin,
+                                                   w.counts);
   prof_after(MSA_K_BUCKET_HIST, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_before(MSA_K_BUCKET_SCAN, s);
@@ -194,10 +203,10 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   prof_before(MSA_K_BUCKET_SCATTER, s);
   if (lds)
     bucket_scatter_kernel<true><<<grid, 256, bucket_lds_bytes(d, 2), s>>>(
-        ids, d.Nq, d.Hkv, d.K, d.nb, w.cursor, w.entries, (int)d.entries_max);
+        ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin, w.cursor, w.entries, (int)d.entries_max);
   else
-    bucket_scatter_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, w.cursor,
-                                                     w.entries, (int)d.entries_max);
+    bucket_scatter_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin,
+                                                     w.cursor, w.entries, (int)d.entries_max);
   prof_after(MSA_K_BUCKET_SCATTER, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (d.items_max > 0) {
@@ -261,7 +270,7 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
                    const int4* __restrict__ items, const int32_t* __restrict__ entries,
                    const int32_t* __restrict__ totals, T* __restrict__ opart,
                    float* __restrict__ lpart, int N, int Nq, int q_start, int Hkv, int nb,
-                   int topk, float scale_log2) {
+                   int nbw, int topk, float scale_log2) {
   constexpr bool TR = sizeof(T) == 2;  // bf16: row-major V + transposing reads
   constexpr int KSD = D / 16;          // k-steps over the head dim
   constexpr int DT = D / 32;           // 32-wide output d tiles
@@ -280,7 +289,7 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   const int4 item = items[it];
   const int bkt = item.x, start = item.y, cnt = item.z;
   const int blk = bkt % nb;
-  const int br = bkt / nb;
+  const int br = bkt / nbw;
   const int r = br % Hkv;
   const int b = br / Hkv;
   const int tid = threadIdx.x;
@@ -407,25 +416,36 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 //
 // One workgroup of 8 waves per CU, looping over a contiguous range of work
 // items of its XCD (consecutive items mostly share one K/V block). A work item
-// is 256 (query, head) rows, 32 per wave. K and V of the next item are copied
-// HBM/L2 -> LDS asynchronously (global_load_lds, 16 B per lane) into the
-// second of two LDS buffers while the current item computes, and are not
-// reloaded at all when the next item uses the same block. The next item's row
-// entries and Q fragments are also requested one item ahead.
+// is 256 (query, head) rows, 32 per wave.
+//  - K and V of a block are copied HBM/L2 -> LDS with global_load_lds (16 B per
+//    lane) only when the next item needs a different block.
+//  - The MFMA operand layouts tie a lane to one (query, head) row, so a direct
+//    load or store of Q or O would touch 32 rows per instruction. Both go
+//    through a per-wave LDS region instead: the next item's Q rows are loaded
+//    row-contiguously (1 KB per instruction) and re-read as fragments, and the
+//    output tile is written to LDS and stored row-contiguously. The memory
+//    address path, not the matrix cores, is otherwise the limit.
 // LDS tiles are row-major without padding; the 16-byte chunk c of row rho is
-// stored at chunk c ^ swz(rho) so that both the K fragment reads (8 rows, one
-// chunk) and the transposing V reads (4 rows, two chunks) hit distinct banks.
+// stored at chunk c ^ swz(rho) (patterns below).
 
 constexpr int kPipeWaves = 8;
 
+// K fragment reads touch one chunk of 16 consecutive rows; the transposing V
+// reads touch 4 chunks of 4 consecutive rows. Each tile gets its own XOR
+// pattern so that both access shapes spread over all 64 LDS banks.
 template <int D>
-__device__ __forceinline__ int swz(int rho) {
-  return D == 128 ? 2 * (rho & 7) : 2 * (rho & 3);
+__device__ __forceinline__ int swz_k(int rho) {
+  return rho & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int rho) {
+  return D == 128 ? 4 * (rho & 3) : 2 * (rho & 3);
 }
 // element offset of (row, col) in a swizzled [128][D] tile
-template <int D>
+template <int D, bool IS_V>
 __device__ __forceinline__ int tile_off(int rho, int col) {
-  return rho * D + 8 * ((col >> 3) ^ swz<D>(rho)) + (col & 7);
+  const int sw = IS_V ? swz_v<D>(rho) : swz_k<D>(rho);
+  return rho * D + 8 * ((col >> 3) ^ sw) + (col & 7);
 }
 
 template <int D, int G>
@@ -434,14 +454,18 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         const bf16* __restrict__ v, const int4* __restrict__ items,
                         const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
                         bf16* __restrict__ opart, float* __restrict__ lpart, int N, int Nq,
-                        int q_start, int Hkv, int nb, int topk, float scale_log2) {
+                        int q_start, int Hkv, int nb, int nbw, int topk, float scale_log2,
+                        size_t dummy_entry) {
   constexpr int KSD = D / 16;
   constexpr int DT = D / 32;
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int TILE = 128 * D;                   // elements per K or V tile
-  constexpr int LOADS = 128 * CPR / (64 * kPipeWaves);  // global_load_lds per wave per tile
-  __shared__ bf16 Kb[2][TILE];
-  __shared__ bf16 Vb[2][TILE];
+  constexpr int CPR = D / 8;                             // 16-byte chunks per row
+  constexpr int TILE = 128 * D;                          // elements per K or V tile
+  constexpr int LOADS = 128 * CPR / (64 * kPipeWaves);   // global_load_lds per wave per tile
+  constexpr int LDW = D + 8;                             // staging row stride (elements)
+  constexpr int RCH = 32 * CPR / 64;                     // row chunks per lane per wave tile
+  __shared__ bf16 Kb[TILE];
+  __shared__ bf16 Vb[TILE];
+  __shared__ bf16 Wst[kPipeWaves][32 * LDW];
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int total = totals[1];
@@ -458,66 +482,93 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int qi = row / G, hg = row % G;
   const int Hq = Hkv * G;
   const size_t kvrow = (size_t)Hkv * D;
+  bf16* const W = Wst[wave];
 
-  // async copy of the K and V tiles of bucket `bkt` into buffer `buf`
-  auto stage = [&](int bkt, int buf) {
-    const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+  // async copy of the K and V tiles of bucket `bkt`
+  auto stage = [&](int bkt) {
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
     const int nvalid = min(128, N - blk * 128);
     const size_t base = ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int p = (wave * LOADS + j) * 64 + lane;  // 16-byte LDS position in the tile
       const int rho = p / CPR, cs = p % CPR;
-      const int c = cs ^ swz<D>(rho);                // source chunk stored at cs
-      const size_t src = base + (size_t)min(rho, nvalid - 1) * kvrow + 8 * c;
-      lds_void* kd = (lds_void*)(&Kb[buf][(wave * LOADS + j) * 512]);
-      lds_void* vd = (lds_void*)(&Vb[buf][(wave * LOADS + j) * 512]);
-      __builtin_amdgcn_global_load_lds((const void*)(k + src), kd, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(v + src), vd, 16, 0, 0);
+      const size_t rowbase = base + (size_t)min(rho, nvalid - 1) * kvrow;
+      const size_t srck = rowbase + 8 * (cs ^ swz_k<D>(rho));
+      const size_t srcv = rowbase + 8 * (cs ^ swz_v<D>(rho));
+      __builtin_amdgcn_global_load_lds((const void*)(k + srck),
+                                       (lds_void*)(&Kb[(wave * LOADS + j) * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(v + srcv),
+                                       (lds_void*)(&Vb[(wave * LOADS + j) * 512]), 16, 0, 0);
     }
   };
-  auto load_q = [&](int b, int r, int t, bool ok, vec8<bf16>* qf) {
-    const bf16* qp = q + ((size_t)(b * (size_t)Nq + t) * Hq + r * G + hg) * D + 8 * h;
+  // Row-contiguous load of the wave's 32 Q rows of an item: lane chunk
+  // c = lane + 64*u covers row c / CPR, 16-byte chunk c % CPR. `ent_row` is
+  // the entry of this lane's MFMA row (row l32); rows are fetched by shuffle.
+  auto load_q_rows = [&](int bkt, int ent_row, vec8<bf16>* raw) {
+    const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ok ? ld8<bf16>(qp + 16 * ks) : zero8<bf16>();
+    for (int u = 0; u < RCH; ++u) {
+      const int c = lane + 64 * u;
+      const int rr = c / CPR;  // row within the wave tile
+      const int e = __shfl(ent_row, rr, 64);
+      const int rg = 32 * wave + rr;
+      raw[u] = ld8<bf16>(q + ((size_t)(b * (size_t)Nq + (e >> 6)) * Hq + r * G + rg % G) * D +
+                         8 * (c % CPR));
+    }
+  };
+  // raw rows -> staging region -> MFMA B fragments (lane row l32, k-half h)
+  auto rows_to_frags = [&](const vec8<bf16>* raw, vec8<bf16>* qf) {
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int c = lane + 64 * u;
+      st8<bf16>(W + (c / CPR) * LDW + 8 * (c % CPR), raw[u]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ld8<bf16>(W + l32 * LDW + 16 * ks + 8 * h);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
   };
 
-  // prologue: item i0 staged and its Q loaded
+  // Every load reads a clamped, in-bounds address and is issued
+  // unconditionally: rows past an item's count compute on a valid but unused
+  // query and are stored to a scratch slot.
+  const int ent_last = max(0, totals[0] - 1);
+  auto entry_of = [&](const int4& itm) { return entries[min(itm.y + qi, ent_last)]; };
+
+  // prologue: item i0 staged and its Q fragments ready. Prefetch depths:
+  // descriptors three items ahead, row entries two, Q rows one.
   int4 cur = items[i0];
-  int buf = 0;
-  stage(cur.x, buf);
-  int ent = qi < cur.z ? entries[cur.y + qi] : 0;
+  stage(cur.x);
+  int ent = entry_of(cur);
   vec8<bf16> qf[KSD];
   {
-    const int br = (cur.x / nb);
-    load_q(br / Hkv, br % Hkv, ent >> 6, qi < cur.z, qf);
+    vec8<bf16> raw[RCH];
+    load_q_rows(cur.x, ent, raw);
+    rows_to_frags(raw, qf);
   }
-  int4 nxt = i0 + 1 < i1 ? items[i0 + 1] : make_int4(-1, 0, 0, 0);
+  int4 nxt = items[min(i0 + 1, i1 - 1)];
+  int4 nxt2 = items[min(i0 + 2, i1 - 1)];
+  int ent_n = entry_of(nxt);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = i0; it < i1; ++it) {
     const int bkt = cur.x, cnt = cur.z;
-    const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
     const bool have_next = it + 1 < i1;
-    // ---- requests for the next item
-    int nbuf = buf;
-    int ent_n = 0;
-    if (have_next) {
-      if (nxt.x != bkt) {
-        nbuf = buf ^ 1;
-        stage(nxt.x, nbuf);
-      }
-      ent_n = qi < nxt.z ? entries[nxt.y + qi] : 0;
-    }
-    const int4 nxt2 = it + 2 < i1 ? items[it + 2] : make_int4(-1, 0, 0, 0);
+    // ---- requests for later items (unconditional, clamped)
+    const int ent_n2 = entry_of(nxt2);
+    const int4 nxt3 = items[min(it + 3, i1 - 1)];
+    vec8<bf16> qraw[RCH];
+    load_q_rows(nxt.x, ent_n, qraw);
 
     // ---- S^T = K Q^T for the current item
     const bool rv = qi < cnt;
     const int t = ent >> 6, slot = ent & 63;
     const int i_row = q_start + t;
-    const bf16* Kt = Kb[buf];
-    const bf16* Vt = Vb[buf];
     f32x16 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -526,13 +577,7 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const int rho = kt * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks)
-        mma(sacc[kt], ld8<bf16>(Kt + tile_off<D>(rho, 16 * ks + 8 * h)), qf[ks]);
-    }
-    // Q of the next item (its entry has arrived by now)
-    vec8<bf16> qn[KSD];
-    {
-      const int nbr = have_next ? nxt.x / nb : 0;
-      load_q(nbr / Hkv, nbr % Hkv, ent_n >> 6, have_next && qi < nxt.z, qn);
+        mma(sacc[kt], ld8<bf16>(Kb + tile_off<D, false>(rho, 16 * ks + 8 * h)), qf[ks]);
     }
     // ---- softmax over the block's 128 keys (log2 domain)
     float mx = -INFINITY;
@@ -579,9 +624,9 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int dt = 0; dt < DT; ++dt) {
         const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4*)(Vt + tile_off<D>(krow, dcol)));
+            (lds_short4*)(Vb + tile_off<D, true>(krow, dcol)));
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4*)(Vt + tile_off<D>(krow + 8, dcol)));
+            (lds_short4*)(Vb + tile_off<D, true>(krow + 8, dcol)));
         const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
         bf16x8 vf;
 #pragma unroll
@@ -592,11 +637,10 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         mma(oacc[dt], vf, pf);
       }
     }
-    // ---- partial output and its log-sum-exp
-    if (rv) {
+    // ---- partial output: O tile -> staging region -> row-contiguous stores.
+    // Rows past the item's count go to the scratch slot `dummy_entry`.
+    {
       const float inv = 1.0f / ls;
-      const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + slot;
-      bf16* op = opart + (entry * G + hg) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -604,18 +648,43 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           vec4<bf16> o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = cvt<bf16>(oacc[dt][4 * jg + e] * inv);
-          st4<bf16>(op + dt * 32 + 8 * jg + 4 * h, o);
+          st4<bf16>(W + l32 * LDW + dt * 32 + 8 * jg + 4 * h, o);
         }
       }
-      if (h == 0) lpart[entry * G + hg] = (mxs + __log2f(ls)) * kLn2;
+      const size_t my_entry =
+          rv ? ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + slot : dummy_entry;
+      lpart[my_entry * G + hg] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < RCH; ++u) {
+        const int c = lane + 64 * u;
+        const int rr = c / CPR;
+        const int e = __shfl(ent, rr, 64);
+        const int rg = 32 * wave + rr;
+        const bool ok = rg / G < cnt;
+        const size_t entry =
+            ok ? ((size_t)(b * (size_t)Nq + (e >> 6)) * Hkv + r) * topk + (e & 63) : dummy_entry;
+        st8<bf16>(opart + (entry * G + rg % G) * D + 8 * (c % CPR),
+                  ld8<bf16>(W + rr * LDW + 8 * (c % CPR)));
+      }
     }
-    // ---- advance: next item's tiles, entry and Q become current
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // ---- next item's Q fragments (the staging region is free again)
+    vec8<bf16> qn[KSD];
+    rows_to_frags(qraw, qn);
+    // ---- a new block for the next item: reload the tiles once every wave is
+    // done with the current ones (uniform: all waves see the same items).
+    if (have_next && nxt.x != bkt) {
+      __syncthreads();
+      stage(nxt.x);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
     cur = nxt;
     nxt = nxt2;
-    buf = nbuf;
+    nxt2 = nxt3;
     ent = ent_n;
+    ent_n = ent_n2;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) qf[ks] = qn[ks];
   }
@@ -630,7 +699,7 @@ static hipError_t attn_dispatch_g(const Dims& d, const void* q, const void* k, c
   case GG:                                                                                    \
     sparse_attn_kernel<T, D, GG><<<grid, 256, 0, s>>>(                                        \
         (const T*)q, (const T*)k, (const T*)v, w.items, w.entries, w.totals, (T*)opart, lpart, \
-        d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K, scale_log2);                                  \
+        d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K, scale_log2);                   \
     break;
   switch (d.G) {
     MSA_ATTN_CASE(1)
@@ -654,7 +723,8 @@ static hipError_t attn_pipe_dispatch_g(const Dims& d, const void* q, const void*
   case GG:                                                                                      \
     sparse_attn_pipe_kernel<D, GG><<<grid, 64 * kPipeWaves, 0, s>>>(                           \
         (const bf16*)q, (const bf16*)k, (const bf16*)v, w.items, w.entries, w.totals,          \
-        (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K, scale_log2);              \
+        (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K, scale_log2, \
+        (size_t)d.slots);                                                                       \
     break;
   switch (d.G) {
     MSA_PIPE_CASE(1)
@@ -686,30 +756,33 @@ hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const
 // One thread per (query row, head, 8-wide d chunk). Partials of a (query,
 // group) are contiguous: [slot][head in group][d].
 
+// One wave per (query row, group): lanes cover the G heads x D/8 chunks of
+// the group's output (G*D/8/64 chunks each, one head per lane), so every
+// partial-output load is row-contiguous and each slot id and LSE is read once
+// per wave.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
                const int32_t* __restrict__ ids, T* __restrict__ out, float* __restrict__ lse,
                int64_t rows, int Hkv, int topk) {
-  constexpr int C = D / 8;
-  constexpr int SMAX = 32;  // largest supported topk
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = rows * Hkv * G * C;
-  if (idx >= total) return;
-  const int c = (int)(idx % C);
-  int64_t rest = idx / C;
-  const int hg = (int)(rest % G);
-  rest /= G;
-  const int r = (int)(rest % Hkv);
-  const int64_t row = rest / Hkv;
-  const size_t e0 = (size_t)(row * Hkv + r) * topk;
+  constexpr int CPH = D / 8;                 // chunks per head row
+  constexpr int CPL = (G * CPH + 63) / 64;   // chunks per lane
+  constexpr int LPH = CPH / CPL > 0 ? CPH / CPL : 1;  // lanes per head
+  constexpr int SMAX = 32;
+  const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, group)
+  if (rr >= rows * Hkv) return;
+  const int lane = threadIdx.x & 63;
+  const int hg = lane / LPH;              // head of this lane
+  const int c0 = (lane % LPH) * CPL;      // first chunk of this lane
+  const bool active = hg < G;
+  const size_t e0 = (size_t)rr * topk;
   const int32_t* id = ids + e0;
   float lsv[SMAX];
   float m = -INFINITY;
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     if (s < topk) {
-      lsv[s] = id[s] >= 0 ? lpart[(e0 + s) * G + hg] : -INFINITY;
+      lsv[s] = (active && id[s] >= 0) ? lpart[(e0 + s) * G + hg] : -INFINITY;
       m = fmaxf(m, lsv[s]);
     }
   }
@@ -718,39 +791,51 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
   for (int s = 0; s < SMAX; ++s)
     if (s < topk) z += __expf(lsv[s] - m);
   const float L = m + __logf(z);
-  float acc[8];
+  float acc[CPL][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-  const T* op = opart + (e0 * G + hg) * D + c * 8;
+  for (int u = 0; u < CPL; ++u)
 #pragma unroll
-  for (int s0 = 0; s0 < SMAX; s0 += 8) {
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
+  const T* op = opart + (e0 * G + (active ? hg : 0)) * D + c0 * 8;
+#pragma unroll
+  for (int s0 = 0; s0 < SMAX; s0 += 4) {
     if (s0 >= topk) break;
-    vec8<T> o[8];
+    vec8<T> o[4][CPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)  // every slot of the row is in bounds; unused ones get weight 0
-      if (s0 + u < topk) o[u] = ld8<T>(op + (size_t)(s0 + u) * G * D);
+    for (int u = 0; u < 4; ++u)  // every slot of the row is in bounds; unused ones get weight 0
+      if (s0 + u < topk)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+        for (int c = 0; c < CPL; ++c) o[u][c] = ld8<T>(op + (size_t)(s0 + u) * G * D + 8 * c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       if (s0 + u < topk) {
         const float wgt = __expf(lsv[s0 + u] - L);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += wgt > 0.0f ? wgt * (float)o[u][e] : 0.0f;
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[c][e] += wgt > 0.0f ? wgt * (float)o[u][c][e] : 0.0f;
       }
     }
   }
-  vec8<T> res;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) res[e] = cvt<T>(acc[e]);
+  if (!active) return;
+  const int r = (int)(rr % Hkv);
+  const int64_t row = rr / Hkv;
   const int64_t hq = (int64_t)r * G + hg;
-  st8<T>(out + ((size_t)row * Hkv * G + hq) * D + c * 8, res);
-  if (c == 0) lse[row * Hkv * G + hq] = L;
+  T* dst = out + ((size_t)row * Hkv * G + hq) * D + c0 * 8;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    vec8<T> res;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) res[e] = cvt<T>(acc[c][e]);
+    st8<T>(dst + 8 * c, res);
+  }
+  if (lane % LPH == 0) lse[row * Hkv * G + hq] = L;
 }
 
 template <typename T, int D>
 static hipError_t combine_dispatch_g(const Dims& d, const void* opart, const float* lpart,
                                      const int32_t* ids, void* out, float* lse, hipStream_t s) {
-  const int64_t total = d.rows * d.Hq * (D / 8);
-  const unsigned grid = (unsigned)((total + 255) / 256);
+  const unsigned grid = (unsigned)((d.rows * d.Hkv + 3) / 4);
 #define MSA_COMB_CASE(GG)                                                                   \
   case GG:                                                                                  \
     combine_kernel<T, D, GG><<<grid, 256, 0, s>>>((const T*)opart, lpart, ids, (T*)out, lse, \

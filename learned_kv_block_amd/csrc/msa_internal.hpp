@@ -82,9 +82,15 @@ struct Dims {
   int64_t buckets;  // B * Hkv * nb
   int64_t entries_max;  // upper bound of used slots
   int64_t items_max;    // upper bound of attention work items
+  int nwin;             // query windows of kQueryWindow rows per sequence
   int qt;               // queries per work item: 256/G (bf16 attention), else 128/G
   int num_cus;          // compute units of the device (persistent grids)
 };
+
+// Work items are ordered by (batch, group, query window, block): the rows of
+// one window of kQueryWindow queries are revisited by many consecutive items
+// and stay in L2 / Infinity Cache. Bucket id = ((b*Hkv + r)*nwin + w)*nb + blk.
+constexpr int kQueryWindow = 1 << 30;  // one window: plain (batch, group, block) order
 
 // Workspace of the attention and KL calls (bucketing + partials).
 struct AttnWs {

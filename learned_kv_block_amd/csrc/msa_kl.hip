@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256)
 kl_idx_stats_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
                     const int4* __restrict__ items, const int32_t* __restrict__ entries,
                     const int32_t* __restrict__ totals, float* __restrict__ slot_lse, int N,
-                    int Nq, int q_start, int Hkv, int nb, int topk) {
+                    int Nq, int q_start, int Hkv, int nb, int nbw, int topk) {
   constexpr int QT = 128 / G;
   __shared__ float zs[QT][128 + 4];
   __shared__ int s_t[QT], s_s[QT];
@@ -78,7 +78,7 @@ kl_idx_stats_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   if ((g >> 3) >= per || it >= total) return;
   const int4 item = items[it];
   const int bkt = item.x, start = item.y, cnt = item.z;
-  const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+  const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
   const int tid = threadIdx.x;
   if (tid < QT) {
     const int e = tid < cnt ? entries[start + tid] : 0;
@@ -140,7 +140,7 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
                const float* __restrict__ lse_idx, const int4* __restrict__ items,
                const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
                float* __restrict__ kl_part, float* __restrict__ dlogits, int N, int Nq,
-               int q_start, int Hkv, int nb, int topk, float scale_log2) {
+               int q_start, int Hkv, int nb, int nbw, int topk, float scale_log2) {
   constexpr int QT = 128 / G;
   constexpr int KSD = D / 16;
   constexpr int PK = KlPad<T>::K;
@@ -159,7 +159,7 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   if ((g >> 3) >= per || it >= total) return;
   const int4 item = items[it];
   const int bkt = item.x, start = item.y, cnt = item.z;
-  const int blk = bkt % nb, br = bkt / nb, r = br % Hkv, b = br / Hkv;
+  const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
   const int tid = threadIdx.x;
   if (tid < QT) {
     const int e = tid < cnt ? entries[start + tid] : 0;
@@ -312,7 +312,7 @@ static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void
     prof_before(MSA_K_KL_IDX_STATS, s);
     kl_idx_stats_kernel<T, DI, G><<<grid, 256, 0, s>>>(
         (const T*)q_idx, (const T*)k_idx, w.items, w.entries, w.totals, slot_lse, d.N, d.Nq,
-        d.q_start, d.Hkv, d.nb, d.K);
+        d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K);
     prof_after(MSA_K_KL_IDX_STATS, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -330,8 +330,8 @@ static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void
     prof_before(MSA_K_KL_MAIN, s);
     kl_main_kernel<T, D, DI, G><<<grid, 256, 0, s>>>(
         (const T*)q, (const T*)k, (const T*)q_idx, (const T*)k_idx, lse_main, lse_idx, w.items,
-        w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.K,
-        scale_log2);
+        w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv, d.nb,
+        d.nb * d.nwin, d.K, scale_log2);
     prof_after(MSA_K_KL_MAIN, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -81,28 +81,30 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const int row = 32 * ct + l32;
     const int tq = t0 + row / HKV;
     const int r = row % HKV;
-    const T* qp = q_idx + ((size_t)(b * (size_t)Nq + tq) * HKV + r) * DI + 8 * h;
+    // rows past the last query read a valid row and are never stored
+    const T* qp = q_idx + ((size_t)(b * (size_t)Nq + min(tq, Nq - 1)) * HKV + r) * DI + 8 * h;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = (tq < Nq) ? ld8<T>(qp + 16 * ks) : zero8<T>();
+    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = ld8<T>(qp + 16 * ks);
   }
 
+  // K_idx fragments are prefetched three key blocks ahead (a block's MFMAs
+  // take far less time than an L2 or HBM round trip). Keys at or past N are
+  // read from row N-1: in bounds, and unconditional loads keep the prefetch
+  // countable for the compiler; every such key is > i for all rows and is
+  // masked below.
   const T* kbase = k_idx + (size_t)b * N * DI + 8 * h;
-  vec8<T> af[KS];
-  {
-    const int j = kb0 * 128 + 32 * wave + l32;
+  auto load_blk = [&](int kb, vec8<T>* f) {
+    const int j = min(min(kb, kb1) * 128 + 32 * wave + l32, N - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      af[ks] = (j < N) ? ld8<T>(kbase + (size_t)j * DI + 16 * ks) : zero8<T>();
-  }
+    for (int ks = 0; ks < KS; ++ks) f[ks] = ld8<T>(kbase + (size_t)j * DI + 16 * ks);
+  };
+  vec8<T> af[KS], a1[KS], a2[KS];
+  load_blk(kb0, af);
+  load_blk(kb0 + 1, a1);
+  load_blk(kb0 + 2, a2);
   for (int kb = kb0; kb <= kb1; ++kb) {
     vec8<T> an[KS];
-    {
-      const int j = (kb + 1) * 128 + 32 * wave + l32;
-      const bool ok = kb < kb1 && j < N;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        an[ks] = ok ? ld8<T>(kbase + (size_t)j * DI + 16 * ks) : zero8<T>();
-    }
+    load_blk(kb + 3, an);
     f32x16 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -128,13 +130,17 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
       if (h == 0) red_m[kb - kb0][wave][row] = m;
     }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) af[ks] = an[ks];
+    for (int ks = 0; ks < KS; ++ks) {
+      af[ks] = a1[ks];
+      a1[ks] = a2[ks];
+      a2[ks] = an[ks];
+    }
   }
   __syncthreads();
   // combine the four waves: thread = (row, block of the chunk)
   const int nblk = kb1 - kb0 + 1;
   for (int x = tid; x < 128 * nblk; x += 256) {
-    const int row = x % 128, kk = x / 128;
+    const int row = x / nblk, kk = x % nblk;  // a row's blocks are contiguous in M
     const int tq = t0 + row / HKV;
     const int r = row % HKV;
     if (tq >= Nq || kb0 + kk > (q_start + tq) / 128) continue;
