@@ -46,9 +46,14 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // 16 keys of one GEMM row and a wave's part of the block max is an in-lane
 // reduction plus one exchange with the other lane half. The four waves' parts
 // of every block of the chunk meet in LDS after a single barrier per chunk.
-// K_idx fragments of the next block are requested before the current block's
-// MFMAs. The N x N score matrix never leaves registers; one fp32 per
-// (row, block) is written.
+//  - MFMA fragments tie a lane to one row, so a direct fragment load touches
+//    32 rows per instruction. Q_idx and K_idx are instead read row-contiguously
+//    (1 KB per instruction) and re-read as fragments from LDS.
+//  - Two accumulator sets: the MFMAs of block kb+1 are in flight while the
+//    VALU runs the max epilogue of block kb; raw K_idx rows are loaded two
+//    blocks ahead.
+// The N x N score matrix never leaves registers; one fp32 per (row, block) is
+// written, a row's blocks of the chunk contiguously.
 
 constexpr int kIdxChunk = 8;
 
@@ -60,7 +65,14 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   constexpr int QT = 128 / HKV;
   constexpr int KS = DI / 16;
   constexpr int CB = kIdxChunk;
+  constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+  constexpr int CPR = DI / EPC;            // chunks per row
+  constexpr int LDQ = DI + 2 * EPC;        // staging row stride (elements), breaks bank aliasing
+  constexpr int QCH = 128 * CPR / 256;     // Q_idx chunks per thread
+  constexpr int KCH = 32 * CPR / 64;       // K_idx chunks per lane per block
   __shared__ float red_m[CB][4][128];
+  __shared__ T qs[128 * LDQ];
+  __shared__ T kst[4][32 * LDQ];
 
   const int tile = ntiles - 1 - (int)blockIdx.y;  // longest rows first
   const int b = blockIdx.z;
@@ -74,45 +86,62 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
 
-  // B operand: Q_idx^T fragments of the 128 rows, kept in registers.
+  // Q_idx tile: 128 rows (query t0 + row/HKV, group row%HKV) are contiguous.
+  // Rows past the last query read a valid row and are never stored.
+  {
+    const size_t rbase = (size_t)(b * (size_t)Nq) * HKV;
+    const size_t rmax = rbase + (size_t)Nq * HKV - 1;
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) {
+      const int c = tid + 256 * u, row = c / CPR, ch = c % CPR;
+      const size_t grow = min(rbase + (size_t)t0 * HKV + row, rmax);
+      st8<T>(&qs[row * LDQ + ch * EPC], ld8<T>(q_idx + grow * DI + ch * EPC));
+    }
+  }
+  __syncthreads();
   vec8<T> qf[4][KS];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int row = 32 * ct + l32;
-    const int tq = t0 + row / HKV;
-    const int r = row % HKV;
-    // rows past the last query read a valid row and are never stored
-    const T* qp = q_idx + ((size_t)(b * (size_t)Nq + min(tq, Nq - 1)) * HKV + r) * DI + 8 * h;
+  for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = ld8<T>(qp + 16 * ks);
-  }
+    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = ld8<T>(&qs[(32 * ct + l32) * LDQ + 16 * ks + 8 * h]);
 
-  // K_idx fragments are prefetched three key blocks ahead (a block's MFMAs
-  // take far less time than an L2 or HBM round trip). Keys at or past N are
-  // read from row N-1: in bounds, and unconditional loads keep the prefetch
-  // countable for the compiler; every such key is > i for all rows and is
-  // masked below.
-  const T* kbase = k_idx + (size_t)b * N * DI + 8 * h;
-  auto load_blk = [&](int kb, vec8<T>* f) {
-    const int j = min(min(kb, kb1) * 128 + 32 * wave + l32, N - 1);
+  // raw K_idx rows of this wave's 32 keys of block kb (keys past N read row N-1;
+  // every such key is > i for all rows and is masked)
+  const T* kb_base = k_idx + (size_t)b * N * DI;
+  T* const kw = kst[wave];
+  auto load_raw = [&](int kb, vec8<T>* raw) {
+    const int kc = min(kb, kb1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) f[ks] = ld8<T>(kbase + (size_t)j * DI + 16 * ks);
+    for (int u = 0; u < KCH; ++u) {
+      const int c = lane + 64 * u, row = c / CPR, ch = c % CPR;
+      const int j = min(kc * 128 + 32 * wave + row, N - 1);
+      raw[u] = ld8<T>(kb_base + (size_t)j * DI + ch * EPC);
+    }
   };
-  vec8<T> af[KS], a1[KS], a2[KS];
-  load_blk(kb0, af);
-  load_blk(kb0 + 1, a1);
-  load_blk(kb0 + 2, a2);
-  for (int kb = kb0; kb <= kb1; ++kb) {
-    vec8<T> an[KS];
-    load_blk(kb + 3, an);
-    f32x16 acc[4];
+  auto raw_to_frags = [&](const vec8<T>* raw, vec8<T>* f) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int c = lane + 64 * u;
+      st8<T>(&kw[(c / CPR) * LDQ + (c % CPR) * EPC], raw[u]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) f[ks] = ld8<T>(&kw[l32 * LDQ + 16 * ks + 8 * h]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto mma_blk = [&](const vec8<T>* f, f32x16* acc) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma(acc[ct], af[ks], qf[ct][ks]);
+      for (int ks = 0; ks < KS; ++ks) mma(acc[ct], f[ks], qf[ct][ks]);
     }
+  };
+  // causal mask, per-wave block max, partial result to LDS
+  auto epilogue = [&](f32x16* acc, int kb) {
     const bool need_mask = (kb * 128 + 127 > i_first);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -129,12 +158,31 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
       m = fmaxf(m, shfl_xor_f(m, 32));
       if (h == 0) red_m[kb - kb0][wave][row] = m;
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      af[ks] = a1[ks];
-      a1[ks] = a2[ks];
-      a2[ks] = an[ks];
+  };
+
+  vec8<T> raw0[KCH], raw1[KCH], f[KS];
+  f32x16 acc0[4], acc1[4];
+  load_raw(kb0, raw0);
+  load_raw(kb0 + 1, raw1);
+  raw_to_frags(raw0, f);
+  mma_blk(f, acc0);
+  load_raw(kb0 + 2, raw0);
+  for (int kb = kb0; kb <= kb1; kb += 2) {
+    // acc0: block kb; raw1: block kb+1; raw0: block kb+2 (in flight)
+    if (kb + 1 <= kb1) {
+      raw_to_frags(raw1, f);
+      load_raw(kb + 3, raw1);
+      mma_blk(f, acc1);
     }
+    epilogue(acc0, kb);
+    if (kb + 1 > kb1) break;
+    // acc1: block kb+1; raw0: block kb+2; raw1: block kb+3
+    if (kb + 2 <= kb1) {
+      raw_to_frags(raw0, f);
+      load_raw(kb + 4, raw0);
+      mma_blk(f, acc0);
+    }
+    epilogue(acc1, kb + 1);
   }
   __syncthreads();
   // combine the four waves: thread = (row, block of the chunk)
