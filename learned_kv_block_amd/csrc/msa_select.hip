@@ -39,177 +39,214 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 
 // ============================================================== index GEMM + block max
 //
-// Workgroup = one tile of QT = 128/HKV consecutive query rows (all HKV groups:
-// 128 GEMM rows, contiguous in Q_idx) x a chunk of kIdxChunk key blocks.
-// Wave w owns keys [32w, 32w+32) of each 128-key block. The product is formed
-// transposed, D = K_idx_tile (keys as rows) * Q_idx_tile^T, so each lane holds
-// 16 keys of one GEMM row and a wave's part of the block max is an in-lane
-// reduction plus one exchange with the other lane half. The four waves' parts
-// of every block of the chunk meet in LDS after a single barrier per chunk.
-//  - MFMA fragments tie a lane to one row, so a direct fragment load touches
-//    32 rows per instruction. Q_idx and K_idx are instead read row-contiguously
-//    (1 KB per instruction) and re-read as fragments from LDS.
-//  - Two accumulator sets: the MFMAs of block kb+1 are in flight while the
-//    VALU runs the max epilogue of block kb; raw K_idx rows are loaded two
-//    blocks ahead.
-// The N x N score matrix never leaves registers; one fp32 per (row, block) is
-// written, a row's blocks of the chunk contiguously.
+// Workgroup = one tile of RT = 64*NW consecutive GEMM rows (QT = RT/HKV
+// queries x all HKV groups; the rows are contiguous in Q_idx) x a chunk of CB
+// key blocks. Wave w owns GEMM rows [64w, 64w+64): its Q_idx rows stay in
+// registers as MFMA B fragments for the whole chunk. Each 128-key block of
+// K_idx is read from HBM/L2 once per workgroup, row-contiguously, and shared by
+// all NW waves through a double-buffered LDS tile (one barrier per block).
+// The product is formed transposed, D = K_idx_tile (32 keys as rows) x
+// Q_idx^T, so a lane holds 16 keys of one GEMM row and the block max is an
+// in-lane reduction over the four key tiles plus one exchange between the two
+// lane halves. Block maxima of the chunk are collected in LDS and written row
+// by row (CB contiguous floats per row) at the end: the N x N score matrix
+// never leaves registers.
+//
+// LDS tiles hold 16-byte chunks; chunk c of row r sits at position
+// c ^ swz(r) inside the row, so that the 32 rows a fragment read touches (and
+// the rows a store touches) spread over all banks.
 
-constexpr int kIdxChunk = 8;
+__device__ __forceinline__ int idx_swz(int r) { return r ^ (r >> 3); }
 
-template <typename T, int DI, int HKV>
-__global__ void __launch_bounds__(256, 2)
-index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
-                      float* __restrict__ M, int N, int Nq, int q_start, int nb, int ntiles,
-                      float scale) {
-  constexpr int QT = 128 / HKV;
-  constexpr int KS = DI / 16;
-  constexpr int CB = kIdxChunk;
-  constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
-  constexpr int CPR = DI / EPC;            // chunks per row
-  constexpr int LDQ = DI + 2 * EPC;        // staging row stride (elements), breaks bank aliasing
-  constexpr int QCH = 128 * CPR / 256;     // Q_idx chunks per thread
-  constexpr int KCH = 32 * CPR / 64;       // K_idx chunks per lane per block
-  __shared__ float red_m[CB][4][128];
-  __shared__ T qs[128 * LDQ];
-  __shared__ T kst[4][32 * LDQ];
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-  const int tile = ntiles - 1 - (int)blockIdx.y;  // longest rows first
-  const int b = blockIdx.z;
-  const int t0 = tile * QT;
-  const int t_last = min(Nq, t0 + QT) - 1;
-  const int i_first = q_start + t0;
-  const int i_last = q_start + t_last;
-  const int kb0 = (int)blockIdx.x * CB;
-  if (kb0 * 128 > i_last) return;  // whole workgroup: chunk is after every row's window
-  const int kb1 = min(kb0 + CB - 1, i_last / 128);
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
-
-  // Q_idx tile: 128 rows (query t0 + row/HKV, group row%HKV) are contiguous.
-  // Rows past the last query read a valid row and are never stored.
-  {
-    const size_t rbase = (size_t)(b * (size_t)Nq) * HKV;
-    const size_t rmax = rbase + (size_t)Nq * HKV - 1;
+template <typename T, int CPR>
+__device__ __forceinline__ vec8<T> lds_frag(const i32x4* tile, int r, int c0) {
+  constexpr int M = (CPR < 8 ? CPR : 8) - 1;
+  const i32x4* row = tile + r * CPR;
+  const int s = idx_swz(r) & M;
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8<T>, row[c0 ^ s]);
+  } else {
+    const i32x4 lo = row[c0 ^ s], hi = row[(c0 + 1) ^ s];
+    f32x8 v;
 #pragma unroll
-    for (int u = 0; u < QCH; ++u) {
-      const int c = tid + 256 * u, row = c / CPR, ch = c % CPR;
-      const size_t grow = min(rbase + (size_t)t0 * HKV + row, rmax);
-      st8<T>(&qs[row * LDQ + ch * EPC], ld8<T>(q_idx + grow * DI + ch * EPC));
+    for (int e = 0; e < 4; ++e) {
+      v[e] = __int_as_float(lo[e]);
+      v[4 + e] = __int_as_float(hi[e]);
     }
-  }
-  __syncthreads();
-  vec8<T> qf[4][KS];
-#pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = ld8<T>(&qs[(32 * ct + l32) * LDQ + 16 * ks + 8 * h]);
-
-  // raw K_idx rows of this wave's 32 keys of block kb (keys past N read row N-1;
-  // every such key is > i for all rows and is masked)
-  const T* kb_base = k_idx + (size_t)b * N * DI;
-  T* const kw = kst[wave];
-  auto load_raw = [&](int kb, vec8<T>* raw) {
-    const int kc = min(kb, kb1);
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = lane + 64 * u, row = c / CPR, ch = c % CPR;
-      const int j = min(kc * 128 + 32 * wave + row, N - 1);
-      raw[u] = ld8<T>(kb_base + (size_t)j * DI + ch * EPC);
-    }
-  };
-  auto raw_to_frags = [&](const vec8<T>* raw, vec8<T>* f) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int c = lane + 64 * u;
-      st8<T>(&kw[(c / CPR) * LDQ + (c % CPR) * EPC], raw[u]);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) f[ks] = ld8<T>(&kw[l32 * LDQ + 16 * ks + 8 * h]);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-  };
-  auto mma_blk = [&](const vec8<T>* f, f32x16* acc) {
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) mma(acc[ct], f[ks], qf[ct][ks]);
-    }
-  };
-  // causal mask, per-wave block max, partial result to LDS
-  auto epilogue = [&](f32x16* acc, int kb) {
-    const bool need_mask = (kb * 128 + 127 > i_first);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int row = 32 * ct + l32;
-      const int i_row = q_start + t0 + row / HKV;
-      if (need_mask) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (kb * 128 + 32 * wave + drow(e, h) > i_row) acc[ct][e] = -INFINITY;
-      }
-      float m = acc[ct][0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) m = fmaxf(m, acc[ct][e]);
-      m = fmaxf(m, shfl_xor_f(m, 32));
-      if (h == 0) red_m[kb - kb0][wave][row] = m;
-    }
-  };
-
-  vec8<T> raw0[KCH], raw1[KCH], f[KS];
-  f32x16 acc0[4], acc1[4];
-  load_raw(kb0, raw0);
-  load_raw(kb0 + 1, raw1);
-  raw_to_frags(raw0, f);
-  mma_blk(f, acc0);
-  load_raw(kb0 + 2, raw0);
-  for (int kb = kb0; kb <= kb1; kb += 2) {
-    // acc0: block kb; raw1: block kb+1; raw0: block kb+2 (in flight)
-    if (kb + 1 <= kb1) {
-      raw_to_frags(raw1, f);
-      load_raw(kb + 3, raw1);
-      mma_blk(f, acc1);
-    }
-    epilogue(acc0, kb);
-    if (kb + 1 > kb1) break;
-    // acc1: block kb+1; raw0: block kb+2; raw1: block kb+3
-    if (kb + 2 <= kb1) {
-      raw_to_frags(raw0, f);
-      load_raw(kb + 4, raw0);
-      mma_blk(f, acc0);
-    }
-    epilogue(acc1, kb + 1);
-  }
-  __syncthreads();
-  // combine the four waves: thread = (row, block of the chunk)
-  const int nblk = kb1 - kb0 + 1;
-  for (int x = tid; x < 128 * nblk; x += 256) {
-    const int row = x / nblk, kk = x % nblk;  // a row's blocks are contiguous in M
-    const int tq = t0 + row / HKV;
-    const int r = row % HKV;
-    if (tq >= Nq || kb0 + kk > (q_start + tq) / 128) continue;
-    const float m = fmaxf(fmaxf(red_m[kk][0][row], red_m[kk][1][row]),
-                          fmaxf(red_m[kk][2][row], red_m[kk][3][row]));
-    const size_t o = ((size_t)(b * (size_t)Nq + tq) * HKV + r) * nb + kb0 + kk;
-    M[o] = m * scale;  // scale > 0 commutes with max
+    return v;
   }
 }
+
+template <typename T, int DI, int HKV, int NW, int CB>
+__global__ void __launch_bounds__(64 * NW, sizeof(T) == 2 ? 8 / NW : 1)
+index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
+                      float* __restrict__ M, int N, int Nq, int q_start, int nb, float scale) {
+  constexpr int NT = 64 * NW;
+  constexpr int RT = 64 * NW;              // GEMM rows per tile
+  constexpr int QT = RT / HKV;             // queries per tile
+  constexpr int KS = DI / 16;
+  constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
+  constexpr int CPR = DI / EPC;            // chunks per row
+  constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;
+  constexpr int KCH = 128 * CPR / NT;      // K_idx chunks per thread per block
+  constexpr int QCH = 32 * CPR / 64;       // Q_idx chunks per lane per 32-row half
+  constexpr int MST = CB + 1;              // block-max row stride (floats)
+  constexpr int QBYTES = NW * 32 * CPR * 16;
+  constexpr int MBYTES = RT * MST * 4;
+  constexpr int UBYTES = QBYTES > MBYTES ? QBYTES : MBYTES;
+  static_assert((128 * CPR) % NT == 0 && (32 * CPR) % 64 == 0, "tile shape");
+  __shared__ __attribute__((aligned(16))) char ubuf[UBYTES];  // Q_idx staging, then block maxima
+  __shared__ i32x4 kbuf[2][128 * CPR];
+
+  const int tile = blockIdx.x;
+  const int b = blockIdx.z;
+  const int t0 = tile * QT;
+  if (t0 >= Nq) return;
+  const int t_last = min(Nq, t0 + QT) - 1;
+  const int i_last = q_start + t_last;
+  const int kb0 = (int)blockIdx.y * CB;
+  if (kb0 * 128 > i_last) return;  // whole workgroup: chunk is after every row's window
+  const int kb1 = min(kb0 + CB - 1, i_last >> 7);
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // raw K_idx chunks of block kb (keys past N read row N-1; every such key is
+  // > i for all rows and is masked)
+  const char* kbase = reinterpret_cast<const char*>(k_idx + (size_t)b * N * DI);
+  i32x4 raw[KCH];
+  auto load_raw = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int q = tid + NT * u, r = q / CPR, c = q % CPR;
+      const int j = min(kb * 128 + r, N - 1);
+      raw[u] = *reinterpret_cast<const i32x4*>(kbase + ((size_t)j * CPR + c) * 16);
+    }
+  };
+  auto store_raw = [&](i32x4* dst) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int q = tid + NT * u, r = q / CPR, c = q % CPR;
+      dst[r * CPR + (c ^ (idx_swz(r) & SWM))] = raw[u];
+    }
+  };
+  load_raw(kb0);
+
+  // Q_idx: the wave's 64 rows, in two halves of 32 rows staged through LDS.
+  // Rows past the last query read a valid row and are never stored.
+  vec8<T> qf[2][KS];
+  {
+    i32x4* qs = reinterpret_cast<i32x4*>(ubuf) + wave * 32 * CPR;
+    const char* qbase = reinterpret_cast<const char*>(q_idx);
+    const size_t rbase = (size_t)b * Nq * HKV;
+    const size_t rmax = rbase + (size_t)Nq * HKV - 1;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int u = 0; u < QCH; ++u) {
+        const int q = lane + 64 * u, r = q / CPR, c = q % CPR;
+        const size_t grow = min(rbase + (size_t)t0 * HKV + wave * 64 + 32 * ct + r, rmax);
+        qs[r * CPR + (c ^ (idx_swz(r) & SWM))] =
+            *reinterpret_cast<const i32x4*>(qbase + (grow * CPR + c) * 16);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = lds_frag<T, CPR>(qs, l32, (16 * ks + 8 * h) / EPC);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  store_raw(kbuf[0]);
+  if (kb0 + 1 <= kb1) load_raw(kb0 + 1);
+  __syncthreads();  // block kb0 is in LDS; every wave has its Q fragments
+
+  float* mbuf = reinterpret_cast<float*>(ubuf);
+  const int row0 = wave * 64;  // first GEMM row of the wave
+  int i_row[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
+  const int i_wave_first = q_start + t0 + row0 / HKV;
+
+  for (int kb = kb0; kb <= kb1; ++kb) {
+    const int cur = (kb - kb0) & 1;
+    if (kb + 1 <= kb1) {
+      store_raw(kbuf[cur ^ 1]);  // last read in the previous iteration, before its barrier
+      if (kb + 2 <= kb1) load_raw(kb + 2);
+    }
+    const i32x4* kt_lds = kbuf[cur];
+    const bool need_mask = (kb * 128 + 127 > i_wave_first);
+    float m[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      vec8<T> af[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(kt_lds, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
+      f32x16 acc[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        if (need_mask) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (kb * 128 + 32 * kt + drow(e, h) > i_row[ct]) acc[ct][e] = -INFINITY;
+        }
+        float x = m[ct];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) x = fmaxf(x, fmaxf(acc[ct][e], acc[ct][e + 1]));
+        m[ct] = x;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const float x = fmaxf(m[ct], shfl_xor_f(m[ct], 32));
+      if (h == 0) mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0)] = x;
+    }
+    __syncthreads();  // next block is in LDS; this block's tile may be overwritten
+  }
+
+  // write the chunk's block maxima, CB contiguous floats per row
+  const int nblk = kb1 - kb0 + 1;
+  const size_t grow0 = ((size_t)b * Nq + t0) * HKV;
+  for (int x = tid; x < RT * nblk; x += NT) {
+    const int row = x / nblk, kk = x - row * nblk;
+    const int tq = t0 + row / HKV;
+    if (tq >= Nq || kb0 + kk > ((q_start + tq) >> 7)) continue;
+    M[(grow0 + row) * nb + kb0 + kk] = mbuf[row * MST + kk] * scale;  // scale > 0 commutes with max
+  }
+}
+
+#ifndef MSA_IDX_NW
+#define MSA_IDX_NW 8
+#endif
+#ifndef MSA_IDX_CB
+#define MSA_IDX_CB 32
+#endif
 
 template <typename T, int DI, int HKV>
 static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, float* M,
                                  hipStream_t s) {
-  constexpr int QT = 128 / HKV;
+  constexpr int NW = sizeof(T) == 4 ? 4 : MSA_IDX_NW;  // fp32 tiles: LDS and register limits
+  constexpr int CB = MSA_IDX_CB;
+  constexpr int QT = 64 * NW / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
-  const int nchunks = (d.nb + kIdxChunk - 1) / kIdxChunk;
+  const int nchunks = (d.nb + CB - 1) / CB;
   if (ntiles == 0 || d.B == 0) return hipSuccess;
-  dim3 grid(nchunks, ntiles, d.B);
+  dim3 grid(ntiles, nchunks, d.B);
   const float scale = 1.0f / sqrtf((float)DI);
-  index_blockmax_kernel<T, DI, HKV><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, M, d.N, d.Nq,
-                                                         d.q_start, d.nb, ntiles, scale);
+  index_blockmax_kernel<T, DI, HKV, NW, CB><<<grid, 64 * NW, 0, s>>>(
+      (const T*)qi, (const T*)ki, M, d.N, d.Nq, d.q_start, d.nb, scale);
   return hipGetLastError();
 }
 
