@@ -76,7 +76,8 @@ msa_status make_dims(const msa_shape* s, Dims* d) {
   // index ranges the kernels keep in 32-bit integers
   if (d->entries_max >= (int64_t)1 << 31 || d->buckets >= (int64_t)1 << 30 ||
       d->items_max >= (int64_t)1 << 30 || s->seqlen_q >= (1 << 25) ||
-      (int64_t)s->batch * s->seqlen_q >= (int64_t)1 << 31)
+      (int64_t)s->batch * s->seqlen_q >= (int64_t)1 << 31 || d->slots + 1 >= (int64_t)1 << 31 ||
+      d->rows * s->num_q_heads >= (int64_t)1 << 31)
     return MSA_ERR_UNSUPPORTED;
   if (((d->Nq + 127) / 128 > 65535) || s->batch > 65535) return MSA_ERR_UNSUPPORTED;
   return MSA_OK;

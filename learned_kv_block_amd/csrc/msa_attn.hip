@@ -477,12 +477,21 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
   if (i0 >= i1) return;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = 32 * wave + l32;
   const int qi = row / G, hg = row % G;
   const int Hq = Hkv * G;
   const size_t kvrow = (size_t)Hkv * D;
   bf16* const W = Wst[wave];
+  // One 1 KB row-contiguous access covers RPI rows. With G >= RPI they belong
+  // to one query, so their addresses are a wave-uniform base plus a
+  // lane-constant offset; the entries of the wave's QPW queries are read as
+  // scalars.
+  constexpr int RPI = 64 / CPR;
+  constexpr bool kUniformRows = G >= RPI;
+  constexpr int QPW = kUniformRows ? 32 / G : 1;  // queries per wave
+  const int qw0 = (32 * wave) / G;                // first query of the wave in an item
 
   // async copy of the K and V tiles of bucket `bkt`
   auto stage = [&](int bkt) {
@@ -505,8 +514,21 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // Row-contiguous load of the wave's 32 Q rows of an item: lane chunk
   // c = lane + 64*u covers row c / CPR, 16-byte chunk c % CPR. `ent_row` is
   // the entry of this lane's MFMA row (row l32); rows are fetched by shuffle.
-  auto load_q_rows = [&](int bkt, int ent_row, vec8<bf16>* raw) {
+  auto load_q_rows = [&](int bkt, int ent_row, const int* es, vec8<bf16>* raw) {
     const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    if constexpr (kUniformRows) {
+      // Q row of (query j of the wave, head 0 of group r); < 2^31 (checked by the caller)
+      int qrow[QPW];
+#pragma unroll
+      for (int j = 0; j < QPW; ++j) qrow[j] = ((b * Nq + (es[j] >> 6)) * Hkv + r) * G;
+#pragma unroll
+      for (int u = 0; u < RCH; ++u) {
+        const int j = (RPI * u) / G, hd = (RPI * u) % G;  // 32*wave is a multiple of G
+        const bf16* base = q + (size_t)(uint32_t)qrow[j] * D + hd * D;
+        raw[u] = ld8<bf16>(base + (lane / CPR) * D + 8 * (lane % CPR));
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < RCH; ++u) {
       const int c = lane + 64 * u;
@@ -537,21 +559,30 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // query and are stored to a scratch slot.
   const int ent_last = max(0, totals[0] - 1);
   auto entry_of = [&](const int4& itm) { return entries[min(itm.y + qi, ent_last)]; };
+  // entries of the wave's queries of an item (uniform loads)
+  auto wave_entries = [&](const int4& itm, int* es) {
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) es[j] = entries[min(itm.y + qw0 + j, ent_last)];
+  };
 
   // prologue: item i0 staged and its Q fragments ready. Prefetch depths:
   // descriptors three items ahead, row entries two, Q rows one.
   int4 cur = items[i0];
   stage(cur.x);
   int ent = entry_of(cur);
+  int es[QPW];
+  wave_entries(cur, es);
   vec8<bf16> qf[KSD];
   {
     vec8<bf16> raw[RCH];
-    load_q_rows(cur.x, ent, raw);
+    load_q_rows(cur.x, ent, es, raw);
     rows_to_frags(raw, qf);
   }
   int4 nxt = items[min(i0 + 1, i1 - 1)];
   int4 nxt2 = items[min(i0 + 2, i1 - 1)];
   int ent_n = entry_of(nxt);
+  int es_n[QPW];
+  wave_entries(nxt, es_n);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -561,9 +592,11 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bool have_next = it + 1 < i1;
     // ---- requests for later items (unconditional, clamped)
     const int ent_n2 = entry_of(nxt2);
+    int es_n2[QPW];
+    wave_entries(nxt2, es_n2);
     const int4 nxt3 = items[min(it + 3, i1 - 1)];
     vec8<bf16> qraw[RCH];
-    load_q_rows(nxt.x, ent_n, qraw);
+    load_q_rows(nxt.x, ent_n, es_n, qraw);
 
     // ---- S^T = K Q^T for the current item
     const bool rv = qi < cnt;
@@ -592,8 +625,8 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kt][e]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      for (int e = 0; e < 16; e += 2) mx = vmax(vmax(mx, sacc[kt][e]), sacc[kt][e + 1]);
+    mx = vmax(mx, shfl_xor_f(mx, 32));
     const float mxs = mx * scale_log2;
     float ls = 0.0f;
 #pragma unroll
@@ -656,17 +689,33 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       lpart[my_entry * G + hg] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
+      if constexpr (kUniformRows) {
+        // slot of query j of the wave (the scratch slot past the item's count); < 2^31
+        int oslot[QPW];
 #pragma unroll
-      for (int u = 0; u < RCH; ++u) {
-        const int c = lane + 64 * u;
-        const int rr = c / CPR;
-        const int e = __shfl(ent, rr, 64);
-        const int rg = 32 * wave + rr;
-        const bool ok = rg / G < cnt;
-        const size_t entry =
-            ok ? ((size_t)(b * (size_t)Nq + (e >> 6)) * Hkv + r) * topk + (e & 63) : dummy_entry;
-        st8<bf16>(opart + (entry * G + rg % G) * D + 8 * (c % CPR),
-                  ld8<bf16>(W + rr * LDW + 8 * (c % CPR)));
+        for (int j = 0; j < QPW; ++j)
+          oslot[j] = qw0 + j < cnt ? ((b * Nq + (es[j] >> 6)) * Hkv + r) * topk + (es[j] & 63)
+                                   : (int)dummy_entry;
+#pragma unroll
+        for (int u = 0; u < RCH; ++u) {
+          const int j = (RPI * u) / G, hd = (RPI * u) % G;  // 32*wave is a multiple of G
+          bf16* base = opart + (size_t)(uint32_t)oslot[j] * (G * D) + hd * D;
+          st8<bf16>(base + (lane / CPR) * D + 8 * (lane % CPR),
+                    ld8<bf16>(W + (RPI * u + lane / CPR) * LDW + 8 * (lane % CPR)));
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < RCH; ++u) {
+          const int c = lane + 64 * u;
+          const int rr = c / CPR;
+          const int e = __shfl(ent, rr, 64);
+          const int rg = 32 * wave + rr;
+          const bool ok = rg / G < cnt;
+          const size_t entry =
+              ok ? ((size_t)(b * (size_t)Nq + (e >> 6)) * Hkv + r) * topk + (e & 63) : dummy_entry;
+          st8<bf16>(opart + (entry * G + rg % G) * D + 8 * (c % CPR),
+                    ld8<bf16>(W + rr * LDW + 8 * (c % CPR)));
+        }
       }
     }
     // ---- next item's Q fragments (the staging region is free again)
@@ -685,6 +734,11 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     nxt2 = nxt3;
     ent = ent_n;
     ent_n = ent_n2;
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      es[j] = es_n[j];
+      es_n[j] = es_n2[j];
+    }
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) qf[ks] = qn[ks];
   }

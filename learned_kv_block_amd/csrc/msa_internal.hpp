@@ -70,6 +70,10 @@ __device__ __forceinline__ constexpr int drow(int e, int h) { return 8 * (e / 4)
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// NaN-propagating maximum. Unlike fmaxf it needs no quieting of its operands,
+// and chains m = vmax(vmax(m, a), b) become one v_maximum3_f32 per two inputs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 

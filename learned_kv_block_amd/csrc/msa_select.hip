@@ -204,13 +204,13 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
         }
         float x = m[ct];
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) x = fmaxf(x, fmaxf(acc[ct][e], acc[ct][e + 1]));
+        for (int e = 0; e < 16; e += 2) x = vmax(vmax(x, acc[ct][e]), acc[ct][e + 1]);
         m[ct] = x;
       }
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float x = fmaxf(m[ct], shfl_xor_f(m[ct], 32));
+      const float x = vmax(m[ct], shfl_xor_f(m[ct], 32));
       if (h == 0) mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0)] = x;
     }
     __syncthreads();  // next block is in LDS; this block's tile may be overwritten
