@@ -6,6 +6,8 @@
 // j <= i of 128-token block b, then Top-k blocks with the query's local block
 // always included. "MiniMax Sparse Attention：教长上下文模型使用索引" (MSA blog),
 // kernel section: the Top-k runs on raw scores (softmax keeps the order).
+#include <type_traits>
+
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -92,7 +94,7 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;
   constexpr int KCH = 128 * CPR / NT;      // K_idx chunks per thread per block
   constexpr int QCH = 32 * CPR / 64;       // Q_idx chunks per lane per 32-row half
-  constexpr int MST = CB + 1;              // block-max row stride (floats)
+  constexpr int MST = CB + 1;              // block-max row stride (floats): empty column + CB
   constexpr int QBYTES = NW * 32 * CPR * 16;
   constexpr int MBYTES = RT * MST * 4;
   constexpr int UBYTES = QBYTES > MBYTES ? QBYTES : MBYTES;
@@ -168,53 +170,86 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   int i_row[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
-  const int i_wave_first = q_start + t0 + row0 / HKV;
 
-  for (int kb = kb0; kb <= kb1; ++kb) {
+  // One key tile (32 keys) of the block: D^T tiles for the wave's two row tiles.
+  auto mma_tile = [&](const i32x4* tile, int kt, f32x16* acc) {
+    vec8<T> af[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(tile, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
+    }
+  };
+  // causal mask (MASK) and running in-lane block max of one key tile
+  auto reduce_tile = [&](auto masked, f32x16* acc, float* m, int kb, int kt) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 128 + 32 * kt + drow(e, h) > i_row[ct]) acc[ct][e] = -INFINITY;
+      }
+      float x = m[ct];
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) x = vmax(vmax(x, acc[ct][e]), acc[ct][e + 1]);
+      m[ct] = x;
+    }
+  };
+  // block kb's maxima -> LDS column kb - kb0 + 1 (column 0 takes the empty
+  // block before kb0); both lane halves hold the value and store it
+  auto finish_block = [&](float* m, int kb) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const float x = vmax(m[ct], shfl_xor_f(m[ct], 32));
+      mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0 + 1)] = x;
+    }
+  };
+
+  // Software pipeline: the MFMAs of key tile kt+1 are issued before the VALU
+  // reduces tile kt; tile 3 of a block is reduced under tile 0 of the next.
+  // The body is branch-free so that the two streams can interleave; blocks
+  // that need the causal mask (the tile's last one or two) run in a second loop.
+  f32x16 accA[2], accB[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accB[ct][e] = -INFINITY;
+  }
+  float m[2] = {-INFINITY, -INFINITY};
+  auto block_body = [&](auto masked, int kb) {
     const int cur = (kb - kb0) & 1;
     if (kb + 1 <= kb1) {
       store_raw(kbuf[cur ^ 1]);  // last read in the previous iteration, before its barrier
       if (kb + 2 <= kb1) load_raw(kb + 2);
     }
     const i32x4* kt_lds = kbuf[cur];
-    const bool need_mask = (kb * 128 + 127 > i_wave_first);
-    float m[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      vec8<T> af[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(kt_lds, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
-      f32x16 acc[2];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
-      }
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        if (need_mask) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            if (kb * 128 + 32 * kt + drow(e, h) > i_row[ct]) acc[ct][e] = -INFINITY;
-        }
-        float x = m[ct];
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) x = vmax(vmax(x, acc[ct][e]), acc[ct][e + 1]);
-        m[ct] = x;
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const float x = vmax(m[ct], shfl_xor_f(m[ct], 32));
-      if (h == 0) mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0)] = x;
-    }
+    mma_tile(kt_lds, 0, accA);
+    reduce_tile(masked, accB, m, kb - 1, 3);
+    finish_block(m, kb - 1);
+    m[0] = m[1] = -INFINITY;
+    mma_tile(kt_lds, 1, accB);
+    reduce_tile(masked, accA, m, kb, 0);
+    mma_tile(kt_lds, 2, accA);
+    reduce_tile(masked, accB, m, kb, 1);
+    mma_tile(kt_lds, 3, accB);
+    reduce_tile(masked, accA, m, kb, 2);
     __syncthreads();  // next block is in LDS; this block's tile may be overwritten
-  }
+  };
+  // first block with a key after the tile's first query
+  const int kb_mask = min(max(kb0, (q_start + t0 + 1) >> 7), kb1 + 1);
+  int kb = kb0;
+  for (; kb < kb_mask; ++kb) block_body(std::false_type(), kb);
+  for (; kb <= kb1; ++kb) block_body(std::true_type(), kb);
+  reduce_tile(std::true_type(), accB, m, kb1, 3);
+  finish_block(m, kb1);
+  __syncthreads();
 
   // write the chunk's block maxima, CB contiguous floats per row
   const int nblk = kb1 - kb0 + 1;
@@ -223,7 +258,7 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const int row = x / nblk, kk = x - row * nblk;
     const int tq = t0 + row / HKV;
     if (tq >= Nq || kb0 + kk > ((q_start + tq) >> 7)) continue;
-    M[(grow0 + row) * nb + kb0 + kk] = mbuf[row * MST + kk] * scale;  // scale > 0 commutes with max
+    M[(grow0 + row) * nb + kb0 + kk] = mbuf[row * MST + kk + 1] * scale;  // scale > 0 commutes with max
   }
 }
 
