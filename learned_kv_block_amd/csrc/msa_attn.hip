@@ -428,6 +428,15 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 // LDS tiles are row-major without padding; the 16-byte chunk c of row rho is
 // stored at chunk c ^ swz(rho) (patterns below).
 
+// Partials are written once and read once, long after: stream them past the
+// caches (non-temporal stores in the attention kernel, loads in the combine).
+#ifndef MSA_NT_LOAD
+#define MSA_NT_LOAD 1
+#endif
+#ifndef MSA_NT_STORE
+#define MSA_NT_STORE 1
+#endif
+
 constexpr int kPipeWaves = 8;
 
 // K fragment reads touch one chunk of 16 consecutive rows; the transposing V
@@ -700,8 +709,13 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int u = 0; u < RCH; ++u) {
           const int j = (RPI * u) / G, hd = (RPI * u) % G;  // 32*wave is a multiple of G
           bf16* base = opart + (size_t)(uint32_t)oslot[j] * (G * D) + hd * D;
+#if MSA_NT_STORE
+          st8_nt<bf16>(base + (lane / CPR) * D + 8 * (lane % CPR),
+                       ld8<bf16>(W + (RPI * u + lane / CPR) * LDW + 8 * (lane % CPR)));
+#else
           st8<bf16>(base + (lane / CPR) * D + 8 * (lane % CPR),
                     ld8<bf16>(W + (RPI * u + lane / CPR) * LDW + 8 * (lane % CPR)));
+#endif
         }
       } else {
 #pragma unroll
@@ -807,37 +821,43 @@ hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const
 
 // ============================================================== LSE combine
 //
-// One thread per (query row, head, 8-wide d chunk). Partials of a (query,
-// group) are contiguous: [slot][head in group][d].
-
-// One wave per (query row, group): lanes cover the G heads x D/8 chunks of
-// the group's output (G*D/8/64 chunks each, one head per lane), so every
-// partial-output load is row-contiguous and each slot id and LSE is read once
-// per wave.
+// One wave per (query row, group). The partials of a (query, group) are
+// contiguous, [slot][head in group][d], and so is the group's output row.
+//  1. Lane-per-head layout (64/G lanes per head): each lane reads the slot
+//     LSEs of its head, forms L = log sum_s exp(lse_s) and the merge weights
+//     w_s = exp(lse_s - L), and one lane per head stores them in a per-wave
+//     LDS table [head][slot].
+//  2. Lane unit u = lane + 64c (8 elements) of a slot block: every load and
+//     the output store move 64 consecutive units (1 KB in bf16) per
+//     instruction. Slots without a block (id < 0) are skipped by a
+//     wave-uniform branch, so their (never written) partials are not used.
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
                const int32_t* __restrict__ ids, T* __restrict__ out, float* __restrict__ lse,
                int64_t rows, int Hkv, int topk) {
-  constexpr int CPH = D / 8;                 // chunks per head row
-  constexpr int CPL = (G * CPH + 63) / 64;   // chunks per lane
-  constexpr int LPH = CPH / CPL > 0 ? CPH / CPL : 1;  // lanes per head
+  constexpr int UPH = D / 8;            // units per head row
+  constexpr int UPS = G * UPH;          // units per slot block
+  constexpr int NCH = (UPS + 63) / 64;  // units per lane
+  constexpr int LPH = 64 / G;           // lanes per head in the weight phase
   constexpr int SMAX = 32;
-  const int64_t rr = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, group)
+  __shared__ float wt[4][G][SMAX + 1];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t rr = (int64_t)blockIdx.x * 4 + wave;  // (row, group), uniform
   if (rr >= rows * Hkv) return;
   const int lane = threadIdx.x & 63;
-  const int hg = lane / LPH;              // head of this lane
-  const int c0 = (lane % LPH) * CPL;      // first chunk of this lane
-  const bool active = hg < G;
   const size_t e0 = (size_t)rr * topk;
   const int32_t* id = ids + e0;
+
+  // 1. weights
+  const int hg = lane / LPH;
   float lsv[SMAX];
   float m = -INFINITY;
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     if (s < topk) {
-      lsv[s] = (active && id[s] >= 0) ? lpart[(e0 + s) * G + hg] : -INFINITY;
-      m = fmaxf(m, lsv[s]);
+      lsv[s] = id[s] >= 0 ? lpart[(e0 + s) * G + hg] : -INFINITY;
+      m = vmax(m, lsv[s]);
     }
   }
   float z = 0.0f;
@@ -845,45 +865,68 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
   for (int s = 0; s < SMAX; ++s)
     if (s < topk) z += __expf(lsv[s] - m);
   const float L = m + __logf(z);
-  float acc[CPL][8];
+  if (lane % LPH == 0) {
 #pragma unroll
-  for (int u = 0; u < CPL; ++u)
+    for (int s = 0; s < SMAX; ++s)
+      if (s < topk) wt[wave][hg][s] = __expf(lsv[s] - L);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is written
+  __builtin_amdgcn_wave_barrier();
+
+  // 2. weighted sum of the slot blocks
+  float acc[NCH][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-  const T* op = opart + (e0 * G + (active ? hg : 0)) * D + c0 * 8;
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
-  for (int s0 = 0; s0 < SMAX; s0 += 4) {
-    if (s0 >= topk) break;
-    vec8<T> o[4][CPL];
+    for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
+  const T* op = opart + e0 * (size_t)(G * D);
+  bool ok[NCH];
+  int hd[NCH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)  // every slot of the row is in bounds; unused ones get weight 0
-      if (s0 + u < topk)
+  for (int c = 0; c < NCH; ++c) {
+    const int u = lane + 64 * c;
+    ok[c] = UPS % 64 == 0 || u < UPS;
+    hd[c] = ok[c] ? u / UPH : 0;
+  }
+  for (int s0 = 0; s0 < topk; s0 += 4) {
+    vec8<T> o[4][NCH];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) o[u][c] = ld8<T>(op + (size_t)(s0 + u) * G * D + 8 * c);
+    for (int j = 0; j < 4; ++j) {
+      const int sl = min(s0 + j, topk - 1);  // in bounds; repeats are skipped below
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (s0 + u < topk) {
-        const float wgt = __expf(lsv[s0 + u] - L);
+      for (int c = 0; c < NCH; ++c)
+        if (ok[c]) {
+#if MSA_NT_LOAD
+          o[j][c] = ld8_nt<T>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
+#else
+          o[j][c] = ld8<T>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
+#endif
+        }
+    }
 #pragma unroll
-        for (int c = 0; c < CPL; ++c)
+    for (int j = 0; j < 4; ++j) {
+      if (s0 + j >= topk || id[s0 + j] < 0) continue;  // uniform
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[c][e] += wgt > 0.0f ? wgt * (float)o[u][c][e] : 0.0f;
+      for (int c = 0; c < NCH; ++c) {
+        if (!ok[c]) continue;
+        const float w = wt[wave][hd[c]][s0 + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)o[j][c][e];
       }
     }
   }
-  if (!active) return;
   const int r = (int)(rr % Hkv);
   const int64_t row = rr / Hkv;
-  const int64_t hq = (int64_t)r * G + hg;
-  T* dst = out + ((size_t)row * Hkv * G + hq) * D + c0 * 8;
+  T* dst = out + ((size_t)row * Hkv + r) * (size_t)(G * D);
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
+  for (int c = 0; c < NCH; ++c) {
+    if (!ok[c]) continue;
     vec8<T> res;
 #pragma unroll
     for (int e = 0; e < 8; ++e) res[e] = cvt<T>(acc[c][e]);
-    st8<T>(dst + 8 * c, res);
+    st8<T>(dst + 8 * (lane + 64 * c), res);
   }
-  if (lane % LPH == 0) lse[row * Hkv * G + hq] = L;
+  if (lane % LPH == 0) lse[((size_t)row * Hkv + r) * G + hg] = L;
 }
 
 template <typename T, int D>

@@ -57,6 +57,13 @@ template <typename T> __device__ __forceinline__ vec8<T> ld8(const T* p) {
 template <typename T> __device__ __forceinline__ void st8(T* p, const vec8<T>& v) {
   *reinterpret_cast<vec8<T>*>(p) = v;
 }
+// Streaming (non-temporal) access for data touched once.
+template <typename T> __device__ __forceinline__ vec8<T> ld8_nt(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const vec8<T>*>(p));
+}
+template <typename T> __device__ __forceinline__ void st8_nt(T* p, const vec8<T>& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<vec8<T>*>(p));
+}
 template <typename T> __device__ __forceinline__ vec4<T> ld4(const T* p) {
   return *reinterpret_cast<const vec4<T>*>(p);
 }
