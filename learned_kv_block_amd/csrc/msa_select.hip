@@ -314,10 +314,13 @@ hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k
 // One wavefront per (b, t, r) row of block scores M[0..L], L = local block.
 // Keys are 64-bit: (order-preserving bits of the score) << 32 | ~block, so a
 // larger key means a higher score, or an equal score and a lower block index;
-// every key is distinct. Lane l owns blocks v*64 + l (coalesced loads).
-//  1. T = the (k-1)-th largest per-lane maximum score (bitonic sort of the 64
-//     lane maxima). Every block of the true top-(k-1) scores >= T, and at
-//     least k-1 blocks do, so the blocks with score >= T are the candidates.
+// every key is distinct. Lane l owns blocks v*64 + l; the scores are read with
+// buffer loads whose range ends at block L, so blocks past it need no branch.
+//  1. T = the (k-1)-th largest per-lane maximum score, found by bisection on
+//     its order-preserving bits (one ballot per bit, stopping as soon as
+//     exactly k-1 lane maxima are >= T). Every block of the true top-(k-1)
+//     scores >= T, and at least k-1 blocks do, so the blocks with score >= T
+//     are the candidates.
 //  2. Candidates are compacted into LDS in (v, lane) order = ascending block.
 //  3. Each candidate's exact rank among candidates gives the selection; the
 //     selected ones keep their ascending order; the local block L (the
@@ -357,15 +360,16 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 constexpr int kTopkMax = 32;
+constexpr int kCandMax = 128;  // candidates ranked exactly (two passes of 64)
 
 template <int V>
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int Hkv, int nb,
             int k, int32_t* __restrict__ ids, float* __restrict__ margin) {
-  constexpr int CMAX = (kTopkMax - 1) * V;
-  __shared__ uint64_t cand[4][CMAX];
+  __shared__ uint64_t cand[4][kCandMax + 1];  // + a sink for non-candidate lanes
   __shared__ uint64_t msel[4][2];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= nrows) return;  // wave-uniform; the kernel has no workgroup barrier
   const int t = (int)((row / Hkv) % Nq);
@@ -377,52 +381,49 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
     if (margin && lane == 0) margin[row] = INFINITY;
     return;
   }
-  const float* mr = M + row * (int64_t)nb;
-  uint64_t key[V];
-  uint32_t lmax = 0;
+  // scores of the candidate blocks 0..L-1; loads past block L-1 return 0
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(M + row * (int64_t)nb), 0, L * 4, 0x00020000);
+  float x[V];
+  float lm = -INFINITY;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int blk = v * 64 + lane;
-    if (blk < L) {
-      const float sc = mr[blk];
-      key[v] = make_key(sc, blk);
-      lmax = max(lmax, ord_f32(sc));
-    } else {
-      key[v] = 0;  // not a candidate (every real key is > 0)
+    const float raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (v * 64 + lane) * 4, 0, 0));
+    x[v] = v * 64 + lane < L ? raw : -INFINITY;
+    lm = vmax(lm, x[v]);
+  }
+  // 1. threshold: bisection on the order-preserving bits of the lane maxima
+  const uint32_t om = ord_f32(lm);
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t tt = T | (1u << bit);
+    const int cnt = __popcll(__ballot(om >= tt));
+    if (cnt >= k - 1) {
+      T = tt;
+      if (cnt == k - 1) break;
     }
   }
-  // 1. threshold from the lane maxima: bitonic sort, descending
-  uint32_t x = lmax;
-#pragma unroll
-  for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const uint32_t y = __shfl_xor(x, stride, 64);
-      const bool lower = (lane & stride) == 0;
-      const bool desc = (lane & size) == 0;
-      const uint32_t hi = max(x, y), lo = min(x, y);
-      x = (lower == desc) ? hi : lo;
-    }
-  }
-  const uint32_t T = __shfl(x, k - 2, 64);
+  // ord(x) >= T implies x >= Tf; the float test may add a signed-zero tie,
+  // which the exact ranking below handles
+  const float Tf = f32_of_ord(T);
 
-  // 2. count candidates
+  // 2. count and compact the candidates
   int C = 0;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
-    C += __popcll(__ballot(c));
-  }
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int v = 0; v < V; ++v) C += __popcll(__ballot(x[v] >= Tf));
   uint64_t worst_sel = 0, best_unsel = 0;
-  if (C <= CMAX) {
+  if (C <= kCandMax) {
     int base = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
+      const bool c = x[v] >= Tf;
       const uint64_t bal = __ballot(c);
-      if (c) cand[wave][base + __popcll(bal & lt_mask)] = key[v];
-      base += __popcll(bal);
+      if (bal) {  // uniform
+        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        cand[wave][c ? pos : kCandMax] = make_key(x[v] + 0.0f, v * 64 + lane);  // -0 -> +0
+        base += __popcll(bal);
+      }
     }
     if (margin && lane < 2) msel[wave][lane] = 0;
     wave_sync();
@@ -436,7 +437,10 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
       for (int c2 = 0; c2 < C; ++c2) rank += cand[wave][c2] > kc;
       const bool sel = have && rank < k - 1;
       const uint64_t bal = __ballot(sel);
-      if (sel) out[pos_base + __popcll(bal & lt_mask)] = key_blk(kc);
+      if (sel)
+        out[pos_base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] =
+            key_blk(kc);
       pos_base += __popcll(bal);
       if (margin && have) {
         if (rank == k - 2) msel[wave][0] = kc;
@@ -450,25 +454,32 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
       uint64_t nc = 0;  // best non-candidate
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const bool c = key[v] != 0 && (uint32_t)(key[v] >> 32) >= T;
-        if (!c && key[v] > nc) nc = key[v];
+        const uint64_t kv = x[v] > -INFINITY ? make_key(x[v] + 0.0f, v * 64 + lane) : 0;
+        if (!(x[v] >= Tf) && kv > nc) nc = kv;
       }
       nc = wave_max_u64(nc);
       best_unsel = nc > best_unsel ? nc : best_unsel;
     }
   } else {
     // fallback: k-1 rounds of wave argmax over all blocks
+    uint64_t key[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) key[v] = x[v] > -INFINITY ? make_key(x[v] + 0.0f, v * 64 + lane) : 0;
     uint32_t taken = 0;
     for (int round = 0; round < k - 1; ++round) {
       uint64_t bestl = 0;
       int bestv = -1;
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (!((taken >> v) & 1u) && key[v] > bestl) { bestl = key[v]; bestv = v; }
+        if (!((taken >> v) & 1u) && key[v] > bestl) {
+          bestl = key[v];
+          bestv = v;
+        }
       const uint64_t best = wave_max_u64(bestl);
       if (bestv >= 0 && bestl == best) taken |= 1u << bestv;
       if (round == k - 2) worst_sel = best;
     }
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     int base = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
