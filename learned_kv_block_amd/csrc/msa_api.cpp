@@ -259,15 +259,21 @@ msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, co
   if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   const AttnWs w = carve(L, workspace);
-  if (launch_bucketing(d, block_ids, w, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  // bf16: each row's local block is attended query-outer inside the combine,
+  // so the KV-outer work lists leave it out
+  const bool local_in_combine = d.dtype == MSA_BF16;
+  if (launch_bucketing(d, block_ids, w, local_in_combine, stream) != hipSuccess)
+    return MSA_ERR_DEVICE;
   prof_before(MSA_K_SPARSE_ATTN, stream);
   hipError_t e = launch_sparse_attn(d, q, k, v, w, ws + L.opart,
                                     reinterpret_cast<float*>(ws + L.lpart), stream);
   prof_after(MSA_K_SPARSE_ATTN, stream);
   if (e != hipSuccess) return MSA_ERR_DEVICE;
   prof_before(MSA_K_COMBINE, stream);
-  e = launch_combine(d, ws + L.opart, reinterpret_cast<const float*>(ws + L.lpart), block_ids,
-                     out, lse, stream);
+  const float* lpart = reinterpret_cast<const float*>(ws + L.lpart);
+  e = local_in_combine
+          ? launch_combine_local(d, q, k, v, ws + L.opart, lpart, block_ids, out, lse, stream)
+          : launch_combine(d, ws + L.opart, lpart, block_ids, out, lse, stream);
   prof_after(MSA_K_COMBINE, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
@@ -293,7 +299,7 @@ msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, co
     return launch_fill_f32(kl_mean, 1, 0.0f, stream) == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
   char* ws = static_cast<char*>(workspace);
   const AttnWs w = carve(L, workspace);
-  if (launch_bucketing(d, block_ids, w, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  if (launch_bucketing(d, block_ids, w, false, stream) != hipSuccess) return MSA_ERR_DEVICE;
   hipError_t e = launch_kl(d, q, k, q_idx, k_idx, block_ids, lse_main, w,
                            reinterpret_cast<float*>(ws + L.slot_lse),
                            reinterpret_cast<float*>(ws + L.lse_idx),

@@ -21,13 +21,15 @@ namespace msa {
 //
 // bucket(b, r, w, blk) = ((b*Hkv + r)*nwin + w)*nb + blk with w = t / kQueryWindow;
 // entry = (t << 6) | slot. A histogram workgroup's rows lie in one window.
+// With skip_local, a row's own block floor((q_start + t)/128) gets no entry: the
+// combine computes that block's attention query-outer instead.
 
 constexpr int kBucketRows = 256;  // query rows per histogram workgroup
 
 template <bool LDSH>
 __global__ void __launch_bounds__(256)
-bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb, int nwin,
-                   int32_t* __restrict__ counts) {
+bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int q_start, int Hkv, int K, int nb,
+                   int nwin, bool skip_local, int32_t* __restrict__ counts) {
   extern __shared__ int32_t hist[];
   const int HB = Hkv * nb;
   const int b = blockIdx.y;
@@ -46,7 +48,8 @@ bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int 
   };
   for (int e = threadIdx.x; e < n; e += 256) {
     const int id = base[e];
-    if (id >= 0 && id < nb) {
+    const bool local = skip_local && id == (q_start + t0 + e / (Hkv * K)) >> 7;
+    if (id >= 0 && id < nb && !local) {
       const int r = (e / K) % Hkv;
       if (LDSH) atomicAdd(&hist[r * nb + id], 1);
       else atomicAdd(&counts[gbin(r * nb + id)], 1);
@@ -108,9 +111,9 @@ bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
 
 template <bool LDSH>
 __global__ void __launch_bounds__(256)
-bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, int nb,
-                      int nwin, int32_t* __restrict__ cursor, int32_t* __restrict__ entries,
-                      int entries_max) {
+bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int q_start, int Hkv, int K, int nb,
+                      int nwin, bool skip_local, int32_t* __restrict__ cursor,
+                      int32_t* __restrict__ entries, int entries_max) {
   extern __shared__ int32_t sh[];
   const int HB = Hkv * nb;
   int32_t* hist = sh;
@@ -129,7 +132,8 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, i
     __syncthreads();
     for (int e = threadIdx.x; e < n; e += 256) {
       const int id = idp[e];
-      if (id >= 0 && id < nb) atomicAdd(&hist[((e / K) % Hkv) * nb + id], 1);
+      const bool local = skip_local && id == (q_start + t0 + e / (Hkv * K)) >> 7;
+      if (id >= 0 && id < nb && !local) atomicAdd(&hist[((e / K) % Hkv) * nb + id], 1);
     }
     __syncthreads();
     for (int x = threadIdx.x; x < HB; x += 256) {
@@ -141,7 +145,8 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int Hkv, int K, i
   }
   for (int e = threadIdx.x; e < n; e += 256) {
     const int id = idp[e];
-    if (id >= 0 && id < nb) {
+    const bool local = skip_local && id == (q_start + t0 + e / (Hkv * K)) >> 7;
+    if (id >= 0 && id < nb && !local) {
       const int bin = ((e / K) % Hkv) * nb + id;
       const int p = LDSH ? base[bin] + atomicAdd(&hist[bin], 1) : atomicAdd(&cursor[gbin(bin)], 1);
       const int t = t0 + e / (Hkv * K);
@@ -175,7 +180,8 @@ static size_t bucket_lds_bytes(const Dims& d, int arrays) {
 }
 static bool bucket_use_lds(const Dims& d) { return bucket_lds_bytes(d, 2) <= 64 * 1024; }
 
-hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, hipStream_t s) {
+hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
+                            hipStream_t s) {
   hipError_t e;
   if ((e = launch_fill_i32(w.counts, d.buckets, 0, s)) != hipSuccess) return e;
   if (d.rows == 0) {
@@ -187,11 +193,11 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   const bool lds = bucket_use_lds(d);
   prof_before(MSA_K_BUCKET_HIST, s);
   if (lds)
-    bucket_hist_kernel<true><<<grid, 256, bucket_lds_bytes(d, 1), s>>>(ids, d.Nq, d.Hkv, d.K,
-                                                                      d.nb, d.nwin, w.counts);
+    bucket_hist_kernel<true><<<grid, 256, bucket_lds_bytes(d, 1), s>>>(
+        ids, d.Nq, d.q_start, d.Hkv, d.K, d.nb, d.nwin, skip_local, w.counts);
   else
-    bucket_hist_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin,
-                                                   w.counts);
+    bucket_hist_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.q_start, d.Hkv, d.K, d.nb,
+                                                   d.nwin, skip_local, w.counts);
   prof_after(MSA_K_BUCKET_HIST, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_before(MSA_K_BUCKET_SCAN, s);
@@ -203,10 +209,12 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   prof_before(MSA_K_BUCKET_SCATTER, s);
   if (lds)
     bucket_scatter_kernel<true><<<grid, 256, bucket_lds_bytes(d, 2), s>>>(
-        ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin, w.cursor, w.entries, (int)d.entries_max);
+        ids, d.Nq, d.q_start, d.Hkv, d.K, d.nb, d.nwin, skip_local, w.cursor, w.entries,
+        (int)d.entries_max);
   else
-    bucket_scatter_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.Hkv, d.K, d.nb, d.nwin,
-                                                     w.cursor, w.entries, (int)d.entries_max);
+    bucket_scatter_kernel<false><<<grid, 256, 0, s>>>(ids, d.Nq, d.q_start, d.Hkv, d.K, d.nb,
+                                                     d.nwin, skip_local, w.cursor, w.entries,
+                                                     (int)d.entries_max);
   prof_after(MSA_K_BUCKET_SCATTER, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (d.items_max > 0) {
@@ -927,6 +935,323 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
     st8<T>(dst + 8 * (lane + 64 * c), res);
   }
   if (lane % LPH == 0) lse[((size_t)row * Hkv + r) * G + hg] = L;
+}
+
+// ============================================================== local block + combine (bf16)
+//
+// The local block floor(i/128) is the one selected block that a row sees only
+// in part (causal mask), and every query of a block selects it. Its attention
+// therefore runs query-outer here, inside the combine, instead of as KV-outer
+// work items (the bucketing skips it): no gathered Q rows and no partial
+// written and read back for it.
+// Workgroup = one (128-token block L, group r): K and V of the block are
+// copied to LDS once (global_load_lds, swizzled as in the KV-outer kernel) and
+// serve the block's QW-query tiles in turn (RW = QW*G (query, head) rows, 32
+// per wave). Per tile:
+//  A. S^T = K Q^T with the causal mask, softmax, O^T = V^T P^T; the
+//     normalised O (bf16) and its LSE go to an LDS region of their own. The
+//     next tile's Q rows are loaded while B runs.
+//  B. One wave per (query, group) at a time: lane-per-head, the slot LSEs (the
+//     local one from LDS) give L and the weights (a per-wave LDS table); then
+//     lane unit u = lane + 64c (8 elements) of each slot block, so every
+//     partial load and the output store move 64 consecutive units per
+//     instruction; the local O comes from LDS.
+#ifndef MSA_CL_SB
+#define MSA_CL_SB 4
+#endif
+
+template <int D, int G, int SMAX>
+__global__ void __launch_bounds__(G == 1 ? 256 : 512, 1)
+combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                     const bf16* __restrict__ v, const bf16* __restrict__ opart,
+                     const float* __restrict__ lpart, const int32_t* __restrict__ ids,
+                     bf16* __restrict__ out, float* __restrict__ lse, int N, int Nq, int q_start,
+                     int Hkv, int topk, float scale_log2) {
+  constexpr int QW = G == 1 ? 128 : 256 / G;  // positions per tile
+  constexpr int RW = QW * G;                  // (query, head) rows per tile
+  constexpr int NWV = RW / 32;                // waves
+  constexpr int KSD = D / 16, DT = D / 32, CPR = D / 8;
+  constexpr int TILE = 128 * D;
+  constexpr int LOADS = 128 * CPR / (64 * NWV);  // global_load_lds per wave per tile
+  __shared__ __attribute__((aligned(16))) bf16 kv[2 * TILE];
+  __shared__ __attribute__((aligned(16))) bf16 Ob[RW * D];  // chunk c of row rho at c ^ (rho % CPR)
+  __shared__ float lse_loc[RW];
+  __shared__ float wt[NWV][G][SMAX];  // per-wave merge weights [head][slot]
+  bf16* const Kb = kv;
+  bf16* const Vb = kv + TILE;
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+
+  const int b = blockIdx.z, r = blockIdx.x;
+  const int L = q_start / 128 + (int)blockIdx.y;  // this workgroup's block
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = Hkv * G;
+  const size_t kvrow = (size_t)Hkv * D;
+  // tiles of the block that hold rows of this call
+  const int p_lo = max(L * 128, q_start), p_hi = min(L * 128 + 128, q_start + Nq);
+  const int tile_lo = (p_lo - L * 128) / QW, tile_hi = (p_hi - 1 - L * 128) / QW;
+
+  {  // K and V of block L (rows past N read row N-1: masked)
+    const int nvalid = min(128, N - L * 128);
+    const size_t base = ((size_t)b * N + (size_t)L * 128) * kvrow + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int p = (wave * LOADS + j) * 64 + lane;  // 16-byte LDS position in the tile
+      const int rho = p / CPR, cs = p % CPR;
+      const size_t rowbase = base + (size_t)min(rho, nvalid - 1) * kvrow;
+      __builtin_amdgcn_global_load_lds((const void*)(k + rowbase + 8 * (cs ^ swz_k<D>(rho))),
+                                       (lds_void*)(&Kb[(wave * LOADS + j) * 512]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(v + rowbase + 8 * (cs ^ swz_v<D>(rho))),
+                                       (lds_void*)(&Vb[(wave * LOADS + j) * 512]), 16, 0, 0);
+    }
+  }
+  // this lane's MFMA row in a tile; positions outside the call's rows read a
+  // valid Q row and are never stored
+  const int rho_q = 32 * wave + l32;
+  auto load_q = [&](int tile, vec8<bf16>* qf) {
+    const int a_row = L * 128 + tile * QW + rho_q / G;
+    const int t_row = min(max(a_row - q_start, 0), Nq - 1);
+    const bf16* qrow = q + ((size_t)(b * (size_t)Nq + t_row) * Hq + r * G + rho_q % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ld8<bf16>(qrow + 16 * ks + 8 * h);
+  };
+  vec8<bf16> qf[KSD];
+  load_q(tile_lo, qf);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // phase B constants
+  constexpr int UPH = D / 8;            // units per head row
+  constexpr int UPS = G * UPH;          // units per slot block
+  constexpr int NCH = (UPS + 63) / 64;  // units per lane
+  constexpr int LPH = 64 / G;           // lanes per head in the weight phase
+  const int hg = lane / LPH;
+  bool ok[NCH];
+  int hd[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int u = lane + 64 * c;
+    ok[c] = UPS % 64 == 0 || u < UPS;
+    hd[c] = ok[c] ? u / UPH : 0;
+  }
+  const int g16 = lane >> 4, s16 = lane & 15;
+
+  for (int tile = tile_lo; tile <= tile_hi; ++tile) {
+    const int a0 = L * 128 + tile * QW;  // first position of the tile
+    const int a_row = a0 + rho_q / G;
+    // ---- A. attention of the local block for the tile's rows
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kt][e] = 0.0f;
+      const int rho = kt * 32 + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+        mma(sacc[kt], ld8<bf16>(Kb + tile_off<D, false>(rho, 16 * ks + 8 * h)), qf[ks]);
+    }
+    if (tile < tile_hi) load_q(tile + 1, qf);  // uniform; lands while the rest of the tile runs
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (L * 128 + kt * 32 + drow(e, h) > a_row) sacc[kt][e] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = vmax(vmax(mx, sacc[kt][e]), sacc[kt][e + 1]);
+    }
+    mx = vmax(mx, shfl_xor_f(mx, 32));
+    const float mxs = mx * scale_log2;
+    float ls = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], scale_log2, -mxs));
+        sacc[kt][e] = pe;
+        ls += pe;
+      }
+    }
+    ls += shfl_xor_f(ls, 32);
+    f32x16 oacc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      vec8<bf16> pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = cvt<bf16>(sacc[st >> 1][8 * (st & 1) + e]);
+      const int krow = 16 * st + 4 * (g16 >> 1) + (s16 >> 2);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(Vb + tile_off<D, true>(krow, dcol)));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4*)(Vb + tile_off<D, true>(krow + 8, dcol)));
+        const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+        bf16x8 vf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[e] = l4[e];
+          vf[4 + e] = h4[e];
+        }
+        mma(oacc[dt], vf, pf);
+      }
+    }
+    if (tile > tile_lo) __syncthreads();  // every wave is done with the previous tile's O
+    {
+      const float inv = 1.0f / ls;
+      const int sw = rho_q % CPR;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          vec4<bf16> o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = cvt<bf16>(oacc[dt][4 * jg + e] * inv);
+          st4<bf16>(Ob + rho_q * D + 8 * ((dt * 4 + jg) ^ sw) + 4 * h, o);
+        }
+      }
+      lse_loc[rho_q] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
+    }
+    __syncthreads();
+
+    // ---- B. combine, one (query, group) per wave at a time
+    for (int p = wave; p < QW; p += NWV) {
+      const int t = a0 + p - q_start;
+      if (t < 0 || t >= Nq) continue;  // uniform
+      const size_t rg = ((size_t)b * Nq + t) * Hkv + r;
+      const size_t e0 = rg * topk;
+      const int32_t* id = ids + e0;
+      float lsv[SMAX];
+      float m = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        if (s < topk) {
+          const int sid = id[s];
+          lsv[s] = sid < 0 ? -INFINITY : sid == L ? lse_loc[p * G + hg] : lpart[(e0 + s) * G + hg];
+          m = vmax(m, lsv[s]);
+        }
+      }
+      float z = 0.0f;
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s)
+        if (s < topk) z += __expf(lsv[s] - m);
+      const float Lw = m + __logf(z);
+      if (lane % LPH == 0) {
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+          if (s < topk) wt[wave][hg][s] = __expf(lsv[s] - Lw);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is written
+      __builtin_amdgcn_wave_barrier();
+      float acc[NCH][8];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
+      const bf16* op = opart + e0 * (size_t)(G * D);
+      constexpr int SB = MSA_CL_SB < SMAX ? MSA_CL_SB : SMAX;  // slots in flight per wave
+#pragma unroll
+      for (int s0 = 0; s0 < SMAX; s0 += SB) {
+        if (s0 >= topk) break;
+        vec8<bf16> o[SB][NCH];
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int sl = min(s0 + j, topk - 1);  // in bounds; repeats are skipped below
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            if (ok[c]) o[j][c] = ld8_nt<bf16>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
+        }
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          if (s0 + j >= topk) continue;
+          const int sid = id[s0 + j];
+          if (sid < 0 || sid == L) continue;  // uniform: no partial for these slots
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            if (!ok[c]) continue;
+            const float w = wt[wave][hd[c]][s0 + j];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)o[j][c][e];
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        if (s < topk && id[s] == L) {  // uniform: the local slot, from LDS
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            if (!ok[c]) continue;
+            const int u = lane + 64 * c;
+            const int orow = p * G + hd[c];
+            const float w = wt[wave][hd[c]][s];
+            const vec8<bf16> ol = ld8<bf16>(Ob + orow * D + 8 * ((u % UPH) ^ (orow % CPR)));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)ol[e];
+          }
+        }
+      }
+      bf16* dst = out + ((size_t)(b * (size_t)Nq + t) * Hq + r * G) * D;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        if (!ok[c]) continue;
+        vec8<bf16> res;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) res[e] = cvt<bf16>(acc[c][e]);
+        st8<bf16>(dst + 8 * (lane + 64 * c), res);
+      }
+      if (lane % LPH == 0) lse[((size_t)b * Nq + t) * Hq + r * G + hg] = Lw;
+    }
+  }
+}
+
+template <int D>
+static hipError_t combine_local_dispatch_g(const Dims& d, const void* q, const void* k,
+                                           const void* v, const void* opart, const float* lpart,
+                                           const int32_t* ids, void* out, float* lse,
+                                           hipStream_t s) {
+  const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+  const int nblk = (d.q_start + d.Nq - 1) / 128 - d.q_start / 128 + 1;
+  // grid (group, block, batch): the groups of a block run side by side
+  const dim3 grid((unsigned)d.Hkv, (unsigned)nblk, (unsigned)d.B);
+#define MSA_CL_CASE(GG)                                                                        \
+  case GG: {                                                                                   \
+    constexpr int NT = GG == 1 ? 256 : 512;                                                    \
+    if (d.K <= 16)                                                                             \
+      combine_local_kernel<D, GG, 16><<<grid, NT, 0, s>>>(                                     \
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)opart, lpart, ids,      \
+          (bf16*)out, lse, d.N, d.Nq, d.q_start, d.Hkv, d.K, scale_log2);                      \
+    else                                                                                       \
+      combine_local_kernel<D, GG, 32><<<grid, NT, 0, s>>>(                                     \
+          (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)opart, lpart, ids,      \
+          (bf16*)out, lse, d.N, d.Nq, d.q_start, d.Hkv, d.K, scale_log2);                      \
+    break;                                                                                     \
+  }
+  switch (d.G) {
+    MSA_CL_CASE(1)
+    MSA_CL_CASE(2)
+    MSA_CL_CASE(4)
+    MSA_CL_CASE(8)
+    MSA_CL_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MSA_CL_CASE
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_local(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* opart, const float* lpart, const int32_t* ids,
+                                void* out, float* lse, hipStream_t s) {
+  if (d.rows == 0) return hipSuccess;
+  if (d.dtype != MSA_BF16) return hipErrorInvalidValue;
+  if (d.D == 128) return combine_local_dispatch_g<128>(d, q, k, v, opart, lpart, ids, out, lse, s);
+  if (d.D == 64) return combine_local_dispatch_g<64>(d, q, k, v, opart, lpart, ids, out, lse, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>

@@ -126,11 +126,16 @@ hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k
                                  hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s);
 
-hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, hipStream_t s);
+hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
+                            hipStream_t s);
 hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const void* v,
                               const AttnWs& w, void* opart, float* lpart, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const void* opart, const float* lpart,
                           const int32_t* ids, void* out, float* lse, hipStream_t s);
+// bf16: attention of each row's local block (query-outer) fused with the combine
+hipError_t launch_combine_local(const Dims& d, const void* q, const void* k, const void* v,
+                                const void* opart, const float* lpart, const int32_t* ids,
+                                void* out, float* lse, hipStream_t s);
 
 hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* ids, const float* lse_main,
