@@ -45,6 +45,12 @@ SMALL = [
     # short sequence: one partial block
     _small("bf16_short", seqlen_kv=77, seqlen_q=77, num_q_heads=8, num_kv_heads=4, topk=3,
            with_kl=True),
+    # bf16, G=1 (one query head per KV head), k > 16
+    _small("bf16_g1_k20", seqlen_kv=3000, seqlen_q=3000, num_q_heads=4, num_kv_heads=4,
+           topk=20, with_kl=True),
+    # bf16, G=2, chunked prefill starting inside a block, d=64, d_idx=32
+    _small("bf16_g2_chunk", seqlen_kv=2600, seqlen_q=700, q_start=1900, num_q_heads=4,
+           num_kv_heads=2, head_dim=64, idx_dim=32, topk=6),
 ]
 
 
@@ -88,6 +94,28 @@ def test_deterministic_and_decode_matches_prefill():
     assert torch.equal(d["ids"][:, 0], a["ids"][:, -1])
     assert torch.equal(d["out"][:, 0], a["out"][:, -1])
     assert torch.equal(d["lse"][:, 0], a["lse"][:, -1])
+
+
+def test_slot_order_does_not_matter():
+    # msa_attn_fwd takes any order of the selected ids (the local block need
+    # not be last): reversing each row's slots gives the same output
+    import learned_kv_block_amd as msa
+    cfg = _small("perm", seqlen_kv=1500, seqlen_q=1400, q_start=100, topk=6)
+    x = parity.gpu_inputs(cfg)
+    sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                         num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    ids = sel["ids"]
+    out_a, lse_a = msa.msa_attn_fwd(x["q"], x["k"], x["v"], ids, q_start=cfg.q_start,
+                                    idx_dim=cfg.idx_dim)
+    rev = torch.flip(ids, dims=[3]).contiguous()
+    out_b, lse_b = msa.msa_attn_fwd(x["q"], x["k"], x["v"], rev, q_start=cfg.q_start,
+                                    idx_dim=cfg.idx_dim)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.sort(ids, dim=3).values, torch.sort(rev, dim=3).values)
+    d_out = (out_a.float() - out_b.float()).abs().max().item()
+    d_lse = (lse_a - lse_b).abs().max().item()
+    print(f"[parity] perm: out {d_out:.3g} lse {d_lse:.3g}", flush=True)
+    assert d_out <= 1e-2 and d_lse <= 1e-5
 
 
 def test_empty_inputs():
