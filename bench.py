@@ -97,6 +97,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="skewed_n131072")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kl", action="store_true",
+                    help="add msa_kl_align (with the index-logit gradient) to the step; "
+                         "a training-side measurement, not the headline line")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for HBM counter calibration)")
@@ -124,6 +127,8 @@ def main():
                           device=dev)
     out = torch.empty_like(x["q"])
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev)
+    ws_kl = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_KL), dtype=torch.uint8,
+                         device=dev) if args.kl else None)
 
     def step():
         sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
@@ -131,6 +136,9 @@ def main():
                              workspace=ws_sel)
         msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], q_start=cfg.q_start,
                          idx_dim=cfg.idx_dim, workspace=ws_attn, out=out, lse=lse)
+        if args.kl:
+            msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse,
+                             q_start=cfg.q_start, want_dlogits=True, workspace=ws_kl)
         return sel["ids"]
 
     if args.copy_calibration:
@@ -166,8 +174,11 @@ def main():
 
     kernels = {}
     if args.breakdown:
-        for name in ("index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
-                     "work_items", "sparse_attn", "combine"):
+        names = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
+                 "work_items", "sparse_attn", "combine"]
+        if args.kl:
+            names += ["kl_idx_stats", "kl_idx_lse", "kl_main", "kl_reduce"]
+        for name in names:
             with msa.KernelTimer(name, max_launches=2) as t:
                 step()
                 step()
@@ -212,7 +223,10 @@ def main():
     }
     if kernels:
         line["kernel_ms"] = kernels
-    del x, ws_sel, ws_attn, out, lse
+    if args.kl:
+        line["metric"] = "MSA-layer training step (select + attention + KL align) query-tokens/s"
+        line["config"]["kl"] = True
+    del x, ws_sel, ws_attn, ws_kl, out, lse
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

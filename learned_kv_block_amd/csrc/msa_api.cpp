@@ -86,7 +86,8 @@ msa_status make_dims(const msa_shape* s, Dims* d) {
 size_t elem_size(const Dims& d) { return d.dtype == MSA_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t counts, offsets, cursor, item_off, totals, items, entries;  // bucketing
+  size_t counts, offsets, cursor, item_off, totals, items, entries, chunks;  // bucketing
+  size_t nchunks;  // scan chunks of 4096 buckets (+1)
   size_t opart, lpart;                                               // attention
   size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
   size_t total;
@@ -112,6 +113,8 @@ Layout layout(const Dims& d, int op) {
   L.totals = take(16);
   L.items = take(d.items_max * 16);
   L.entries = take(d.entries_max * 4);
+  L.nchunks = (size_t)(d.buckets / 4096 + 1);
+  L.chunks = take(L.nchunks * 2 * 4);  // per-chunk scan sums (entries, items)
   if (op == MSA_OP_ATTN) {
     // one extra slot: scratch target of the attention kernel's unused rows
     L.opart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
@@ -136,6 +139,8 @@ AttnWs carve(const Layout& L, void* ws) {
   w.totals = reinterpret_cast<int32_t*>(p + L.totals);
   w.items = reinterpret_cast<int4*>(p + L.items);
   w.entries = reinterpret_cast<int32_t*>(p + L.entries);
+  w.chunk_e = reinterpret_cast<int32_t*>(p + L.chunks);
+  w.chunk_i = w.chunk_e + L.nchunks;
   return w;
 }
 

@@ -62,17 +62,68 @@ bucket_hist_kernel(const int32_t* __restrict__ ids, int Nq, int q_start, int Hkv
   }
 }
 
-// Single workgroup: exclusive scans of entry counts and of item counts
-// (ceil(count / qt)) over all buckets.
+// Exclusive scans of entry counts and of item counts (ceil(count / qt)) over
+// all buckets, in two passes over chunks of kScanChunk buckets: chunk sums,
+// then each workgroup adds the sums of the chunks before it and scans its own
+// chunk. The last chunk writes the grand totals.
+constexpr int kScanChunk = 4096;  // buckets per workgroup (1024 threads x 4)
+
+__global__ void __launch_bounds__(1024)
+bucket_chunk_sum_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
+                        int32_t* __restrict__ chunk_e, int32_t* __restrict__ chunk_i) {
+  __shared__ int32_t se[32], si[32];
+  const int tid = threadIdx.x;
+  const int64_t lo = (int64_t)blockIdx.x * kScanChunk;
+  int32_t ce = 0, ci = 0;
+  for (int j = 0; j < kScanChunk / 1024; ++j) {
+    const int64_t x = lo + j * 1024 + tid;
+    if (x < nbk) {
+      const int32_t c = counts[x];
+      ce += c;
+      ci += (c + qt - 1) / qt;
+    }
+  }
+  for (int m = 32; m >= 1; m >>= 1) {
+    ce += __shfl_xor(ce, m, 64);
+    ci += __shfl_xor(ci, m, 64);
+  }
+  if ((tid & 63) == 0) {
+    se[tid >> 6] = ce;
+    si[tid >> 6] = ci;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t te = 0, ti = 0;
+    for (int w = 0; w < 16; ++w) {
+      te += se[w];
+      ti += si[w];
+    }
+    chunk_e[blockIdx.x] = te;
+    chunk_i[blockIdx.x] = ti;
+  }
+}
+
 __global__ void __launch_bounds__(1024)
 bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
+                   const int32_t* __restrict__ chunk_e, const int32_t* __restrict__ chunk_i,
                    int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
                    int32_t* __restrict__ item_off, int32_t* __restrict__ totals,
                    int entries_max, int items_max) {
   __shared__ int32_t se[1024], si[1024];
+  __shared__ int32_t base_e, base_i;
   const int tid = threadIdx.x;
-  const int64_t per = (nbk + 1023) / 1024;
-  const int64_t lo = min(nbk, (int64_t)tid * per), hi = min(nbk, lo + per);
+  const int chunk = blockIdx.x;
+  if (tid == 0) {
+    int32_t be = 0, bi = 0;
+    for (int c = 0; c < chunk; ++c) {
+      be += chunk_e[c];
+      bi += chunk_i[c];
+    }
+    base_e = be;
+    base_i = bi;
+  }
+  const int64_t lo = (int64_t)chunk * kScanChunk + (int64_t)tid * (kScanChunk / 1024);
+  const int64_t hi = min(nbk, lo + kScanChunk / 1024);
   int32_t ce = 0, ci = 0;
   for (int64_t x = lo; x < hi; ++x) {
     const int32_t c = counts[x];
@@ -90,7 +141,7 @@ bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
     si[tid] += ai;
     __syncthreads();
   }
-  int32_t re = se[tid] - ce, ri = si[tid] - ci;  // exclusive
+  int32_t re = base_e + se[tid] - ce, ri = base_i + si[tid] - ci;  // exclusive
   for (int64_t x = lo; x < hi; ++x) {
     const int32_t c = counts[x];
     offsets[x] = re;
@@ -99,13 +150,14 @@ bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
     re += c;
     ri += (c + qt - 1) / qt;
   }
-  if (tid == 1023) {
-    offsets[nbk] = se[1023];
-    item_off[nbk] = si[1023];
+  if (chunk == (int)gridDim.x - 1 && tid == 1023) {
+    const int32_t te = base_e + se[1023], ti = base_i + si[1023];
+    offsets[nbk] = te;
+    item_off[nbk] = ti;
     // both bounds hold for valid ids; clamping keeps malformed ids from
     // indexing past the work arrays
-    totals[0] = min(se[1023], entries_max);
-    totals[1] = min(si[1023], items_max);
+    totals[0] = min(te, entries_max);
+    totals[1] = min(ti, items_max);
   }
 }
 
@@ -184,9 +236,16 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
                             hipStream_t s) {
   hipError_t e;
   if ((e = launch_fill_i32(w.counts, d.buckets, 0, s)) != hipSuccess) return e;
+  const unsigned nchunks = (unsigned)((d.buckets + kScanChunk - 1) / kScanChunk);
+  auto scan = [&](int entries_max, int items_max) {
+    bucket_chunk_sum_kernel<<<nchunks, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.chunk_e,
+                                                     w.chunk_i);
+    bucket_scan_kernel<<<nchunks, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.chunk_e,
+                                                w.chunk_i, w.offsets, w.cursor, w.item_off,
+                                                w.totals, entries_max, items_max);
+  };
   if (d.rows == 0) {
-    bucket_scan_kernel<<<1, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.offsets, w.cursor,
-                                          w.item_off, w.totals, 0, 0);
+    scan(0, 0);
     return hipGetLastError();
   }
   const dim3 grid((d.Nq + kBucketRows - 1) / kBucketRows, d.B);
@@ -201,9 +260,7 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   prof_after(MSA_K_BUCKET_HIST, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_before(MSA_K_BUCKET_SCAN, s);
-  bucket_scan_kernel<<<1, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.offsets, w.cursor,
-                                        w.item_off, w.totals, (int)d.entries_max,
-                                        (int)d.items_max);
+  scan((int)d.entries_max, (int)d.items_max);
   prof_after(MSA_K_BUCKET_SCAN, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   prof_before(MSA_K_BUCKET_SCATTER, s);
@@ -350,24 +407,27 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   }
   // softmax over the 128 keys of this block, in the log2 domain
   const bool need_mask = blk * 128 + 127 > i_row;
+  // the same arithmetic, in the same order, as the persistent kernel: a row
+  // gets identical P, O and LSE whichever kernel processes it
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
+    if (need_mask) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = sacc[kt][e] * scale_log2;
-      if (need_mask && blk * 128 + kt * 32 + drow(e, h) > i_row) x = -INFINITY;
-      sacc[kt][e] = x;
-      mx = fmaxf(mx, x);
+      for (int e = 0; e < 16; ++e)
+        if (blk * 128 + kt * 32 + drow(e, h) > i_row) sacc[kt][e] = -INFINITY;
     }
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) mx = vmax(vmax(mx, sacc[kt][e]), sacc[kt][e + 1]);
   }
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  mx = vmax(mx, shfl_xor_f(mx, 32));
+  const float mxs = mx * scale_log2;
   float ls = 0.0f;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = exp2f(sacc[kt][e] - mx);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], scale_log2, -mxs));
       sacc[kt][e] = p;
       ls += p;
     }
@@ -416,7 +476,7 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
         st4<T>(op + dt * 32 + 8 * jg + 4 * h, o);
       }
     }
-    if (h == 0) lpart[entry * G + hg] = (mx + __log2f(ls)) * kLn2;
+    if (h == 0) lpart[entry * G + hg] = (mxs + __log2f(ls)) * kLn2;
   }
 }
 

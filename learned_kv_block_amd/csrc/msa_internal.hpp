@@ -112,6 +112,8 @@ struct AttnWs {
   int32_t* totals;    // [4]: entries, items
   int4* items;        // [items_max]: bucket, first entry, count, 0
   int32_t* entries;   // [entries_max]: (t << 6) | slot
+  int32_t* chunk_e;   // [buckets / 4096 + 1]: entry count per scan chunk
+  int32_t* chunk_i;   // [buckets / 4096 + 1]: item count per scan chunk
 };
 
 // Process-wide kernel timing hook (msa_prof_begin / msa_prof_end).

@@ -269,10 +269,9 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
 #define MSA_IDX_CB 32
 #endif
 
-template <typename T, int DI, int HKV>
-static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, float* M,
-                                 hipStream_t s) {
-  constexpr int NW = sizeof(T) == 4 ? 4 : MSA_IDX_NW;  // fp32 tiles: LDS and register limits
+template <typename T, int DI, int HKV, int NW>
+static hipError_t index_launch(const Dims& d, const void* qi, const void* ki, float* M,
+                               hipStream_t s) {
   constexpr int CB = MSA_IDX_CB;
   constexpr int QT = 64 * NW / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
@@ -283,6 +282,19 @@ static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, 
   index_blockmax_kernel<T, DI, HKV, NW, CB><<<grid, 64 * NW, 0, s>>>(
       (const T*)qi, (const T*)ki, M, d.N, d.Nq, d.q_start, d.nb, scale);
   return hipGetLastError();
+}
+
+template <typename T, int DI, int HKV>
+static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, float* M,
+                                 hipStream_t s) {
+  if constexpr (sizeof(T) == 4) {
+    return index_launch<T, DI, HKV, 4>(d, qi, ki, M, s);  // fp32 tiles: LDS and register limits
+  } else {
+    // a decode step has a few rows per sequence: one-wave tiles (64 rows)
+    // instead of 512-row tiles keep the MFMA work near the rows that exist
+    if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1>(d, qi, ki, M, s);
+    return index_launch<T, DI, HKV, MSA_IDX_NW>(d, qi, ki, M, s);
+  }
 }
 
 template <typename T, int DI>
