@@ -204,6 +204,24 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
                  ? lse_main[(size_t)(b * (size_t)Nq + s_t[qi]) * Hq + r * G + row % G] * kLog2e
                  : 0.0f;
   }
+  // per query of this lane: position, log2 LSE_idx, gradient row base; all in
+  // the log2 domain (raw v_exp_f32 / v_log_f32, scales folded into FMAs)
+  int q_i[NLQ];
+  float li2[NLQ];
+  float* dbase[NLQ];
+  bool qown[NLQ];
+#pragma unroll
+  for (int lq = 0; lq < NLQ; ++lq) {
+    const int row = 32 * wave + drow(lq * RPQ, h);
+    const int qi = row / G;
+    qown[lq] = qi < cnt && (!PARTNER || h == 0);
+    const int qc = qi < cnt ? qi : 0;
+    const int t = s_t[qc];
+    q_i[lq] = q_start + t;
+    li2[lq] = s_li[qc] * kLog2e;
+    const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + s_s[qc];
+    dbase[lq] = dlogits ? dlogits + entry * 128 : nullptr;
+  }
   float klacc[NLQ];
 #pragma unroll
   for (int lq = 0; lq < NLQ; ++lq) klacc[lq] = 0.0f;
@@ -220,40 +238,36 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
     const int tok = blk * 128 + key;
 #pragma unroll
     for (int lq = 0; lq < NLQ; ++lq) {
+      // teacher: mean over the group's heads of exp(S - LSE_main)
       float P = 0.0f;
 #pragma unroll
-      for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e) P += exp2f(acc[e] * scale_log2 - lm2[e]);
+      for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e)
+        P += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], scale_log2, -lm2[e]));
       if (PARTNER) P += shfl_xor_f(P, 32);
       P *= inv_g;
-      const int row = 32 * wave + drow(lq * RPQ, h);
-      const int qi = row / G;
-      const bool owner = !PARTNER || h == 0;
-      if (qi < cnt && owner) {
-        const int t = s_t[qi];
-        const bool vis = tok <= q_start + t;
-        const float lpi = zs[qi][key] - s_li[qi];  // log P_idx
-        float dS = 0.0f;
-        if (vis) {
-          dS = __expf(lpi) - P;
-          if (P > 0.0f) klacc[lq] += P * (__logf(P) - lpi);
-        }
-        if (dlogits) {
-          const size_t entry = ((size_t)(b * (size_t)Nq + t) * Hkv + r) * topk + s_s[qi];
-          dlogits[entry * 128 + key] = dS;
-        }
+      const int qi = (32 * wave + drow(lq * RPQ, h)) / G;
+      const float lpi2 = __builtin_fmaf(zs[qi < cnt ? qi : 0][key], kLog2e, -li2[lq]);  // log2 P_idx
+      const bool vis = tok <= q_i[lq];
+      const float dS = vis ? __builtin_amdgcn_exp2f(lpi2) - P : 0.0f;
+      // P below the smallest normal float adds nothing to P log P (and v_log_f32
+      // may treat it as 0)
+      const float kt_term =
+          (vis && P >= 1.17549435e-38f) ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
+      if (qown[lq]) {
+        klacc[lq] += kt_term;
+        if (dlogits) dbase[lq][key] = dS;
       }
     }
   }
   // reduce the KL partial of each query over the 32 key columns of a lane half
 #pragma unroll
   for (int lq = 0; lq < NLQ; ++lq) {
-    float v = klacc[lq];
+    float v = klacc[lq] * kLn2;  // log2 -> natural log
 #pragma unroll
     for (int m = 16; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
     const int row = 32 * wave + drow(lq * RPQ, h);
     const int qi = row / G;
-    const bool owner = !PARTNER || h == 0;
-    if (l32 == 0 && owner && qi < cnt) {
+    if (l32 == 0 && qown[lq]) {
       const size_t entry = ((size_t)(b * (size_t)Nq + s_t[qi]) * Hkv + r) * topk + s_s[qi];
       kl_part[entry] = v;
     }
