@@ -1011,11 +1011,12 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
 //  A. S^T = K Q^T with the causal mask, softmax, O^T = V^T P^T; the
 //     normalised O (bf16) and its LSE go to an LDS region of their own. The
 //     next tile's Q rows are loaded while B runs.
-//  B. One wave per (query, group) at a time: lane-per-head, the slot LSEs (the
-//     local one from LDS) give L and the weights (a per-wave LDS table); then
-//     lane unit u = lane + 64c (8 elements) of each slot block, so every
-//     partial load and the output store move 64 consecutive units per
-//     instruction; the local O comes from LDS.
+//  B. Each wave merges the 32/G queries whose rows it computed, one at a
+//     time: lane-per-head, the slot LSEs (the local one from LDS) give L and
+//     the weights (a per-wave LDS table); then lane unit u = lane + 64c (8
+//     elements) of each slot block, so every partial load and the output
+//     store move 64 consecutive units per instruction; the local O comes
+//     from LDS. Only the K/V copy needs a workgroup barrier.
 #ifndef MSA_CL_SB
 #define MSA_CL_SB 4
 #endif
@@ -1162,7 +1163,6 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         mma(oacc[dt], vf, pf);
       }
     }
-    if (tile > tile_lo) __syncthreads();  // every wave is done with the previous tile's O
     {
       const float inv = 1.0f / ls;
       const int sw = rho_q % CPR;
@@ -1178,15 +1178,33 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       lse_loc[rho_q] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
     }
-    __syncthreads();
+    // A wave merges exactly the queries whose rows it computed, so O and LSE
+    // stay private to the wave: no workgroup barrier, and the waves drift
+    // apart, one wave's MFMA work overlapping the others' partial streams.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's O rows are in LDS
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- B. combine, one (query, group) per wave at a time
-    for (int p = wave; p < QW; p += NWV) {
+    // ---- B. combine, the wave's 32/G queries one at a time
+    constexpr int QPW = 32 / G;  // queries of a wave's 32 rows
+    for (int p = wave * QPW; p < wave * QPW + QPW; ++p) {
       const int t = a0 + p - q_start;
       if (t < 0 || t >= Nq) continue;  // uniform
       const size_t rg = ((size_t)b * Nq + t) * Hkv + r;
       const size_t e0 = rg * topk;
       const int32_t* id = ids + e0;
+      const bf16* op = opart + e0 * (size_t)(G * D);
+      constexpr int SB = MSA_CL_SB < SMAX ? MSA_CL_SB : SMAX;  // slots in flight per wave
+      vec8<bf16> o[SB][NCH];
+      auto load_slots = [&](int s0) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j) {
+          const int sl = min(s0 + j, topk - 1);  // in bounds; repeats are skipped below
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+            if (ok[c]) o[j][c] = ld8_nt<bf16>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
+        }
+      };
+      load_slots(0);  // the first partials load while the weights are formed
       float lsv[SMAX];
       float m = -INFINITY;
 #pragma unroll
@@ -1214,19 +1232,10 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
-      const bf16* op = opart + e0 * (size_t)(G * D);
-      constexpr int SB = MSA_CL_SB < SMAX ? MSA_CL_SB : SMAX;  // slots in flight per wave
 #pragma unroll
       for (int s0 = 0; s0 < SMAX; s0 += SB) {
         if (s0 >= topk) break;
-        vec8<bf16> o[SB][NCH];
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int sl = min(s0 + j, topk - 1);  // in bounds; repeats are skipped below
-#pragma unroll
-          for (int c = 0; c < NCH; ++c)
-            if (ok[c]) o[j][c] = ld8_nt<bf16>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
-        }
+        if (s0 > 0) load_slots(s0);
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
           if (s0 + j >= topk) continue;
