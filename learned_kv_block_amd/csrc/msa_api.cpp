@@ -27,10 +27,11 @@ void set_item_size(Dims* d, int qt) {
   d->items_max = per_item < d->entries_max ? per_item : d->entries_max;
 }
 
-// The bf16 attention kernel runs 256 (query, head) rows per work item; the
-// fp32 attention and the KL passes run 128.
+// The bf16 attention kernel and the bf16 KL passes with G >= 8 run 256
+// (query, head) rows per work item; the fp32 kernels and other KL shapes run 128.
 Dims for_op(Dims d, int op) {
   if (op == MSA_OP_ATTN && d.dtype == MSA_BF16) set_item_size(&d, 256 / d.G);
+  if (op == MSA_OP_KL && d.dtype == MSA_BF16 && d.G >= 8) set_item_size(&d, 256 / d.G);
   return d;
 }
 
@@ -290,6 +291,7 @@ msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, co
   Dims d;
   msa_status st = make_dims(shape, &d);
   if (st != MSA_OK) return st;
+  d = for_op(d, MSA_OP_KL);
   if (!kl_mean) return MSA_ERR_NULL;
   if (d.rows > 0) {
     if (!q || !k || !q_idx || !k_idx || !block_ids || !lse_main || !kl_rows) return MSA_ERR_NULL;

@@ -507,24 +507,6 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
 constexpr int kPipeWaves = 8;
 
-// K fragment reads touch one chunk of 16 consecutive rows; the transposing V
-// reads touch 4 chunks of 4 consecutive rows. Each tile gets its own XOR
-// pattern so that both access shapes spread over all 64 LDS banks.
-template <int D>
-__device__ __forceinline__ int swz_k(int rho) {
-  return rho & (D / 8 - 1);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int rho) {
-  return D == 128 ? 4 * (rho & 3) : 2 * (rho & 3);
-}
-// element offset of (row, col) in a swizzled [128][D] tile
-template <int D, bool IS_V>
-__device__ __forceinline__ int tile_off(int rho, int col) {
-  const int sw = IS_V ? swz_v<D>(rho) : swz_k<D>(rho);
-  return rho * D + 8 * ((col >> 3) ^ sw) + (col & 7);
-}
-
 template <int D, int G>
 __global__ void __launch_bounds__(512, 1)
 sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,

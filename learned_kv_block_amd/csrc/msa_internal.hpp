@@ -81,6 +81,25 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(
 // and chains m = vmax(vmax(m, a), b) become one v_maximum3_f32 per two inputs.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// ---- swizzled [128][D] bf16 K/V tiles in LDS (16-byte chunk c of row rho at c ^ swz(rho))
+// K fragment reads touch one chunk of 16 consecutive rows; the transposing V
+// reads touch 4 chunks of 4 consecutive rows. Each tile gets its own XOR
+// pattern so that both access shapes spread over all 64 LDS banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int rho) {
+  return rho & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int rho) {
+  return D == 128 ? 4 * (rho & 3) : 2 * (rho & 3);
+}
+// element offset of (row, col) in a swizzled [128][D] tile
+template <int D, bool IS_V>
+__device__ __forceinline__ int tile_off(int rho, int col) {
+  const int sw = IS_V ? swz_v<D>(rho) : swz_k<D>(rho);
+  return rho * D + 8 * ((col >> 3) ^ sw) + (col & 7);
+}
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 

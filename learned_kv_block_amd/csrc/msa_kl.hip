@@ -62,13 +62,12 @@ __device__ __forceinline__ void item_index_logits(const T* __restrict__ q_idx,
 }
 
 // ---------------------------------------------------------------- pass A
-template <typename T, int DI, int G>
+template <typename T, int DI, int QT>
 __global__ void __launch_bounds__(256)
 kl_idx_stats_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
                     const int4* __restrict__ items, const int32_t* __restrict__ entries,
                     const int32_t* __restrict__ totals, float* __restrict__ slot_lse, int N,
                     int Nq, int q_start, int Hkv, int nb, int nbw, int topk) {
-  constexpr int QT = 128 / G;
   __shared__ float zs[QT][128 + 4];
   __shared__ int s_t[QT], s_s[QT];
   const int total = totals[1];
@@ -274,6 +273,250 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
   }
 }
 
+// ---------------------------------------------------------------- pass C, bf16, G >= 8
+//
+// Persistent: one workgroup of 8 waves per CU over a contiguous range of its
+// XCD's items (as the KV-outer attention kernel); an item is 256 (query,
+// head) rows = 256/G queries of one block, 32 rows per wave.
+//  - K and K_idx of the block are copied to LDS (global_load_lds, swizzled)
+//    only when the next item needs another block.
+//  - Q rows are loaded row-contiguously one item ahead and turned into MFMA A
+//    fragments through a per-wave LDS region.
+//  - Index logits of the item's queries: waves 0-3 form 32 keys x the item's
+//    queries each (MFMA) into a double-buffered LDS table; one workgroup
+//    barrier per item.
+//  - S = Q K^T, keys in lanes: the teacher is the mean over the group's heads
+//    of exp(S - LSE_main), an in-lane sum plus one exchange of lane halves;
+//    student, KL and dS in the log2 domain; dS rows are streamed out.
+constexpr int kKlWaves = 8;
+
+template <int D, int DI, int G>
+__global__ void __launch_bounds__(512, 1)
+kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                    const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx,
+                    const float* __restrict__ lse_main, const float* __restrict__ lse_idx,
+                    const int4* __restrict__ items, const int32_t* __restrict__ entries,
+                    const int32_t* __restrict__ totals, float* __restrict__ kl_part,
+                    float* __restrict__ dlogits, int N, int Nq, int q_start, int Hkv, int nb,
+                    int nbw, int topk, float scale_log2, float zscale_log2) {
+  static_assert(G >= 8, "two lane halves per query");
+  constexpr int QT = 256 / G;            // queries per item
+  constexpr int KSD = D / 16, KSI = DI / 16;
+  constexpr int CPR = D / 8, CPI = DI / 8;
+  constexpr int TILE = 128 * D, ITILE = 128 * DI;
+  constexpr int LOADS = 128 * CPR / (64 * kKlWaves);
+  constexpr int ILOADS = 128 * CPI / (64 * kKlWaves);
+  constexpr int LDW = D + 8;
+  constexpr int RCH = 32 * CPR / 64;     // Q row chunks per lane per wave tile
+  constexpr int RPI = 64 / CPR;          // rows per 1 KB access
+  static_assert(G >= RPI, "rows of one access belong to one query");
+  constexpr int QPW = 32 / G;            // queries per wave
+  constexpr int RPQ = G / 2;             // rows of one query per lane
+  constexpr int NLQ = 16 / RPQ;          // queries per lane (= QPW)
+  __shared__ bf16 Kb[TILE];
+  __shared__ bf16 KIb[ITILE];
+  __shared__ bf16 Wst[kKlWaves][32 * LDW];
+  __shared__ float zs[2][QT][128 + 4];
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  const int total = totals[1];
+  const int nwg_x = gridDim.x / 8;
+  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
+  const int per_x = (total + 7) / 8;
+  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
+  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  if (i0 >= i1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = Hkv * G;
+  const size_t kvrow = (size_t)Hkv * D;
+  bf16* const W = Wst[wave];
+  const int qw0 = wave * QPW;  // first query of the wave in an item
+  const int ent_last = max(0, totals[0] - 1);
+
+  auto stage = [&](int bkt) {
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    const int nvalid = min(128, N - blk * 128);
+    const size_t base = ((size_t)b * N + (size_t)blk * 128) * kvrow + (size_t)r * D;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int p = (wave * LOADS + j) * 64 + lane;
+      const int rho = p / CPR, cs = p % CPR;
+      const size_t src = base + (size_t)min(rho, nvalid - 1) * kvrow + 8 * (cs ^ swz_k<D>(rho));
+      __builtin_amdgcn_global_load_lds((const void*)(k + src),
+                                       (lds_void*)(&Kb[(wave * LOADS + j) * 512]), 16, 0, 0);
+    }
+    const size_t ibase = ((size_t)b * N + (size_t)blk * 128) * DI;
+#pragma unroll
+    for (int j = 0; j < ILOADS; ++j) {
+      const int p = (wave * ILOADS + j) * 64 + lane;
+      const int rho = p / CPI, cs = p % CPI;
+      const size_t src = ibase + (size_t)min(rho, nvalid - 1) * DI + 8 * (cs ^ swz_k<DI>(rho));
+      __builtin_amdgcn_global_load_lds((const void*)(k_idx + src),
+                                       (lds_void*)(&KIb[(wave * ILOADS + j) * 512]), 16, 0, 0);
+    }
+  };
+  auto wave_entries = [&](const int4& itm, int* es) {
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) es[j] = entries[min(itm.y + qw0 + j, ent_last)];
+  };
+  // Q rows of the wave's queries (row-contiguous) and LSE_main of its rows
+  auto load_rows = [&](int bkt, const int* es, vec8<bf16>* raw, float* lm2) {
+    const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int j = (RPI * u) / G, hd = (RPI * u) % G;
+      const bf16* base = q + (((size_t)b * Nq + (es[j] >> 6)) * Hkv + r) * (size_t)(G * D) + hd * D;
+      raw[u] = ld8<bf16>(base + (lane / CPR) * D + 8 * (lane % CPR));
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = drow(e, h);  // row within the wave
+      const int j = row / G;
+      lm2[e] = lse_main[(((size_t)b * Nq + (es[j] >> 6)) * Hkv + r) * G + row % G] * kLog2e;
+    }
+  };
+  auto rows_to_frags = [&](const vec8<bf16>* raw, vec8<bf16>* qf) {
+#pragma unroll
+    for (int u = 0; u < RCH; ++u) {
+      const int c = lane + 64 * u;
+      st8<bf16>(W + (c / CPR) * LDW + 8 * (c % CPR), raw[u]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ld8<bf16>(W + l32 * LDW + 16 * ks + 8 * h);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  int4 cur = items[i0];
+  stage(cur.x);
+  int es[QPW];
+  wave_entries(cur, es);
+  vec8<bf16> qf[KSD];
+  float lm2[16];
+  {
+    vec8<bf16> raw[RCH];
+    load_rows(cur.x, es, raw, lm2);
+    rows_to_frags(raw, qf);
+  }
+  int4 nxt = items[min(i0 + 1, i1 - 1)];
+  int es_n[QPW];
+  wave_entries(nxt, es_n);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const float inv_g = 1.0f / (float)G;
+  for (int it = i0; it < i1; ++it) {
+    const int bkt = cur.x, start = cur.y, cnt = cur.z;
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    const int buf = (it - i0) & 1;
+    const bool have_next = it + 1 < i1;
+    const int4 nxt2 = items[min(it + 2, i1 - 1)];
+    int es_n2[QPW];
+    wave_entries(nxt2, es_n2);
+    vec8<bf16> qraw[RCH];
+    float lm2_n[16];
+    load_rows(nxt.x, es_n, qraw, lm2_n);
+
+    // ---- index logits of the item's queries (waves 0-3: keys 32w..32w+31)
+    if (wave < 4) {
+      const int qi = l32 < QT ? l32 : 0;
+      const int e = entries[min(start + min(qi, cnt - 1), ent_last)];
+      const bf16* qp = q_idx + (((size_t)b * Nq + (e >> 6)) * Hkv + r) * DI + 8 * h;
+      f32x16 zacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zacc[i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks)
+        mma(zacc, ld8<bf16>(KIb + tile_off<DI, false>(32 * wave + l32, 16 * ks + 8 * h)),
+            ld8<bf16>(qp + 16 * ks));
+      if (l32 < QT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zs[buf][l32][32 * wave + drow(i, h)] = zacc[i] * zscale_log2;
+      }
+    }
+    // ---- S = Q K^T
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks)
+        mma(sacc[kt], qf[ks], ld8<bf16>(Kb + tile_off<D, false>(kt * 32 + l32, 16 * ks + 8 * h)));
+    }
+    // per query of the lane: position, log2 LSE_idx, gradient row, ownership
+    int q_i[NLQ];
+    float li2[NLQ];
+    size_t drow0[NLQ];
+    bool qown[NLQ];
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) {
+      const int t = es[lq] >> 6;
+      qown[lq] = qw0 + lq < cnt && h == 0;
+      q_i[lq] = q_start + t;
+      const size_t rg = ((size_t)b * Nq + t) * Hkv + r;
+      li2[lq] = lse_idx[rg] * kLog2e;
+      drow0[lq] = (rg * topk + (es[lq] & 63)) * 128;
+    }
+    __syncthreads();  // the index-logit table of this item is complete
+    float klacc[NLQ];
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) klacc[lq] = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = kt * 32 + l32;
+      const int tok = blk * 128 + key;
+#pragma unroll
+      for (int lq = 0; lq < NLQ; ++lq) {
+        float P = 0.0f;
+#pragma unroll
+        for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e)
+          P += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], scale_log2, -lm2[e]));
+        P += shfl_xor_f(P, 32);
+        P *= inv_g;
+        const float lpi2 = zs[buf][qw0 + lq][key] - li2[lq];  // log2 P_idx
+        const bool vis = tok <= q_i[lq];
+        const float dS = vis ? __builtin_amdgcn_exp2f(lpi2) - P : 0.0f;
+        const float term =
+            (vis && P >= 1.17549435e-38f) ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
+        if (qown[lq]) {
+          klacc[lq] += term;
+          if (dlogits) __builtin_nontemporal_store(dS, dlogits + drow0[lq] + key);
+        }
+      }
+    }
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) {
+      float v = klacc[lq] * kLn2;
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+      if (l32 == 0 && qown[lq]) kl_part[drow0[lq] / 128] = v;
+    }
+    // ---- next item's Q fragments
+    rows_to_frags(qraw, qf);
+    if (have_next && nxt.x != bkt) {
+      __syncthreads();
+      stage(nxt.x);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    cur = nxt;
+    nxt = nxt2;
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      es[j] = es_n[j];
+      es_n[j] = es_n2[j];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lm2[e] = lm2_n[e];
+  }
+}
+
 // ---------------------------------------------------------------- pass D
 __global__ void __launch_bounds__(256)
 kl_reduce_kernel(const int32_t* __restrict__ ids, const float* __restrict__ kl_part,
@@ -322,9 +565,12 @@ static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void
                          hipStream_t s) {
   const unsigned grid = (unsigned)(d.items_max + 8);
   const int64_t nrows = d.rows * d.Hkv;
+  // bf16 with G >= 8: 256-row items and the persistent main pass
+  constexpr bool kPipe = sizeof(T) == 2 && G >= 8;
+  constexpr int QT = kPipe ? 256 / G : 128 / G;
   if (d.items_max > 0) {
     prof_before(MSA_K_KL_IDX_STATS, s);
-    kl_idx_stats_kernel<T, DI, G><<<grid, 256, 0, s>>>(
+    kl_idx_stats_kernel<T, DI, QT><<<grid, 256, 0, s>>>(
         (const T*)q_idx, (const T*)k_idx, w.items, w.entries, w.totals, slot_lse, d.N, d.Nq,
         d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K);
     prof_after(MSA_K_KL_IDX_STATS, s);
@@ -342,10 +588,20 @@ static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void
   if (d.items_max > 0) {
     const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
     prof_before(MSA_K_KL_MAIN, s);
-    kl_main_kernel<T, D, DI, G><<<grid, 256, 0, s>>>(
-        (const T*)q, (const T*)k, (const T*)q_idx, (const T*)k_idx, lse_main, lse_idx, w.items,
-        w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv, d.nb,
-        d.nb * d.nwin, d.K, scale_log2);
+    if constexpr (kPipe) {
+      // one workgroup per CU, a multiple of 8 (one share per XCD)
+      const unsigned pgrid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+      const float zscale_log2 = (float)(1.0 / sqrt((double)DI) * 1.4426950408889634);
+      kl_main_pipe_kernel<D, DI, G><<<pgrid, 64 * kKlWaves, 0, s>>>(
+          (const bf16*)q, (const bf16*)k, (const bf16*)q_idx, (const bf16*)k_idx, lse_main,
+          lse_idx, w.items, w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv,
+          d.nb, d.nb * d.nwin, d.K, scale_log2, zscale_log2);
+    } else {
+      kl_main_kernel<T, D, DI, G><<<grid, 256, 0, s>>>(
+          (const T*)q, (const T*)k, (const T*)q_idx, (const T*)k_idx, lse_main, lse_idx,
+          w.items, w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv, d.nb,
+          d.nb * d.nwin, d.K, scale_log2);
+    }
     prof_after(MSA_K_KL_MAIN, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
