@@ -1175,18 +1175,25 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       const size_t e0 = rg * topk;
       const int32_t* id = ids + e0;
       const bf16* op = opart + e0 * (size_t)(G * D);
+      // the local slot has no partial: the j-th loaded slot is j, or j + 1 past it
+      int loc = topk;
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s)
+        if (s < topk && id[s] == L) loc = s;  // uniform
+      const int nsl = loc < topk ? topk - 1 : topk;
+      auto slot_at = [&](int j) { return j + (j >= loc ? 1 : 0); };
       constexpr int SB = MSA_CL_SB < SMAX ? MSA_CL_SB : SMAX;  // slots in flight per wave
       vec8<bf16> o[SB][NCH];
       auto load_slots = [&](int s0) {
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-          const int sl = min(s0 + j, topk - 1);  // in bounds; repeats are skipped below
+          const int sl = slot_at(min(s0 + j, nsl - 1));  // in bounds; repeats are skipped below
 #pragma unroll
           for (int c = 0; c < NCH; ++c)
             if (ok[c]) o[j][c] = ld8_nt<bf16>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
         }
       };
-      load_slots(0);  // the first partials load while the weights are formed
+      if (nsl > 0) load_slots(0);  // the first partials load while the weights are formed
       float lsv[SMAX];
       float m = -INFINITY;
 #pragma unroll
@@ -1216,17 +1223,17 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
 #pragma unroll
       for (int s0 = 0; s0 < SMAX; s0 += SB) {
-        if (s0 >= topk) break;
+        if (s0 >= nsl) break;
         if (s0 > 0) load_slots(s0);
 #pragma unroll
         for (int j = 0; j < SB; ++j) {
-          if (s0 + j >= topk) continue;
-          const int sid = id[s0 + j];
-          if (sid < 0 || sid == L) continue;  // uniform: no partial for these slots
+          if (s0 + j >= nsl) continue;
+          const int sl = slot_at(s0 + j);
+          if (id[sl] < 0) continue;  // uniform: unused slot, no partial
 #pragma unroll
           for (int c = 0; c < NCH; ++c) {
             if (!ok[c]) continue;
-            const float w = wt[wave][hd[c]][s0 + j];
+            const float w = wt[wave][hd[c]][sl];
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)o[j][c][e];
           }
