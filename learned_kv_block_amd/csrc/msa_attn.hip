@@ -988,19 +988,30 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
 // written and read back for it.
 // Workgroup = one (128-token block L, group r): K and V of the block are
 // copied to LDS once (global_load_lds, swizzled as in the KV-outer kernel) and
-// serve the block's QW-query tiles in turn (RW = QW*G (query, head) rows, 32
-// per wave). Per tile:
-//  A. S^T = K Q^T with the causal mask, softmax, O^T = V^T P^T; the
-//     normalised O (bf16) and its LSE go to an LDS region of their own. The
-//     next tile's Q rows are loaded while B runs.
-//  B. Each wave merges the 32/G queries whose rows it computed, one at a
-//     time: lane-per-head, the slot LSEs (the local one from LDS) give L and
-//     the weights (a per-wave LDS table); then lane unit u = lane + 64c (8
-//     elements) of each slot block, so every partial load and the output
-//     store move 64 consecutive units per instruction; the local O comes
-//     from LDS. Only the K/V copy needs a workgroup barrier.
-#ifndef MSA_CL_SB
-#define MSA_CL_SB 4
+// serve the block's QW-query tiles (RW = QW*G (query, head) rows, 32 per
+// wave). A wave owns the same 32 rows of every tile, i.e. QPW = 32/G queries
+// per tile, and works through its queries in order:
+//  A. at a query that opens a tile: S^T = K Q^T with the causal mask,
+//     softmax, O^T = V^T P^T for the wave's 32 rows; the normalised O (bf16)
+//     and its LSE go to the wave's rows of an LDS region.
+//  B. per query, eq. (16)/(18): the slot LSEs (the local one from LDS) give
+//     L and the weights w_s = exp(LSE_s - L), kept in a per-wave LDS table;
+//     the accumulator starts with the local O (from LDS), then the non-local
+//     partials stream in: lane unit u = lane + 64c (8 elements) of a slot
+//     block, so every load moves 64 consecutive units.
+// The partial loads form one continuous stream per wave: a query always has
+// NE = SMAX stream entries (entry k is the k-th non-local slot; entries past
+// the row's slots repeat its last one and are not accumulated), so entry k
+// sits in ring position k % W, and the loads run W entries ahead across query
+// and tile boundaries. Everything else a query needs is loaded early enough
+// not to stall the stream: the next query's slot ids and LSEs during the
+// current one, the next tile's Q fragments (registers) when the tile's last
+// query starts. (A global_load_lds copy of Q would make the compiler hold
+// every later LDS read until all vector loads land.)
+// Only the K/V copy needs a workgroup barrier.
+
+#ifndef MSA_CL_W4
+#define MSA_CL_W4 2
 #endif
 
 template <int D, int G, int SMAX>
@@ -1013,13 +1024,21 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int QW = G == 1 ? 128 : 256 / G;  // positions per tile
   constexpr int RW = QW * G;                  // (query, head) rows per tile
   constexpr int NWV = RW / 32;                // waves
+  constexpr int QPW = 32 / G;                 // queries of a wave's 32 rows
   constexpr int KSD = D / 16, DT = D / 32, CPR = D / 8;
   constexpr int TILE = 128 * D;
-  constexpr int LOADS = 128 * CPR / (64 * NWV);  // global_load_lds per wave per tile
+  constexpr int LOADS = 128 * CPR / (64 * NWV);  // global_load_lds per wave for K (and V)
+  constexpr int UPH = D / 8;                     // 8-element units per head row
+  constexpr int UPS = G * UPH;                   // units per slot block
+  constexpr int NCH = (UPS + 63) / 64;           // units per lane
+  constexpr int LPH = 64 / G;                    // lanes per head in the weight phase
+  constexpr int NE = SMAX;                       // stream entries per query
+  constexpr int W = MSA_CL_W4 * 4 / NCH;  // entries in flight per wave (W * NCH loads)
+  static_assert(NE % W == 0 && SMAX <= 64, "ring layout");
   __shared__ __attribute__((aligned(16))) bf16 kv[2 * TILE];
   __shared__ __attribute__((aligned(16))) bf16 Ob[RW * D];  // chunk c of row rho at c ^ (rho % CPR)
   __shared__ float lse_loc[RW];
-  __shared__ float wt[NWV][G][SMAX];  // per-wave merge weights [head][slot]
+  __shared__ __attribute__((aligned(16))) float wt[NWV][SMAX * G];  // per-wave weights [slot][head]
   bf16* const Kb = kv;
   bf16* const Vb = kv + TILE;
   typedef __attribute__((address_space(3))) void lds_void;
@@ -1031,10 +1050,31 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hq = Hkv * G;
   const size_t kvrow = (size_t)Hkv * D;
-  // tiles of the block that hold rows of this call
+  // positions of the block that are rows of this call
   const int p_lo = max(L * 128, q_start), p_hi = min(L * 128 + 128, q_start + Nq);
   const int tile_lo = (p_lo - L * 128) / QW, tile_hi = (p_hi - 1 - L * 128) / QW;
 
+  // The wave's queries qi, in order; qi -> position apos(qi). Positions grow
+  // with qi, so the rows of this call are one range [qi_lo, qi_hi].
+  auto apos = [&](int qi) { return L * 128 + (qi / QPW) * QW + wave * QPW + qi % QPW; };
+  int qi_lo = 1 << 30, qi_hi = -1;
+  for (int qi = tile_lo * QPW; qi < (tile_hi + 1) * QPW; ++qi) {
+    const int a = apos(qi);
+    if (a >= p_lo && a < p_hi) {
+      qi_lo = min(qi_lo, qi);
+      qi_hi = qi;
+    }
+  }
+  // Q fragments of this lane's MFMA row of a tile (rows outside the call read a
+  // valid Q row and are never stored)
+  auto load_q = [&](int tile, vec8<bf16>* qf) {
+    const int rq = 32 * wave + l32;
+    const int a = L * 128 + tile * QW + rq / G;
+    const int t_row = min(max(a - q_start, 0), Nq - 1);
+    const bf16* qrow = q + ((size_t)(b * (size_t)Nq + t_row) * Hq + r * G + rq % G) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ld8<bf16>(qrow + 16 * ks + 8 * h);
+  };
   {  // K and V of block L (rows past N read row N-1: masked)
     const int nvalid = min(128, N - L * 128);
     const size_t base = ((size_t)b * N + (size_t)L * 128) * kvrow + (size_t)r * D;
@@ -1049,27 +1089,45 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                        (lds_void*)(&Vb[(wave * LOADS + j) * 512]), 16, 0, 0);
     }
   }
-  // this lane's MFMA row in a tile; positions outside the call's rows read a
-  // valid Q row and are never stored
-  const int rho_q = 32 * wave + l32;
-  auto load_q = [&](int tile, vec8<bf16>* qf) {
-    const int a_row = L * 128 + tile * QW + rho_q / G;
-    const int t_row = min(max(a_row - q_start, 0), Nq - 1);
-    const bf16* qrow = q + ((size_t)(b * (size_t)Nq + t_row) * Hq + r * G + rho_q % G) * D;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) qf[ks] = ld8<bf16>(qrow + 16 * ks + 8 * h);
-  };
-  vec8<bf16> qf[KSD];
-  load_q(tile_lo, qf);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // phase B constants
-  constexpr int UPH = D / 8;            // units per head row
-  constexpr int UPS = G * UPH;          // units per slot block
-  constexpr int NCH = (UPS + 63) / 64;  // units per lane
-  constexpr int LPH = 64 / G;           // lanes per head in the weight phase
-  const int hg = lane / LPH;
+  if (qi_hi < 0) return;  // uniform; no barrier follows
+
+  // ---- per-query slot table (uniform values)
+  auto row_e0 = [&](int qi) {  // first (query, group, slot) entry of the row
+    const int t = apos(min(qi, qi_hi)) - q_start;
+    return (((size_t)b * Nq + t) * Hkv + r) * (size_t)topk;
+  };
+  // lane s < topk holds slot s's block id
+  auto load_ids = [&](int qi) {
+    const size_t e0 = row_e0(qi);
+    return ids[e0 + min(lane, topk - 1)];
+  };
+  struct Desc {
+    size_t e0;
+    int loc;        // slot of the local block (topk if absent)
+    int nsl;        // non-local slots
+    uint64_t used;  // bit s: slot s holds a block
+  };
+  auto make_desc = [&](int qi, int32_t idv) {
+    Desc d;
+    d.e0 = row_e0(qi);
+    const uint64_t isloc = __ballot(lane < topk && idv == L);
+    d.used = __ballot(lane < topk && idv >= 0);
+    d.loc = isloc ? (int)__builtin_ctzll(isloc) : topk;
+    d.nsl = d.loc < topk ? topk - 1 : topk;
+    return d;
+  };
+  auto slot_of = [&](const Desc& d, int e) { return e + (e >= d.loc ? 1 : 0); };
+  auto entry_valid = [&](const Desc& d, int e) {
+    return e < d.nsl && ((d.used >> slot_of(d, e)) & 1);
+  };
+  // address of stream entry e (entries past the row's slots repeat the last one)
+  auto entry_ptr = [&](const Desc& d, int e) {
+    const int sl = d.nsl > 0 ? slot_of(d, min(e, d.nsl - 1)) : 0;
+    return opart + (d.e0 + (size_t)sl) * (size_t)(G * D);
+  };
   bool ok[NCH];
   int hd[NCH];
 #pragma unroll
@@ -1078,12 +1136,41 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     ok[c] = UPS % 64 == 0 || u < UPS;
     hd[c] = ok[c] ? u / UPH : 0;
   }
-  const int g16 = lane >> 4, s16 = lane & 15;
+  const int hg = lane / LPH;
+  vec8<bf16> o[W][NCH];
+  auto issue = [&](int j, const Desc& d, int e) {
+    const bf16* p = entry_ptr(d, e);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (ok[c]) o[j][c] = ld8_nt<bf16>(p + 8 * (lane + 64 * c));
+  };
+  // A row's slot LSEs ([topk][G] floats, contiguous). With G >= 4, lane l
+  // holds elements 256c + 4l + j (one 16-byte load per c): slot
+  // (256c + 4l) / G, head (4l + j) % G, so the lanes of one head differ in
+  // the lane bits from G/4 up. Otherwise lane-per-head, one slot per value.
+  constexpr bool kPack = G >= 4;
+  constexpr int NCL = kPack ? (SMAX * G + 255) / 256 : SMAX;
+  constexpr int NLV = kPack ? 4 : 1;
+  auto load_lse = [&](size_t e0, float (*x)[NLV]) {
+    if constexpr (kPack) {
+#pragma unroll
+      for (int c = 0; c < NCL; ++c) {
+        const int f = min(256 * c + 4 * lane, topk * G - 4);
+        const vec4<float> v4 = ld4<float>(lpart + e0 * G + f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[c][j] = v4[j];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) x[s][0] = lpart[(e0 + (size_t)min(s, topk - 1)) * G + hg];
+    }
+  };
 
-  for (int tile = tile_lo; tile <= tile_hi; ++tile) {
-    const int a0 = L * 128 + tile * QW;  // first position of the tile
-    const int a_row = a0 + rho_q / G;
-    // ---- A. attention of the local block for the tile's rows
+  // ---- phase A: the local block's attention for the wave's rows of a tile
+  const int rho_q = 32 * wave + l32;  // this lane's MFMA row in a tile
+  const int g16 = lane >> 4, s16 = lane & 15;
+  auto phase_a = [&](int tile, const vec8<bf16>* qf) {
+    const int a_row = L * 128 + tile * QW + rho_q / G;
     f32x16 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -1094,26 +1181,30 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int ks = 0; ks < KSD; ++ks)
         mma(sacc[kt], ld8<bf16>(Kb + tile_off<D, false>(rho, 16 * ks + 8 * h)), qf[ks]);
     }
-    if (tile < tile_hi) load_q(tile + 1, qf);  // uniform; lands while the rest of the tile runs
+    // causal mask: key kt*32 + drow(e, h) of the block lies past the row when
+    // its lane-free part kt*32 + drow(e, 0) exceeds thr (compile-time
+    // constants against one register)
+    const int thr = a_row - L * 128 - 4 * h;
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (L * 128 + kt * 32 + drow(e, h) > a_row) sacc[kt][e] = -INFINITY;
+        if (kt * 32 + drow(e, 0) > thr) sacc[kt][e] = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = vmax(vmax(mx, sacc[kt][e]), sacc[kt][e + 1]);
     }
     mx = vmax(mx, shfl_xor_f(mx, 32));
     const float mxs = mx * scale_log2;
     float ls = 0.0f;
+    vec8<bf16> pf[8];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][e], scale_log2, -mxs));
-        sacc[kt][e] = pe;
         ls += pe;
+        pf[2 * kt + e / 8][e % 8] = cvt<bf16>(pe);
       }
     }
     ls += shfl_xor_f(ls, 32);
@@ -1124,9 +1215,6 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.0f;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      vec8<bf16> pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = cvt<bf16>(sacc[st >> 1][8 * (st & 1) + e]);
       const int krow = 16 * st + 4 * (g16 >> 1) + (s16 >> 2);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -1142,130 +1230,178 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           vf[e] = l4[e];
           vf[4 + e] = h4[e];
         }
-        mma(oacc[dt], vf, pf);
+        mma(oacc[dt], vf, pf[st]);
       }
     }
-    {
-      const float inv = 1.0f / ls;
-      const int sw = rho_q % CPR;
+    const float inv = 1.0f / ls;
+    const int sw = rho_q % CPR;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          vec4<bf16> o;
+      for (int jg = 0; jg < 4; ++jg) {
+        vec4<bf16> ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = cvt<bf16>(oacc[dt][4 * jg + e] * inv);
-          st4<bf16>(Ob + rho_q * D + 8 * ((dt * 4 + jg) ^ sw) + 4 * h, o);
-        }
+        for (int e = 0; e < 4; ++e) ov[e] = cvt<bf16>(oacc[dt][4 * jg + e] * inv);
+        st4<bf16>(Ob + rho_q * D + 8 * ((dt * 4 + jg) ^ sw) + 4 * h, ov);
       }
-      lse_loc[rho_q] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
     }
-    // A wave merges exactly the queries whose rows it computed, so O and LSE
-    // stay private to the wave: no workgroup barrier, and the waves drift
-    // apart, one wave's MFMA work overlapping the others' partial streams.
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's O rows are in LDS
+    lse_loc[rho_q] = (mxs + __log2f(ls)) * kLn2;  // both lane halves hold it
+    __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0): the wave's O rows are in LDS
     __builtin_amdgcn_wave_barrier();
+  };
 
-    // ---- B. combine, the wave's 32/G queries one at a time
-    constexpr int QPW = 32 / G;  // queries of a wave's 32 rows
-    for (int p = wave * QPW; p < wave * QPW + QPW; ++p) {
-      const int t = a0 + p - q_start;
-      if (t < 0 || t >= Nq) continue;  // uniform
-      const size_t rg = ((size_t)b * Nq + t) * Hkv + r;
-      const size_t e0 = rg * topk;
-      const int32_t* id = ids + e0;
-      const bf16* op = opart + e0 * (size_t)(G * D);
-      // the local slot has no partial: the j-th loaded slot is j, or j + 1 past it
-      int loc = topk;
+  // ---- the stream
+  vec8<bf16> qf[KSD];
+  load_q(qi_lo / QPW, qf);
+  int32_t id_cur = load_ids(qi_lo);
+  Desc dc = make_desc(qi_lo, id_cur);
+  float lsv[NCL][NLV];
+  load_lse(dc.e0, lsv);
 #pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < topk && id[s] == L) loc = s;  // uniform
-      const int nsl = loc < topk ? topk - 1 : topk;
-      auto slot_at = [&](int j) { return j + (j >= loc ? 1 : 0); };
-      constexpr int SB = MSA_CL_SB < SMAX ? MSA_CL_SB : SMAX;  // slots in flight per wave
-      vec8<bf16> o[SB][NCH];
-      auto load_slots = [&](int s0) {
+  for (int j = 0; j < W; ++j) issue(j, dc, j);
+
+  for (int qi = qi_lo; qi <= qi_hi; ++qi) {
+    const int i = qi % QPW;  // query within the wave's rows of its tile
+    if (i == 0 || qi == qi_lo) phase_a(qi / QPW, qf);  // uniform
+    // the next query's slot ids and LSEs (clamped past the last query)
+    const int32_t id_n = load_ids(qi + 1);
+    float lsv_n[NCL][NLV];
+    load_lse(row_e0(qi + 1), lsv_n);
+
+    // weights: LSE = logsumexp of the slot LSEs, w_s = exp(LSE_s - LSE)
+    const int orow0 = (wave * QPW + i) * G;  // the query's first row in a tile
+    float Lw[NLV];
+    if constexpr (kPack) {
+      const int hh0 = (4 * lane) % G;  // heads hh0 .. hh0+3
+      const vec4<float> lloc = ld4<float>(&lse_loc[orow0 + hh0]);
+      float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          const int sl = slot_at(min(s0 + j, nsl - 1));  // in bounds; repeats are skipped below
+      for (int c = 0; c < NCL; ++c) {
+        const int f = 256 * c + 4 * lane, sl = f / G;
+        const int sid = __shfl(id_cur, min(sl, 63), 64);
+        const bool used = f < topk * G && sid >= 0;
 #pragma unroll
-          for (int c = 0; c < NCH; ++c)
-            if (ok[c]) o[j][c] = ld8_nt<bf16>(op + (size_t)sl * (G * D) + 8 * (lane + 64 * c));
+        for (int j = 0; j < 4; ++j) {
+          lsv[c][j] = used ? (sid == L ? lloc[j] : lsv[c][j]) : -INFINITY;
+          m[j] = vmax(m[j], lsv[c][j]);
         }
-      };
-      if (nsl > 0) load_slots(0);  // the first partials load while the weights are formed
-      float lsv[SMAX];
+      }
+#pragma unroll
+      for (int msk = G / 4; msk < 64; msk *= 2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m[j] = vmax(m[j], shfl_xor_f(m[j], msk));
+      float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCL; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] += __expf(lsv[c][j] - m[j]);
+#pragma unroll
+      for (int msk = G / 4; msk < 64; msk *= 2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] += shfl_xor_f(z[j], msk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Lw[j] = m[j] + __logf(z[j]);
+#pragma unroll
+      for (int c = 0; c < NCL; ++c) {
+        const int f = 256 * c + 4 * lane;
+        if (f < SMAX * G) {
+          vec4<float> w4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w4[j] = __expf(lsv[c][j] - Lw[j]);
+          st4<float>(&wt[wave][f], w4);
+        }
+      }
+    } else {
+      const float lloc = lse_loc[orow0 + hg];
       float m = -INFINITY;
 #pragma unroll
       for (int s = 0; s < SMAX; ++s) {
-        if (s < topk) {
-          const int sid = id[s];
-          lsv[s] = sid < 0 ? -INFINITY : sid == L ? lse_loc[p * G + hg] : lpart[(e0 + s) * G + hg];
-          m = vmax(m, lsv[s]);
-        }
+        const int sid = __builtin_amdgcn_readlane(id_cur, s);
+        lsv[s][0] = (s < topk && sid >= 0) ? (sid == L ? lloc : lsv[s][0]) : -INFINITY;
+        m = vmax(m, lsv[s][0]);
       }
       float z = 0.0f;
 #pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < topk) z += __expf(lsv[s] - m);
-      const float Lw = m + __logf(z);
+      for (int s = 0; s < SMAX; ++s) z += __expf(lsv[s][0] - m);
+      Lw[0] = m + __logf(z);
       if (lane % LPH == 0) {
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < topk) wt[wave][hg][s] = __expf(lsv[s] - Lw);
+        for (int s = 0; s < SMAX; ++s) wt[wave][s * G + hg] = __expf(lsv[s][0] - Lw[0]);
       }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is written
-      __builtin_amdgcn_wave_barrier();
-      float acc[NCH][8];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the table is written
+    __builtin_amdgcn_wave_barrier();
+
+    // the accumulator starts with the local slot's share (its O from LDS)
+    float acc[NCH][8];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
+    for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c][e] = 0.0f;
-#pragma unroll
-      for (int s0 = 0; s0 < SMAX; s0 += SB) {
-        if (s0 >= nsl) break;
-        if (s0 > 0) load_slots(s0);
-#pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          if (s0 + j >= nsl) continue;
-          const int sl = slot_at(s0 + j);
-          if (id[sl] < 0) continue;  // uniform: unused slot, no partial
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            if (!ok[c]) continue;
-            const float w = wt[wave][hd[c]][sl];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)o[j][c][e];
-          }
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s) {
-        if (s < topk && id[s] == L) {  // uniform: the local slot, from LDS
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            if (!ok[c]) continue;
-            const int u = lane + 64 * c;
-            const int orow = p * G + hd[c];
-            const float w = wt[wave][hd[c]][s];
-            const vec8<bf16> ol = ld8<bf16>(Ob + orow * D + 8 * ((u % UPH) ^ (orow % CPR)));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[c][e] += w * (float)ol[e];
-          }
-        }
-      }
-      bf16* dst = out + ((size_t)(b * (size_t)Nq + t) * Hq + r * G) * D;
+      for (int x = 0; x < 8; ++x) acc[c][x] = 0.0f;
+    if (dc.loc < topk) {  // uniform
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         if (!ok[c]) continue;
-        vec8<bf16> res;
+        const int u = lane + 64 * c;
+        const int orow = orow0 + hd[c];
+        const float w = wt[wave][dc.loc * G + hd[c]];
+        const vec8<bf16> ol = ld8<bf16>(Ob + orow * D + 8 * ((u % UPH) ^ (orow % CPR)));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) res[e] = cvt<bf16>(acc[c][e]);
-        st8<bf16>(dst + 8 * (lane + 64 * c), res);
+        for (int x = 0; x < 8; ++x) acc[c][x] = w * (float)ol[x];
       }
-      if (lane % LPH == 0) lse[((size_t)b * Nq + t) * Hq + r * G + hg] = Lw;
     }
+    if (i == QPW - 1) load_q(min(qi + 1, qi_hi) / QPW, qf);  // uniform: the next tile's Q
+
+    Desc dn;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int j = e % W;
+      if (e == NE - W) dn = make_desc(qi + 1, id_n);
+      if (entry_valid(dc, e)) {  // uniform
+        const int sl = slot_of(dc, e);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (!ok[c]) continue;
+          const float w = wt[wave][sl * G + hd[c]];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[c][x] += w * (float)o[j][c][x];
+        }
+      }
+      // refill ring position j: W entries ahead, into the next query
+      if (e + W < NE)
+        issue(j, dc, e + W);
+      else
+        issue(j, dn, e + W - NE);
+    }
+    const int t = apos(qi) - q_start;
+    bf16* dst = out + ((size_t)(b * (size_t)Nq + t) * Hq + r * G) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (!ok[c]) continue;
+      vec8<bf16> res;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) res[x] = cvt<bf16>(acc[c][x]);
+      st8_nt<bf16>(dst + 8 * (lane + 64 * c), res);  // read back only by the caller
+    }
+    if constexpr (kPack) {  // lanes of slot 0 hold every head once
+      if (4 * lane < G) {
+        vec4<float> l4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l4[j] = Lw[j];
+        st4<float>(&lse[((size_t)b * Nq + t) * Hq + r * G + 4 * lane], l4);
+      }
+    } else if (lane % LPH == 0) {
+      lse[((size_t)b * Nq + t) * Hq + r * G + hg] = Lw[0];
+    }
+
+    dc = dn;
+    id_cur = id_n;
+#pragma unroll
+    for (int c = 0; c < NCL; ++c)
+#pragma unroll
+      for (int j = 0; j < NLV; ++j) lsv[c][j] = lsv_n[c][j];
   }
+  // the ring's last W loads (the repeated last row) drain before the wave ends
 }
 
 template <int D>
