@@ -374,25 +374,14 @@ __device__ __forceinline__ void wave_sync() {
 constexpr int kTopkMax = 32;
 constexpr int kCandMax = 128;  // candidates ranked exactly (two passes of 64)
 
-template <int V>
-__global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int Hkv, int nb,
-            int k, int32_t* __restrict__ ids, float* __restrict__ margin) {
-  __shared__ uint64_t cand[4][kCandMax + 1];  // + a sink for non-candidate lanes
-  __shared__ uint64_t msel[4][2];
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= nrows) return;  // wave-uniform; the kernel has no workgroup barrier
-  const int t = (int)((row / Hkv) % Nq);
-  const int i = q_start + t;
-  const int L = i / 128;
-  int32_t* out = ids + row * k;
-  if (L + 1 <= k) {  // every visible block is selected
-    for (int s = lane; s < k; s += 64) out[s] = s <= L ? s : -1;
-    if (margin && lane == 0) margin[row] = INFINITY;
-    return;
-  }
+// One (query, group) row with L candidate blocks, VV*64 >= L: lane l holds
+// blocks v*64 + l, v < VV.
+template <int VV>
+__device__ __forceinline__ void topk_row(const float* __restrict__ M, int64_t row, int L, int nb,
+                                         int k, int32_t* __restrict__ out,
+                                         float* __restrict__ margin, uint64_t* __restrict__ candw,
+                                         uint64_t* __restrict__ mselw, int lane) {
+  constexpr int V = VV;
   // scores of the candidate blocks 0..L-1; loads past block L-1 return 0
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(M + row * (int64_t)nb), 0, L * 4, 0x00020000);
@@ -433,20 +422,20 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
       if (bal) {  // uniform
         const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        cand[wave][c ? pos : kCandMax] = make_key(x[v] + 0.0f, v * 64 + lane);  // -0 -> +0
+        candw[c ? pos : kCandMax] = make_key(x[v] + 0.0f, v * 64 + lane);  // -0 -> +0
         base += __popcll(bal);
       }
     }
-    if (margin && lane < 2) msel[wave][lane] = 0;
+    if (margin && lane < 2) mselw[lane] = 0;
     wave_sync();
     // 3. exact ranks among candidates
     int pos_base = 0;
     for (int c0 = 0; c0 < C; c0 += 64) {
       const int c = c0 + lane;
       const bool have = c < C;
-      const uint64_t kc = have ? cand[wave][c] : 0;
+      const uint64_t kc = have ? candw[c] : 0;
       int rank = 0;
-      for (int c2 = 0; c2 < C; ++c2) rank += cand[wave][c2] > kc;
+      for (int c2 = 0; c2 < C; ++c2) rank += candw[c2] > kc;
       const bool sel = have && rank < k - 1;
       const uint64_t bal = __ballot(sel);
       if (sel)
@@ -455,14 +444,14 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
             key_blk(kc);
       pos_base += __popcll(bal);
       if (margin && have) {
-        if (rank == k - 2) msel[wave][0] = kc;
-        if (rank == k - 1) msel[wave][1] = kc;
+        if (rank == k - 2) mselw[0] = kc;
+        if (rank == k - 1) mselw[1] = kc;
       }
     }
     if (margin) {
       wave_sync();
-      worst_sel = msel[wave][0];
-      best_unsel = msel[wave][1];
+      worst_sel = mselw[0];
+      best_unsel = mselw[1];
       uint64_t nc = 0;  // best non-candidate
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -511,6 +500,45 @@ topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int
     if (margin)
       margin[row] = best_unsel ? key_score(worst_sel) - key_score(best_unsel) : INFINITY;
   }
+}
+
+template <int VV, int STEP, int V>
+__device__ __forceinline__ void topk_row_fit(const float* __restrict__ M, int64_t row, int L, int nb,
+                                             int k, int32_t* __restrict__ out,
+                                             float* __restrict__ margin, uint64_t* __restrict__ candw,
+                                             uint64_t* __restrict__ mselw, int lane) {
+  if constexpr (VV >= V) {
+    topk_row<V>(M, row, L, nb, k, out, margin, candw, mselw, lane);
+  } else {
+    if (L <= VV * 64)  // uniform
+      topk_row<VV>(M, row, L, nb, k, out, margin, candw, mselw, lane);
+    else
+      topk_row_fit<VV + STEP, STEP, V>(M, row, L, nb, k, out, margin, candw, mselw, lane);
+  }
+}
+
+template <int V>
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ M, int64_t nrows, int Nq, int q_start, int Hkv, int nb,
+            int k, int32_t* __restrict__ ids, float* __restrict__ margin) {
+  __shared__ uint64_t cand[4][kCandMax + 1];  // + a sink for non-candidate lanes
+  __shared__ uint64_t msel[4][2];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= nrows) return;  // wave-uniform; the kernel has no workgroup barrier
+  const int t = (int)((row / Hkv) % Nq);
+  const int i = q_start + t;
+  const int L = i / 128;
+  int32_t* out = ids + row * k;
+  if (L + 1 <= k) {  // every visible block is selected
+    for (int s = lane; s < k; s += 64) out[s] = s <= L ? s : -1;
+    if (margin && lane == 0) margin[row] = INFINITY;
+    return;
+  }
+  // L, and with it the register count of the row, is uniform per wave
+  constexpr int STEP = V >= 16 ? V / 4 : V;
+  topk_row_fit<STEP, STEP, V>(M, row, L, nb, k, out, margin, cand[wave], msel[wave], lane);
 }
 
 hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s) {
