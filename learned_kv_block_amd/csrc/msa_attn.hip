@@ -227,6 +227,55 @@ work_items_kernel(const int32_t* __restrict__ item_off, const int32_t* __restric
   items[it] = make_int4((int)bkt, start, cnt, 0);
 }
 
+// One query per sequence (decode): a row's valid ids are distinct, so every
+// (batch, group, block) bucket holds one entry and each entry is its own work
+// item; one workgroup compacts them in order, skipping empty slots (and the
+// local block with skip_local).
+constexpr int64_t kDirectMax = 1 << 15;  // slots one workgroup compacts (32 passes)
+
+__global__ void __launch_bounds__(1024)
+direct_items_kernel(const int32_t* __restrict__ ids, int64_t nrows, int K, int nb, int nwin,
+                    int q_start, bool skip_local, int32_t* __restrict__ entries,
+                    int4* __restrict__ items, int32_t* __restrict__ totals) {
+  __shared__ int wsum[16];
+  __shared__ int wbase[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = q_start / 128;
+  const int64_t n = nrows * K;
+  int base = 0;
+  for (int64_t e0 = 0; e0 < n; e0 += 1024) {
+    const int64_t e = e0 + tid;
+    const int id = e < n ? ids[e] : -1;
+    const bool valid = id >= 0 && !(skip_local && id == L);
+    const uint64_t bal = __ballot(valid);
+    const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int w = 0; w < 16; ++w) {
+        wbase[w] = acc;
+        acc += wsum[w];
+      }
+      wsum[0] = acc;  // the chunk's total, read after the next barrier
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = base + wbase[wave] + before;
+      const int64_t row = e / K;  // (b, r) of Nq = 1
+      entries[pos] = (int)(e % K);  // (t = 0) << 6 | slot
+      items[pos] = make_int4((int)(row * nwin * nb + id), pos, 1, 0);
+    }
+    base += wsum[0];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    totals[0] = base;
+    totals[1] = base;
+  }
+}
+
 static size_t bucket_lds_bytes(const Dims& d, int arrays) {
   return (size_t)arrays * d.Hkv * d.nb * sizeof(int32_t);
 }
@@ -235,6 +284,14 @@ static bool bucket_use_lds(const Dims& d) { return bucket_lds_bytes(d, 2) <= 64 
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
                             hipStream_t s) {
   hipError_t e;
+  if (d.Nq == 1 && d.rows > 0 && d.items_max >= d.entries_max &&
+      d.rows * d.Hkv * d.K <= kDirectMax) {
+    prof_before(MSA_K_BUCKET_HIST, s);
+    direct_items_kernel<<<1, 1024, 0, s>>>(ids, d.rows * d.Hkv, d.K, d.nb, d.nwin, d.q_start,
+                                           skip_local, w.entries, w.items, w.totals);
+    prof_after(MSA_K_BUCKET_HIST, s);
+    return hipGetLastError();
+  }
   if ((e = launch_fill_i32(w.counts, d.buckets, 0, s)) != hipSuccess) return e;
   const unsigned nchunks = (unsigned)((d.buckets + kScanChunk - 1) / kScanChunk);
   auto scan = [&](int entries_max, int items_max) {
@@ -505,10 +562,11 @@ sparse_attn_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #define MSA_NT_STORE 1
 #endif
 
-constexpr int kPipeWaves = 8;
-
-template <int D, int G>
-__global__ void __launch_bounds__(512, 1)
+// NWV waves per workgroup, 32 (query, head) rows each: 8 for prefill (one
+// workgroup per CU); 1 when a bucket holds at most 32/G queries (decode), so
+// that two workgroups share a CU and one's K/V copy overlaps the other's work.
+template <int D, int G, int NWV>
+__global__ void __launch_bounds__(64 * NWV, 1)
 sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         const bf16* __restrict__ v, const int4* __restrict__ items,
                         const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
@@ -519,12 +577,12 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int DT = D / 32;
   constexpr int CPR = D / 8;                             // 16-byte chunks per row
   constexpr int TILE = 128 * D;                          // elements per K or V tile
-  constexpr int LOADS = 128 * CPR / (64 * kPipeWaves);   // global_load_lds per wave per tile
+  constexpr int LOADS = 128 * CPR / (64 * NWV);   // global_load_lds per wave per tile
   constexpr int LDW = D + 8;                             // staging row stride (elements)
   constexpr int RCH = 32 * CPR / 64;                     // row chunks per lane per wave tile
   __shared__ bf16 Kb[TILE];
   __shared__ bf16 Vb[TILE];
-  __shared__ bf16 Wst[kPipeWaves][32 * LDW];
+  __shared__ bf16 Wst[NWV][32 * LDW];
   typedef __attribute__((address_space(3))) void lds_void;
 
   const int total = totals[1];
@@ -834,15 +892,22 @@ static hipError_t attn_dispatch_g(const Dims& d, const void* q, const void* k, c
 template <int D>
 static hipError_t attn_pipe_dispatch_g(const Dims& d, const void* q, const void* k, const void* v,
                                        const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
-  // one workgroup per CU, a multiple of 8 (one share per XCD)
-  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  // persistent grid, a multiple of 8 (one share per XCD): one 8-wave workgroup
+  // per CU, or two 1-wave workgroups per CU for items of at most 32/G queries
+  const bool one_wave = d.qt * d.G <= 32;
+  const unsigned grid = (unsigned)((((one_wave ? 2 : 1) * d.num_cus + 7) / 8) * 8);
   const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
+#define MSA_PIPE_LAUNCH(GG, NW)                                                                 \
+  sparse_attn_pipe_kernel<D, GG, NW><<<grid, 64 * NW, 0, s>>>(                                 \
+      (const bf16*)q, (const bf16*)k, (const bf16*)v, w.items, w.entries, w.totals,            \
+      (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K, scale_log2,   \
+      (size_t)d.slots)
 #define MSA_PIPE_CASE(GG)                                                                       \
   case GG:                                                                                      \
-    sparse_attn_pipe_kernel<D, GG><<<grid, 64 * kPipeWaves, 0, s>>>(                           \
-        (const bf16*)q, (const bf16*)k, (const bf16*)v, w.items, w.entries, w.totals,          \
-        (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K, scale_log2, \
-        (size_t)d.slots);                                                                       \
+    if (one_wave)                                                                               \
+      MSA_PIPE_LAUNCH(GG, 1);                                                                   \
+    else                                                                                        \
+      MSA_PIPE_LAUNCH(GG, 8);                                                                   \
     break;
   switch (d.G) {
     MSA_PIPE_CASE(1)
@@ -853,6 +918,7 @@ static hipError_t attn_pipe_dispatch_g(const Dims& d, const void* q, const void*
     default: return hipErrorInvalidValue;
   }
 #undef MSA_PIPE_CASE
+#undef MSA_PIPE_LAUNCH
   return hipGetLastError();
 }
 

@@ -51,6 +51,17 @@ SMALL = [
     # bf16, G=2, chunked prefill starting inside a block, d=64, d_idx=32
     _small("bf16_g2_chunk", seqlen_kv=2600, seqlen_q=700, q_start=1900, num_q_heads=4,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=6),
+    # decode: one query per sequence at its last position (work items built
+    # straight from the ids; one-wave attention workgroups), with KL
+    _small("bf16_decode_b3", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
+           num_kv_heads=4, topk=6, with_kl=True),
+    # two queries per sequence, G=8, d=64: one-wave attention on bucketed items
+    _small("bf16_g8_q2", batch=2, seqlen_kv=2000, seqlen_q=2, q_start=1998, num_q_heads=16,
+           num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
+    # fp32 decode, ragged last block
+    _small("f32_decode_b2", batch=2, seqlen_kv=1500, seqlen_q=1, q_start=1499, num_q_heads=8,
+           num_kv_heads=2, head_dim=64, idx_dim=32, topk=4, dtype=si.F32, scale=1.0,
+           with_kl=True),
 ]
 
 
