@@ -57,8 +57,10 @@ def _L():
         lib.msa_ref_attn.argtypes = [sp, P, P, P, P, P, I64, P, P, ctypes.c_int]
         lib.msa_ref_kl_row.argtypes = [ctypes.c_int, I64, P, P, P, P, P, P, P]
         lib.msa_ref_kl.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, P, ctypes.c_int]
+        lib.msa_ref_attn_bwd.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, ctypes.c_int]
+        lib.msa_ref_idx_bwd.argtypes = [sp, P, P, P, P, ctypes.c_double, P, I64, P, P]
         for f in ("msa_ref_topk_row", "msa_ref_select", "msa_ref_attn", "msa_ref_kl_row",
-                  "msa_ref_kl"):
+                  "msa_ref_kl", "msa_ref_attn_bwd", "msa_ref_idx_bwd"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -187,3 +189,39 @@ def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True):
     if want_dlogits:
         out["dlogits"] = dl
     return out
+
+
+def attn_bwd(shape: RefShape, q, k, v, ids, dout, rows=None):
+    """Gradients with the selection fixed: (dq [n, Hq, d], dk, dv [B, N, Hkv, d]) in float64.
+
+    q and dout are compact [n, Hq, d] in the input dtype; dk/dv sum over the listed rows."""
+    q = _raw(q, shape.dtype)
+    k = _raw(k, shape.dtype)
+    v = _raw(v, shape.dtype)
+    dout = _raw(dout, shape.dtype)
+    ids = _c(ids, np.int32)
+    r, n = _rows(shape, rows)
+    d = shape.head_dim
+    dq = np.empty((n, shape.num_q_heads, d), dtype=np.float64)
+    kv_shape = (shape.batch, shape.seqlen_kv, shape.num_kv_heads, d)
+    dk = np.empty(kv_shape, dtype=np.float64)
+    dv = np.empty(kv_shape, dtype=np.float64)
+    rc = _L().msa_ref_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(ids), _p(dout), _p(r),
+                               n, _p(dq), _p(dk), _p(dv), threads())
+    assert rc == 0, rc
+    return dq, dk, dv
+
+
+def idx_bwd(shape: RefShape, q_idx, k_idx, ids, dlogits, coef=1.0, rows=None):
+    """(dq_idx [n, Hkv, d_idx], dk_idx [B, N, d_idx]) in float64 from dlogits [n, Hkv, k, Bk]."""
+    q_idx = _raw(q_idx, shape.dtype)
+    k_idx = _raw(k_idx, shape.dtype)
+    ids = _c(ids, np.int32)
+    dl = _c(dlogits, np.float64)
+    r, n = _rows(shape, rows)
+    dq = np.empty((n, shape.num_kv_heads, shape.idx_dim), dtype=np.float64)
+    dk = np.empty((shape.batch, shape.seqlen_kv, shape.idx_dim), dtype=np.float64)
+    rc = _L().msa_ref_idx_bwd(ctypes.byref(shape), _p(q_idx), _p(k_idx), _p(ids), _p(dl),
+                              float(coef), _p(r), n, _p(dq), _p(dk))
+    assert rc == 0, rc
+    return dq, dk

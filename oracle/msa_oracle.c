@@ -35,6 +35,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 typedef struct {
   int32_t batch, seqlen_kv, seqlen_q, q_start, num_q_heads, num_kv_heads;
@@ -429,6 +432,168 @@ int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void
     double acc = 0.0;
     for (int64_t a = 0; a < nrows * Hkv; ++a) acc += kl_rows[a];
     *kl_mean = nrows > 0 ? acc / (double)(nrows * Hkv) : 0.0;
+  }
+  return REF_OK;
+}
+
+/* ------------------------------------------------------------------------ backward */
+
+/*
+ * Gradients of the sparse attention with the selection held fixed.
+ *  - [Native] eq. (11): with alpha the softmax weights over the selected set,
+ *    o the output and g = dL/do, the gradient of the logit z_s of a selected
+ *    position is alpha_s g.(v_s - o); unselected positions get no gradient
+ *    (eq. 12: the hard selection has zero derivative almost everywhere).
+ *  - z_s = q.k_s / sqrt(d) ([Blog] "核心思想"), so dL/dq = sum_s dz_s k_s / sqrt(d),
+ *    dL/dk_s = dz_s q / sqrt(d), and o = sum_s alpha_s v_s gives dL/dv_s = alpha_s g.
+ *  - [Indexer] §2.3: the G heads of group r read KV head r, so k and v of group
+ *    r collect the gradients of all G heads.
+ * q and dout are compact [nrows, Hq, d] (dout in the input dtype); k, v are
+ * [B, N, Hkv, d]; ids [nrows, Hkv, k]. Writes dq [nrows, Hq, d] and, summed
+ * over the listed rows, dk and dv [B, N, Hkv, d] (double; fully overwritten).
+ * Rows run in parallel with per-thread dk/dv sums added in thread order.
+ */
+int msa_ref_attn_bwd(const msa_ref_shape* s, const void* q, const void* kk, const void* v,
+                     const int32_t* ids, const void* dout, const int64_t* rows, int64_t nrows,
+                     double* dq, double* dk, double* dv, int nthreads) {
+  if (!shape_ok(s) || !q || !kk || !v || !ids || !dout || !dq || !dk || !dv || nrows < 0)
+    return REF_ERR_ARG;
+  const int Hq = s->num_q_heads, Hkv = s->num_kv_heads, G = Hq / Hkv, d = s->head_dim;
+  const int Bk = s->block_size, k = s->topk;
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const int64_t nkv = (int64_t)s->batch * N * Hkv * d;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  if (nthreads < 1) nthreads = 1;
+  double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)nkv, sizeof(double));
+  if (!part && nkv > 0) return REF_ERR_ARG;
+  int err = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    int tid = 0;
+#ifdef _OPENMP
+    tid = omp_get_thread_num();
+#endif
+    double* pdk = part + (size_t)tid * 2 * (size_t)nkv;
+    double* pdv = pdk + nkv;
+    const int64_t cap = (int64_t)k * Bk;
+    int64_t* J = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
+    double* z = (double*)malloc(sizeof(double) * (size_t)cap);
+    double* o = (double*)malloc(sizeof(double) * (size_t)d);
+    if (!J || !z || !o) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t qq = 0; qq < nrows; ++qq) {
+      if (err) continue;
+      const int64_t row = rows ? rows[qq] : qq;
+      const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+      const int64_t i = s->q_start + t;
+      for (int r = 0; r < Hkv; ++r) {
+        const int64_t n = support(ids + (qq * Hkv + r) * k, k, Bk, i, N, J, NULL, NULL);
+        for (int h = r * G; h < (r + 1) * G; ++h) {
+          double* dqh = dq + (qq * Hq + h) * d;
+          for (int c = 0; c < d; ++c) dqh[c] = 0.0;
+          if (n == 0) continue;
+          /* forward on the support: logits, LSE, weights, output */
+          double m = -INFINITY;
+          for (int64_t a = 0; a < n; ++a) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c)
+              acc += ld(q, s->dtype, (qq * Hq + h) * d + c) *
+                     ld(kk, s->dtype, ((b * N + J[a]) * Hkv + r) * d + c);
+            z[a] = acc * inv_sqrt_d;
+            m = z[a] > m ? z[a] : m;
+          }
+          double zs = 0.0;
+          for (int64_t a = 0; a < n; ++a) zs += exp(z[a] - m);
+          const double LSE = m + log(zs);
+          for (int c = 0; c < d; ++c) o[c] = 0.0;
+          for (int64_t a = 0; a < n; ++a) {
+            const double w = exp(z[a] - LSE);
+            for (int c = 0; c < d; ++c) o[c] += w * ld(v, s->dtype, ((b * N + J[a]) * Hkv + r) * d + c);
+          }
+          double go = 0.0;
+          for (int c = 0; c < d; ++c) go += ld(dout, s->dtype, (qq * Hq + h) * d + c) * o[c];
+          /* eq. (11) per selected position, then the chain through z = q.k/sqrt(d) */
+          for (int64_t a = 0; a < n; ++a) {
+            const int64_t kv = ((b * N + J[a]) * Hkv + r) * d;
+            const double alpha = exp(z[a] - LSE);
+            double gv = 0.0;
+            for (int c = 0; c < d; ++c) gv += ld(dout, s->dtype, (qq * Hq + h) * d + c) * ld(v, s->dtype, kv + c);
+            const double dz = alpha * (gv - go);
+            for (int c = 0; c < d; ++c) {
+              const double gc = ld(dout, s->dtype, (qq * Hq + h) * d + c);
+              dqh[c] += dz * ld(kk, s->dtype, kv + c) * inv_sqrt_d;
+              pdk[kv + c] += dz * ld(q, s->dtype, (qq * Hq + h) * d + c) * inv_sqrt_d;
+              pdv[kv + c] += alpha * gc;
+            }
+          }
+        }
+      }
+    }
+    free(J);
+    free(z);
+    free(o);
+  }
+  if (!err) {
+    for (int64_t x = 0; x < nkv; ++x) {
+      double sk = 0.0, sv = 0.0;
+      for (int th = 0; th < nthreads; ++th) {
+        sk += part[(size_t)th * 2 * (size_t)nkv + x];
+        sv += part[(size_t)th * 2 * (size_t)nkv + nkv + x];
+      }
+      dk[x] = sk;
+      dv[x] = sv;
+    }
+  }
+  free(part);
+  return err ? REF_ERR_ARG : REF_OK;
+}
+
+/*
+ * Chain of the index-logit gradient into the index projections.
+ *  - [Indexer] §2.1: S_idx[i,j] = q_idx[i,r] . k_idx[j] / sqrt(d_idx) with one
+ *    k_idx head shared by every group r, so dL/dq_idx[i,r] = sum_j
+ *    dS_idx[i,r,j] k_idx[j] / sqrt(d_idx) and dL/dk_idx[j] = sum over (i, r)
+ *    of dS_idx[i,r,j] q_idx[i,r] / sqrt(d_idx).
+ *  - [KL] §3: the gradient in the index logits is P_idx - P (dlogits, laid out
+ *    [nrows, Hkv, k, Bk] by slot and offset in the slot's block, as
+ *    msa_ref_kl writes it); coef carries the loss weight and the 1/(N Hkv) mean.
+ * q_idx compact [nrows, Hkv, d_idx]; k_idx [B, N, d_idx]. Writes dq_idx
+ * [nrows, Hkv, d_idx] and dk_idx [B, N, d_idx] summed over the listed rows
+ * (double; fully overwritten). Sequential.
+ */
+int msa_ref_idx_bwd(const msa_ref_shape* s, const void* q_idx, const void* k_idx,
+                    const int32_t* ids, const double* dlogits, double coef, const int64_t* rows,
+                    int64_t nrows, double* dq_idx, double* dk_idx) {
+  if (!shape_ok(s) || !q_idx || !k_idx || !ids || !dlogits || !dq_idx || !dk_idx || nrows < 0)
+    return REF_ERR_ARG;
+  const int Hkv = s->num_kv_heads, di = s->idx_dim, Bk = s->block_size, k = s->topk;
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const double sc = coef / sqrt((double)di);
+  for (int64_t x = 0; x < (int64_t)s->batch * N * di; ++x) dk_idx[x] = 0.0;
+  for (int64_t qq = 0; qq < nrows; ++qq) {
+    const int64_t row = rows ? rows[qq] : qq;
+    const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+    const int64_t i = s->q_start + t;
+    for (int r = 0; r < Hkv; ++r) {
+      double* dqr = dq_idx + (qq * Hkv + r) * di;
+      for (int c = 0; c < di; ++c) dqr[c] = 0.0;
+      for (int sl = 0; sl < k; ++sl) {
+        const int32_t blk = ids[(qq * Hkv + r) * k + sl];
+        if (blk < 0) continue;
+        for (int off = 0; off < Bk; ++off) {
+          const int64_t j = (int64_t)blk * Bk + off;
+          if (j > i || j >= N) break;
+          const double g = dlogits[((qq * Hkv + r) * (int64_t)k + sl) * Bk + off] * sc;
+          for (int c = 0; c < di; ++c) {
+            dqr[c] += g * ld(k_idx, s->dtype, (b * N + j) * di + c);
+            dk_idx[(b * N + j) * di + c] += g * ld(q_idx, s->dtype, (qq * Hkv + r) * di + c);
+          }
+        }
+      }
+    }
   }
   return REF_OK;
 }

@@ -401,3 +401,136 @@ def test_kl_dense_support_matches_full_context_logits():
             two = logsumexp(sel["block_lse"][t, r, :L + 1])
             assert abs(two - out["lse_idx"][t, r]) < 1e-12
     assert abs(out["kl_mean"] - out["kl_rows"].mean()) < 1e-15
+
+
+# ----------------------------------------------------------------------- backward
+
+
+def test_native_eq11_hand_gradient():
+    """"2.4 · 训练原生稀疏" eq. (11) hand calculation: weights (0.75, 0.25), v1=(2,0), v2=(0,2),
+    g=(1,-1) give logit gradients (0.75, -0.75). With z = q.k/sqrt(2), q = (sqrt(2) ln3, 0),
+    k1 = (1, 0), k2 = (0, 0): dk_s = dz_s q/sqrt(2) = dz_s (ln3, 0), dv_s = alpha_s g,
+    dq = sum_s dz_s k_s/sqrt(2)."""
+    g = json.load(open(os.path.join(GOLD, "native_eq11_gradient_example.json")))
+    d = 2
+    sh = shape(seqlen_kv=2, seqlen_q=1, q_start=1, num_q_heads=1, num_kv_heads=1, head_dim=d,
+               idx_dim=1, block_size=128, topk=1)
+    q = np.array([[[math.sqrt(2.0) * g["logits"][0], 0.0]]], dtype=np.float32)
+    k = np.array([[[[1.0, 0.0]], [[0.0, 0.0]]]], dtype=np.float32)
+    v = np.array([[[g["values"][0]], [g["values"][1]]]], dtype=np.float32)
+    dout = np.array([[g["upstream"]]], dtype=np.float32)
+    ids = np.zeros((1, 1, 1), dtype=np.int32)
+    dq, dk, dv = oracle.attn_bwd(sh, q, k, v, ids, dout)
+    ln3 = float(q[0, 0, 0]) / math.sqrt(2.0)
+    dz = [dk[0, 0, 0, 0] / ln3, dk[0, 1, 0, 0] / ln3]
+    np.testing.assert_allclose(dz, g["logit_grad"], atol=1e-6)
+    assert abs(dk[0, 0, 0, 1]) < 1e-12 and abs(dk[0, 1, 0, 1]) < 1e-12
+    for s in range(2):
+        np.testing.assert_allclose(dv[0, s, 0], np.array(g["upstream"]) * g["weights"][s], atol=1e-6)
+    np.testing.assert_allclose(dq[0, 0], [g["logit_grad"][0] / math.sqrt(2.0), 0.0], atol=1e-6)
+
+
+def _bwd_case(rng, B=1, N=200, Nq=200, q_start=0, Hq=4, Hkv=2, d=8, di=4, Bk=32, topk=3):
+    sh = shape(batch=B, seqlen_kv=N, seqlen_q=Nq, q_start=q_start, num_q_heads=Hq,
+               num_kv_heads=Hkv, head_dim=d, idx_dim=di, block_size=Bk, topk=topk)
+    x = dict(q=rnd(rng, B * Nq, Hq, d), k=rnd(rng, B, N, Hkv, d), v=rnd(rng, B, N, Hkv, d),
+             q_idx=rnd(rng, B * Nq, Hkv, di), k_idx=rnd(rng, B, N, di),
+             dout=rnd(rng, B * Nq, Hq, d))
+    x["ids"] = oracle.select(sh, x["q_idx"], x["k_idx"])["ids"]
+    return sh, x
+
+
+def test_attn_bwd_is_finite_difference_of_forward():
+    """Gradients of L = sum(dout * O) with the selection held fixed ("2.4" eq. (12): the hard
+    selection has zero derivative almost everywhere), by central differences of the oracle's
+    own forward on fp32 inputs (the step is the fp32-rounded difference)."""
+    rng = np.random.default_rng(21)
+    sh, x = _bwd_case(rng, q_start=100, Nq=100, N=200)
+    dq, dk, dv = oracle.attn_bwd(sh, x["q"], x["k"], x["v"], x["ids"], x["dout"])
+
+    def loss(q, k, v):
+        o, _ = oracle.attn(sh, q, k, v, x["ids"])
+        return float(np.sum(o * x["dout"].astype(np.float64)))
+
+    def fd(name, idx):
+        a = x[name]
+        p, m = a.copy(), a.copy()
+        p[idx] = np.float32(a[idx] + np.float32(2e-3))
+        m[idx] = np.float32(a[idx] - np.float32(2e-3))
+        args = {n: x[n] for n in ("q", "k", "v")}
+        lp = loss(**{**args, name: p})
+        lm = loss(**{**args, name: m})
+        return (lp - lm) / (float(p[idx]) - float(m[idx]))
+
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        a = x[name]
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, s)) for s in a.shape)
+            f = fd(name, idx)
+            assert abs(f - grad[idx]) < 2e-5 * max(1.0, abs(f)), (name, idx, f, grad[idx])
+
+
+def test_attn_bwd_k_all_blocks_is_dense_autograd():
+    """With k covering every block the sparse attention is dense causal attention ("2.4"), so
+    its gradients equal the library's autograd of causal scaled_dot_product_attention in fp64
+    (GQA G=2, ragged last block, chunked queries)."""
+    rng = np.random.default_rng(22)
+    B, N, Nq, q_start, Hq, Hkv, d, Bk = 2, 150, 60, 90, 4, 2, 8, 32
+    nb = (N + Bk - 1) // Bk
+    sh, x = _bwd_case(rng, B=B, N=N, Nq=Nq, q_start=q_start, Hq=Hq, Hkv=Hkv, d=d, Bk=Bk, topk=nb)
+    dq, dk, dv = oracle.attn_bwd(sh, x["q"], x["k"], x["v"], x["ids"], x["dout"])
+    G = Hq // Hkv
+    qt = torch.tensor(x["q"].reshape(B, Nq, Hq, d), dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(x["k"], dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(x["v"], dtype=torch.float64, requires_grad=True)
+    i = torch.arange(Nq)[:, None] + q_start
+    mask = torch.arange(N)[None, :] <= i
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(0, 2, 1, 3), kt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3),
+        vt.repeat_interleave(G, dim=2).permute(0, 2, 1, 3), attn_mask=mask)
+    g = torch.tensor(x["dout"].reshape(B, Nq, Hq, d), dtype=torch.float64).permute(0, 2, 1, 3)
+    (o * g).sum().backward()
+    np.testing.assert_allclose(dq.reshape(B, Nq, Hq, d), qt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-11)
+
+
+def test_attn_bwd_closed_form_sums():
+    """Per row and head the weights sum to 1 and the logit gradients of eq. (11) sum to
+    g.o - g.o = 0, so summed over all keys dV[b, :, r] equals the sum of dout over the group's
+    heads and rows, and dK[b, :, r] sums to zero (any selection)."""
+    rng = np.random.default_rng(23)
+    B, Nq, Hq, Hkv, d = 2, 120, 4, 2, 8
+    sh, x = _bwd_case(rng, B=B, N=180, Nq=Nq, q_start=60, Hq=Hq, Hkv=Hkv, d=d, topk=2)
+    dq, dk, dv = oracle.attn_bwd(sh, x["q"], x["k"], x["v"], x["ids"], x["dout"])
+    G = Hq // Hkv
+    dout = x["dout"].astype(np.float64).reshape(B, Nq, Hkv, G, d)
+    np.testing.assert_allclose(dv.sum(axis=1), dout.sum(axis=(1, 3)), atol=1e-10)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-10)
+
+
+def test_idx_bwd_is_finite_difference_of_kl():
+    """"KL alignment" §3 / indexer note §2.1: with the selection fixed, the gradient of
+    sum(kl_rows) in q_idx and k_idx is the chain of dlogits = P_idx - P through
+    S_idx = q_idx.k_idx/sqrt(d_idx) (one shared k_idx head); central differences of the
+    oracle's own KL on fp32 inputs."""
+    rng = np.random.default_rng(24)
+    sh, x = _bwd_case(rng, B=1, N=160, Nq=80, q_start=80, Hq=4, Hkv=2, d=8, di=4, topk=2)
+    base = oracle.kl(sh, x["q"], x["k"], x["q_idx"], x["k_idx"], x["ids"])
+    dqi, dki = oracle.idx_bwd(sh, x["q_idx"], x["k_idx"], x["ids"], base["dlogits"], coef=1.0)
+
+    def total(qi, ki):
+        return float(oracle.kl(sh, x["q"], x["k"], qi, ki, x["ids"],
+                               want_dlogits=False)["kl_rows"].sum())
+
+    for name, grad in (("q_idx", dqi), ("k_idx", dki)):
+        a = x[name]
+        for _ in range(10):
+            idx = tuple(int(rng.integers(0, s)) for s in a.shape)
+            p, m = a.copy(), a.copy()
+            p[idx] = np.float32(a[idx] + np.float32(2e-3))
+            m[idx] = np.float32(a[idx] - np.float32(2e-3))
+            args = {"qi": x["q_idx"], "ki": x["k_idx"]}
+            key = "qi" if name == "q_idx" else "ki"
+            f = (total(**{**args, key: p}) - total(**{**args, key: m})) / (float(p[idx]) - float(m[idx]))
+            assert abs(f - grad[idx]) < 2e-5 * max(1.0, abs(f)), (name, idx, f, grad[idx])
