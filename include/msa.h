@@ -86,7 +86,7 @@ typedef struct {
   int32_t dtype;        /* msa_dtype of every floating-point input and of `out` */
 } msa_shape;
 
-enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2 };
+enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_ATTN_BWD = 3 };
 
 /*
  * Bytes of workspace the call `op` (MSA_OP_*) needs for `shape`; 0 for an
@@ -169,6 +169,32 @@ msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, co
                         float* kl_rows, float* kl_mean, float* dlogits_idx, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * msa_attn_bwd — gradients of msa_attn_fwd with the selection held fixed
+ * ("2.4 · 训练原生稀疏" eq. (11): the logit gradient of a selected position is
+ * alpha_s g.(v_s - o); eq. (12): the hard selection itself has no gradient;
+ * the same page requires the backward to stay on the selected blocks). Through
+ * z = q.k / sqrt(d): dq = sum_s dz_s k_s / sqrt(d), dk_s gets dz_s q / sqrt(d)
+ * and dv_s gets alpha_s g, summed over every (query, head) of the group that
+ * selected the key's block.
+ *
+ *  in   q, k, v, block_ids  as for msa_attn_fwd (the same ids)
+ *  in   out, lse            device: the outputs of msa_attn_fwd for these inputs
+ *  in   dout                device [batch, seqlen_q, num_q_heads, head_dim], dtype: dL/dout
+ *  out  dq                  device [batch, seqlen_q, num_q_heads, head_dim], dtype
+ *  out  dk, dv              device [batch, seqlen_kv, num_kv_heads, head_dim], dtype:
+ *                           the contributions of this call's query rows; keys no
+ *                           row selected get 0 (fully overwritten)
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_ATTN_BWD) bytes
+ * Accumulation is fp32 (dk, dv through fp32 atomics, so their last bits may
+ * vary from run to run). fp32 inputs need head_dim 64 (MSA_ERR_UNSUPPORTED
+ * otherwise).
+ */
+msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* block_ids, const void* out, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* msa_status_string(msa_status status);
 
@@ -183,7 +209,7 @@ enum {
   MSA_K_INDEX_BLOCKMAX = 0, MSA_K_TOPK = 1, MSA_K_BUCKET_HIST = 2, MSA_K_BUCKET_SCAN = 3,
   MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
-  MSA_K_COUNT = 12
+  MSA_K_ATTN_BWD = 12, MSA_K_COUNT = 13
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* total_ms, int* launches);

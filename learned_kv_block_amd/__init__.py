@@ -11,6 +11,8 @@ Functions (same names as the C entry points):
   msa_attn_fwd(q, k, v, block_ids, q_start=0, ...)   -> (out, lse)
   msa_kl_align(q, k, q_idx, k_idx, block_ids, lse_main, q_start=0, ...)
                                                      -> kl_rows, kl_mean, dlogits
+  msa_attn_bwd(q, k, v, block_ids, out, lse, dout, q_start=0, ...)
+                                                     -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -25,11 +27,11 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
 MSA_F32, MSA_BF16 = 0, 1
-MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL = 0, 1, 2
+MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD = 0, 1, 2, 3
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce"]
-EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align",
+           "kl_reduce", "attn_bwd"]
+EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_status_string", "msa_prof_begin", "msa_prof_end"]
 
 
@@ -62,7 +64,9 @@ def lib() -> ctypes.CDLL:
         L.msa_select.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_attn_fwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_kl_align.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_prof_begin", "msa_prof_end"):
+        L.msa_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_prof_begin",
+                  "msa_prof_end"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -207,6 +211,29 @@ def msa_kl_align(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: t
     if want_dlogits:
         out["dlogits"] = dl
     return out
+
+
+def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: torch.Tensor,
+                 out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, q_start: int = 0,
+                 idx_dim: int = 64, workspace: Optional[torch.Tensor] = None):
+    """Gradients of msa_attn_fwd with the selection fixed: (dq like q, dk like k, dv like v)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (block_ids, "block_ids"), (out, "out"),
+                 (dout, "dout")):
+        _check(t, n, 4)
+    _check(lse, "lse", 3)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, block_ids.shape[3], _dtype_code(q))
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws, nws = _workspace(sh, MSA_OP_ATTN_BWD, q.device, workspace)
+    st = lib().msa_attn_bwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(block_ids),
+                            _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(ws), nws, _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_attn_bwd")
+    return dq, dk, dv
 
 
 class KernelTimer:

@@ -34,6 +34,8 @@ Dims for_op(Dims d, int op) {
   // hold more (Nq * G <= 32, decode), for the one-wave attention workgroups
   if (op == MSA_OP_ATTN && d.dtype == MSA_BF16) set_item_size(&d, (d.Nq * d.G <= 32 ? 32 : 256) / d.G);
   if (op == MSA_OP_KL && d.dtype == MSA_BF16 && d.G >= 8) set_item_size(&d, 256 / d.G);
+  // attention backward: 32 (query, head) rows per item
+  if (op == MSA_OP_ATTN_BWD) set_item_size(&d, 32 / d.G);
   return d;
 }
 
@@ -92,6 +94,7 @@ struct Layout {
   size_t counts, offsets, cursor, item_off, totals, items, entries, chunks;  // bucketing
   size_t nchunks;  // scan chunks of 4096 buckets (+1)
   size_t opart, lpart;                                               // attention
+  size_t drow, dqpart, dk_acc, dv_acc;                               // attention backward
   size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
   size_t total;
 };
@@ -122,6 +125,12 @@ Layout layout(const Dims& d, int op) {
     // one extra slot: scratch target of the attention kernel's unused rows
     L.opart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
     L.lpart = take((size_t)(d.slots + 1) * d.G * 4);
+  } else if (op == MSA_OP_ATTN_BWD) {
+    const size_t nkv = (size_t)d.B * d.N * d.Hkv * d.D;
+    L.drow = take((size_t)d.rows * d.Hq * 4);
+    L.dqpart = take((size_t)d.slots * d.G * d.D * elem_size(d));
+    L.dk_acc = take(nkv * 4);
+    L.dv_acc = take(nkv * 4);
   } else {
     L.slot_lse = take((size_t)d.slots * 4);
     L.lse_idx = take((size_t)d.rows * d.Hkv * 4);
@@ -222,7 +231,8 @@ const char* msa_status_string(msa_status st) {
 size_t msa_workspace_size(const msa_shape* shape, int op) {
   Dims d;
   if (make_dims(shape, &d) != MSA_OK) return 0;
-  if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL) return 0;
+  if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_ATTN_BWD)
+    return 0;
   return layout(for_op(d, op), op).total;
 }
 
@@ -283,6 +293,46 @@ msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, co
           ? launch_combine_local(d, q, k, v, ws + L.opart, lpart, block_ids, out, lse, stream)
           : launch_combine(d, ws + L.opart, lpart, block_ids, out, lse, stream);
   prof_after(MSA_K_COMBINE, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                        const int32_t* block_ids, const void* out, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.dtype == MSA_F32 && d.D != 64) return MSA_ERR_UNSUPPORTED;  // LDS tiles of the fp32 kernel
+  d = for_op(d, MSA_OP_ATTN_BWD);
+  const int64_t nkv = (int64_t)d.B * d.N * d.Hkv * d.D;
+  if (nkv > 0) {
+    if (!dk || !dv) return MSA_ERR_NULL;
+    if (!aligned16(dk) || !aligned16(dv)) return MSA_ERR_SHAPE;
+  }
+  if (d.rows > 0) {
+    if (!q || !k || !v || !block_ids || !out || !lse || !dout || !dq) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(dq))
+      return MSA_ERR_SHAPE;
+  }
+  const Layout L = layout(d, MSA_OP_ATTN_BWD);
+  if (d.rows > 0 && (st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  if (d.rows == 0) {  // no query row: dk = dv = 0 (the zero bit pattern of fp32 and bf16)
+    const int64_t words = nkv * (int64_t)elem_size(d) / 4;
+    if (launch_fill_i32(static_cast<int32_t*>(dk), words, 0, stream) != hipSuccess ||
+        launch_fill_i32(static_cast<int32_t*>(dv), words, 0, stream) != hipSuccess)
+      return MSA_ERR_DEVICE;
+    return MSA_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  const AttnWs w = carve(L, workspace);
+  if (launch_bucketing(d, block_ids, w, false, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  const hipError_t e = launch_attn_bwd(
+      d, q, k, v, block_ids, out, lse, dout, w, reinterpret_cast<float*>(ws + L.drow),
+      ws + L.dqpart, reinterpret_cast<float*>(ws + L.dk_acc),
+      reinterpret_cast<float*>(ws + L.dv_acc), dq, dk, dv, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 

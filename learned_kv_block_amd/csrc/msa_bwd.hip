@@ -1,0 +1,353 @@
+// msa_bwd.hip — backward of the sparse attention over the selected blocks,
+// and the chain of the index-logit gradient into the index projections.
+//
+// The selection is held fixed ("2.4 · 训练原生稀疏" (training-native sparse
+// attention) eq. (12): the hard top-k has zero derivative almost everywhere),
+// and every step stays on the selected support (same page: a backward that
+// rebuilds the full score matrix would pay the quadratic cost again). With
+// alpha the softmax weights of a (query, head) over its support, o its output
+// and g = dL/do, eq. (11) gives the logit gradient dz_s = alpha_s g.(v_s - o)
+// = P (dP - D) with dP = g.v_s and D = g.o; then, through z = q.k / sqrt(d),
+//   dq = sum_s dz_s k_s / sqrt(d),  dk_s += dz_s q / sqrt(d),  dv_s += alpha_s g.
+//
+// Execution is KV-outer like the forward: the (query, slot) pairs are inverted
+// into per-(batch, group, block) buckets (the counting sort of msa_attn.hip,
+// local block included) and cut into items of 32 (query, head) rows. A
+// persistent workgroup (4 waves) walks a contiguous range of items; wave w owns
+// keys 32w..32w+31 of the current block and keeps their dK and dV in registers
+// across the consecutive items of a bucket, adding them to fp32 accumulators
+// (atomics) when the bucket changes. dQ gets one partial per (query, slot),
+// summed per row afterwards.
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// D[row, h] = dO . O (fp32), one thread per (row, head)
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+bwd_rowdot_kernel(const T* __restrict__ out, const T* __restrict__ dout, int64_t n,
+                  float* __restrict__ drow) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  const T* o = out + x * D;
+  const T* g = dout + x * D;
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < D; c += 8) {
+    const vec8<T> a = ld8<T>(o + c), b = ld8<T>(g + c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  }
+  drow[x] = acc;
+}
+
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256, 1)
+attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                const T* __restrict__ dout, const float* __restrict__ lse,
+                const float* __restrict__ rowdot, const int4* __restrict__ items,
+                const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
+                T* __restrict__ dqpart, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
+                int N, int Nq, int q_start, int Hkv, int nb, int nbw, int topk, float scale) {
+  constexpr int R = 32;          // (query, head) rows per item
+  constexpr int QI = R / G;      // queries per item
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LK = D + PAD;    // row stride of the row-major K, V, Q, dO tiles
+  constexpr int LT = 128 + PAD;  // row stride of K^T [D][128] and of dS [R][128]
+  constexpr int LR = R + PAD;    // row stride of Q^T, dO^T [D][R]
+  constexpr int KSD = D / 16, DT = D / 32, CH = D / 8;
+  __shared__ __attribute__((aligned(16))) T Ks[128 * LK];
+  __shared__ __attribute__((aligned(16))) T Vs[128 * LK];
+  __shared__ __attribute__((aligned(16))) T KT[D * LT];
+  __shared__ __attribute__((aligned(16))) T Qs[R * LK];
+  __shared__ __attribute__((aligned(16))) T dOs[R * LK];
+  __shared__ __attribute__((aligned(16))) T QT[D * LR];
+  __shared__ __attribute__((aligned(16))) T dOT[D * LR];
+  __shared__ __attribute__((aligned(16))) T dSs[R * LT];
+  __shared__ float lse_s[R], d_s[R];
+  __shared__ int irow_s[R];
+
+  // contiguous item range of this workgroup inside its XCD's share
+  const int total = totals[1];
+  const int nwg_x = gridDim.x / 8;
+  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
+  const int per_x = (total + 7) / 8;
+  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
+  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  if (i0 >= i1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = Hkv * G;
+  const size_t kvrow = (size_t)Hkv * D;
+  const float sl2 = scale * kLog2e;
+
+  f32x16 dka[DT], dva[DT];  // dK^T, dV^T of keys 32w + l32: element e is d = 32dt + drow(e, h)
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dka[dt][e] = 0.0f;
+        dva[dt][e] = 0.0f;
+      }
+  };
+  auto flush = [&](int bkt) {
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    const int key = blk * 128 + 32 * w + l32;
+    if (key >= N) return;
+    const size_t base = ((size_t)b * N + key) * kvrow + (size_t)r * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int dd = 32 * dt + drow(e, h);
+        unsafeAtomicAdd(dk_acc + base + dd, dka[dt][e] * scale);
+        unsafeAtomicAdd(dv_acc + base + dd, dva[dt][e]);
+      }
+  };
+  // two 4-element runs of a contiguous row: k-indices {16c+4h+0..3, 16c+8+4h+0..3},
+  // the rows an accumulator's elements 8c..8c+7 hold
+  auto frag_rows = [&](const T* row, int c) {
+    const vec4<T> lo = ld4<T>(row + 16 * c + 4 * h), hi = ld4<T>(row + 16 * c + 8 + 4 * h);
+    vec8<T> a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = lo[e];
+      a[4 + e] = hi[e];
+    }
+    return a;
+  };
+
+  zero_acc();
+  int cur = -1;
+  for (int it = i0; it < i1; ++it) {
+    const int4 itm = items[it];
+    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    __syncthreads();  // every wave is done with the previous item's tiles
+    if (bkt != cur) {  // uniform
+      if (cur >= 0) flush(cur);
+      zero_acc();
+      cur = bkt;
+      // K, V (row-major) and K^T of block blk; rows past N are zero
+      for (int c = tid; c < 128 * CH; c += 256) {
+        const int rho = c / CH, dc = c % CH;
+        const int key = blk * 128 + rho;
+        vec8<T> kk = zero8<T>(), vv = zero8<T>();
+        if (key < N) {
+          const size_t off = ((size_t)b * N + key) * kvrow + (size_t)r * D + 8 * dc;
+          kk = ld8<T>(k + off);
+          vv = ld8<T>(v + off);
+        }
+        st8<T>(Ks + rho * LK + 8 * dc, kk);
+        st8<T>(Vs + rho * LK + 8 * dc, vv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) KT[(8 * dc + e) * LT + rho] = kk[e];
+      }
+    }
+    // the item's rows: row rho = (query rho / G of the item, head rho % G)
+    for (int c = tid; c < R * CH; c += 256) {
+      const int rho = c / CH, dc = c % CH;
+      const int j = rho / G;
+      vec8<T> qq = zero8<T>(), gg = zero8<T>();
+      if (j < cnt) {
+        const int t = entries[start + j] >> 6;
+        const size_t off = ((size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G) * D + 8 * dc;
+        qq = ld8<T>(q + off);
+        gg = ld8<T>(dout + off);
+      }
+      st8<T>(Qs + rho * LK + 8 * dc, qq);
+      st8<T>(dOs + rho * LK + 8 * dc, gg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        QT[(8 * dc + e) * LR + rho] = qq[e];
+        dOT[(8 * dc + e) * LR + rho] = gg[e];
+      }
+    }
+    if (tid < R) {
+      const int j = tid / G;
+      if (j < cnt) {
+        const int t = entries[start + j] >> 6;
+        const size_t rr = (size_t)(b * (size_t)Nq + t) * Hq + r * G + tid % G;
+        lse_s[tid] = lse[rr];
+        d_s[tid] = rowdot[rr];
+        irow_s[tid] = q_start + t;
+      } else {  // unused row: every key masked, so P = dS = 0
+        lse_s[tid] = 0.0f;
+        d_s[tid] = 0.0f;
+        irow_s[tid] = -1;
+      }
+    }
+    __syncthreads();
+
+    // ---- phase 1: wave w, keys 32w..32w+31: S = Q K^T, dP = dO V^T (rows x keys)
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sacc[e] = 0.0f;
+      pacc[e] = 0.0f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+      const vec8<T> kf = ld8<T>(Ks + (32 * w + l32) * LK + 16 * ks + 8 * h);
+      const vec8<T> vf = ld8<T>(Vs + (32 * w + l32) * LK + 16 * ks + 8 * h);
+      mma(sacc, ld8<T>(Qs + l32 * LK + 16 * ks + 8 * h), kf);
+      mma(pacc, ld8<T>(dOs + l32 * LK + 16 * ks + 8 * h), vf);
+    }
+    // P = exp(S - LSE) on the support (causal mask), dS = P (dP - D)
+    const int key = blk * 128 + 32 * w + l32;
+    float p[16], ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = drow(e, h);
+      const bool vis = key <= irow_s[row];
+      p[e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lse_s[row] * kLog2e))
+                 : 0.0f;
+      ds[e] = p[e] * (pacc[e] - d_s[row]);
+      dSs[row * LT + 32 * w + l32] = cvt<T>(ds[e]);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (d x keys; contraction over the item's rows)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      vec8<T> pf, sf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pf[e] = cvt<T>(p[8 * c + e]);
+        sf[e] = cvt<T>(ds[8 * c + e]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR, c), pf);
+        mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR, c), sf);
+      }
+    }
+    __syncthreads();  // dS of every wave's keys is in LDS
+
+    // ---- phase 2: dQ = dS K (rows x d); wave w takes d columns 32w..32w+31
+    if (32 * w < D) {  // uniform
+      f32x16 qacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qacc[e] = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        mma(qacc, ld8<T>(dSs + l32 * LT + 16 * kc + 8 * h),
+            ld8<T>(KT + (32 * w + l32) * LT + 16 * kc + 8 * h));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = drow(e, h);
+        const int j = row / G;
+        if (j < cnt) {
+          const int ent = entries[start + j];
+          const size_t slot =
+              ((size_t)(b * (size_t)Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
+          dqpart[(slot * G + row % G) * D + 32 * w + l32] = cvt<T>(qacc[e] * scale);
+        }
+      }
+    }
+  }
+  if (cur >= 0) flush(cur);
+}
+
+// dq[row, r*G + hh] = sum over the row's used slots of the slot partials
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(256)
+dq_sum_kernel(const T* __restrict__ dqpart, const int32_t* __restrict__ ids, int64_t nrg,
+              int topk, T* __restrict__ dq) {
+  constexpr int CH = D / 8;
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row*Hkv + r, hh, chunk)
+  if (x >= nrg * G * CH) return;
+  const int ch = (int)(x % CH);
+  const int hh = (int)((x / CH) % G);
+  const int64_t rg = x / (CH * G);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < topk; ++s) {
+    if (ids[rg * topk + s] < 0) continue;
+    const vec8<T> a = ld8<T>(dqpart + ((rg * topk + s) * G + hh) * D + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (float)a[e];
+  }
+  vec8<T> res;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) res[e] = cvt<T>(acc[e]);
+  st8<T>(dq + (rg * G + hh) * D + 8 * ch, res);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+f32_to_kernel(const float* __restrict__ src, int64_t n, T* __restrict__ dst) {
+  for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n;
+       x += (int64_t)gridDim.x * 256)
+    dst[x] = cvt<T>(src[x]);
+}
+
+template <typename T, int D>
+static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const void* v,
+                          const int32_t* ids, const void* out, const float* lse,
+                          const void* dout, const AttnWs& w,
+                          float* drow, void* dqpart, float* dk_acc, float* dv_acc, void* dq,
+                          void* dk, void* dv, hipStream_t s) {
+  const int64_t nkv = (int64_t)d.B * d.N * d.Hkv * D;
+  hipError_t e;
+  if ((e = launch_fill_f32(dk_acc, nkv, 0.0f, s)) != hipSuccess) return e;
+  if ((e = launch_fill_f32(dv_acc, nkv, 0.0f, s)) != hipSuccess) return e;
+  const int64_t nrh = d.rows * d.Hq;
+  bwd_rowdot_kernel<T, D><<<(unsigned)((nrh + 255) / 256), 256, 0, s>>>(
+      (const T*)out, (const T*)dout, nrh, drow);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  const float scale = (float)(1.0 / sqrt((double)D));
+  const int64_t nrg = d.rows * d.Hkv;
+  const unsigned sgrid = (unsigned)((nrg * d.G * (D / 8) + 255) / 256);
+  const unsigned cgrid = (unsigned)std::min<int64_t>((nkv + 255) / 256, 4096);
+#define MSA_BWD_CASE(GG)                                                                        \
+  case GG:                                                                                      \
+    prof_before(MSA_K_ATTN_BWD, s);                                                             \
+    attn_bwd_kernel<T, D, GG><<<grid, 256, 0, s>>>(                                            \
+        (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, drow, w.items, w.entries,   \
+        w.totals, (T*)dqpart, dk_acc, dv_acc, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, \
+        d.K, scale);                                                                            \
+    prof_after(MSA_K_ATTN_BWD, s);                                                              \
+    if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
+    if (nrg > 0)                                                                                \
+      dq_sum_kernel<T, D, GG><<<sgrid, 256, 0, s>>>((const T*)dqpart, ids, nrg, d.K,         \
+                                                    (T*)dq);                                    \
+    break;
+  switch (d.G) {
+    MSA_BWD_CASE(1)
+    MSA_BWD_CASE(2)
+    MSA_BWD_CASE(4)
+    MSA_BWD_CASE(8)
+    MSA_BWD_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef MSA_BWD_CASE
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (nkv > 0) {
+    f32_to_kernel<T><<<cgrid, 256, 0, s>>>(dk_acc, nkv, (T*)dk);
+    f32_to_kernel<T><<<cgrid, 256, 0, s>>>(dv_acc, nkv, (T*)dv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const Dims& d, const void* q, const void* k, const void* v,
+                           const int32_t* ids, const void* out, const float* lse,
+                           const void* dout, const AttnWs& w,
+                           float* drow, void* dqpart, float* dk_acc, float* dv_acc, void* dq,
+                           void* dk, void* dv, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128)
+      return bwd_run<bf16, 128>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq,
+                                dk, dv, s);
+    if (d.D == 64)
+      return bwd_run<bf16, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq,
+                               dk, dv, s);
+  } else if (d.D == 64) {
+    return bwd_run<float, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq, dk,
+                              dv, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -158,6 +158,11 @@ hipError_t launch_combine_local(const Dims& d, const void* q, const void* k, con
                                 const void* opart, const float* lpart, const int32_t* ids,
                                 void* out, float* lse, hipStream_t s);
 
+hipError_t launch_attn_bwd(const Dims& d, const void* q, const void* k, const void* v,
+                           const int32_t* ids, const void* out, const float* lse,
+                           const void* dout, const AttnWs& w, float* drow, void* dqpart,
+                           float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
+                           hipStream_t s);
 hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* ids, const float* lse_main,
                      const AttnWs& w, float* idx_stats, float* lse_idx, float* kl_part,

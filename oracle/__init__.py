@@ -191,10 +191,11 @@ def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True):
     return out
 
 
-def attn_bwd(shape: RefShape, q, k, v, ids, dout, rows=None):
+def attn_bwd(shape: RefShape, q, k, v, ids, dout, rows=None, want_kv=True):
     """Gradients with the selection fixed: (dq [n, Hq, d], dk, dv [B, N, Hkv, d]) in float64.
 
-    q and dout are compact [n, Hq, d] in the input dtype; dk/dv sum over the listed rows."""
+    q and dout are compact [n, Hq, d] in the input dtype; dk/dv sum over the listed rows
+    (None when want_kv is False)."""
     q = _raw(q, shape.dtype)
     k = _raw(k, shape.dtype)
     v = _raw(v, shape.dtype)
@@ -204,8 +205,8 @@ def attn_bwd(shape: RefShape, q, k, v, ids, dout, rows=None):
     d = shape.head_dim
     dq = np.empty((n, shape.num_q_heads, d), dtype=np.float64)
     kv_shape = (shape.batch, shape.seqlen_kv, shape.num_kv_heads, d)
-    dk = np.empty(kv_shape, dtype=np.float64)
-    dv = np.empty(kv_shape, dtype=np.float64)
+    dk = np.empty(kv_shape, dtype=np.float64) if want_kv else None
+    dv = np.empty(kv_shape, dtype=np.float64) if want_kv else None
     rc = _L().msa_ref_attn_bwd(ctypes.byref(shape), _p(q), _p(k), _p(v), _p(ids), _p(dout), _p(r),
                                n, _p(dq), _p(dk), _p(dv), threads())
     assert rc == 0, rc

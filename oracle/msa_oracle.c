@@ -450,21 +450,22 @@ int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void
  *    r collect the gradients of all G heads.
  * q and dout are compact [nrows, Hq, d] (dout in the input dtype); k, v are
  * [B, N, Hkv, d]; ids [nrows, Hkv, k]. Writes dq [nrows, Hq, d] and, summed
- * over the listed rows, dk and dv [B, N, Hkv, d] (double; fully overwritten).
- * Rows run in parallel with per-thread dk/dv sums added in thread order.
+ * over the listed rows, dk and dv [B, N, Hkv, d] (double; fully overwritten;
+ * both may be NULL to get dq alone). Rows run in parallel with per-thread
+ * dk/dv sums added in thread order.
  */
 int msa_ref_attn_bwd(const msa_ref_shape* s, const void* q, const void* kk, const void* v,
                      const int32_t* ids, const void* dout, const int64_t* rows, int64_t nrows,
                      double* dq, double* dk, double* dv, int nthreads) {
-  if (!shape_ok(s) || !q || !kk || !v || !ids || !dout || !dq || !dk || !dv || nrows < 0)
+  if (!shape_ok(s) || !q || !kk || !v || !ids || !dout || !dq || nrows < 0 || (!dk != !dv))
     return REF_ERR_ARG;
   const int Hq = s->num_q_heads, Hkv = s->num_kv_heads, G = Hq / Hkv, d = s->head_dim;
   const int Bk = s->block_size, k = s->topk;
   const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
-  const int64_t nkv = (int64_t)s->batch * N * Hkv * d;
+  const int64_t nkv = dk ? (int64_t)s->batch * N * Hkv * d : 0;
   const double inv_sqrt_d = 1.0 / sqrt((double)d);
   if (nthreads < 1) nthreads = 1;
-  double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)nkv, sizeof(double));
+  double* part = nkv > 0 ? (double*)calloc((size_t)nthreads * 2 * (size_t)nkv, sizeof(double)) : NULL;
   if (!part && nkv > 0) return REF_ERR_ARG;
   int err = 0;
 #pragma omp parallel num_threads(nthreads)
@@ -473,8 +474,8 @@ int msa_ref_attn_bwd(const msa_ref_shape* s, const void* q, const void* kk, cons
 #ifdef _OPENMP
     tid = omp_get_thread_num();
 #endif
-    double* pdk = part + (size_t)tid * 2 * (size_t)nkv;
-    double* pdv = pdk + nkv;
+    double* pdk = part ? part + (size_t)tid * 2 * (size_t)nkv : NULL;
+    double* pdv = part ? pdk + nkv : NULL;
     const int64_t cap = (int64_t)k * Bk;
     int64_t* J = (int64_t*)malloc(sizeof(int64_t) * (size_t)cap);
     double* z = (double*)malloc(sizeof(double) * (size_t)cap);
@@ -525,8 +526,10 @@ int msa_ref_attn_bwd(const msa_ref_shape* s, const void* q, const void* kk, cons
             for (int c = 0; c < d; ++c) {
               const double gc = ld(dout, s->dtype, (qq * Hq + h) * d + c);
               dqh[c] += dz * ld(kk, s->dtype, kv + c) * inv_sqrt_d;
-              pdk[kv + c] += dz * ld(q, s->dtype, (qq * Hq + h) * d + c) * inv_sqrt_d;
-              pdv[kv + c] += alpha * gc;
+              if (pdk) {
+                pdk[kv + c] += dz * ld(q, s->dtype, (qq * Hq + h) * d + c) * inv_sqrt_d;
+                pdv[kv + c] += alpha * gc;
+              }
             }
           }
         }

@@ -42,7 +42,8 @@ _DEV_SO = os.path.join(_HERE, "libmsa_gen_hip.so")
 F32, BF16 = 0, 1
 
 # Tensor ids of the generator streams.
-TID = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "hot": 6, "dir": 7, "boost": 8}
+TID = {"q": 1, "k": 2, "v": 3, "q_idx": 4, "k_idx": 5, "hot": 6, "dir": 7, "boost": 8,
+       "dout": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -80,7 +81,7 @@ class MsaConfig:
     # [rows, cols] views of every tensor
     def view(self, name: str):
         B, N, Nq = self.batch, self.seqlen_kv, self.seqlen_q
-        if name == "q":
+        if name in ("q", "dout"):
             return B * Nq, self.num_q_heads * self.head_dim
         if name in ("k", "v"):
             return B * N, self.num_kv_heads * self.head_dim
@@ -92,7 +93,7 @@ class MsaConfig:
 
     def shape(self, name: str):
         B, N, Nq = self.batch, self.seqlen_kv, self.seqlen_q
-        if name == "q":
+        if name in ("q", "dout"):
             return (B, Nq, self.num_q_heads, self.head_dim)
         if name in ("k", "v"):
             return (B, N, self.num_kv_heads, self.head_dim)
@@ -291,9 +292,9 @@ def host_tensor(cfg: MsaConfig, name: str) -> np.ndarray:
 def host_query_rows(cfg: MsaConfig, name: str, qrows: Sequence[int]) -> np.ndarray:
     """q or q_idx for the listed query rows (flat b*Nq + t), compact [n, heads, dim]."""
     qrows = np.asarray(qrows, dtype=np.int64)
-    if name == "q":
-        return host_view_rows(cfg, "q", qrows).reshape(qrows.shape[0], cfg.num_q_heads,
-                                                         cfg.head_dim)
+    if name in ("q", "dout"):
+        return host_view_rows(cfg, name, qrows).reshape(qrows.shape[0], cfg.num_q_heads,
+                                                          cfg.head_dim)
     if name == "q_idx":
         H = cfg.num_kv_heads
         vr = (qrows[:, None] * H + np.arange(H)[None, :]).reshape(-1)
