@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--kl", action="store_true",
                     help="add msa_kl_align (with the index-logit gradient) to the step; "
                          "a training-side measurement, not the headline line")
+    ap.add_argument("--bwd", action="store_true",
+                    help="add msa_attn_bwd (dq, dk, dv for a seeded dout) to the step; "
+                         "a training-side measurement, not the headline line")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for HBM counter calibration)")
@@ -139,7 +142,8 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    x = {n: si.device_tensor(cfg, n, dev) for n in ("q", "k", "v", "q_idx", "k_idx")}
+    names_in = ("q", "k", "v", "q_idx", "k_idx") + (("dout",) if args.bwd else ())
+    x = {n: si.device_tensor(cfg, n, dev) for n in names_in}
     sh_sel = msa.shape_for(x["q_idx"], x["k_idx"], cfg.topk, cfg.q_start, cfg.num_q_heads,
                            cfg.head_dim)
     ws_sel = torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_SELECT), dtype=torch.uint8,
@@ -150,6 +154,8 @@ def main():
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev)
     ws_kl = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_KL), dtype=torch.uint8,
                          device=dev) if args.kl else None)
+    ws_bwd = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_ATTN_BWD), dtype=torch.uint8,
+                          device=dev) if args.bwd else None)
 
     def step():
         sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
@@ -160,6 +166,9 @@ def main():
         if args.kl:
             msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse,
                              q_start=cfg.q_start, want_dlogits=True, workspace=ws_kl)
+        if args.bwd:
+            msa.msa_attn_bwd(x["q"], x["k"], x["v"], sel["ids"], out, lse, x["dout"],
+                             q_start=cfg.q_start, idx_dim=cfg.idx_dim, workspace=ws_bwd)
         return sel["ids"]
 
     if args.copy_calibration:
@@ -200,6 +209,8 @@ def main():
                  "work_items", "sparse_attn", "combine"]
         if args.kl:
             names += ["kl_idx_stats", "kl_idx_lse", "kl_main", "kl_reduce"]
+        if args.bwd:
+            names += ["attn_bwd"]
         for name in names:
             with msa.KernelTimer(name, max_launches=2) as t:
                 step()
@@ -253,7 +264,16 @@ def main():
     if args.kl:
         line["metric"] = "MSA-layer training step (select + attention + KL align) query-tokens/s"
         line["config"]["kl"] = True
-    del x, ws_sel, ws_attn, ws_kl, out, lse
+    if args.bwd:
+        parts = "select + attention" + (" + KL align" if args.kl else "") + " + attention backward"
+        line["metric"] = f"MSA-layer training step ({parts}) query-tokens/s"
+        line["config"]["bwd"] = True
+        # recomputed S and P, dP, dV, dK, dQ: five products of the forward's two,
+        # on every selected (query, head, key) including the local blocks
+        line["attn_bwd_flops_per_step"] = 2.5 * f_attn
+        if "attn_bwd" in kernels:
+            line["attn_bwd_mfma_frac"] = 2.5 * f_attn / (kernels["attn_bwd"] * 1e-3) / PEAK_BF16
+    del x, ws_sel, ws_attn, ws_kl, ws_bwd, out, lse
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -362,7 +362,6 @@ template <typename T> struct AttnPad;
 template <> struct AttnPad<bf16> { static constexpr int K = 8, V = 8; };
 template <> struct AttnPad<float> { static constexpr int K = 4, V = 2; };
 
-typedef short short4v __attribute__((ext_vector_type(4)));
 
 // A operand of O^T = V^T P^T for k-step st and d tile dt from row-major V:
 // elements 0..3 = V[16st + 4h + 0..3][d], 4..7 = V[16st + 4h + 8..11][d],

@@ -61,8 +61,11 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) T KT[D * LT];
   __shared__ __attribute__((aligned(16))) T Qs[R * LK];
   __shared__ __attribute__((aligned(16))) T dOs[R * LK];
-  __shared__ __attribute__((aligned(16))) T QT[D * LR];
-  __shared__ __attribute__((aligned(16))) T dOT[D * LR];
+  // bf16: Q^T and dO^T operands come from the row-major tiles through the
+  // transposing LDS read; fp32 keeps transposed copies
+  constexpr bool kTr = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) T QT[kTr ? 8 : D * LR];
+  __shared__ __attribute__((aligned(16))) T dOT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dSs[R * LT];
   __shared__ float lse_s[R], d_s[R];
   __shared__ int irow_s[R];
@@ -120,8 +123,61 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     return a;
   };
 
+  // rows of an item -> registers (issued one item ahead): chunk c = tid + 256u
+  // covers row c / CH, 8-element chunk c % CH
+  constexpr int RU = R * CH / 256;  // chunks per thread
+  static_assert(R * CH % 256 == 0, "row chunks");
+  vec8<T> qr[RU], gr[RU];
+  float lr = 0.0f, dr = 0.0f;
+  int ir = -1;
+  auto load_rows = [&](int it) {
+    const int4 itm = items[it];
+    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int c = tid + 256 * u;
+      const int rho = c / CH, dc = c % CH;
+      const int j = rho / G;
+      const int t = entries[start + min(j, cnt - 1)] >> 6;  // rows past cnt: a valid row
+      const size_t off = ((size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G) * D + 8 * dc;
+      qr[u] = ld8<T>(q + off);
+      gr[u] = ld8<T>(dout + off);
+    }
+    if (tid < R) {
+      const int j = tid / G;
+      const int t = entries[start + min(j, cnt - 1)] >> 6;
+      const size_t rr = (size_t)(b * (size_t)Nq + t) * Hq + r * G + tid % G;
+      lr = lse[rr];
+      dr = rowdot[rr];
+      ir = j < cnt ? q_start + t : -1;  // an unused row masks every key: P = dS = 0
+    }
+  };
+
+  // A operand X^T (d x rows) of a row-major [R][LK] tile for rows 16c.. and d
+  // tile dt, by the transposing LDS read (16-lane groups: output lane j gets
+  // element j of 4 consecutive rows), with the k-set of frag_rows (bf16 only)
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  auto frag_tr = [&](const T* tile, int c, int dt) {
+    const int krow = 16 * c + 4 * (g16 >> 1) + (s16 >> 2);
+    const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + krow * LK + dcol));
+    const short4v hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + (krow + 8) * LK + dcol));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    vec8<T> a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = l4[e];
+      a[4 + e] = h4[e];
+    }
+    return a;
+  };
+
   zero_acc();
   int cur = -1;
+  load_rows(i0);
   for (int it = i0; it < i1; ++it) {
     const int4 itm = items[it];
     const int bkt = itm.x, start = itm.y, cnt = itm.z;
@@ -147,39 +203,27 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         for (int e = 0; e < 8; ++e) KT[(8 * dc + e) * LT + rho] = kk[e];
       }
     }
-    // the item's rows: row rho = (query rho / G of the item, head rho % G)
-    for (int c = tid; c < R * CH; c += 256) {
-      const int rho = c / CH, dc = c % CH;
-      const int j = rho / G;
-      vec8<T> qq = zero8<T>(), gg = zero8<T>();
-      if (j < cnt) {
-        const int t = entries[start + j] >> 6;
-        const size_t off = ((size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G) * D + 8 * dc;
-        qq = ld8<T>(q + off);
-        gg = ld8<T>(dout + off);
-      }
-      st8<T>(Qs + rho * LK + 8 * dc, qq);
-      st8<T>(dOs + rho * LK + 8 * dc, gg);
+    // the item's rows (row rho = query rho / G of the item, head rho % G), prefetched
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        QT[(8 * dc + e) * LR + rho] = qq[e];
-        dOT[(8 * dc + e) * LR + rho] = gg[e];
+    for (int u = 0; u < RU; ++u) {
+      const int c = tid + 256 * u;
+      const int rho = c / CH, dc = c % CH;
+      st8<T>(Qs + rho * LK + 8 * dc, qr[u]);
+      st8<T>(dOs + rho * LK + 8 * dc, gr[u]);
+      if constexpr (!kTr) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          QT[(8 * dc + e) * LR + rho] = qr[u][e];
+          dOT[(8 * dc + e) * LR + rho] = gr[u][e];
+        }
       }
     }
     if (tid < R) {
-      const int j = tid / G;
-      if (j < cnt) {
-        const int t = entries[start + j] >> 6;
-        const size_t rr = (size_t)(b * (size_t)Nq + t) * Hq + r * G + tid % G;
-        lse_s[tid] = lse[rr];
-        d_s[tid] = rowdot[rr];
-        irow_s[tid] = q_start + t;
-      } else {  // unused row: every key masked, so P = dS = 0
-        lse_s[tid] = 0.0f;
-        d_s[tid] = 0.0f;
-        irow_s[tid] = -1;
-      }
+      lse_s[tid] = lr;
+      d_s[tid] = dr;
+      irow_s[tid] = ir;
     }
+    load_rows(min(it + 1, i1 - 1));  // the next item's rows land during this item
     __syncthreads();
 
     // ---- phase 1: wave w, keys 32w..32w+31: S = Q K^T, dP = dO V^T (rows x keys)
@@ -219,8 +263,13 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR, c), pf);
-        mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR, c), sf);
+        if constexpr (kTr) {
+          mma(dva[dt], frag_tr(dOs, c, dt), pf);
+          mma(dka[dt], frag_tr(Qs, c, dt), sf);
+        } else {
+          mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR, c), pf);
+          mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR, c), sf);
+        }
       }
     }
     __syncthreads();  // dS of every wave's keys is in LDS

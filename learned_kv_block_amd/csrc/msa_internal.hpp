@@ -27,6 +27,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));  // ds_read_tr16_b64 result
 
 template <typename T> struct V8;
 template <> struct V8<bf16> { typedef bf16x8 type; };
