@@ -29,13 +29,17 @@ void set_item_size(Dims* d, int qt) {
 
 // The bf16 attention kernel and the bf16 KL passes with G >= 8 run 256
 // (query, head) rows per work item; the fp32 kernels and other KL shapes run 128.
+#ifndef MSA_BWD_R16
+#define MSA_BWD_R16 64
+#endif
+
 Dims for_op(Dims d, int op) {
   // bf16 attention: 256 (query, head) rows per item; 32 when no bucket can
   // hold more (Nq * G <= 32, decode), for the one-wave attention workgroups
   if (op == MSA_OP_ATTN && d.dtype == MSA_BF16) set_item_size(&d, (d.Nq * d.G <= 32 ? 32 : 256) / d.G);
   if (op == MSA_OP_KL && d.dtype == MSA_BF16 && d.G >= 8) set_item_size(&d, 256 / d.G);
-  // attention backward: 32 (query, head) rows per item
-  if (op == MSA_OP_ATTN_BWD) set_item_size(&d, 32 / d.G);
+  // attention backward: 64 (query, head) rows per item for bf16, 32 for fp32
+  if (op == MSA_OP_ATTN_BWD) set_item_size(&d, (d.dtype == MSA_BF16 ? MSA_BWD_R16 : 32) / d.G);
   return d;
 }
 

@@ -41,6 +41,19 @@ bwd_rowdot_kernel(const T* __restrict__ out, const T* __restrict__ dout, int64_t
   drow[x] = acc;
 }
 
+// (query, head) rows per work item: 64 for bf16; 32 for fp32, whose tiles
+// also keep transposed copies in LDS
+#ifndef MSA_BWD_R16
+#define MSA_BWD_R16 64
+#endif
+#ifndef MSA_BWD_KT16
+#define MSA_BWD_KT16 1
+#endif
+template <typename T>
+constexpr int bwd_rows() {
+  return sizeof(T) == 2 ? MSA_BWD_R16 : 32;
+}
+
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256, 1)
 attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
@@ -49,8 +62,12 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
                 T* __restrict__ dqpart, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
                 int N, int Nq, int q_start, int Hkv, int nb, int nbw, int topk, float scale) {
-  constexpr int R = 32;          // (query, head) rows per item
-  constexpr int QI = R / G;      // queries per item
+  constexpr int R = bwd_rows<T>();  // (query, head) rows per item
+  constexpr int RT = R / 32;        // 32-row tiles per item
+  // bf16: the X^T operands (Q^T, dO^T, K^T) come from the row-major tiles
+  // through the transposing LDS read; fp32 keeps transposed copies
+  constexpr bool kTr = sizeof(T) == 2;
+  constexpr bool kKT = !kTr || MSA_BWD_KT16;  // K^T copy in LDS for dQ
   constexpr int PAD = 16 / (int)sizeof(T);
   constexpr int LK = D + PAD;    // row stride of the row-major K, V, Q, dO tiles
   constexpr int LT = 128 + PAD;  // row stride of K^T [D][128] and of dS [R][128]
@@ -58,12 +75,9 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   constexpr int KSD = D / 16, DT = D / 32, CH = D / 8;
   __shared__ __attribute__((aligned(16))) T Ks[128 * LK];
   __shared__ __attribute__((aligned(16))) T Vs[128 * LK];
-  __shared__ __attribute__((aligned(16))) T KT[D * LT];
+  __shared__ __attribute__((aligned(16))) T KT[kKT ? D * LT : 8];
   __shared__ __attribute__((aligned(16))) T Qs[R * LK];
   __shared__ __attribute__((aligned(16))) T dOs[R * LK];
-  // bf16: Q^T and dO^T operands come from the row-major tiles through the
-  // transposing LDS read; fp32 keeps transposed copies
-  constexpr bool kTr = sizeof(T) == 2;
   __shared__ __attribute__((aligned(16))) T QT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dOT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dSs[R * LT];
@@ -111,7 +125,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       }
   };
   // two 4-element runs of a contiguous row: k-indices {16c+4h+0..3, 16c+8+4h+0..3},
-  // the rows an accumulator's elements 8c..8c+7 hold
+  // the rows (or keys) an accumulator's elements 8c..8c+7 hold
   auto frag_rows = [&](const T* row, int c) {
     const vec4<T> lo = ld4<T>(row + 16 * c + 4 * h), hi = ld4<T>(row + 16 * c + 8 + 4 * h);
     vec8<T> a;
@@ -122,11 +136,32 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     }
     return a;
   };
+  // X^T fragment (d x rows) of a row-major [.][LK] tile: d tile dt, rows 16c..16c+15,
+  // by the transposing LDS read (16-lane groups: output lane j gets element j of 4
+  // consecutive rows), with the k-set of frag_rows (bf16 only)
+  typedef __attribute__((address_space(3))) short4v lds_short4;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  auto frag_tr = [&](const T* tile, int c, int dt) {
+    const int krow = 16 * c + 4 * (g16 >> 1) + (s16 >> 2);
+    const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+    const short4v lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + krow * LK + dcol));
+    const short4v hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + (krow + 8) * LK + dcol));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    vec8<T> a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = l4[e];
+      a[4 + e] = h4[e];
+    }
+    return a;
+  };
 
   // rows of an item -> registers (issued one item ahead): chunk c = tid + 256u
   // covers row c / CH, 8-element chunk c % CH
-  constexpr int RU = R * CH / 256;  // chunks per thread
-  static_assert(R * CH % 256 == 0, "row chunks");
+  constexpr int RU = R * CH / 256;
+  static_assert(R * CH % 256 == 0 && R <= 256, "row chunks");
   vec8<T> qr[RU], gr[RU];
   float lr = 0.0f, dr = 0.0f;
   int ir = -1;
@@ -138,8 +173,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     for (int u = 0; u < RU; ++u) {
       const int c = tid + 256 * u;
       const int rho = c / CH, dc = c % CH;
-      const int j = rho / G;
-      const int t = entries[start + min(j, cnt - 1)] >> 6;  // rows past cnt: a valid row
+      const int t = entries[start + min(rho / G, cnt - 1)] >> 6;  // rows past cnt: a valid row
       const size_t off = ((size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G) * D + 8 * dc;
       qr[u] = ld8<T>(q + off);
       gr[u] = ld8<T>(dout + off);
@@ -154,27 +188,6 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     }
   };
 
-  // A operand X^T (d x rows) of a row-major [R][LK] tile for rows 16c.. and d
-  // tile dt, by the transposing LDS read (16-lane groups: output lane j gets
-  // element j of 4 consecutive rows), with the k-set of frag_rows (bf16 only)
-  typedef __attribute__((address_space(3))) short4v lds_short4;
-  const int g16 = lane >> 4, s16 = lane & 15;
-  auto frag_tr = [&](const T* tile, int c, int dt) {
-    const int krow = 16 * c + 4 * (g16 >> 1) + (s16 >> 2);
-    const int dcol = dt * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
-    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + krow * LK + dcol));
-    const short4v hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + (krow + 8) * LK + dcol));
-    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
-    vec8<T> a;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = l4[e];
-      a[4 + e] = h4[e];
-    }
-    return a;
-  };
-
   zero_acc();
   int cur = -1;
   load_rows(i0);
@@ -187,7 +200,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       if (cur >= 0) flush(cur);
       zero_acc();
       cur = bkt;
-      // K, V (row-major) and K^T of block blk; rows past N are zero
+      // K and V of block blk (row-major; fp32 also K^T); rows past N are zero
       for (int c = tid; c < 128 * CH; c += 256) {
         const int rho = c / CH, dc = c % CH;
         const int key = blk * 128 + rho;
@@ -199,8 +212,10 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         }
         st8<T>(Ks + rho * LK + 8 * dc, kk);
         st8<T>(Vs + rho * LK + 8 * dc, vv);
+        if constexpr (kKT) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) KT[(8 * dc + e) * LT + rho] = kk[e];
+          for (int e = 0; e < 8; ++e) KT[(8 * dc + e) * LT + rho] = kk[e];
+        }
       }
     }
     // the item's rows (row rho = query rho / G of the item, head rho % G), prefetched
@@ -226,49 +241,52 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     load_rows(min(it + 1, i1 - 1));  // the next item's rows land during this item
     __syncthreads();
 
-    // ---- phase 1: wave w, keys 32w..32w+31: S = Q K^T, dP = dO V^T (rows x keys)
-    f32x16 sacc, pacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = 0.0f;
-      pacc[e] = 0.0f;
-    }
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const vec8<T> kf = ld8<T>(Ks + (32 * w + l32) * LK + 16 * ks + 8 * h);
-      const vec8<T> vf = ld8<T>(Vs + (32 * w + l32) * LK + 16 * ks + 8 * h);
-      mma(sacc, ld8<T>(Qs + l32 * LK + 16 * ks + 8 * h), kf);
-      mma(pacc, ld8<T>(dOs + l32 * LK + 16 * ks + 8 * h), vf);
-    }
-    // P = exp(S - LSE) on the support (causal mask), dS = P (dP - D)
+    // ---- phase 1: wave w, keys 32w..32w+31, each 32-row tile of the item:
+    // S = Q K^T, dP = dO V^T (rows x keys), P = exp(S - LSE) on the support,
+    // dS = P (dP - D); dV^T += dO^T P, dK^T += Q^T dS
     const int key = blk * 128 + 32 * w + l32;
-    float p[16], ds[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = drow(e, h);
-      const bool vis = key <= irow_s[row];
-      p[e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lse_s[row] * kLog2e))
-                 : 0.0f;
-      ds[e] = p[e] * (pacc[e] - d_s[row]);
-      dSs[row * LT + 32 * w + l32] = cvt<T>(ds[e]);
-    }
-    // dV^T += dO^T P, dK^T += Q^T dS (d x keys; contraction over the item's rows)
+    for (int rt = 0; rt < RT; ++rt) {
+      f32x16 sacc, pacc;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      vec8<T> pf, sf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pf[e] = cvt<T>(p[8 * c + e]);
-        sf[e] = cvt<T>(ds[8 * c + e]);
+      for (int e = 0; e < 16; ++e) {
+        sacc[e] = 0.0f;
+        pacc[e] = 0.0f;
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if constexpr (kTr) {
-          mma(dva[dt], frag_tr(dOs, c, dt), pf);
-          mma(dka[dt], frag_tr(Qs, c, dt), sf);
-        } else {
-          mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR, c), pf);
-          mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR, c), sf);
+      for (int ks = 0; ks < KSD; ++ks) {
+        const vec8<T> kf = ld8<T>(Ks + (32 * w + l32) * LK + 16 * ks + 8 * h);
+        const vec8<T> vf = ld8<T>(Vs + (32 * w + l32) * LK + 16 * ks + 8 * h);
+        mma(sacc, ld8<T>(Qs + (32 * rt + l32) * LK + 16 * ks + 8 * h), kf);
+        mma(pacc, ld8<T>(dOs + (32 * rt + l32) * LK + 16 * ks + 8 * h), vf);
+      }
+      float p[16], ds[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * rt + drow(e, h);
+        const bool vis = key <= irow_s[row];
+        p[e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lse_s[row] * kLog2e))
+                   : 0.0f;
+        ds[e] = p[e] * (pacc[e] - d_s[row]);
+        dSs[row * LT + 32 * w + l32] = cvt<T>(ds[e]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        vec8<T> pf, sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[e] = cvt<T>(p[8 * c + e]);
+          sf[e] = cvt<T>(ds[8 * c + e]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          if constexpr (kTr) {
+            mma(dva[dt], frag_tr(dOs, 2 * rt + c, dt), pf);
+            mma(dka[dt], frag_tr(Qs, 2 * rt + c, dt), sf);
+          } else {
+            mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR + 32 * rt, c), pf);
+            mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR + 32 * rt, c), sf);
+          }
         }
       }
     }
@@ -276,22 +294,30 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
     // ---- phase 2: dQ = dS K (rows x d); wave w takes d columns 32w..32w+31
     if (32 * w < D) {  // uniform
-      f32x16 qacc;
+      const int dq_t = w;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) qacc[e] = 0.0f;
+      for (int rq = 0; rq < RT; ++rq) {
+        f32x16 qacc;
 #pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        mma(qacc, ld8<T>(dSs + l32 * LT + 16 * kc + 8 * h),
-            ld8<T>(KT + (32 * w + l32) * LT + 16 * kc + 8 * h));
+        for (int e = 0; e < 16; ++e) qacc[e] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = drow(e, h);
-        const int j = row / G;
-        if (j < cnt) {
-          const int ent = entries[start + j];
-          const size_t slot =
-              ((size_t)(b * (size_t)Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
-          dqpart[(slot * G + row % G) * D + 32 * w + l32] = cvt<T>(qacc[e] * scale);
+        for (int kc = 0; kc < 8; ++kc) {
+          if constexpr (!kKT)
+            mma(qacc, frag_rows(dSs + (32 * rq + l32) * LT, kc), frag_tr(Ks, kc, dq_t));
+          else
+            mma(qacc, ld8<T>(dSs + (32 * rq + l32) * LT + 16 * kc + 8 * h),
+                ld8<T>(KT + (32 * dq_t + l32) * LT + 16 * kc + 8 * h));
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 32 * rq + drow(e, h);
+          const int j = row / G;
+          if (j < cnt) {
+            const int ent = entries[start + j];
+            const size_t slot =
+                ((size_t)(b * (size_t)Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
+            dqpart[(slot * G + row % G) * D + 32 * dq_t + l32] = cvt<T>(qacc[e] * scale);
+          }
         }
       }
     }
