@@ -86,7 +86,7 @@ typedef struct {
   int32_t dtype;        /* msa_dtype of every floating-point input and of `out` */
 } msa_shape;
 
-enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_ATTN_BWD = 3 };
+enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_ATTN_BWD = 3, MSA_OP_IDX_BWD = 4 };
 
 /*
  * Bytes of workspace the call `op` (MSA_OP_*) needs for `shape`; 0 for an
@@ -195,6 +195,31 @@ msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, co
                         const void* dout, void* dq, void* dk, void* dv, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * msa_idx_bwd — the index-logit gradient chained into the index projections
+ * (MSA vs DSA indexer note §2.1: S_idx = q_idx . k_idx / sqrt(d_idx) with one
+ * k_idx head shared by every group; KL alignment note §3: the index branch
+ * receives only the KL gradient P_idx - P, the selection held fixed).
+ *   dq_idx[i, r] = coef / sqrt(d_idx) * sum_j dlogits[i, r, j] k_idx[j]
+ *   dk_idx[j]    = coef / sqrt(d_idx) * sum over (i, r) that selected j of dlogits[i, r, j] q_idx[i, r]
+ *
+ *  in   q_idx, k_idx        device, layouts above
+ *  in   block_ids           as for msa_kl_align (the same ids)
+ *  in   dlogits_idx         device fp32 [batch, seqlen_q, num_kv_heads, topk, 128] as
+ *                           msa_kl_align writes it (P_idx - P; 0 off the support)
+ *  in   coef                loss coefficient (e.g. lambda / (N * Hkv) for the mean KL)
+ *  out  dq_idx              device [batch, seqlen_q, num_kv_heads, idx_dim], dtype
+ *  out  dk_idx              device [batch, seqlen_kv, idx_dim], dtype: the
+ *                           contributions of this call's query rows; keys no row
+ *                           selected get 0 (fully overwritten)
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_IDX_BWD) bytes
+ * Accumulation is fp32 (dk_idx through fp32 atomics).
+ */
+msa_status msa_idx_bwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                       const int32_t* block_ids, const float* dlogits_idx, float coef,
+                       void* dq_idx, void* dk_idx, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* msa_status_string(msa_status status);
 
@@ -209,7 +234,7 @@ enum {
   MSA_K_INDEX_BLOCKMAX = 0, MSA_K_TOPK = 1, MSA_K_BUCKET_HIST = 2, MSA_K_BUCKET_SCAN = 3,
   MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
-  MSA_K_ATTN_BWD = 12, MSA_K_COUNT = 13
+  MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_COUNT = 14
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* total_ms, int* launches);

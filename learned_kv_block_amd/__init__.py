@@ -13,6 +13,8 @@ Functions (same names as the C entry points):
                                                      -> kl_rows, kl_mean, dlogits
   msa_attn_bwd(q, k, v, block_ids, out, lse, dout, q_start=0, ...)
                                                      -> (dq, dk, dv)
+  msa_idx_bwd(q_idx, k_idx, block_ids, dlogits, coef, q_start=0, ...)
+                                                     -> (dq_idx, dk_idx)
 """
 from __future__ import annotations
 
@@ -27,11 +29,12 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
 MSA_F32, MSA_BF16 = 0, 1
-MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD = 0, 1, 2, 3
+MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2, 3, 4
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce", "attn_bwd"]
+           "kl_reduce", "attn_bwd", "idx_bwd"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
+           "msa_idx_bwd",
            "msa_status_string", "msa_prof_begin", "msa_prof_end"]
 
 
@@ -65,8 +68,9 @@ def lib() -> ctypes.CDLL:
         L.msa_attn_fwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_kl_align.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_prof_begin",
-                  "msa_prof_end"):
+        L.msa_idx_bwd.argtypes = [S, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
+                  "msa_prof_begin", "msa_prof_end"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
@@ -234,6 +238,27 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: t
     if st != MSA_OK:
         raise MsaError(st, "msa_attn_bwd")
     return dq, dk, dv
+
+
+def msa_idx_bwd(q_idx: torch.Tensor, k_idx: torch.Tensor, block_ids: torch.Tensor,
+                dlogits: torch.Tensor, coef: float = 1.0, q_start: int = 0, num_q_heads: int = 64,
+                head_dim: int = 128, workspace: Optional[torch.Tensor] = None):
+    """Index-logit gradient chained into the index projections: (dq_idx like q_idx,
+    dk_idx like k_idx). dlogits [B, Nq, Hkv, topk, 128] fp32 as msa_kl_align returns it."""
+    _check(q_idx, "q_idx", 4)
+    _check(k_idx, "k_idx", 3)
+    _check(block_ids, "block_ids", 4)
+    _check(dlogits, "dlogits", 5)
+    sh = shape_for(q_idx, k_idx, block_ids.shape[3], q_start, num_q_heads, head_dim)
+    dq = torch.empty_like(q_idx)
+    dk = torch.empty_like(k_idx)
+    ws, nws = _workspace(sh, MSA_OP_IDX_BWD, q_idx.device, workspace)
+    st = lib().msa_idx_bwd(ctypes.byref(sh), _ptr(q_idx), _ptr(k_idx), _ptr(block_ids),
+                           _ptr(dlogits), float(coef), _ptr(dq), _ptr(dk), _ptr(ws), nws,
+                           _stream(q_idx))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_idx_bwd")
+    return dq, dk
 
 
 class KernelTimer:

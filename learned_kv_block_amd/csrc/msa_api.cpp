@@ -40,6 +40,8 @@ Dims for_op(Dims d, int op) {
   if (op == MSA_OP_KL && d.dtype == MSA_BF16 && d.G >= 8) set_item_size(&d, 256 / d.G);
   // attention backward: 64 (query, head) rows per item for bf16, 32 for fp32
   if (op == MSA_OP_ATTN_BWD) set_item_size(&d, (d.dtype == MSA_BF16 ? MSA_BWD_R16 : 32) / d.G);
+  // index chain: 32 queries (of one group) per item
+  if (op == MSA_OP_IDX_BWD) set_item_size(&d, 32);
   return d;
 }
 
@@ -99,6 +101,7 @@ struct Layout {
   size_t nchunks;  // scan chunks of 4096 buckets (+1)
   size_t opart, lpart;                                               // attention
   size_t drow, dqpart, dk_acc, dv_acc;                               // attention backward
+  size_t dqi_part, dki_acc;                                          // index chain
   size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
   size_t total;
 };
@@ -135,6 +138,9 @@ Layout layout(const Dims& d, int op) {
     L.dqpart = take((size_t)d.slots * d.G * d.D * elem_size(d));
     L.dk_acc = take(nkv * 4);
     L.dv_acc = take(nkv * 4);
+  } else if (op == MSA_OP_IDX_BWD) {
+    L.dqi_part = take((size_t)d.slots * d.DI * 4);
+    L.dki_acc = take((size_t)d.B * d.N * d.DI * 4);
   } else {
     L.slot_lse = take((size_t)d.slots * 4);
     L.lse_idx = take((size_t)d.rows * d.Hkv * 4);
@@ -235,7 +241,8 @@ const char* msa_status_string(msa_status st) {
 size_t msa_workspace_size(const msa_shape* shape, int op) {
   Dims d;
   if (make_dims(shape, &d) != MSA_OK) return 0;
-  if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_ATTN_BWD)
+  if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_ATTN_BWD &&
+      op != MSA_OP_IDX_BWD)
     return 0;
   return layout(for_op(d, op), op).total;
 }
@@ -337,6 +344,43 @@ msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, co
       d, q, k, v, block_ids, out, lse, dout, w, reinterpret_cast<float*>(ws + L.drow),
       ws + L.dqpart, reinterpret_cast<float*>(ws + L.dk_acc),
       reinterpret_cast<float*>(ws + L.dv_acc), dq, dk, dv, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_idx_bwd(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                       const int32_t* block_ids, const float* dlogits_idx, float coef,
+                       void* dq_idx, void* dk_idx, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  d = for_op(d, MSA_OP_IDX_BWD);
+  const int64_t nk = (int64_t)d.B * d.N * d.DI;
+  if (nk > 0) {
+    if (!dk_idx) return MSA_ERR_NULL;
+    if (!aligned16(dk_idx)) return MSA_ERR_SHAPE;
+  }
+  if (d.rows > 0) {
+    if (!q_idx || !k_idx || !block_ids || !dlogits_idx || !dq_idx) return MSA_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(dq_idx)) return MSA_ERR_SHAPE;
+  }
+  if (!std::isfinite(coef)) return MSA_ERR_SHAPE;
+  const Layout L = layout(d, MSA_OP_IDX_BWD);
+  if (d.rows > 0 && (st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  if (d.rows == 0) {  // no query row: dk_idx = 0
+    const int64_t words = nk * (int64_t)elem_size(d) / 4;
+    return launch_fill_i32(static_cast<int32_t*>(dk_idx), words, 0, stream) == hipSuccess
+               ? MSA_OK
+               : MSA_ERR_DEVICE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  const AttnWs w = carve(L, workspace);
+  if (launch_bucketing(d, block_ids, w, false, stream) != hipSuccess) return MSA_ERR_DEVICE;
+  const hipError_t e = launch_idx_bwd(d, q_idx, k_idx, block_ids, dlogits_idx, coef, w,
+                                      reinterpret_cast<float*>(ws + L.dqi_part),
+                                      reinterpret_cast<float*>(ws + L.dki_acc), dq_idx, dk_idx,
+                                      stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 

@@ -349,12 +349,193 @@ dq_sum_kernel(const T* __restrict__ dqpart, const int32_t* __restrict__ ids, int
   st8<T>(dq + (rg * G + hh) * D + 8 * ch, res);
 }
 
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 f32_to_kernel(const float* __restrict__ src, int64_t n, T* __restrict__ dst) {
   for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n;
        x += (int64_t)gridDim.x * 256)
     dst[x] = cvt<T>(src[x]);
+}
+
+// ============================================================== index chain
+//
+// dlogits = P_idx - P in the index logits (the KL pass), on the selected
+// support; S_idx = q_idx . k_idx / sqrt(d_idx) with one k_idx head shared by
+// every group (indexer note §2.1), so
+//   dq_idx[i, r] = c/sqrt(d_idx) sum_j dl[i, r, j] k_idx[j],
+//   dk_idx[j]    = c/sqrt(d_idx) sum over (i, r) that selected j of dl[i, r, j] q_idx[i, r],
+// c = the caller's loss coefficient. Same buckets as the attention (items of up
+// to 32 queries of one (batch, group, block)); a persistent workgroup (4
+// waves) keeps the block's dk_idx in registers across the bucket's items (wave
+// w: keys 32w..32w+31) and adds it to an fp32 accumulator at bucket changes;
+// dq_idx gets one fp32 partial per (query, slot), summed per row afterwards.
+// Products use fp32 matrix cores (dlogits are fp32).
+template <typename T, int DI>
+__global__ void __launch_bounds__(256, 1)
+idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* __restrict__ dl,
+               const int4* __restrict__ items, const int32_t* __restrict__ entries,
+               const int32_t* __restrict__ totals, float* __restrict__ dqpart,
+               float* __restrict__ dk_acc, int N, int Nq, int Hkv, int nb, int nbw, int topk,
+               float coef) {
+  constexpr int Q = 32;         // queries per item
+  constexpr int LKT = 128 + 4;  // row stride of K_idx^T [DI][128] and of dl [Q][128]
+  constexpr int LQ = Q + 4;     // row stride of dl^T [128][Q] and Q_idx^T [DI][Q]
+  constexpr int DIT = DI / 32;
+  __shared__ __attribute__((aligned(16))) float KIT[DI * LKT];
+  __shared__ __attribute__((aligned(16))) float DLs[Q * LKT];
+  __shared__ __attribute__((aligned(16))) float DLT[128 * LQ];
+  __shared__ __attribute__((aligned(16))) float QIT[DI * LQ];
+
+  const int total = totals[1];
+  const int nwg_x = gridDim.x / 8;
+  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
+  const int per_x = (total + 7) / 8;
+  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
+  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  if (i0 >= i1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  f32x16 dka[DIT];  // dk_idx of keys 32w + drow(e, h), d columns 32dt + l32
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int dt = 0; dt < DIT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dka[dt][e] = 0.0f;
+  };
+  auto flush = [&](int bkt) {
+    const int blk = bkt % nb, b = bkt / nbw / Hkv;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = blk * 128 + 32 * w + drow(e, h);
+      if (key >= N) continue;
+#pragma unroll
+      for (int dt = 0; dt < DIT; ++dt)
+        unsafeAtomicAdd(dk_acc + ((size_t)b * N + key) * DI + 32 * dt + l32, dka[dt][e] * coef);
+    }
+  };
+
+  zero_acc();
+  int cur = -1;
+  for (int it = i0; it < i1; ++it) {
+    const int4 itm = items[it];
+    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    __syncthreads();
+    if (bkt != cur) {  // uniform
+      if (cur >= 0) flush(cur);
+      zero_acc();
+      cur = bkt;
+      for (int c = tid; c < 128 * DI; c += 256) {  // K_idx^T of the block, keys past N zero
+        const int key = c / DI, dd = c % DI;
+        const int kk = blk * 128 + key;
+        KIT[dd * LKT + key] = kk < N ? (float)ki[((size_t)b * N + kk) * DI + dd] : 0.0f;
+      }
+    }
+    for (int c = tid; c < Q * 128; c += 256) {  // dl rows (zero past cnt) and dl^T
+      const int j = c / 128, o = c % 128;
+      float val = 0.0f;
+      if (j < cnt) {
+        const int ent = entries[start + j];
+        val = dl[(((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk * 128 + (ent & 63) * 128 + o];
+      }
+      DLs[j * LKT + o] = val;
+      DLT[o * LQ + j] = val;
+    }
+    for (int c = tid; c < Q * DI; c += 256) {  // Q_idx^T of the item's queries
+      const int j = c / DI, dd = c % DI;
+      float val = 0.0f;
+      if (j < cnt) {
+        const int t = entries[start + j] >> 6;
+        val = (float)qi[(((size_t)b * Nq + t) * Hkv + r) * DI + dd];
+      }
+      QIT[dd * LQ + j] = val;
+    }
+    __syncthreads();
+    // dq_idx partial of the item's queries: dl (Q x 128) K_idx (128 x DI); wave w < DIT
+    if (w < DIT) {  // uniform
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc)
+        mma(acc, ld8<float>(DLs + l32 * LKT + 16 * kc + 8 * h),
+            ld8<float>(KIT + (32 * w + l32) * LKT + 16 * kc + 8 * h));
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = drow(e, h);
+        if (j < cnt) {
+          const int ent = entries[start + j];
+          const size_t slot = (((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
+          dqpart[slot * DI + 32 * w + l32] = acc[e] * coef;
+        }
+      }
+    }
+    // dk_idx of keys 32w..: dl^T (keys x Q) Q_idx (Q x DI)
+#pragma unroll
+    for (int kc = 0; kc < Q / 16; ++kc) {
+      const vec8<float> a = ld8<float>(DLT + (32 * w + l32) * LQ + 16 * kc + 8 * h);
+#pragma unroll
+      for (int dt = 0; dt < DIT; ++dt)
+        mma(dka[dt], a, ld8<float>(QIT + (32 * dt + l32) * LQ + 16 * kc + 8 * h));
+    }
+  }
+  if (cur >= 0) flush(cur);
+}
+
+// dq_idx[row, r] = sum over the row's used slots of the slot partials
+template <typename T, int DI>
+__global__ void __launch_bounds__(256)
+dqi_sum_kernel(const float* __restrict__ dqpart, const int32_t* __restrict__ ids, int64_t nrg,
+               int topk, T* __restrict__ dq) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row*Hkv + r, d)
+  if (x >= nrg * DI) return;
+  const int64_t rg = x / DI;
+  const int dd = (int)(x % DI);
+  float acc = 0.0f;
+  for (int s = 0; s < topk; ++s)
+    if (ids[rg * topk + s] >= 0) acc += dqpart[(rg * topk + s) * DI + dd];
+  dq[x] = cvt<T>(acc);
+}
+
+template <typename T, int DI>
+static hipError_t idx_bwd_run(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
+                              const float* dl, float coef, const AttnWs& w, float* dqpart,
+                              float* dk_acc, void* dq, void* dk, hipStream_t s) {
+  const int64_t nk = (int64_t)d.B * d.N * DI;
+  hipError_t e;
+  if ((e = launch_fill_f32(dk_acc, nk, 0.0f, s)) != hipSuccess) return e;
+  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  const float c = coef / sqrtf((float)DI);
+  prof_before(MSA_K_IDX_BWD, s);
+  idx_bwd_kernel<T, DI><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, dl, w.items, w.entries,
+                                             w.totals, dqpart, dk_acc, d.N, d.Nq, d.Hkv, d.nb,
+                                             d.nb * d.nwin, d.K, c);
+  prof_after(MSA_K_IDX_BWD, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t nrg = d.rows * d.Hkv;
+  dqi_sum_kernel<T, DI><<<(unsigned)((nrg * DI + 255) / 256), 256, 0, s>>>(dqpart, ids, nrg, d.K,
+                                                                           (T*)dq);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (nk > 0)
+    f32_to_kernel<T><<<(unsigned)std::min<int64_t>((nk + 255) / 256, 4096), 256, 0, s>>>(
+        dk_acc, nk, (T*)dk);
+  return hipGetLastError();
+}
+
+hipError_t launch_idx_bwd(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
+                          const float* dl, float coef, const AttnWs& w, float* dqpart,
+                          float* dk_acc, void* dq, void* dk, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.DI == 64) return idx_bwd_run<bf16, 64>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+    if (d.DI == 32) return idx_bwd_run<bf16, 32>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+  } else {
+    if (d.DI == 64) return idx_bwd_run<float, 64>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+    if (d.DI == 32) return idx_bwd_run<float, 32>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D>

@@ -164,6 +164,9 @@ hipError_t launch_attn_bwd(const Dims& d, const void* q, const void* k, const vo
                            const void* dout, const AttnWs& w, float* drow, void* dqpart,
                            float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
                            hipStream_t s);
+hipError_t launch_idx_bwd(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
+                          const float* dl, float coef, const AttnWs& w, float* dqpart,
+                          float* dk_acc, void* dq, void* dk, hipStream_t s);
 hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* ids, const float* lse_main,
                      const AttnWs& w, float* idx_stats, float* lse_idx, float* kl_part,

@@ -129,3 +129,45 @@ def test_bwd_full_size_sampled():
     print(f"[bwd] {cfg.name}: " + json.dumps(rep), flush=True)
     assert ev <= 1e-2, ev
     assert ek <= 1e-3, ek
+
+
+IDX_CASES = [
+    si.CONFIGS["tiny_f32_n1024"],
+    _cfg("bf16_g16_idx", seqlen_kv=1000, seqlen_q=1000, num_q_heads=64, num_kv_heads=4, topk=4),
+    _cfg("bf16_g8_chunk_d32", batch=2, seqlen_kv=1500, seqlen_q=300, q_start=1200,
+         num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
+    _cfg("bf16_decode_idx", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
+         num_kv_heads=4, topk=6),
+]
+
+
+@pytest.mark.parametrize("cfg", IDX_CASES, ids=[c.name for c in IDX_CASES])
+def test_idx_bwd_every_row(cfg):
+    """msa_idx_bwd on the GPU's own ids and dlogits (from msa_kl_align) against the oracle's
+    chain of the same dlogits; coef 0.37 checks the scaling."""
+    import learned_kv_block_amd as msa
+    print(f"[idx_bwd] start {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg)
+    sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                         num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], q_start=cfg.q_start,
+                                idx_dim=cfg.idx_dim)
+    kl = msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse,
+                          q_start=cfg.q_start)
+    coef = 0.37
+    dqi, dki = msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], kl["dlogits"], coef,
+                               q_start=cfg.q_start, num_q_heads=cfg.num_q_heads,
+                               head_dim=cfg.head_dim)
+    torch.cuda.synchronize()
+    n = cfg.batch * cfg.seqlen_q
+    rows = np.arange(n, dtype=np.int64)
+    q_idx = si.host_query_rows(cfg, "q_idx", rows)
+    k_idx = si.host_tensor(cfg, "k_idx")
+    gids = sel["ids"].reshape(n, cfg.num_kv_heads, cfg.topk).cpu().numpy()
+    dl = kl["dlogits"].reshape(n, cfg.num_kv_heads, cfg.topk, 128).cpu().numpy().astype(np.float64)
+    rq, rk = oracle.idx_bwd(oracle.shape_of(cfg), q_idx, k_idx, gids, dl, coef=coef)
+    t = _tol(cfg)
+    rep = {}
+    _check("dq_idx", dqi.float().cpu().numpy().reshape(rq.shape), rq, t, rep)
+    _check("dk_idx", dki.float().cpu().numpy(), rk, t, rep)
+    print(f"[idx_bwd] {cfg.name}: " + json.dumps(rep), flush=True)
