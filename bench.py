@@ -156,6 +156,8 @@ def main():
                          device=dev) if args.kl else None)
     ws_bwd = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_ATTN_BWD), dtype=torch.uint8,
                           device=dev) if args.bwd else None)
+    ws_ibwd = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_IDX_BWD), dtype=torch.uint8,
+                           device=dev) if args.bwd and args.kl else None)
 
     def step():
         sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
@@ -164,11 +166,16 @@ def main():
         msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], q_start=cfg.q_start,
                          idx_dim=cfg.idx_dim, workspace=ws_attn, out=out, lse=lse)
         if args.kl:
-            msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse,
-                             q_start=cfg.q_start, want_dlogits=True, workspace=ws_kl)
+            kl = msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse,
+                                  q_start=cfg.q_start, want_dlogits=True, workspace=ws_kl)
         if args.bwd:
             msa.msa_attn_bwd(x["q"], x["k"], x["v"], sel["ids"], out, lse, x["dout"],
                              q_start=cfg.q_start, idx_dim=cfg.idx_dim, workspace=ws_bwd)
+            if args.kl:  # the KL gradient into the index projections
+                msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], kl["dlogits"],
+                                1.0 / (cfg.batch * cfg.seqlen_q * cfg.num_kv_heads),
+                                q_start=cfg.q_start, num_q_heads=cfg.num_q_heads,
+                                head_dim=cfg.head_dim, workspace=ws_ibwd)
         return sel["ids"]
 
     if args.copy_calibration:
@@ -210,7 +217,7 @@ def main():
         if args.kl:
             names += ["kl_idx_stats", "kl_idx_lse", "kl_main", "kl_reduce"]
         if args.bwd:
-            names += ["attn_bwd"]
+            names += ["attn_bwd"] + (["idx_bwd"] if args.kl else [])
         for name in names:
             with msa.KernelTimer(name, max_launches=2) as t:
                 step()
@@ -265,7 +272,8 @@ def main():
         line["metric"] = "MSA-layer training step (select + attention + KL align) query-tokens/s"
         line["config"]["kl"] = True
     if args.bwd:
-        parts = "select + attention" + (" + KL align" if args.kl else "") + " + attention backward"
+        parts = ("select + attention" + (" + KL align" if args.kl else "") + " + attention backward" +
+                 (" + index backward" if args.kl else ""))
         line["metric"] = f"MSA-layer training step ({parts}) query-tokens/s"
         line["config"]["bwd"] = True
         # recomputed S and P, dP, dV, dK, dQ: five products of the forward's two,
@@ -273,7 +281,7 @@ def main():
         line["attn_bwd_flops_per_step"] = 2.5 * f_attn
         if "attn_bwd" in kernels:
             line["attn_bwd_mfma_frac"] = 2.5 * f_attn / (kernels["attn_bwd"] * 1e-3) / PEAK_BF16
-    del x, ws_sel, ws_attn, ws_kl, ws_bwd, out, lse
+    del x, ws_sel, ws_attn, ws_kl, ws_bwd, ws_ibwd, out, lse
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

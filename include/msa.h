@@ -206,7 +206,8 @@ msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, co
  *  in   q_idx, k_idx        device, layouts above
  *  in   block_ids           as for msa_kl_align (the same ids)
  *  in   dlogits_idx         device fp32 [batch, seqlen_q, num_kv_heads, topk, 128] as
- *                           msa_kl_align writes it (P_idx - P; 0 off the support)
+ *                           msa_kl_align writes it (P_idx - P; 0 off the support),
+ *                           16-byte aligned
  *  in   coef                loss coefficient (e.g. lambda / (N * Hkv) for the mean KL)
  *  out  dq_idx              device [batch, seqlen_q, num_kv_heads, idx_dim], dtype
  *  out  dk_idx              device [batch, seqlen_kv, idx_dim], dtype: the

@@ -362,7 +362,8 @@ msa_status msa_idx_bwd(const msa_shape* shape, const void* q_idx, const void* k_
   }
   if (d.rows > 0) {
     if (!q_idx || !k_idx || !block_ids || !dlogits_idx || !dq_idx) return MSA_ERR_NULL;
-    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(dq_idx)) return MSA_ERR_SHAPE;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || !aligned16(dq_idx) || !aligned16(dlogits_idx))
+      return MSA_ERR_SHAPE;
   }
   if (!std::isfinite(coef)) return MSA_ERR_SHAPE;
   const Layout L = layout(d, MSA_OP_IDX_BWD);

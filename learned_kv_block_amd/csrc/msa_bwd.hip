@@ -417,8 +417,35 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
     }
   };
 
+  // the item's dl rows (4 floats per chunk) and Q_idx rows, loaded one item ahead
+  constexpr int DU = Q * 128 / 4 / 256;  // dl chunks per thread
+  constexpr int QU = (Q * DI + 255) / 256;  // Q_idx values per thread
+  vec4<float> dlr[DU];
+  float qir[QU];
+  auto load_rows = [&](int it) {
+    const int4 itm = items[it];
+    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {
+      const int c = tid + 256 * u;
+      const int j = c / 32, o4 = c % 32;
+      const int ent = entries[start + min(j, cnt - 1)];  // rows past cnt: zeroed when stored
+      dlr[u] = ld4<float>(dl + (((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk * 128 +
+                          (ent & 63) * 128 + 4 * o4);
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const int c = min(tid + 256 * u, Q * DI - 1);
+      const int j = c / DI, dd = c % DI;
+      const int t = entries[start + min(j, cnt - 1)] >> 6;
+      qir[u] = (float)qi[(((size_t)b * Nq + t) * Hkv + r) * DI + dd];
+    }
+  };
+
   zero_acc();
   int cur = -1;
+  load_rows(i0);
   for (int it = i0; it < i1; ++it) {
     const int4 itm = items[it];
     const int bkt = itm.x, start = itm.y, cnt = itm.z;
@@ -434,25 +461,25 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
         KIT[dd * LKT + key] = kk < N ? (float)ki[((size_t)b * N + kk) * DI + dd] : 0.0f;
       }
     }
-    for (int c = tid; c < Q * 128; c += 256) {  // dl rows (zero past cnt) and dl^T
-      const int j = c / 128, o = c % 128;
-      float val = 0.0f;
-      if (j < cnt) {
-        const int ent = entries[start + j];
-        val = dl[(((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk * 128 + (ent & 63) * 128 + o];
-      }
-      DLs[j * LKT + o] = val;
-      DLT[o * LQ + j] = val;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) {  // dl rows (zero past cnt) and dl^T
+      const int c = tid + 256 * u;
+      const int j = c / 32, o4 = c % 32;
+      vec4<float> val = dlr[u];
+      if (j >= cnt) val = vec4<float>{0.0f, 0.0f, 0.0f, 0.0f};
+      st4<float>(DLs + j * LKT + 4 * o4, val);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DLT[(4 * o4 + e) * LQ + j] = val[e];
     }
-    for (int c = tid; c < Q * DI; c += 256) {  // Q_idx^T of the item's queries
-      const int j = c / DI, dd = c % DI;
-      float val = 0.0f;
-      if (j < cnt) {
-        const int t = entries[start + j] >> 6;
-        val = (float)qi[(((size_t)b * Nq + t) * Hkv + r) * DI + dd];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {  // Q_idx^T of the item's queries (zero past cnt)
+      const int c = tid + 256 * u;
+      if (c < Q * DI) {
+        const int j = c / DI, dd = c % DI;
+        QIT[dd * LQ + j] = j < cnt ? qir[u] : 0.0f;
       }
-      QIT[dd * LQ + j] = val;
     }
+    load_rows(min(it + 1, i1 - 1));  // the next item's rows land during this item
     __syncthreads();
     // dq_idx partial of the item's queries: dl (Q x 128) K_idx (128 x DI); wave w < DIT
     if (w < DIT) {  // uniform
