@@ -56,7 +56,7 @@ def _L():
         lib.msa_ref_select.argtypes = [sp, P, P, P, I64, P, P, P, P, ctypes.c_int]
         lib.msa_ref_attn.argtypes = [sp, P, P, P, P, P, I64, P, P, ctypes.c_int]
         lib.msa_ref_kl_row.argtypes = [ctypes.c_int, I64, P, P, P, P, P, P, P]
-        lib.msa_ref_kl.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, P, ctypes.c_int]
+        lib.msa_ref_kl.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, P, P, ctypes.c_int]
         lib.msa_ref_attn_bwd.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, ctypes.c_int]
         lib.msa_ref_idx_bwd.argtypes = [sp, P, P, P, P, ctypes.c_double, P, I64, P, P]
         for f in ("msa_ref_topk_row", "msa_ref_select", "msa_ref_attn", "msa_ref_kl_row",
@@ -169,8 +169,9 @@ def kl_row(s_main, s_idx):
     return {"kl": float(kl[0]), "dS": dS, "P": P, "P_idx": Pi, "lse_idx": float(li[0])}
 
 
-def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True):
-    """KL alignment: dict(kl_rows [n, Hkv], kl_mean, lse_idx [n, Hkv], dlogits [n, Hkv, k, Bk])."""
+def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True, want_mass=False):
+    """KL alignment: dict(kl_rows [n, Hkv], kl_mean, lse_idx [n, Hkv], dlogits [n, Hkv, k, Bk],
+    block_mass [n, Hkv, k] when want_mass: teacher probability per slot's block)."""
     q = _raw(q, shape.dtype)
     k = _raw(k, shape.dtype)
     q_idx = _raw(q_idx, shape.dtype)
@@ -181,14 +182,36 @@ def kl(shape: RefShape, q, k, q_idx, k_idx, ids, rows=None, want_dlogits=True):
     klr = np.empty((n, H), dtype=np.float64)
     li = np.empty((n, H), dtype=np.float64)
     dl = np.empty((n, H, shape.topk, shape.block_size), dtype=np.float64) if want_dlogits else None
+    bm = np.empty((n, H, shape.topk), dtype=np.float64) if want_mass else None
     mean = np.zeros(1)
     rc = _L().msa_ref_kl(ctypes.byref(shape), _p(q), _p(k), _p(q_idx), _p(k_idx), _p(ids), _p(r),
-                         n, _p(klr), _p(dl), _p(li), _p(mean), threads())
+                         n, _p(klr), _p(dl), _p(li), _p(mean), _p(bm), threads())
     assert rc == 0, rc
     out = {"kl_rows": klr, "kl_mean": float(mean[0]), "lse_idx": li}
     if want_dlogits:
         out["dlogits"] = dl
+    if want_mass:
+        out["block_mass"] = bm
     return out
+
+
+def dense_shape(shape: RefShape) -> RefShape:
+    """The same shape with k = every block: the warm-up stage's full causal context."""
+    nb = (shape.seqlen_kv + shape.block_size - 1) // shape.block_size
+    return RefShape(shape.batch, shape.seqlen_kv, shape.seqlen_q, shape.q_start,
+                    shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.idx_dim,
+                    shape.block_size, nb, shape.dtype)
+
+
+def dense_ids(shape: RefShape, rows=None) -> np.ndarray:
+    """[n, Hkv, nb] block lists 0..floor(i/Bk) (then -1) of the listed rows: with
+    dense_shape(shape) the support of every row is its full causal context."""
+    nb = (shape.seqlen_kv + shape.block_size - 1) // shape.block_size
+    r = np.arange(shape.batch * shape.seqlen_q) if rows is None else np.asarray(rows, np.int64)
+    i = shape.q_start + r % max(shape.seqlen_q, 1)
+    blk = np.arange(nb)[None, :]
+    ids = np.where(blk <= (i // shape.block_size)[:, None], blk, -1).astype(np.int32)
+    return np.ascontiguousarray(np.repeat(ids[:, None, :], shape.num_kv_heads, axis=1))
 
 
 def attn_bwd(shape: RefShape, q, k, v, ids, dout, rows=None, want_kv=True):

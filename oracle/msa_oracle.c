@@ -358,11 +358,15 @@ int msa_ref_kl_row(int G, int64_t n, const double* s_main, const double* s_idx, 
  * P_idx - P at (slot, offset in block), 0 at masked or unused positions;
  * lse_idx (optional) [nrows, Hkv]; kl_mean (optional) = mean of kl_rows over
  * the listed rows and all groups ([KL] §3 averages over N*Hkv).
+ * block_mass (optional) [nrows, Hkv, k]: the teacher's probability summed over
+ * the support tokens of each slot's block ([KL] §8 score recall; 0 for unused
+ * slots). With ids listing every block 0..floor(i/Bk) the support is the full
+ * causal context ([KL] §5, warm-up) and these are the full-history block masses.
  */
 int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void* q_idx,
                const void* k_idx, const int32_t* ids, const int64_t* rows, int64_t nrows,
                double* kl_rows, double* dlogits, double* lse_idx, double* kl_mean,
-               int nthreads) {
+               double* block_mass, int nthreads) {
   if (!shape_ok(s) || !q || !kk || !q_idx || !k_idx || !ids || !kl_rows || nrows < 0)
     return REF_ERR_ARG;
   const int Hq = s->num_q_heads, Hkv = s->num_kv_heads, G = Hq / Hkv, d = s->head_dim;
@@ -380,7 +384,8 @@ int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void
     double* sm = (double*)malloc(sizeof(double) * (size_t)(cap * G));
     double* si = (double*)malloc(sizeof(double) * (size_t)cap);
     double* dS = (double*)malloc(sizeof(double) * (size_t)cap);
-    if (!J || !slot || !off || !sm || !si || !dS) {
+    double* Pt = (double*)malloc(sizeof(double) * (size_t)cap);
+    if (!J || !slot || !off || !sm || !si || !dS || !Pt) {
 #pragma omp atomic write
       err = 1;
     }
@@ -410,8 +415,13 @@ int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void
           si[a] = acc * inv_sqrt_di;
         }
         double kl, li;
-        msa_ref_kl_row(G, n, sm, si, &kl, dS, NULL, NULL, &li);
+        msa_ref_kl_row(G, n, sm, si, &kl, dS, Pt, NULL, &li);
         kl_rows[qq * Hkv + r] = kl;
+        if (block_mass) {
+          double* bm = block_mass + (qq * Hkv + r) * (int64_t)k;
+          for (int sl = 0; sl < k; ++sl) bm[sl] = 0.0;
+          for (int64_t a = 0; a < n; ++a) bm[slot[a]] += Pt[a];
+        }
         if (lse_idx) lse_idx[qq * Hkv + r] = li;
         if (dlogits) {
           double* drow = dlogits + (qq * Hkv + r) * (int64_t)k * Bk;
@@ -426,6 +436,7 @@ int msa_ref_kl(const msa_ref_shape* s, const void* q, const void* kk, const void
     free(sm);
     free(si);
     free(dS);
+    free(Pt);
   }
   if (err) return REF_ERR_ARG;
   if (kl_mean) {

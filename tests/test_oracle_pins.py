@@ -406,6 +406,67 @@ def test_kl_dense_support_matches_full_context_logits():
 # ----------------------------------------------------------------------- backward
 
 
+def test_dense_ids_are_the_k_all_selection():
+    """dense_ids (the warm-up support, "KL alignment" §5) equals what the selection returns when
+    k covers every block: blocks 0..floor(i/Bk) in order, then -1."""
+    rng = np.random.default_rng(21)
+    N, Nq, q_start, Bk = 300, 120, 180, 64
+    nb = (N + Bk - 1) // Bk
+    sh = shape(batch=2, seqlen_kv=N, seqlen_q=Nq, q_start=q_start, block_size=Bk, topk=nb)
+    ids = oracle.select(sh, rnd(rng, 2 * Nq, 2, 8), rnd(rng, 2, N, 8))["ids"]
+    np.testing.assert_array_equal(oracle.dense_ids(sh), ids)
+    assert oracle.dense_shape(shape(seqlen_kv=N, block_size=Bk, topk=2)).topk == nb
+
+
+def test_dense_block_mass_uniform_keys_closed_form():
+    """Identical keys make every main logit of a head equal, so each head's softmax over the
+    full causal context is uniform: P_j = 1/(i+1) and the mass of block b is (number of tokens
+    j <= i in b)/(i+1). Ragged last block; G = 2 heads per group."""
+    rng = np.random.default_rng(22)
+    N, Bk, Hq, Hkv, d, di = 200, 32, 4, 2, 16, 8
+    sh = oracle.dense_shape(shape(seqlen_kv=N, seqlen_q=N, num_q_heads=Hq, num_kv_heads=Hkv,
+                                  head_dim=d, idx_dim=di, block_size=Bk))
+    q = rnd(rng, N, Hq, d)
+    kk = np.broadcast_to(rnd(rng, 1, 1, Hkv, d), (1, N, Hkv, d)).copy()
+    out = oracle.kl(sh, q, kk, rnd(rng, N, Hkv, di), rnd(rng, 1, N, di), oracle.dense_ids(sh),
+                    want_dlogits=False, want_mass=True)
+    for t in [0, 5, 31, 32, 100, 199]:
+        want = np.array([max(0, min(Bk, t + 1 - b * Bk)) for b in range(sh.topk)]) / (t + 1)
+        for r in range(Hkv):
+            np.testing.assert_allclose(out["block_mass"][t, r], want, atol=1e-14)
+
+
+def test_dense_block_mass_is_library_softmax_mass():
+    """"KL alignment" §2.2 and §8: the teacher is the mean over the group's heads of each head's
+    softmax (probabilities averaged), and the block mass sums it over each block's tokens. Here
+    the softmax is torch's over an explicit causal mask, the head mean and the block sums are
+    numpy; the masses of every row sum to 1."""
+    rng = np.random.default_rng(23)
+    B, N, Nq, q_start, Bk, Hq, Hkv, d, di = 2, 150, 70, 80, 32, 8, 2, 16, 8
+    sh = oracle.dense_shape(shape(batch=B, seqlen_kv=N, seqlen_q=Nq, q_start=q_start,
+                                  num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d, idx_dim=di,
+                                  block_size=Bk))
+    q = rnd(rng, B, Nq, Hq, d)
+    kk = rnd(rng, B, N, Hkv, d)
+    out = oracle.kl(sh, q.reshape(B * Nq, Hq, d), kk, rnd(rng, B * Nq, Hkv, di),
+                    rnd(rng, B, N, di), oracle.dense_ids(sh), want_dlogits=False,
+                    want_mass=True)
+    G = Hq // Hkv
+    qt = torch.from_numpy(q.astype(np.float64))
+    kt = torch.from_numpy(kk.astype(np.float64))
+    for b in range(B):
+        s = torch.einsum("thd,jhd->thj", qt[b], kt[b].repeat_interleave(G, dim=1)) / math.sqrt(d)
+        i = torch.arange(Nq)[:, None, None] + q_start
+        s = s.masked_fill(torch.arange(N)[None, None, :] > i, float("-inf"))
+        p = torch.softmax(s, dim=-1).numpy().reshape(Nq, Hkv, G, N).mean(axis=2)
+        pad = np.zeros((Nq, Hkv, sh.topk * Bk))
+        pad[..., :N] = p
+        want = pad.reshape(Nq, Hkv, sh.topk, Bk).sum(axis=-1)
+        got = out["block_mass"][b * Nq:(b + 1) * Nq]
+        np.testing.assert_allclose(got, want, atol=1e-13)
+        np.testing.assert_allclose(got.sum(axis=-1), 1.0, atol=1e-13)
+
+
 def test_native_eq11_hand_gradient():
     """"2.4 · 训练原生稀疏" eq. (11) hand calculation: weights (0.75, 0.25), v1=(2,0), v2=(0,2),
     g=(1,-1) give logit gradients (0.75, -0.75). With z = q.k/sqrt(2), q = (sqrt(2) ln3, 0),
