@@ -111,12 +111,146 @@ def cpu_baseline(cfg, seconds_target=15.0):
                       f"(rows are independent; fp64 select + attention in {dt:.1f} s)"}
 
 
+def dense_flops(cfg):
+    """Algorithmic work of the warm-up stage over the causal triangle: exponentials and MFMA
+    FLOPs of the main-branch LSE pass and of the KL pass (main S again, index logits)."""
+    B, Nq, Hq, Hkv = cfg.batch, cfg.seqlen_q, cfg.num_q_heads, cfg.num_kv_heads
+    pairs = B * sum(cfg.q_start + t + 1 for t in range(Nq))  # (query, key) pairs, j <= i
+    return {"pairs": pairs,
+            "lse_flops": 2.0 * cfg.head_dim * Hq * pairs,
+            "lse_exps": float(Hq * pairs),
+            "kl_flops": 2.0 * (cfg.head_dim * Hq + cfg.idx_dim * Hkv) * pairs,
+            "kl_exps": float(Hq * pairs),
+            "idx_lse_flops": 2.0 * cfg.idx_dim * Hkv * pairs}
+
+
+def cpu_baseline_dense(cfg, seconds_target=15.0):
+    """fp64 oracle of the warm-up stage (dense LSE + full-context KL with block masses) on a
+    seeded sample of query rows, timed on the host."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+
+    threads = oracle.threads()
+    k, v, k_idx = (si.host_tensor(cfg, n) for n in ("k", "v", "k_idx"))
+    shp = oracle.dense_shape(oracle.shape_of(cfg))
+    rng = np.random.default_rng(4321)
+
+    def run(rows):
+        q = si.host_query_rows(cfg, "q", rows)
+        qi = si.host_query_rows(cfg, "q_idx", rows)
+        ids = oracle.dense_ids(shp, rows=rows)
+        t0 = time.perf_counter()
+        oracle.attn(shp, q, k, v, ids, rows=rows)
+        oracle.kl(shp, q, k, qi, k_idx, ids, rows=rows, want_dlogits=False, want_mass=True)
+        return time.perf_counter() - t0
+
+    probe = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=threads))
+    dt = run(probe)
+    n = int(max(threads, min(4096, len(probe) * seconds_target / max(dt, 1e-3))))
+    rows = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=n))
+    dt = run(rows)
+    return {"value": n / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} seeded uniformly random query rows of the same workload "
+                      f"(fp64 dense attention LSE + full-context KL and block masses in "
+                      f"{dt:.1f} s; the oracle also forms the attention output)"}
+
+
+def dense_main(args):
+    """Warm-up stage: main-branch LSE over the full causal context, KL on that context with
+    the teacher's block masses, the k-block selection and its block / score recall."""
+    import torch
+
+    import learned_kv_block_amd as msa
+    import seeded_inputs as si
+
+    cfg = si.CONFIGS[args.workload or "train_b2_n32768"]
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    x = {n: si.device_tensor(cfg, n, dev) for n in ("q", "k", "q_idx", "k_idx")}
+    sh = msa.shape_for(x["q_idx"], x["k_idx"], cfg.topk, cfg.q_start, cfg.num_q_heads,
+                       cfg.head_dim)
+    ws_sel = torch.empty(msa.workspace_size(sh, msa.MSA_OP_SELECT), dtype=torch.uint8, device=dev)
+
+    def step():
+        lse = msa.msa_dense_lse(x["q"], x["k"], q_start=cfg.q_start, idx_dim=cfg.idx_dim)
+        kl = msa.msa_kl_dense(x["q"], x["k"], x["q_idx"], x["k_idx"], lse, q_start=cfg.q_start)
+        sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                             num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim,
+                             workspace=ws_sel)
+        rec = msa.msa_block_recall(kl["block_mass"], sel["ids"], q_start=cfg.q_start,
+                                   seqlen_kv=cfg.seqlen_kv)
+        return kl, rec
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(max(1, args.warmup)):
+        kl, rec = step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    with msa.KernelTimer("kl_dense", max_launches=args.steps) as kt:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            kl, rec = step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / max(1, args.steps)
+    kernels = {}
+    for name in ("dense_lse", "dense_lse_idx", "kl_dense", "index_blockmax", "topk", "recall"):
+        with msa.KernelTimer(name, max_launches=4) as t:
+            step()
+            step()
+            torch.cuda.synchronize()
+        kernels[name] = round(t.avg_ms, 4)
+    print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
+    w = dense_flops(cfg)
+    kl_ms = kt.avg_ms
+    peak_exp = 256 * 4 * 16 / 4 * 2.4e9  # v_exp_f32: a quarter of the 16-lane FP32 rate
+    roofline = {"bound": "mfma", "kernel": "kl_dense", "achieved": w["kl_flops"] / (kl_ms * 1e-3) / 1e12,
+                "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": w["kl_flops"] / (kl_ms * 1e-3) / PEAK_BF16, "traffic": None,
+                "avg_ms": kl_ms, "launches": kt.launches, "flops_per_launch": w["kl_flops"],
+                "exps_per_launch": w["kl_exps"],
+                "exp_frac": w["kl_exps"] / (kl_ms * 1e-3) / peak_exp}
+    tokens = cfg.batch * cfg.seqlen_q
+    line = {
+        "metric": "MSA warm-up KL step (dense LSE + full-context KL + block/score recall) "
+                  "query-tokens/s",
+        "value": tokens * args.steps / elapsed,
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seqlen_kv,
+                   "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
+                   "head_dim": cfg.head_dim, "idx_dim": cfg.idx_dim,
+                   "block_size": cfg.block_size, "topk": cfg.topk, "parallelism": "none",
+                   "dense_warmup": True},
+        "work": w,
+        "kernel_ms": kernels,
+        "kl_mean": float(kl["kl_mean"][0]),
+        "block_recall_mean": float(rec["means"][0]),
+        "score_recall_mean": float(rec["means"][1]),
+        "roofline": roofline,
+    }
+    del x, ws_sel, kl, rec
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline_dense(cfg)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="skewed_n131072")
+    ap.add_argument("--workload", default=None,
+                    help="skewed_n131072 by default (train_b2_n32768 with --dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kl", action="store_true",
                     help="add msa_kl_align (with the index-logit gradient) to the step; "
@@ -124,6 +258,9 @@ def main():
     ap.add_argument("--bwd", action="store_true",
                     help="add msa_attn_bwd (dq, dk, dv for a seeded dout) to the step; "
                          "a training-side measurement, not the headline line")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the warm-up stage instead (dense LSE, KL on the full causal "
+                         "context with block masses, selection and block / score recall)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for HBM counter calibration)")
@@ -133,12 +270,16 @@ def main():
               "MI355X; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.dense:
+        dense_main(args)
+        return
+
     import torch
 
     import learned_kv_block_amd as msa
     import seeded_inputs as si
 
-    cfg = si.CONFIGS[args.workload]
+    cfg = si.CONFIGS[args.workload or "skewed_n131072"]
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)

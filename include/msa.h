@@ -221,6 +221,68 @@ msa_status msa_idx_bwd(const msa_shape* shape, const void* q_idx, const void* k_
                        void* dq_idx, void* dk_idx, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/*
+ * msa_dense_lse — log-sum-exp of the main branch over the full causal context
+ * (KL alignment note §5: in the warm-up stage the main branch attends to every
+ * earlier token; §6: the KL needs only each branch's LSE). It stands in for the
+ * LSE that a dense causal attention forward reports.
+ *   lse_main[b, t, h] = log sum over j <= q_start + t of
+ *                       exp(q[b, t, h] . k[b, j, floor(h / G)] / sqrt(head_dim))
+ *
+ *  in   q, k                device, layouts above (v is not read)
+ *  out  lse_main            device fp32 [batch, seqlen_q, num_q_heads]
+ * topk is not used. fp32 inputs need head_dim 64 (MSA_ERR_UNSUPPORTED
+ * otherwise). No workspace. Cost is O(seqlen_q * seqlen_kv) per head.
+ */
+msa_status msa_dense_lse(const msa_shape* shape, const void* q, const void* k, float* lse_main,
+                         hipStream_t stream);
+
+/*
+ * msa_kl_dense — KL alignment on the full causal context, the warm-up stage
+ * (KL alignment note §5: support J = every j <= i; §2 student and teacher;
+ * §3 KL(P || P_idx)), and the teacher's attention mass per 128-token block.
+ *   P_j       = (1/G) sum over the group's heads h of exp(S_h,j - lse_main_h)
+ *   P_idx_j   = exp(z_j - lse_idx), z_j = q_idx . k_idx_j / sqrt(idx_dim)
+ *   kl_rows[b, t, r]       = sum over j <= i of P_j log(P_j / P_idx_j)
+ *   block_mass[b, t, r, c] = sum over j in block c, j <= i, of P_j
+ *
+ *  in   q, k, q_idx, k_idx  device, layouts above
+ *  in   lse_main            device fp32 [batch, seqlen_q, num_q_heads] over the
+ *                           full causal context (msa_dense_lse)
+ *  out  lse_idx             device fp32 [batch, seqlen_q, num_kv_heads]: LSE of
+ *                           the index logits over j <= i
+ *  out  kl_rows             device fp32 [batch, seqlen_q, num_kv_heads]
+ *  out  kl_mean             device fp32 [1]: mean of kl_rows over every row
+ *  out  block_mass (opt)    device fp32 [batch, seqlen_q, num_kv_heads,
+ *                           ceil(seqlen_kv / 128)]; 0 for blocks after the
+ *                           query's own (fully overwritten)
+ * topk is not used. fp32 inputs need head_dim 64. No workspace.
+ */
+msa_status msa_kl_dense(const msa_shape* shape, const void* q, const void* k, const void* q_idx,
+                        const void* k_idx, const float* lse_main, float* lse_idx, float* kl_rows,
+                        float* kl_mean, float* block_mass, hipStream_t stream);
+
+/*
+ * msa_block_recall — block recall and score recall of a selection against the
+ * full-history teacher (KL alignment note §8; selector supervision page
+ * "4.1.1 · 监督与联合训练", eq. 2 set recall and eq. 3 coverage).
+ *   T = the min(topk, L + 1) blocks of largest block_mass among 0..L,
+ *       L = floor(i / 128), the lower index first on equal mass
+ *   block_recall[b, t, r] = |S ∩ T| / |T|, S = the row's block_ids
+ *   score_recall[b, t, r] = sum of block_mass over S
+ * Ids -1 (and ids outside 0..L) count as no block.
+ *
+ *  in   block_mass          device fp32, as msa_kl_dense writes it
+ *  in   block_ids           device int32 [batch, seqlen_q, num_kv_heads, topk]
+ *  out  block_recall, score_recall
+ *                           device fp32 [batch, seqlen_q, num_kv_heads]
+ *  out  means (opt)         device fp32 [2]: the means of the two over every row
+ * No workspace.
+ */
+msa_status msa_block_recall(const msa_shape* shape, const float* block_mass,
+                            const int32_t* block_ids, float* block_recall, float* score_recall,
+                            float* means, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* msa_status_string(msa_status status);
 
@@ -235,7 +297,8 @@ enum {
   MSA_K_INDEX_BLOCKMAX = 0, MSA_K_TOPK = 1, MSA_K_BUCKET_HIST = 2, MSA_K_BUCKET_SCAN = 3,
   MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
-  MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_COUNT = 14
+  MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_DENSE_LSE = 14, MSA_K_KL_DENSE = 15,
+  MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_COUNT = 18
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* total_ms, int* launches);

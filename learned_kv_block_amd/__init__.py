@@ -15,6 +15,11 @@ Functions (same names as the C entry points):
                                                      -> (dq, dk, dv)
   msa_idx_bwd(q_idx, k_idx, block_ids, dlogits, coef, q_start=0, ...)
                                                      -> (dq_idx, dk_idx)
+  msa_dense_lse(q, k, q_start=0, ...)                -> lse_main over the full causal context
+  msa_kl_dense(q, k, q_idx, k_idx, lse_main, q_start=0, ...)
+                                                     -> kl_rows, kl_mean, lse_idx, block_mass
+  msa_block_recall(block_mass, block_ids, q_start=0, ...)
+                                                     -> block_recall, score_recall, means
 """
 from __future__ import annotations
 
@@ -32,9 +37,9 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2, 3, 4
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce", "attn_bwd", "idx_bwd"]
+           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
-           "msa_idx_bwd",
+           "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
            "msa_status_string", "msa_prof_begin", "msa_prof_end"]
 
 
@@ -69,7 +74,11 @@ def lib() -> ctypes.CDLL:
         L.msa_kl_align.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_idx_bwd.argtypes = [S, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+        L.msa_dense_lse.argtypes = [S, P, P, P, P]
+        L.msa_kl_dense.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
+        L.msa_block_recall.argtypes = [S, P, P, P, P, P, P]
         for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
+                  "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
                   "msa_prof_begin", "msa_prof_end"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
@@ -259,6 +268,72 @@ def msa_idx_bwd(q_idx: torch.Tensor, k_idx: torch.Tensor, block_ids: torch.Tenso
     if st != MSA_OK:
         raise MsaError(st, "msa_idx_bwd")
     return dq, dk
+
+
+def msa_dense_lse(q: torch.Tensor, k: torch.Tensor, q_start: int = 0, idx_dim: int = 64):
+    """LSE of the main branch over the full causal context: fp32 [B, Nq, Hq]."""
+    _check(q, "q", 4)
+    _check(k, "k", 4)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, 1, _dtype_code(q))
+    lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
+    st = lib().msa_dense_lse(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(lse), _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_dense_lse")
+    return lse
+
+
+def msa_kl_dense(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                 lse_main: torch.Tensor, q_start: int = 0, want_mass: bool = True):
+    """KL alignment on the full causal context (warm-up stage): dict(kl_rows [B, Nq, Hkv],
+    kl_mean [1], lse_idx [B, Nq, Hkv], block_mass [B, Nq, Hkv, nb] (opt)), all fp32."""
+    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx")):
+        _check(t, n, 4)
+    _check(k_idx, "k_idx", 3)
+    _check(lse_main, "lse_main", 3)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], 1, _dtype_code(q))
+    dev = q.device
+    nb = (N + 127) // 128
+    kl_rows = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+    kl_mean = torch.empty((1,), dtype=torch.float32, device=dev)
+    lse_idx = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+    mass = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev) if want_mass else None
+    st = lib().msa_kl_dense(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
+                            _ptr(lse_main), _ptr(lse_idx), _ptr(kl_rows), _ptr(kl_mean),
+                            _ptr(mass), _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_kl_dense")
+    out = {"kl_rows": kl_rows, "kl_mean": kl_mean, "lse_idx": lse_idx}
+    if want_mass:
+        out["block_mass"] = mass
+    return out
+
+
+def msa_block_recall(block_mass: torch.Tensor, block_ids: torch.Tensor, q_start: int = 0,
+                     seqlen_kv: Optional[int] = None, num_q_heads: Optional[int] = None,
+                     head_dim: int = 128, idx_dim: int = 64):
+    """Block recall and score recall of block_ids [B, Nq, Hkv, topk] against the teacher's
+    block masses [B, Nq, Hkv, nb]: dict(block_recall, score_recall [B, Nq, Hkv], means [2])."""
+    _check(block_mass, "block_mass", 4)
+    _check(block_ids, "block_ids", 4)
+    B, Nq, Hkv, nb = block_mass.shape
+    N = seqlen_kv if seqlen_kv is not None else nb * 128
+    if (N + 127) // 128 != nb:
+        raise ValueError("seqlen_kv does not match the block count of block_mass")
+    Hq = num_q_heads if num_q_heads is not None else Hkv
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, head_dim, idx_dim, block_ids.shape[3], MSA_BF16)
+    dev = block_mass.device
+    brec = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+    srec = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+    means = torch.empty((2,), dtype=torch.float32, device=dev)
+    st = lib().msa_block_recall(ctypes.byref(sh), _ptr(block_mass), _ptr(block_ids), _ptr(brec),
+                                _ptr(srec), _ptr(means), _stream(block_mass))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_block_recall")
+    return {"block_recall": brec, "score_recall": srec, "means": means}
 
 
 class KernelTimer:

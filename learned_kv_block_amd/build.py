@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libmsa.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_kl.hip", "msa_bwd.hip"]
+SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_kl.hip", "msa_bwd.hip",
+           "msa_dense.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

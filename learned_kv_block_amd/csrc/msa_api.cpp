@@ -417,6 +417,77 @@ msa_status msa_kl_align(const msa_shape* shape, const void* q, const void* k, co
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 
+msa_status msa_dense_lse(const msa_shape* shape, const void* q, const void* k, float* lse_main,
+                         hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.dtype == MSA_F32 && d.D != 64) return MSA_ERR_UNSUPPORTED;
+  if (d.rows == 0) return MSA_OK;
+  if (!q || !k || !lse_main) return MSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return MSA_ERR_SHAPE;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  prof_before(MSA_K_DENSE_LSE, stream);
+  const hipError_t e = launch_dense_lse(d, false, q, k, lse_main, stream);
+  prof_after(MSA_K_DENSE_LSE, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_kl_dense(const msa_shape* shape, const void* q, const void* k, const void* q_idx,
+                        const void* k_idx, const float* lse_main, float* lse_idx, float* kl_rows,
+                        float* kl_mean, float* block_mass, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.dtype == MSA_F32 && d.D != 64) return MSA_ERR_UNSUPPORTED;
+  if (!kl_mean) return MSA_ERR_NULL;
+  if (d.rows > 0) {
+    if (!q || !k || !q_idx || !k_idx || !lse_main || !lse_idx || !kl_rows) return MSA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx))
+      return MSA_ERR_SHAPE;
+  }
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  if (d.rows == 0)
+    return launch_fill_f32(kl_mean, 1, 0.0f, stream) == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+  if (block_mass &&
+      launch_fill_f32(block_mass, d.rows * d.Hkv * d.nb, 0.0f, stream) != hipSuccess)
+    return MSA_ERR_DEVICE;
+  prof_before(MSA_K_DENSE_LSE_IDX, stream);
+  hipError_t e = launch_dense_lse(d, true, q_idx, k_idx, lse_idx, stream);
+  prof_after(MSA_K_DENSE_LSE_IDX, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  prof_before(MSA_K_KL_DENSE, stream);
+  e = launch_kl_dense(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, block_mass, stream);
+  prof_after(MSA_K_KL_DENSE, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  e = launch_mean(kl_rows, d.rows * d.Hkv, kl_mean, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_block_recall(const msa_shape* shape, const float* block_mass,
+                            const int32_t* block_ids, float* block_recall, float* score_recall,
+                            float* means, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.rows > 0 && (!block_mass || !block_ids || !block_recall || !score_recall))
+    return MSA_ERR_NULL;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  const int64_t n = d.rows * d.Hkv;
+  if (n > 0) {
+    prof_before(MSA_K_RECALL, stream);
+    const hipError_t e = launch_recall(d, block_mass, block_ids, block_recall, score_recall, stream);
+    prof_after(MSA_K_RECALL, stream);
+    if (e != hipSuccess) return MSA_ERR_DEVICE;
+  }
+  if (means) {
+    if (launch_mean(block_recall, n, means, stream) != hipSuccess ||
+        launch_mean(score_recall, n, means + 1, stream) != hipSuccess)
+      return MSA_ERR_DEVICE;
+  }
+  return MSA_OK;
+}
+
 msa_status msa_prof_begin(int kernel, int max_launches) {
   if (kernel < 0 || kernel >= MSA_K_COUNT || max_launches < 1 || max_launches > 100000)
     return MSA_ERR_SHAPE;

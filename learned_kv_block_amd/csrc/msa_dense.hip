@@ -1,0 +1,556 @@
+// msa_dense.hip — the warm-up stage of the index branch on the full causal context.
+//
+// "MSA 中的 KL 对齐与局部知识蒸馏" (MSA KL alignment note):
+//   §5  before Top-k routing is switched on, the main branch attends to the
+//       whole causal history and the KL support J is the full causal context;
+//   §6  each branch only has to provide its log-sum-exp: probabilities are
+//       rebuilt as p = exp(s - LSE) ("4.1.1 · 监督与联合训练" eq. 15);
+//   §8  block recall (how many of the teacher's best blocks the selection
+//       holds) and score recall (the teacher mass the selected blocks cover;
+//       "4.1.1 · 监督与联合训练" eq. 2 and eq. 3).
+// Nothing here is O(k): every kernel streams the causal history 128 keys at a
+// time and keeps the N x N score matrix in registers.
+//
+//   dense_lse_kernel  causal LSE of either branch, query-outer: keys through a
+//                     double-buffered LDS tile, online (max, sum) per row;
+//   kl_dense_kernel   KL(P || P_idx) per (query, group) on the full causal
+//                     context, and the teacher's mass per 128-token block;
+//   recall_kernel     block recall and score recall of a selection against
+//                     the teacher's block masses;
+//   mean_kernel       fixed-order mean of a vector (one workgroup).
+#include <type_traits>
+
+#include "msa_internal.hpp"
+
+namespace msa {
+
+// Task order of the query-outer kernels: task = (pair, tile) with pair = (b, y),
+// y the KV group (or 0 for the index branch). Pairs are outermost so that the
+// tiles one XCD runs at a time stream the same keys through its L2. Inside a
+// pair the tiles alternate between the long end (late queries, many blocks)
+// and the short end, so any contiguous share of the tasks carries about the
+// same work. Workgroup g runs on XCD g % 8 and takes task (g % 8) * per + g / 8.
+struct Task {
+  int b, y, tile;
+};
+__device__ __forceinline__ bool task_of(int ntasks, int ntiles, int ngroups, Task* t) {
+  const int g = blockIdx.x;
+  const int per = (ntasks + 7) / 8;
+  const int kk = g >> 3;
+  const int task = (g & 7) * per + kk;
+  if (kk >= per || task >= ntasks) return false;
+  const int pair = task / ntiles, u = task - pair * ntiles;
+  t->tile = (u & 1) ? (u >> 1) : ntiles - 1 - (u >> 1);
+  t->b = pair / ngroups;
+  t->y = pair - t->b * ngroups;
+  return true;
+}
+static unsigned task_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 8) * 8); }
+
+// One 128-key tile of a key head ([128][DK], row j0 + r at base + (j0 + r) * stride)
+// moved global -> registers -> swizzled LDS by the NT threads of a workgroup.
+// Rows at or past N repeat row N - 1; such keys are after every query and masked.
+template <typename T, int DK, int NT>
+struct KeyStage {
+  static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  static constexpr int CPR = DK / EPC;        // chunks per row
+  static constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;
+  static constexpr int CH = 128 * CPR / NT;   // chunks per thread
+  static_assert((128 * CPR) % NT == 0, "tile shape");
+  i32x4 raw[CH];
+  __device__ __forceinline__ void load(const T* base, size_t stride, int j0, int N, int tid) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int x = tid + NT * u, r = x / CPR, c = x % CPR;
+      const int j = min(j0 + r, N - 1);
+      raw[u] = *reinterpret_cast<const i32x4*>(base + (size_t)j * stride + c * EPC);
+    }
+  }
+  __device__ __forceinline__ void store(i32x4* dst, int tid) const {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int x = tid + NT * u, r = x / CPR, c = x % CPR;
+      dst[r * CPR + (c ^ (idx_swz(r) & SWM))] = raw[u];
+    }
+  }
+};
+
+// ============================================================== causal LSE
+//
+// LSE[b, t, y*R + u] = log sum_{j <= i} exp(q[b, t, y*R + u] . key_y[j] / sqrt(D)),
+// i = q_start + t. Main branch: R = G query heads of group y read KV head y.
+// Index branch: R = Hkv index heads, y = 0, all reading the one K_idx head.
+// Workgroup = RT = 64*NW consecutive rows (QT = RT/R queries) of one pair;
+// wave w owns rows [64w, 64w+64) as two 32-column MFMA B tiles held in
+// registers. The product is formed transposed (32 keys as rows), so each lane
+// holds 16 keys of one row and the online max / sum stay in the lane; the two
+// lane halves are merged once at the end. All exponentials are base 2 with
+// the scale folded into one FMA.
+template <typename T, int D, int R, int NW>
+__global__ void __launch_bounds__(64 * NW)
+dense_lse_kernel(const T* __restrict__ q, const T* __restrict__ k, float* __restrict__ lse,
+                 int N, int Nq, int q_start, int qrows, int kstride, int ngroups, int ntiles,
+                 int ntasks, float scale_log2) {
+  constexpr int NT = 64 * NW, RT = 64 * NW, QT = RT / R, KS = D / 16;
+  using Stage = KeyStage<T, D, NT>;
+  constexpr int CPR = Stage::CPR, EPC = Stage::EPC;
+  static_assert(RT % R == 0, "rows of a query stay in one tile");
+  __shared__ i32x4 kbuf[2][128 * CPR];
+
+  Task tk;
+  if (!task_of(ntasks, ntiles, ngroups, &tk)) return;
+  const int b = tk.b, y = tk.y, t0 = tk.tile * QT;
+  const int t_last = min(Nq, t0 + QT) - 1;
+  const int kb_last = (q_start + t_last) >> 7;
+  // first block holding a key after the tile's first query
+  const int kb_mask = min((q_start + t0 + 1) >> 7, kb_last + 1);
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const T* kbase = k + (size_t)b * N * kstride + (size_t)y * D;
+
+  Stage st;
+  st.load(kbase, kstride, 0, N, tid);
+  vec8<T> qf[2][KS];
+  int i_row[2];
+  size_t orow[2];
+  bool ovalid[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int rho = 64 * wave + 32 * ct + l32;
+    const int tq = t0 + rho / R, u = rho % R;
+    const int tc = min(tq, Nq - 1);
+    orow[ct] = ((size_t)b * Nq + tc) * qrows + (size_t)y * R + u;
+    ovalid[ct] = tq < Nq;
+    i_row[ct] = q_start + tc;
+    const T* qp = q + orow[ct] * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ct][ks] = ld8<T>(qp + 16 * ks);
+  }
+  st.store(kbuf[0], tid);
+  if (kb_last >= 1) st.load(kbase, kstride, 128, N, tid);
+  __syncthreads();
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  auto key_tile = [&](auto masked, const i32x4* tile, int kb, int kt) {
+    vec8<T> af[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(tile, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
+    f32x16 acc[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (kb * 128 + 32 * kt + drow(e, h) > i_row[ct]) acc[ct][e] = -INFINITY;
+      }
+      float mt = vmax(acc[ct][0], acc[ct][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) mt = vmax(vmax(mt, acc[ct][e]), acc[ct][e + 1]);
+      const float mn = vmax(m[ct], mt * scale_log2);
+      const float mref = mn == -INFINITY ? 0.0f : mn;
+      float s = l[ct] * __builtin_amdgcn_exp2f(m[ct] - mref);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[ct][e], scale_log2, -mref));
+      l[ct] = s;
+      m[ct] = mn;
+    }
+  };
+  auto block = [&](auto masked, int kb) {
+    const int cur = kb & 1;
+    if (kb + 1 <= kb_last) {
+      st.store(kbuf[cur ^ 1], tid);  // last read before the previous barrier
+      if (kb + 2 <= kb_last) st.load(kbase, kstride, (kb + 2) * 128, N, tid);
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) key_tile(masked, kbuf[cur], kb, kt);
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb < kb_mask; ++kb) block(std::false_type(), kb);
+  for (; kb <= kb_last; ++kb) block(std::true_type(), kb);
+
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float mo = shfl_xor_f(m[ct], 32), lo = shfl_xor_f(l[ct], 32);
+    const float M = vmax(m[ct], mo);
+    const float Mr = M == -INFINITY ? 0.0f : M;
+    const float L = l[ct] * __builtin_amdgcn_exp2f(m[ct] - Mr) + lo * __builtin_amdgcn_exp2f(mo - Mr);
+    if (h == 0 && ovalid[ct]) lse[orow[ct]] = (Mr + __builtin_amdgcn_logf(L)) * kLn2;
+  }
+}
+
+// ============================================================== KL on the full causal context
+//
+// Per (query, group) row, with J = {j <= i}:
+//   P_j     = (1/G) sum over the group's heads of exp(S_h,j - LSE_main,h)
+//   log P_idx_j = z_j - LSE_idx,   z_j = q_idx . k_idx_j / sqrt(d_idx)
+//   KL      = sum_j P_j (log P_j - log P_idx_j)         (terms with P_j = 0 vanish)
+//   mass_b  = sum over the keys of block b of P_j
+// Workgroup = RT = 32*NW rows (QT = RT/G queries x the G heads of group y) of
+// one pair; the product S = Q K^T has the wave's 32 rows as MFMA rows (Q in
+// registers) and 32 keys in the lanes, so the G heads of a query sit in G
+// elements of a lane (G/2 plus the other lane half for G >= 8) and the teacher
+// average is an in-lane sum plus at most one exchange. For G >= 8 the two lane
+// halves then split the queries, so the per-(query, key) work is not repeated.
+// The index logits use the same layout: the query's q_idx row is repeated on
+// each of its head rows and multiplied by the K_idx tile.
+template <typename T, int D, int DI, int G, int NW>
+__global__ void __launch_bounds__(64 * NW)
+kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx,
+                const T* __restrict__ k_idx, const float* __restrict__ lse_main,
+                const float* __restrict__ lse_idx, float* __restrict__ kl_rows,
+                float* __restrict__ mass, int N, int Nq, int q_start, int Hkv, int nb, int ntiles,
+                int ntasks, float sc2, float zc2) {
+  constexpr int NT = 64 * NW, RT = 32 * NW, QT = RT / G, KS = D / 16, KSI = DI / 16;
+  constexpr bool PARTNER = G >= 8;
+  constexpr int RPQ = PARTNER ? G / 2 : G;  // rows of one query per lane
+  constexpr int NLQ = 16 / RPQ;             // queries per lane (before the split)
+  constexpr int OWN = PARTNER ? NLQ / 2 : NLQ;
+  constexpr int QPW = 32 / G;               // queries per wave
+  using SK = KeyStage<T, D, NT>;
+  using SI = KeyStage<T, DI, NT>;
+  __shared__ i32x4 kbuf[2][128 * SK::CPR];
+  __shared__ i32x4 ibuf[2][128 * SI::CPR];
+
+  Task tk;
+  if (!task_of(ntasks, ntiles, Hkv, &tk)) return;
+  const int b = tk.b, r = tk.y, t0 = tk.tile * QT;
+  const int t_last = min(Nq, t0 + QT) - 1;
+  const int kb_last = (q_start + t_last) >> 7;
+  const int kb_mask = min((q_start + t0 + 1) >> 7, kb_last + 1);
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = Hkv * G;
+  const size_t kstride = (size_t)Hkv * D;
+  const T* kbase = k + (size_t)b * N * kstride + (size_t)r * D;
+  const T* ibase = k_idx + (size_t)b * N * DI;
+
+  SK sk;
+  SI si;
+  sk.load(kbase, kstride, 0, N, tid);
+  si.load(ibase, DI, 0, N, tid);
+  // A fragments: MFMA row l32 = wave row 32w + l32 = (query, head)
+  vec8<T> qf[KS], qif[KSI];
+  {
+    const int rho = 32 * wave + l32;
+    const int tc = min(t0 + rho / G, Nq - 1);
+    const T* qp = q + (((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G) * D + 8 * h;
+    const T* qip = q_idx + (((size_t)b * Nq + tc) * Hkv + r) * DI + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld8<T>(qp + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qif[ks] = ld8<T>(qip + 16 * ks);
+  }
+  // LSE_main (log2 domain) of the row of each accumulator element
+  float lm2[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int rho = 32 * wave + drow(e, h);
+    const int tc = min(t0 + rho / G, Nq - 1);
+    lm2[e] = lse_main[((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G] * kLog2e;
+  }
+  // the lane's own queries
+  int i_q[OWN];
+  float li2[OWN];
+  size_t grow[OWN];
+  bool qv[OWN];
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) {
+    const int wq = PARTNER ? 2 * m + h : drow(m * RPQ, h) / G;  // query within the wave
+    const int tq = t0 + wave * QPW + wq;
+    const int tc = min(tq, Nq - 1);
+    qv[m] = tq < Nq;
+    i_q[m] = q_start + tc;
+    grow[m] = ((size_t)b * Nq + tc) * Hkv + r;
+    li2[m] = lse_idx[grow[m]] * kLog2e;
+  }
+  sk.store(kbuf[0], tid);
+  si.store(ibuf[0], tid);
+  if (kb_last >= 1) {
+    sk.load(kbase, kstride, 128, N, tid);
+    si.load(ibase, DI, 128, N, tid);
+  }
+  __syncthreads();
+
+  const float inv_g = 1.0f / (float)G;
+  float klacc[OWN], macc[OWN];
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) klacc[m] = macc[m] = 0.0f;
+
+  auto key_tile = [&](auto masked, const i32x4* ktile, const i32x4* itile, int kb, int kt) {
+    f32x16 s, z;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = z[e] = 0.0f;
+    {
+      vec8<T> bf[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bf[ks] = lds_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) mma(s, qf[ks], bf[ks]);
+    }
+    {
+      vec8<T> bi[KSI];
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks)
+        bi[ks] = lds_frag<T, SI::CPR>(itile, 32 * kt + l32, (16 * ks + 8 * h) / SI::EPC);
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks) mma(z, qif[ks], bi[ks]);
+    }
+    float part[NLQ];
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) {
+      float p = 0.0f;
+#pragma unroll
+      for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e)
+        p += __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sc2, -lm2[e]));
+      part[lq] = p;
+    }
+    const int key = kb * 128 + 32 * kt + l32;
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+      float P, zz;
+      if constexpr (PARTNER) {
+        // half h keeps query 2m + h; the other half's partial sum comes across
+        const float send = h ? part[2 * m] : part[2 * m + 1];
+        const float recv = shfl_xor_f(send, 32);
+        P = (h ? part[2 * m + 1] : part[2 * m]) + recv;
+        zz = h ? z[(2 * m + 1) * RPQ] : z[2 * m * RPQ];
+      } else {
+        P = part[m];
+        zz = z[m * RPQ];
+      }
+      P *= inv_g;
+      if constexpr (decltype(masked)::value) P = key > i_q[m] ? 0.0f : P;
+      const float lpi2 = __builtin_fmaf(zz, zc2, -li2[m]);  // log2 P_idx
+      // P below the smallest normal float adds nothing (and v_log_f32 may read it as 0)
+      klacc[m] += P >= 1.17549435e-38f ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
+      macc[m] += P;
+    }
+  };
+  auto block = [&](auto masked, int kb) {
+    const int cur = kb & 1;
+    if (kb + 1 <= kb_last) {
+      sk.store(kbuf[cur ^ 1], tid);
+      si.store(ibuf[cur ^ 1], tid);
+      if (kb + 2 <= kb_last) {
+        sk.load(kbase, kstride, (kb + 2) * 128, N, tid);
+        si.load(ibase, DI, (kb + 2) * 128, N, tid);
+      }
+    }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) key_tile(masked, kbuf[cur], ibuf[cur], kb, kt);
+    if (mass) {
+#pragma unroll
+      for (int m = 0; m < OWN; ++m) {
+        float v = macc[m];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+        if (l32 == 0 && qv[m] && kb <= (i_q[m] >> 7)) mass[grow[m] * nb + kb] = v;
+        macc[m] = 0.0f;
+      }
+    }
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb < kb_mask; ++kb) block(std::false_type(), kb);
+  for (; kb <= kb_last; ++kb) block(std::true_type(), kb);
+
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) {
+    float v = klacc[m] * kLn2;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+    if (l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
+  }
+}
+
+// ============================================================== recall
+//
+// One wavefront per (b, t, r) row. T = the teacher's top min(k, L+1) blocks
+// among the visible blocks 0..L (L = the query's local block) by block mass,
+// the lower index first on equal mass. A selected block is in T when fewer
+// than |T| visible blocks outrank it. block recall = |S ∩ T| / |T|;
+// score recall = the mass on S (ids -1 and ids outside 0..L count as empty).
+__global__ void __launch_bounds__(256)
+recall_kernel(const float* __restrict__ mass, const int32_t* __restrict__ ids,
+              float* __restrict__ brec, float* __restrict__ srec, int64_t nrows, int Nq,
+              int q_start, int Hkv, int nb, int topk) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;
+  const int t = (int)((row / Hkv) % Nq);
+  const int L = (q_start + t) >> 7;
+  const int tsz = min(topk, L + 1);
+  const float* mr = mass + row * nb;
+  const int32_t* id = ids + row * topk;
+  int hits = 0;
+  float score = 0.0f;
+  for (int s = 0; s < topk; ++s) {
+    const int blk = id[s];
+    if (blk < 0 || blk > L) continue;
+    const float v = mr[blk];
+    int above = 0;
+    for (int c = lane; c <= L; c += 64) {
+      const float x = mr[c];
+      above += (x > v || (x == v && c < blk)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) above += __shfl_xor(above, o, 64);
+    hits += above < tsz ? 1 : 0;
+    score += v;
+  }
+  if (lane == 0) {
+    brec[row] = (float)hits / (float)tsz;
+    srec[row] = score;
+  }
+}
+
+// mean of x[0..n) in a fixed order (fp64 partial sums), one workgroup
+__global__ void __launch_bounds__(1024)
+mean_kernel(const float* __restrict__ x, int64_t n, float* __restrict__ out) {
+  __shared__ double red[1024];
+  double v = 0.0;
+  for (int64_t a = threadIdx.x; a < n; a += 1024) v += (double)x[a];
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = n > 0 ? (float)(red[0] / (double)n) : 0.0f;
+}
+
+// ============================================================== launch
+
+constexpr int kDenseWaves = 8;
+
+template <typename T, int D, int R>
+static hipError_t lse_run(const Dims& d, const void* q, const void* k, float* lse, int qrows,
+                          int kstride, int ngroups, hipStream_t s) {
+  constexpr int QT = 64 * kDenseWaves / R;
+  const int ntiles = (d.Nq + QT - 1) / QT;
+  const int ntasks = ntiles * d.B * ngroups;
+  if (ntasks == 0) return hipSuccess;
+  const float scale_log2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
+  dense_lse_kernel<T, D, R, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
+      (const T*)q, (const T*)k, lse, d.N, d.Nq, d.q_start, qrows, kstride, ngroups, ntiles,
+      ntasks, scale_log2);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t lse_by_r(const Dims& d, int R, const void* q, const void* k, float* lse,
+                           int qrows, int kstride, int ngroups, hipStream_t s) {
+  switch (R) {
+    case 1: return lse_run<T, D, 1>(d, q, k, lse, qrows, kstride, ngroups, s);
+    case 2: return lse_run<T, D, 2>(d, q, k, lse, qrows, kstride, ngroups, s);
+    case 4: return lse_run<T, D, 4>(d, q, k, lse, qrows, kstride, ngroups, s);
+    case 8: return lse_run<T, D, 8>(d, q, k, lse, qrows, kstride, ngroups, s);
+    case 16: return lse_run<T, D, 16>(d, q, k, lse, qrows, kstride, ngroups, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t lse_by_dim(const Dims& d, int dim, int R, const void* q, const void* k,
+                             float* lse, int qrows, int kstride, int ngroups, hipStream_t s) {
+  if (dim == 64) return lse_by_r<T, 64>(d, R, q, k, lse, qrows, kstride, ngroups, s);
+  if (dim == 32) return lse_by_r<T, 32>(d, R, q, k, lse, qrows, kstride, ngroups, s);
+  if constexpr (sizeof(T) == 2) {
+    if (dim == 128) return lse_by_r<T, 128>(d, R, q, k, lse, qrows, kstride, ngroups, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dense_lse(const Dims& d, bool index_branch, const void* q, const void* k,
+                            float* lse, hipStream_t s) {
+  // main: G heads per group, K head y at offset y*D of a [Hkv*D] key row;
+  // index: Hkv heads per query, all on the one [DI] key row
+  const int dim = index_branch ? d.DI : d.D;
+  const int R = index_branch ? d.Hkv : d.G;
+  const int qrows = index_branch ? d.Hkv : d.Hq;
+  const int kstride = index_branch ? d.DI : d.Hkv * d.D;
+  const int ngroups = index_branch ? 1 : d.Hkv;
+  if (d.dtype == MSA_BF16) return lse_by_dim<bf16>(d, dim, R, q, k, lse, qrows, kstride, ngroups, s);
+  return lse_by_dim<float>(d, dim, R, q, k, lse, qrows, kstride, ngroups, s);
+}
+
+template <typename T, int D, int DI, int G>
+static hipError_t kl_dense_run(const Dims& d, const void* q, const void* k, const void* qi,
+                               const void* ki, const float* lse_main, const float* lse_idx,
+                               float* kl_rows, float* mass, hipStream_t s) {
+  constexpr int QT = 32 * kDenseWaves / G;
+  const int ntiles = (d.Nq + QT - 1) / QT;
+  const int ntasks = ntiles * d.B * d.Hkv;
+  if (ntasks == 0) return hipSuccess;
+  const float sc2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
+  const float zc2 = (float)(1.0 / std::sqrt((double)DI) * 1.4426950408889634);
+  kl_dense_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
+      (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass, d.N,
+      d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DI>
+static hipError_t kl_dense_by_g(const Dims& d, const void* q, const void* k, const void* qi,
+                                const void* ki, const float* lm, const float* li, float* kl,
+                                float* mass, hipStream_t s) {
+  switch (d.G) {
+    case 1: return kl_dense_run<T, D, DI, 1>(d, q, k, qi, ki, lm, li, kl, mass, s);
+    case 2: return kl_dense_run<T, D, DI, 2>(d, q, k, qi, ki, lm, li, kl, mass, s);
+    case 4: return kl_dense_run<T, D, DI, 4>(d, q, k, qi, ki, lm, li, kl, mass, s);
+    case 8: return kl_dense_run<T, D, DI, 8>(d, q, k, qi, ki, lm, li, kl, mass, s);
+    case 16: return kl_dense_run<T, D, DI, 16>(d, q, k, qi, ki, lm, li, kl, mass, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+static hipError_t kl_dense_by_di(const Dims& d, const void* q, const void* k, const void* qi,
+                                 const void* ki, const float* lm, const float* li, float* kl,
+                                 float* mass, hipStream_t s) {
+  if (d.DI == 64) return kl_dense_by_g<T, D, 64>(d, q, k, qi, ki, lm, li, kl, mass, s);
+  if (d.DI == 32) return kl_dense_by_g<T, D, 32>(d, q, k, qi, ki, lm, li, kl, mass, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kl_dense(const Dims& d, const void* q, const void* k, const void* q_idx,
+                           const void* k_idx, const float* lse_main, const float* lse_idx,
+                           float* kl_rows, float* mass, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128)
+      return kl_dense_by_di<bf16, 128>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
+    if (d.D == 64)
+      return kl_dense_by_di<bf16, 64>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
+  } else if (d.D == 64) {
+    return kl_dense_by_di<float, 64>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_recall(const Dims& d, const float* mass, const int32_t* ids, float* brec,
+                         float* srec, hipStream_t s) {
+  const int64_t nrows = d.rows * d.Hkv;
+  if (nrows == 0) return hipSuccess;
+  recall_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, s>>>(mass, ids, brec, srec, nrows, d.Nq,
+                                                            d.q_start, d.Hkv, d.nb, d.K);
+  return hipGetLastError();
+}
+
+hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s) {
+  mean_kernel<<<1, 1024, 0, s>>>(x, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -101,6 +101,32 @@ __device__ __forceinline__ int tile_off(int rho, int col) {
   return rho * D + 8 * ((col >> 3) ^ sw) + (col & 7);
 }
 
+// ---- LDS tiles of 16-byte chunks: chunk c of row r sits at c ^ (idx_swz(r) & M),
+// M = min(chunks per row, 8) - 1, so that 32-row fragment reads and row-wise
+// stores spread over all banks.
+__device__ __forceinline__ int idx_swz(int r) { return r ^ (r >> 3); }
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int CPR>
+__device__ __forceinline__ vec8<T> lds_frag(const i32x4* tile, int r, int c0) {
+  constexpr int M = (CPR < 8 ? CPR : 8) - 1;
+  const i32x4* row = tile + r * CPR;
+  const int s = idx_swz(r) & M;
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8<T>, row[c0 ^ s]);
+  } else {
+    const i32x4 lo = row[c0 ^ s], hi = row[(c0 + 1) ^ s];
+    f32x8 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = __int_as_float(lo[e]);
+      v[4 + e] = __int_as_float(hi[e]);
+    }
+    return v;
+  }
+}
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -172,5 +198,15 @@ hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_
                      const AttnWs& w, float* idx_stats, float* lse_idx, float* kl_part,
                      float* kl_rows, float* kl_block_sums, float* kl_mean, float* dlogits,
                      hipStream_t s);
+
+// warm-up stage on the full causal context
+hipError_t launch_dense_lse(const Dims& d, bool index_branch, const void* q, const void* k,
+                            float* lse, hipStream_t s);
+hipError_t launch_kl_dense(const Dims& d, const void* q, const void* k, const void* q_idx,
+                           const void* k_idx, const float* lse_main, const float* lse_idx,
+                           float* kl_rows, float* mass, hipStream_t s);
+hipError_t launch_recall(const Dims& d, const float* mass, const int32_t* ids, float* brec,
+                         float* srec, hipStream_t s);
+hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s);
 
 }  // namespace msa

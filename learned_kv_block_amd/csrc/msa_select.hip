@@ -58,29 +58,6 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // c ^ swz(r) inside the row, so that the 32 rows a fragment read touches (and
 // the rows a store touches) spread over all banks.
 
-__device__ __forceinline__ int idx_swz(int r) { return r ^ (r >> 3); }
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-template <typename T, int CPR>
-__device__ __forceinline__ vec8<T> lds_frag(const i32x4* tile, int r, int c0) {
-  constexpr int M = (CPR < 8 ? CPR : 8) - 1;
-  const i32x4* row = tile + r * CPR;
-  const int s = idx_swz(r) & M;
-  if constexpr (sizeof(T) == 2) {
-    return __builtin_bit_cast(vec8<T>, row[c0 ^ s]);
-  } else {
-    const i32x4 lo = row[c0 ^ s], hi = row[(c0 + 1) ^ s];
-    f32x8 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = __int_as_float(lo[e]);
-      v[4 + e] = __int_as_float(hi[e]);
-    }
-    return v;
-  }
-}
-
 template <typename T, int DI, int HKV, int NW, int CB>
 __global__ void __launch_bounds__(64 * NW, sizeof(T) == 2 ? 8 / NW : 1)
 index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,

@@ -103,3 +103,25 @@ def test_workspace_sizes_scale_with_the_workload():
     assert msa.workspace_size(big, msa.MSA_OP_ATTN) >= 131072 * 4 * 16 * 16 * 128 * 2
     assert msa.workspace_size(small, msa.MSA_OP_ATTN) < msa.workspace_size(big, msa.MSA_OP_ATTN)
     assert msa.workspace_size(big, 7) == 0
+
+
+def test_dense_calls_validate_on_host():
+    """msa_dense_lse / msa_kl_dense / msa_block_recall reject NULL outputs, misaligned inputs
+    and fp32 with head_dim 128 before any launch."""
+    L = msa.lib()
+    sh = shape()
+    assert L.msa_dense_lse(ctypes.byref(sh), FAKE, FAKE, None, None) == msa.MSA_ERR_NULL
+    assert L.msa_dense_lse(ctypes.byref(sh), ctypes.c_void_p(0x100002), FAKE, FAKE,
+                           None) == msa.MSA_ERR_SHAPE
+    f32 = shape(dtype=msa.MSA_F32)
+    assert L.msa_dense_lse(ctypes.byref(f32), FAKE, FAKE, FAKE, None) == msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_kl_dense(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          None, None) == msa.MSA_ERR_UNSUPPORTED
+    assert L.msa_kl_dense(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                          None, None) == msa.MSA_ERR_NULL
+    assert L.msa_kl_dense(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                          None, None) == msa.MSA_ERR_NULL
+    assert L.msa_block_recall(ctypes.byref(sh), FAKE, None, FAKE, FAKE, None,
+                              None) == msa.MSA_ERR_NULL
+    assert L.msa_block_recall(ctypes.byref(shape(topk=40)), FAKE, FAKE, FAKE, FAKE, None,
+                              None) == msa.MSA_ERR_UNSUPPORTED
