@@ -59,8 +59,16 @@ def _L():
         lib.msa_ref_kl.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, P, P, ctypes.c_int]
         lib.msa_ref_attn_bwd.argtypes = [sp, P, P, P, P, P, P, I64, P, P, P, ctypes.c_int]
         lib.msa_ref_idx_bwd.argtypes = [sp, P, P, P, P, ctypes.c_double, P, I64, P, P]
+        lib.msa_ref_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.msa_ref_e4m3_encode.restype = ctypes.c_uint8
+        lib.msa_ref_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.msa_ref_e4m3_decode.restype = ctypes.c_double
+        lib.msa_ref_fp8_scale_exp.argtypes = [ctypes.c_double]
+        lib.msa_ref_quantize_fp8.argtypes = [sp, P, P, I64, P, P, P, P]
+        lib.msa_ref_select_fp8.argtypes = [sp, P, P, P, P, P, I64, P, P, P, ctypes.c_int]
         for f in ("msa_ref_topk_row", "msa_ref_select", "msa_ref_attn", "msa_ref_kl_row",
-                  "msa_ref_kl", "msa_ref_attn_bwd", "msa_ref_idx_bwd"):
+                  "msa_ref_kl", "msa_ref_attn_bwd", "msa_ref_idx_bwd", "msa_ref_fp8_scale_exp",
+                  "msa_ref_quantize_fp8", "msa_ref_select_fp8"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -249,3 +257,69 @@ def idx_bwd(shape: RefShape, q_idx, k_idx, ids, dlogits, coef=1.0, rows=None):
                               float(coef), _p(r), n, _p(dq), _p(dk))
     assert rc == 0, rc
     return dq, dk
+
+
+# ----------------------------------------------------------------------- FP8 index scoring
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of values with |v| <= 448: nearest value, ties to the even code."""
+    v = np.asarray(values, dtype=np.float64).ravel()
+    f = _L().msa_ref_e4m3_encode
+    return np.array([f(float(x)) for x in v], dtype=np.uint8).reshape(np.shape(values))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    f = _L().msa_ref_e4m3_decode
+    return np.array([f(int(x)) for x in c], dtype=np.float64).reshape(np.shape(codes))
+
+
+def fp8_scale_exp(amax: float) -> int:
+    """Smallest e with amax <= 448 * 2^e (0 for amax = 0)."""
+    return int(_L().msa_ref_fp8_scale_exp(float(amax)))
+
+
+def quantize_fp8(shape: RefShape, q_idx, k_idx=None):
+    """dict(q8 [n, Hkv, d_idx] uint8, q_exp [n, Hkv] int32, and with k_idx: k8 [B, N, d_idx],
+    k_exp [B, nb]) for compact q_idx rows [n, Hkv, d_idx]."""
+    q_idx = _raw(q_idx, shape.dtype)
+    n = q_idx.shape[0]
+    H, di = shape.num_kv_heads, shape.idx_dim
+    nb = (shape.seqlen_kv + shape.block_size - 1) // shape.block_size
+    q8 = np.empty((n, H, di), dtype=np.uint8)
+    qe = np.empty((n, H), dtype=np.int32)
+    k8 = ke = None
+    if k_idx is not None:
+        k_idx = _raw(k_idx, shape.dtype)
+        k8 = np.zeros((shape.batch, shape.seqlen_kv, di), dtype=np.uint8)
+        ke = np.empty((shape.batch, nb), dtype=np.int32)
+    rc = _L().msa_ref_quantize_fp8(ctypes.byref(shape), _p(q_idx), _p(k_idx), n, _p(q8), _p(qe),
+                                   _p(k8), _p(ke))
+    assert rc == 0, rc
+    out = {"q8": q8, "q_exp": qe}
+    if k_idx is not None:
+        out.update(k8=k8, k_exp=ke)
+    return out
+
+
+def select_fp8(shape: RefShape, q8, q_exp, k8, k_exp, rows=None, want_scores=False,
+               want_margin=False):
+    """Selection on the FP8 index logits: ids [n, Hkv, k] (+ block scores, margin)."""
+    q8, qe = _c(q8, np.uint8), _c(q_exp, np.int32)
+    k8, ke = _c(k8, np.uint8), _c(k_exp, np.int32)
+    r, n = _rows(shape, rows)
+    nb = (shape.seqlen_kv + shape.block_size - 1) // shape.block_size
+    H = shape.num_kv_heads
+    ids = np.empty((n, H, shape.topk), dtype=np.int32)
+    sc = np.empty((n, H, nb), dtype=np.float64) if want_scores else None
+    mg = np.empty((n, H), dtype=np.float64) if want_margin else None
+    rc = _L().msa_ref_select_fp8(ctypes.byref(shape), _p(q8), _p(qe), _p(k8), _p(ke), _p(r), n,
+                                 _p(ids), _p(sc), _p(mg), threads())
+    assert rc == 0, rc
+    out = {"ids": ids}
+    if want_scores:
+        out["block_scores"] = sc
+    if want_margin:
+        out["margin"] = mg
+    return out

@@ -611,3 +611,157 @@ int msa_ref_idx_bwd(const msa_ref_shape* s, const void* q_idx, const void* k_idx
   }
   return REF_OK;
 }
+
+/* ------------------------------------------------------------------------ FP8 index scoring */
+
+/*
+ * FP8 variant of the index branch. [Indexer] §3.1 notes that the DSA indexer
+ * can run in FP8; [Superv] after eq. (9) warns that a small cutoff margin lets
+ * FP8 quantization flip candidates. The pages fix no format or scaling, so
+ * (readings, also in the design notes):
+ *  - format: OCP FP8 E4M3 ("e4m3fn"): sign, 4 exponent bits with bias 7, 3
+ *    mantissa bits; no infinities; S.1111.111 is NaN, so the largest finite
+ *    magnitude is 1.75 * 2^8 = 448; exponent field 0 holds subnormals m * 2^-9;
+ *  - rounding: to the nearest E4M3 value, ties to the even code;
+ *  - scales: a power of two 2^e per Q_idx row (b, t, r) and per 128-token
+ *    K_idx block (b, blk): e is the smallest integer with amax <= 448 * 2^e
+ *    (e = 0 when amax = 0), and the stored value is the E4M3 rounding of
+ *    x * 2^-e (an exact scaling);
+ *  - scores: S8_idx(i, j) = (sum_c q8_c k8_c) * 2^(e_q + e_k) / sqrt(d_idx), then
+ *    the same causal block max and selection rule as msa_ref_select.
+ */
+static double e4m3_value(int code) {
+  const int E = (code >> 3) & 15, m = code & 7;
+  const double mag = E == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, E - 7);
+  return (code & 0x80) ? -mag : mag;
+}
+
+/* Nearest E4M3 code to y (|y| <= 448), by comparing with every finite
+ * non-negative code; on a tie the even code wins. */
+uint8_t msa_ref_e4m3_encode(double y) {
+  const double a = fabs(y);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double d = fabs(a - e4m3_value(c));
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+double msa_ref_e4m3_decode(uint8_t code) { return e4m3_value(code); }
+
+/* smallest e with amax <= 448 * 2^e; 0 for amax = 0 */
+int msa_ref_fp8_scale_exp(double amax) {
+  if (!(amax > 0.0)) return 0;
+  int e = 0;
+  while (amax > ldexp(448.0, e)) ++e;
+  while (amax <= ldexp(448.0, e - 1)) --e;
+  return e;
+}
+
+/*
+ * Quantize the index inputs: q8 [nrows, Hkv, d_idx] and q_exp [nrows, Hkv] for
+ * the listed rows (q_idx compact [nrows, Hkv, d_idx]); when k8 != NULL also
+ * k8 [B, N, d_idx] and k_exp [B, nb] (k_idx [B, N, d_idx]).
+ */
+int msa_ref_quantize_fp8(const msa_ref_shape* s, const void* q_idx, const void* k_idx,
+                         int64_t nrows, uint8_t* q8, int32_t* q_exp, uint8_t* k8,
+                         int32_t* k_exp) {
+  if (!shape_ok(s) || nrows < 0 || (nrows > 0 && (!q_idx || !q8 || !q_exp)) ||
+      (k8 && (!k_idx || !k_exp)))
+    return REF_ERR_ARG;
+  const int Hkv = s->num_kv_heads, di = s->idx_dim, Bk = s->block_size, nb = num_blocks(s);
+  const int64_t N = s->seqlen_kv;
+  for (int64_t x = 0; x < nrows * Hkv; ++x) {
+    double amax = 0.0;
+    for (int c = 0; c < di; ++c) amax = fmax(amax, fabs(ld(q_idx, s->dtype, x * di + c)));
+    const int e = msa_ref_fp8_scale_exp(amax);
+    q_exp[x] = e;
+    for (int c = 0; c < di; ++c)
+      q8[x * di + c] = msa_ref_e4m3_encode(ldexp(ld(q_idx, s->dtype, x * di + c), -e));
+  }
+  if (k8) {
+    for (int64_t b = 0; b < s->batch; ++b)
+      for (int blk = 0; blk < nb; ++blk) {
+        const int64_t j0 = (int64_t)blk * Bk, j1 = j0 + Bk < N ? j0 + Bk : N;
+        double amax = 0.0;
+        for (int64_t j = j0; j < j1; ++j)
+          for (int c = 0; c < di; ++c)
+            amax = fmax(amax, fabs(ld(k_idx, s->dtype, (b * N + j) * di + c)));
+        const int e = msa_ref_fp8_scale_exp(amax);
+        k_exp[b * nb + blk] = e;
+        for (int64_t j = j0; j < j1; ++j)
+          for (int c = 0; c < di; ++c)
+            k8[(b * N + j) * di + c] =
+                msa_ref_e4m3_encode(ldexp(ld(k_idx, s->dtype, (b * N + j) * di + c), -e));
+      }
+  }
+  return REF_OK;
+}
+
+/*
+ * Selection from the quantized index inputs: msa_ref_select with the index
+ * logits S8_idx above (exact products and sums of the E4M3 values in double).
+ * q8 / q_exp compact for the listed rows; k8 [B, N, d_idx], k_exp [B, nb].
+ */
+int msa_ref_select_fp8(const msa_ref_shape* s, const uint8_t* q8, const int32_t* q_exp,
+                       const uint8_t* k8, const int32_t* k_exp, const int64_t* rows,
+                       int64_t nrows, int32_t* ids, double* block_scores, double* margin,
+                       int nthreads) {
+  if (!shape_ok(s) || !q8 || !q_exp || !k8 || !k_exp || !ids || nrows < 0) return REF_ERR_ARG;
+  const int Hkv = s->num_kv_heads, di = s->idx_dim, Bk = s->block_size, k = s->topk;
+  const int nb = num_blocks(s);
+  const int64_t N = s->seqlen_kv, Nq = s->seqlen_q;
+  const double inv_sqrt_di = 1.0 / sqrt((double)di);
+  if (nthreads < 1) nthreads = 1;
+  int err = 0;
+#pragma omp parallel num_threads(nthreads)
+  {
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double* M = (double*)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+    double* ql = (double*)malloc(sizeof(double) * (size_t)di);
+    if (!sc || !M || !ql) {
+#pragma omp atomic write
+      err = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t q = 0; q < nrows; ++q) {
+      if (err) continue;
+      const int64_t row = rows ? rows[q] : q;
+      const int64_t b = row / (Nq > 0 ? Nq : 1), t = row % (Nq > 0 ? Nq : 1);
+      const int64_t i = s->q_start + t;
+      const int L = (int)(i / Bk);
+      for (int r = 0; r < Hkv; ++r) {
+        for (int c = 0; c < di; ++c) ql[c] = e4m3_value(q8[(q * Hkv + r) * di + c]);
+        for (int64_t j = 0; j <= i; ++j) {
+          double acc = 0.0;
+          for (int c = 0; c < di; ++c) acc += ql[c] * e4m3_value(k8[(b * N + j) * di + c]);
+          const int e = q_exp[q * Hkv + r] + k_exp[b * nb + j / Bk];
+          sc[j] = ldexp(acc, e) * inv_sqrt_di;
+        }
+        for (int blk = 0; blk <= L; ++blk) {
+          const int64_t j0 = (int64_t)blk * Bk;
+          int64_t j1 = j0 + Bk - 1;
+          if (j1 > i) j1 = i;
+          double m = -INFINITY;
+          for (int64_t j = j0; j <= j1; ++j) m = sc[j] > m ? sc[j] : m;
+          M[blk] = m;
+        }
+        if (block_scores)
+          for (int blk = 0; blk < nb; ++blk)
+            block_scores[(q * Hkv + r) * nb + blk] = blk <= L ? M[blk] : -INFINITY;
+        double mg;
+        msa_ref_topk_row(M, L, k, ids + (q * Hkv + r) * k, &mg);
+        if (margin) margin[q * Hkv + r] = mg;
+      }
+    }
+    free(sc);
+    free(M);
+    free(ql);
+  }
+  return err ? REF_ERR_ARG : REF_OK;
+}

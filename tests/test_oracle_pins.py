@@ -595,3 +595,84 @@ def test_idx_bwd_is_finite_difference_of_kl():
             key = "qi" if name == "q_idx" else "ki"
             f = (total(**{**args, key: p}) - total(**{**args, key: m})) / (float(p[idx]) - float(m[idx]))
             assert abs(f - grad[idx]) < 2e-5 * max(1.0, abs(f)), (name, idx, f, grad[idx])
+
+
+# ----------------------------------------------------------------------- FP8 index scoring
+
+
+def _e4m3_grid():
+    """Every finite non-negative E4M3 value (OCP: bias 7, 3 mantissa bits, max 448)."""
+    vals = [m * 2.0 ** -9 for m in range(8)]
+    vals += [(1 + m / 8) * 2.0 ** (E - 7) for E in range(1, 16) for m in range(8)
+             if not (E == 15 and m == 7)]
+    return np.array(vals)
+
+
+def test_e4m3_encode_matches_torch_float8_e4m3fn():
+    """The oracle's E4M3 rounding (nearest value, ties to the even code) equals torch's
+    float8_e4m3fn conversion bit for bit: random fp32 values over the whole range
+    (subnormals included, both signs), every exact midpoint between neighbouring codes,
+    and the codes themselves."""
+    rng = np.random.default_rng(31)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 4000))
+    vals = (mag * rng.choice([-1.0, 1.0], 4000)).astype(np.float32)
+    grid = _e4m3_grid()
+    mids = ((grid[:-1] + grid[1:]) / 2).astype(np.float32)
+    allv = np.concatenate([vals, mids, -mids, grid.astype(np.float32), np.float32([0.0, -0.0])])
+    ref = torch.from_numpy(allv).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.e4m3_encode(allv.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    # decode is the inverse on every code, and the spec's landmarks
+    codes = np.arange(0x7F, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.e4m3_decode(codes), grid)
+    assert oracle.e4m3_encode([448.0, 2.0 ** -6, 2.0 ** -9, 1.0]).tolist() == [0x7E, 0x08, 0x01,
+                                                                              0x38]
+
+
+def test_fp8_scale_exponent_is_the_smallest_fit():
+    """e = the smallest integer with amax <= 448 * 2^e, checked by brute force on either side
+    of powers of two and on random magnitudes."""
+    rng = np.random.default_rng(32)
+    tests = list(np.exp2(rng.uniform(-30, 30, 500)))
+    tests += [448.0 * 2.0 ** k for k in range(-20, 20)]
+    tests += [np.nextafter(448.0 * 2.0 ** k, np.inf) for k in range(-20, 20)]
+    for a in tests:
+        e = oracle.fp8_scale_exp(a)
+        assert a <= 448.0 * 2.0 ** e and not (a <= 448.0 * 2.0 ** (e - 1)), (a, e)
+    assert oracle.fp8_scale_exp(0.0) == 0
+
+
+def test_select_fp8_equals_exact_selection_on_representable_inputs():
+    """When every Q_idx row and K_idx block is an E4M3 value times the power of two that the
+    scale rule picks (here: each row and block holds one +-448 * 2^e entry), quantization is
+    exact and the FP8 path must reproduce the exact selection, scores and margin. The K_idx
+    blocks get different exponents, so a per-tensor or per-token scale would not be exact."""
+    rng = np.random.default_rng(33)
+    N, Nq, q_start, Bk, Hkv, di, k = 300, 120, 180, 32, 2, 8, 3
+    nb = (N + Bk - 1) // Bk
+    grid = _e4m3_grid()
+
+    def draw(*shape):
+        v = rng.choice(grid[40:], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        return v
+
+    q = draw(Nq, Hkv, di)
+    q[..., 0] = 448.0
+    q *= np.exp2(rng.integers(-6, 3, size=(Nq, Hkv, 1)))
+    kk = draw(1, N, di)
+    for b in range(nb):
+        kk[0, b * Bk, 0] = -448.0
+        kk[0, b * Bk:(b + 1) * Bk] *= 2.0 ** (-(b % 5))
+    q, kk = q.astype(np.float32), kk.astype(np.float32)
+    sh = shape(seqlen_kv=N, seqlen_q=Nq, q_start=q_start, num_kv_heads=Hkv, idx_dim=di,
+               block_size=Bk, topk=k)
+    qz = oracle.quantize_fp8(sh, q, kk)
+    assert qz["k_exp"][0].tolist() == [-(b % 5) for b in range(nb)]
+    np.testing.assert_array_equal(oracle.e4m3_decode(qz["k8"]) * np.exp2(
+        np.repeat(qz["k_exp"], Bk, axis=1)[:, :N, None]), kk)
+    exact = oracle.select(sh, q, kk, want_scores=True, want_margin=True)
+    f8 = oracle.select_fp8(sh, qz["q8"], qz["q_exp"], qz["k8"], qz["k_exp"], want_scores=True,
+                           want_margin=True)
+    np.testing.assert_array_equal(f8["ids"], exact["ids"])
+    np.testing.assert_array_equal(f8["block_scores"], exact["block_scores"])
+    np.testing.assert_array_equal(f8["margin"], exact["margin"])
