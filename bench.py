@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15  # dense bf16 MFMA, MI355X
 PEAK_HBM = 8.0e12   # bytes/s
+PEAK_FP8 = 5.0e15   # dense fp8 MFMA, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_skewed_n131072_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "learned_kv_block_amd", "csrc", f)
                   for f in ("msa_attn.hip", "msa_internal.hpp")]
@@ -261,6 +262,10 @@ def main():
     ap.add_argument("--dense", action="store_true",
                     help="time the warm-up stage instead (dense LSE, KL on the full causal "
                          "context with block masses, selection and block / score recall)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="select with the FP8 (E4M3) index path: Q_idx quantized every step, "
+                         "K_idx every step for prefill and once (as a cache holds it) for "
+                         "decode; reports the churn against the bf16 selection")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for HBM counter calibration)")
@@ -300,10 +305,27 @@ def main():
     ws_ibwd = (torch.empty(msa.workspace_size(sh_sel, msa.MSA_OP_IDX_BWD), dtype=torch.uint8,
                            device=dev) if args.bwd and args.kl else None)
 
+    decode = cfg.seqlen_q == 1
+    kz = (msa.msa_index_quantize_fp8(None, x["k_idx"], q_start=cfg.q_start)
+          if args.fp8 and decode else None)
+
+    def select():
+        if not args.fp8:
+            return msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                                  num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim,
+                                  workspace=ws_sel)
+        if decode:  # the cache holds K_idx in FP8; only the new query rows are quantized
+            qz = msa.msa_index_quantize_fp8(x["q_idx"], None, seqlen_kv=cfg.seqlen_kv,
+                                            q_start=cfg.q_start)
+            qz.update(kz)
+        else:
+            qz = msa.msa_index_quantize_fp8(x["q_idx"], x["k_idx"], q_start=cfg.q_start)
+        return msa.msa_select_fp8(qz["q8"], qz["q_exp"], qz["k8"], qz["k_exp"], cfg.topk,
+                                  q_start=cfg.q_start, num_q_heads=cfg.num_q_heads,
+                                  head_dim=cfg.head_dim, workspace=ws_sel)
+
     def step():
-        sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
-                             num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim,
-                             workspace=ws_sel)
+        sel = select()
         msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], q_start=cfg.q_start,
                          idx_dim=cfg.idx_dim, workspace=ws_attn, out=out, lse=lse)
         if args.kl:
@@ -353,8 +375,9 @@ def main():
 
     kernels = {}
     if args.breakdown:
-        names = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
-                 "work_items", "sparse_attn", "combine"]
+        names = (["quantize_fp8", "index_fp8"] if args.fp8 else ["index_blockmax"]) + [
+            "topk", "bucket_hist", "bucket_scan", "bucket_scatter", "work_items", "sparse_attn",
+            "combine"]
         if args.kl:
             names += ["kl_idx_stats", "kl_idx_lse", "kl_main", "kl_reduce"]
         if args.bwd:
@@ -409,6 +432,27 @@ def main():
     }
     if kernels:
         line["kernel_ms"] = kernels
+    if args.fp8:
+        line["metric"] = ("MSA-layer prefill query-tokens/s with the FP8 (E4M3) index branch"
+                          if not decode else "MSA decode query-tokens/s with the FP8 index branch")
+        line["config"]["index_dtype"] = "fp8_e4m3"
+        if "index_fp8" in kernels:
+            line["index_fp8_tflops"] = f_idx / (kernels["index_fp8"] * 1e-3) / 1e12
+            line["index_fp8_frac"] = f_idx / (kernels["index_fp8"] * 1e-3) / PEAK_FP8
+        # churn of the FP8 selection against the bf16 one on the same inputs
+        s16 = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
+                             want_margin=True, num_q_heads=cfg.num_q_heads,
+                             head_dim=cfg.head_dim)
+        ids8 = select()["ids"]
+        changed = (s16["ids"] != ids8).any(dim=-1)
+        small = torch.isfinite(s16["margin"]) & (s16["margin"] < 0.03)
+        line["fp8_churn"] = {
+            "changed_share": float(changed.float().mean()),
+            "changed_share_margin_lt_0.03": float(changed[small].float().mean()) if bool(small.any()) else 0.0,
+            "changed_share_margin_ge_0.1": float(changed[torch.isfinite(s16["margin"]) &
+                                                         (s16["margin"] >= 0.1)].float().mean())
+            if bool((s16["margin"] >= 0.1).any()) else 0.0}
+        del s16, ids8, changed, small
     if args.kl:
         line["metric"] = "MSA-layer training step (select + attention + KL align) query-tokens/s"
         line["config"]["kl"] = True
@@ -422,7 +466,7 @@ def main():
         line["attn_bwd_flops_per_step"] = 2.5 * f_attn
         if "attn_bwd" in kernels:
             line["attn_bwd_mfma_frac"] = 2.5 * f_attn / (kernels["attn_bwd"] * 1e-3) / PEAK_BF16
-    del x, ws_sel, ws_attn, ws_kl, ws_bwd, ws_ibwd, out, lse
+    del x, ws_sel, ws_attn, ws_kl, ws_bwd, ws_ibwd, out, lse, kz
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

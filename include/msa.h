@@ -283,6 +283,45 @@ msa_status msa_block_recall(const msa_shape* shape, const float* block_mass,
                             const int32_t* block_ids, float* block_recall, float* score_recall,
                             float* means, hipStream_t stream);
 
+/*
+ * msa_index_quantize_fp8 — FP8 inputs of the index branch (MSA vs DSA indexer
+ * note §3.1: the indexer's scores may run in FP8). Format OCP E4M3 (bias 7, max
+ * 448, no infinities), round to nearest with ties to the even code. Scales are
+ * powers of two: one per Q_idx row (b, t, r) and one per 128-token K_idx block
+ * (b, c); e = the smallest integer with amax <= 448 * 2^e (0 for an all-zero
+ * row or block), and the stored byte encodes x * 2^-e.
+ *
+ *  in   q_idx, k_idx        device, layouts above (fp32 or bf16 by dtype)
+ *  out  q8 (opt)            device uint8 [batch, seqlen_q, num_kv_heads, idx_dim]
+ *  out  q_exp               device int32 [batch, seqlen_q, num_kv_heads] (with q8)
+ *  out  k8 (opt)            device uint8 [batch, seqlen_kv, idx_dim]
+ *  out  k_exp               device int32 [batch, ceil(seqlen_kv / 128)] (with k8)
+ * At least one of q8, k8. q8 and k8 must be 16-byte aligned. K_idx can be
+ * quantized once (e.g. when a cache is written) and reused by later calls.
+ * No workspace.
+ */
+msa_status msa_index_quantize_fp8(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                                  uint8_t* q8, int32_t* q_exp, uint8_t* k8, int32_t* k_exp,
+                                  hipStream_t stream);
+
+/*
+ * msa_select_fp8 — msa_select on the FP8 index inputs: the index logits are
+ * (q8 . k8 on the FP8 matrix cores) * 2^(q_exp + k_exp of the key's block) /
+ * sqrt(idx_dim), then the same causal block max and the same selection rule
+ * (selector supervision page, after eq. 9: a small cutoff margin is where
+ * FP8 quantization flips candidates; cutoff_margin reports it per row).
+ *
+ *  in   q8, q_exp, k8, k_exp  as msa_index_quantize_fp8 writes them
+ *  out  block_ids, block_scores (opt), cutoff_margin (opt)  as for msa_select
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_SELECT) bytes (may be
+ *       NULL when block_scores is given)
+ * dtype is not used (the inputs are FP8).
+ */
+msa_status msa_select_fp8(const msa_shape* shape, const uint8_t* q8, const int32_t* q_exp,
+                          const uint8_t* k8, const int32_t* k_exp, int32_t* block_ids,
+                          float* block_scores, float* cutoff_margin, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* msa_status_string(msa_status status);
 
@@ -298,7 +337,8 @@ enum {
   MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
   MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_DENSE_LSE = 14, MSA_K_KL_DENSE = 15,
-  MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_COUNT = 18
+  MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_INDEX_FP8 = 18, MSA_K_QUANTIZE_FP8 = 19,
+  MSA_K_COUNT = 20
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* total_ms, int* launches);

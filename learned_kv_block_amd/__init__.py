@@ -20,6 +20,8 @@ Functions (same names as the C entry points):
                                                      -> kl_rows, kl_mean, lse_idx, block_mass
   msa_block_recall(block_mass, block_ids, q_start=0, ...)
                                                      -> block_recall, score_recall, means
+  msa_index_quantize_fp8(q_idx, k_idx, ...)          -> q8, q_exp, k8, k_exp (OCP E4M3)
+  msa_select_fp8(q8, q_exp, k8, k_exp, topk, ...)    -> block ids (+ scores, margin)
 """
 from __future__ import annotations
 
@@ -37,9 +39,10 @@ MSA_F32, MSA_BF16 = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2, 3, 4
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx"]
+           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
+           "msa_index_quantize_fp8", "msa_select_fp8",
            "msa_status_string", "msa_prof_begin", "msa_prof_end"]
 
 
@@ -77,8 +80,11 @@ def lib() -> ctypes.CDLL:
         L.msa_dense_lse.argtypes = [S, P, P, P, P]
         L.msa_kl_dense.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
         L.msa_block_recall.argtypes = [S, P, P, P, P, P, P]
+        L.msa_index_quantize_fp8.argtypes = [S, P, P, P, P, P, P, P]
+        L.msa_select_fp8.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
                   "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
+                  "msa_index_quantize_fp8", "msa_select_fp8",
                   "msa_prof_begin", "msa_prof_end"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
@@ -334,6 +340,77 @@ def msa_block_recall(block_mass: torch.Tensor, block_ids: torch.Tensor, q_start:
     if st != MSA_OK:
         raise MsaError(st, "msa_block_recall")
     return {"block_recall": brec, "score_recall": srec, "means": means}
+
+
+def msa_index_quantize_fp8(q_idx: Optional[torch.Tensor], k_idx: Optional[torch.Tensor],
+                           seqlen_kv: Optional[int] = None, q_start: int = 0,
+                           num_q_heads: Optional[int] = None, head_dim: int = 128):
+    """OCP E4M3 index inputs with power-of-two scales per Q_idx row / K_idx block:
+    dict(q8 uint8 [B, Nq, Hkv, d_idx], q_exp int32 [B, Nq, Hkv]) for q_idx and/or
+    dict(k8 uint8 [B, N, d_idx], k_exp int32 [B, nb]) for k_idx (either may be None)."""
+    if q_idx is None and k_idx is None:
+        raise ValueError("nothing to quantize")
+    ref = q_idx if q_idx is not None else k_idx
+    if q_idx is not None:
+        _check(q_idx, "q_idx", 4)
+        B, Nq, Hkv, DI = q_idx.shape
+    if k_idx is not None:
+        _check(k_idx, "k_idx", 3)
+        B, N, DI = k_idx.shape
+    else:
+        N = seqlen_kv if seqlen_kv is not None else q_start + Nq
+    if q_idx is None:
+        Nq, Hkv = 1, 1
+        q_start = N - 1
+    Hq = num_q_heads if num_q_heads is not None else Hkv
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, head_dim, DI, 1, _dtype_code(ref))
+    dev = ref.device
+    out = {}
+    q8 = qe = k8 = ke = None
+    if q_idx is not None:
+        q8 = torch.empty(q_idx.shape, dtype=torch.uint8, device=dev)
+        qe = torch.empty(q_idx.shape[:3], dtype=torch.int32, device=dev)
+        out.update(q8=q8, q_exp=qe)
+    if k_idx is not None:
+        k8 = torch.empty(k_idx.shape, dtype=torch.uint8, device=dev)
+        ke = torch.empty((B, (N + 127) // 128), dtype=torch.int32, device=dev)
+        out.update(k8=k8, k_exp=ke)
+    st = lib().msa_index_quantize_fp8(ctypes.byref(sh), _ptr(q_idx), _ptr(k_idx), _ptr(q8),
+                                      _ptr(qe), _ptr(k8), _ptr(ke), _stream(ref))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_index_quantize_fp8")
+    return out
+
+
+def msa_select_fp8(q8: torch.Tensor, q_exp: torch.Tensor, k8: torch.Tensor, k_exp: torch.Tensor,
+                   topk: int, q_start: int = 0, want_scores: bool = False,
+                   want_margin: bool = False, num_q_heads: Optional[int] = None,
+                   head_dim: int = 128, workspace: Optional[torch.Tensor] = None):
+    """msa_select on FP8 index inputs (as msa_index_quantize_fp8 returns them)."""
+    _check(q8, "q8", 4)
+    _check(k8, "k8", 3)
+    _check(q_exp, "q_exp", 3)
+    _check(k_exp, "k_exp", 2)
+    B, Nq, Hkv, DI = q8.shape
+    N = k8.shape[1]
+    Hq = num_q_heads if num_q_heads is not None else Hkv
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, head_dim, DI, topk, MSA_BF16)
+    nb = (N + 127) // 128
+    dev = q8.device
+    ids = torch.empty((B, Nq, Hkv, topk), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev) if want_scores else None
+    margin = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev) if want_margin else None
+    ws, nws = (None, 0) if want_scores else _workspace(sh, MSA_OP_SELECT, dev, workspace)
+    st = lib().msa_select_fp8(ctypes.byref(sh), _ptr(q8), _ptr(q_exp), _ptr(k8), _ptr(k_exp),
+                              _ptr(ids), _ptr(scores), _ptr(margin), _ptr(ws), nws, _stream(q8))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_select_fp8")
+    out = {"ids": ids}
+    if want_scores:
+        out["block_scores"] = scores
+    if want_margin:
+        out["margin"] = margin
+    return out
 
 
 class KernelTimer:

@@ -14,7 +14,7 @@ OUT = os.path.join(HERE, "libmsa.so")
 BUILD = os.path.join(HERE, "_build")
 
 SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_kl.hip", "msa_bwd.hip",
-           "msa_dense.hip"]
+           "msa_dense.hip", "msa_fp8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -488,6 +488,50 @@ msa_status msa_block_recall(const msa_shape* shape, const float* block_mass,
   return MSA_OK;
 }
 
+msa_status msa_index_quantize_fp8(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                                  uint8_t* q8, int32_t* q_exp, uint8_t* k8, int32_t* k_exp,
+                                  hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (!q8 && !k8) return MSA_ERR_NULL;
+  if (q8 && d.rows > 0 && (!q_idx || !q_exp)) return MSA_ERR_NULL;
+  if (k8 && d.B > 0 && d.N > 0 && (!k_idx || !k_exp)) return MSA_ERR_NULL;
+  if ((q8 && !aligned16(q8)) || (k8 && !aligned16(k8))) return MSA_ERR_SHAPE;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  prof_before(MSA_K_QUANTIZE_FP8, stream);
+  const hipError_t e = launch_quantize_fp8(d, q_idx, k_idx, q8, q_exp, k8, k_exp, stream);
+  prof_after(MSA_K_QUANTIZE_FP8, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_select_fp8(const msa_shape* shape, const uint8_t* q8, const int32_t* q_exp,
+                          const uint8_t* k8, const int32_t* k_exp, int32_t* block_ids,
+                          float* block_scores, float* cutoff_margin, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.rows == 0) return MSA_OK;
+  if (!q8 || !q_exp || !k8 || !k_exp || !block_ids) return MSA_ERR_NULL;
+  if (!aligned16(q8) || !aligned16(k8)) return MSA_ERR_SHAPE;
+  float* M = block_scores;
+  if (!M) {
+    const Layout L = layout(d, MSA_OP_SELECT);
+    if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+    M = static_cast<float*>(workspace);
+  }
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  prof_before(MSA_K_INDEX_FP8, stream);
+  hipError_t e = launch_index_blockmax_fp8(d, q8, q_exp, k8, k_exp, M, stream);
+  prof_after(MSA_K_INDEX_FP8, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  prof_before(MSA_K_TOPK, stream);
+  e = launch_topk(d, M, block_ids, cutoff_margin, stream);
+  prof_after(MSA_K_TOPK, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
 msa_status msa_prof_begin(int kernel, int max_launches) {
   if (kernel < 0 || kernel >= MSA_K_COUNT || max_launches < 1 || max_launches > 100000)
     return MSA_ERR_SHAPE;

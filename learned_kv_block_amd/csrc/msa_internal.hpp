@@ -209,4 +209,11 @@ hipError_t launch_recall(const Dims& d, const float* mass, const int32_t* ids, f
                          float* srec, hipStream_t s);
 hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t s);
 
+// FP8 (E4M3) index branch
+hipError_t launch_quantize_fp8(const Dims& d, const void* q_idx, const void* k_idx, uint8_t* q8,
+                               int32_t* q_exp, uint8_t* k8, int32_t* k_exp, hipStream_t s);
+hipError_t launch_index_blockmax_fp8(const Dims& d, const uint8_t* q8, const int32_t* q_exp,
+                                     const uint8_t* k8, const int32_t* k_exp, float* M,
+                                     hipStream_t s);
+
 }  // namespace msa

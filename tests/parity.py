@@ -98,8 +98,9 @@ def check_close(name, got, ref, t, report):
         assert rl <= t["rel_l2"], f"{name}: rel-L2 {rl:.3g} > {t['rel_l2']}"
 
 
-def check_ids(cfg, gids, ref, report):
-    """gids, ref['ids'] [n, Hkv, k]; ref has block_scores and margin (fp64)."""
+def check_ids(cfg, gids, ref, report, near_tie=NEAR_TIE):
+    """gids, ref['ids'] [n, Hkv, k]; ref has block_scores and margin (fp64). Rows whose
+    oracle margin is below near_tie may differ if the GPU's choice is still valid."""
     n, H, k = gids.shape
     near = 0
     for a in range(n):
@@ -109,7 +110,7 @@ def check_ids(cfg, gids, ref, report):
             if np.array_equal(g, o):
                 continue
             mg = ref["margin"][a, r]
-            assert mg < NEAR_TIE, f"row {a} group {r}: ids {g.tolist()} != oracle {o.tolist()} " \
+            assert mg < near_tie, f"row {a} group {r}: ids {g.tolist()} != oracle {o.tolist()} " \
                                   f"(margin {mg:.3g})"
             near += 1
             # still a valid selection: same local block and size, ascending, distinct,
@@ -121,7 +122,7 @@ def check_ids(cfg, gids, ref, report):
             assert np.all(np.diff(gv) > 0)
             cutoff = min(sc[b] for b in ov[:-1])
             for b in gv[:-1]:
-                assert sc[b] >= cutoff - NEAR_TIE, (a, r, b, sc[b], cutoff)
+                assert sc[b] >= cutoff - near_tie, (a, r, b, sc[b], cutoff)
     report["near_tie_rows"] = near
     report["rows_checked"] = n * H
     return near

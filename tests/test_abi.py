@@ -15,7 +15,7 @@ FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails before 
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "msa.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -125,3 +125,20 @@ def test_dense_calls_validate_on_host():
                               None) == msa.MSA_ERR_NULL
     assert L.msa_block_recall(ctypes.byref(shape(topk=40)), FAKE, FAKE, FAKE, FAKE, None,
                               None) == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_fp8_calls_validate_on_host():
+    L = msa.lib()
+    sh = shape()
+    assert L.msa_index_quantize_fp8(ctypes.byref(sh), FAKE, FAKE, None, None, None, None,
+                                    None) == msa.MSA_ERR_NULL
+    assert L.msa_index_quantize_fp8(ctypes.byref(sh), None, FAKE, FAKE, FAKE, None, None,
+                                    None) == msa.MSA_ERR_NULL
+    assert L.msa_index_quantize_fp8(ctypes.byref(sh), FAKE, FAKE, ctypes.c_void_p(0x100004),
+                                    FAKE, None, None, None) == msa.MSA_ERR_SHAPE
+    assert L.msa_select_fp8(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0,
+                            None) == msa.MSA_ERR_NULL
+    assert L.msa_select_fp8(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 0,
+                            None) == msa.MSA_ERR_WORKSPACE
+    assert L.msa_select_fp8(ctypes.byref(shape(topk=33)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                            None, None, 0, None) == msa.MSA_ERR_UNSUPPORTED
