@@ -145,7 +145,7 @@ quantize_blocks_kernel(const T* __restrict__ x, uint8_t* __restrict__ k8,
 // so a lane holds 16 keys of one row; the block max is in-lane plus one
 // lane-half exchange. Maxima are collected in LDS and scaled on the way out.
 template <int DI, int HKV, int NW, int CB>
-__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 8)
+__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 8 / NW)
 index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restrict__ q_exp,
                           const uint8_t* __restrict__ k8, const int32_t* __restrict__ k_exp,
                           float* __restrict__ M, int N, int Nq, int q_start, int nb,
@@ -348,7 +348,13 @@ hipError_t launch_quantize_fp8(const Dims& d, const void* q_idx, const void* k_i
   return hipErrorInvalidValue;
 }
 
-constexpr int kFp8Cb = 32;
+#ifndef MSA_FP8_CB
+#define MSA_FP8_CB 32
+#endif
+#ifndef MSA_FP8_NW
+#define MSA_FP8_NW 4
+#endif
+constexpr int kFp8Cb = MSA_FP8_CB;
 
 template <int DI, int HKV, int NW>
 static hipError_t fp8_index_launch(const Dims& d, const uint8_t* q8, const int32_t* qe,
@@ -367,7 +373,7 @@ static hipError_t fp8_index_nw(const Dims& d, const uint8_t* q8, const int32_t* 
                                const uint8_t* k8, const int32_t* ke, float* M, hipStream_t s) {
   // one-wave tiles when a sequence has at most 64 GEMM rows (decode)
   if ((int64_t)d.Nq * HKV <= 64) return fp8_index_launch<DI, HKV, 1>(d, q8, qe, k8, ke, M, s);
-  return fp8_index_launch<DI, HKV, 8>(d, q8, qe, k8, ke, M, s);
+  return fp8_index_launch<DI, HKV, MSA_FP8_NW>(d, q8, qe, k8, ke, M, s);
 }
 
 template <int DI>
