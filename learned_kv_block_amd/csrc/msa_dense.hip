@@ -24,28 +24,30 @@
 
 namespace msa {
 
-// Task order of the query-outer kernels: task = (pair, tile) with pair = (b, y),
-// y the KV group (or 0 for the index branch). Pairs are outermost so that the
-// tiles one XCD runs at a time stream the same keys through its L2. Inside a
-// pair the tiles alternate between the long end (late queries, many blocks)
-// and the short end, so any contiguous share of the tasks carries about the
-// same work. Workgroup g runs on XCD g % 8 and takes task (g % 8) * per + g / 8.
+// Task order of the query-outer kernels: task = (tile rank u, pair) with the
+// pairs (b, y) innermost — y the KV group, or 0 for the index branch — and the
+// tiles from the longest (latest queries, most key blocks) to the shortest.
+// The hardware hands workgroups to the 8 XCDs round robin, so when the number
+// of pairs divides 8 (or 8 divides it) each XCD keeps the same pairs, and the
+// workgroups resident on an XCD at one time are tiles of nearly the same
+// length that started together: they stream the same key head in lockstep and
+// share its blocks in L2 (a balanced zig-zag order with contiguous per-XCD
+// ranges measured 27% slower for the same work). Longest first also leaves
+// the short tiles to fill the end of the launch.
 struct Task {
   int b, y, tile;
 };
 __device__ __forceinline__ bool task_of(int ntasks, int ntiles, int ngroups, Task* t) {
   const int g = blockIdx.x;
-  const int per = (ntasks + 7) / 8;
-  const int kk = g >> 3;
-  const int task = (g & 7) * per + kk;
-  if (kk >= per || task >= ntasks) return false;
-  const int pair = task / ntiles, u = task - pair * ntiles;
-  t->tile = (u & 1) ? (u >> 1) : ntiles - 1 - (u >> 1);
+  if (g >= ntasks) return false;
+  const int npairs = ntasks / ntiles;
+  const int u = g / npairs, pair = g - u * npairs;
+  t->tile = ntiles - 1 - u;
   t->b = pair / ngroups;
   t->y = pair - t->b * ngroups;
   return true;
 }
-static unsigned task_grid(int ntasks) { return (unsigned)(((ntasks + 7) / 8) * 8); }
+static unsigned task_grid(int ntasks) { return (unsigned)ntasks; }
 
 // One 128-key tile of a key head ([128][DK], row j0 + r at base + (j0 + r) * stride)
 // moved global -> registers -> swizzled LDS by the NT threads of a workgroup.
