@@ -377,6 +377,205 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   }
 }
 
+// KL pass for G >= 8, with the index logits formed once per workgroup. The
+// workgroup's QT <= 32 queries fit one 32-column MFMA tile, so waves 0-3 form
+// z = S_idx of one 32-key tile each (K_idx tile x Q_idx^T) into a
+// double-buffered LDS table, a block ahead: K_idx is staged one block ahead
+// of K, and the table for block kb+1 is written while block kb is consumed.
+// The registers this frees let each wave issue the MFMAs of key tile kt+1
+// before the exponentials of tile kt. Same arithmetic as kl_dense_kernel.
+template <typename T, int D, int DI, int G, int NW>
+__global__ void __launch_bounds__(64 * NW)
+kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx,
+                   const T* __restrict__ k_idx, const float* __restrict__ lse_main,
+                   const float* __restrict__ lse_idx, float* __restrict__ kl_rows,
+                   float* __restrict__ mass, int N, int Nq, int q_start, int Hkv, int nb,
+                   int ntiles, int ntasks, float sc2, float zc2) {
+  constexpr int NT = 64 * NW, RT = 32 * NW, QT = RT / G, KS = D / 16, KSI = DI / 16;
+  static_assert(G >= 8 && QT <= 32 && NW >= 4, "one table tile, four table waves");
+  constexpr int RPQ = G / 2;    // rows of one query per lane
+  constexpr int NLQ = 16 / RPQ; // queries per lane before the split
+  constexpr int OWN = NLQ / 2;  // queries per lane after it
+  constexpr int QPW = 32 / G;   // queries per wave
+  constexpr int ZST = 128 + 4;  // table row stride (floats)
+  using SK = KeyStage<T, D, NT>;
+  using SI = KeyStage<T, DI, NT>;
+  __shared__ i32x4 kbuf[2][128 * SK::CPR];
+  __shared__ i32x4 ibuf[2][128 * SI::CPR];
+  __shared__ float zs[2][QT * ZST];
+
+  Task tk;
+  if (!task_of(ntasks, ntiles, Hkv, &tk)) return;
+  const int b = tk.b, r = tk.y, t0 = tk.tile * QT;
+  const int t_last = min(Nq, t0 + QT) - 1;
+  const int kb_last = (q_start + t_last) >> 7;
+  const int kb_mask = min((q_start + t0 + 1) >> 7, kb_last + 1);
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Hq = Hkv * G;
+  const size_t kstride = (size_t)Hkv * D;
+  const T* kbase = k + (size_t)b * N * kstride + (size_t)r * D;
+  const T* ibase = k_idx + (size_t)b * N * DI;
+
+  SK sk;
+  SI si;
+  sk.load(kbase, kstride, 0, N, tid);
+  si.load(ibase, DI, 0, N, tid);
+  // A fragments of S = Q K^T: MFMA row l32 = wave row 32w + l32 = (query, head)
+  vec8<T> qf[KS];
+  {
+    const int rho = 32 * wave + l32;
+    const int tc = min(t0 + rho / G, Nq - 1);
+    const T* qp = q + (((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G) * D + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld8<T>(qp + 16 * ks);
+  }
+  // B fragments of the table (waves 0-3): column l32 = query t0 + l32; columns
+  // past the tile's queries repeat a valid row and are never stored
+  vec8<T> qit[KSI];
+  if (wave < 4) {
+    const int tc = min(t0 + min(l32, QT - 1), Nq - 1);
+    const T* qip = q_idx + (((size_t)b * Nq + tc) * Hkv + r) * DI + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qit[ks] = ld8<T>(qip + 16 * ks);
+  }
+  float lm2[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int rho = 32 * wave + drow(e, h);
+    const int tc = min(t0 + rho / G, Nq - 1);
+    lm2[e] = lse_main[((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G] * kLog2e;
+  }
+  int i_q[OWN], zrow[OWN];
+  float li2[OWN];
+  size_t grow[OWN];
+  bool qv[OWN];
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) {
+    const int wq = wave * QPW + 2 * m + h;  // query within the workgroup
+    const int tq = t0 + wq;
+    const int tc = min(tq, Nq - 1);
+    zrow[m] = wq * ZST;
+    qv[m] = tq < Nq;
+    i_q[m] = q_start + tc;
+    grow[m] = ((size_t)b * Nq + tc) * Hkv + r;
+    li2[m] = lse_idx[grow[m]] * kLog2e;
+  }
+
+  auto ztile = [&](int buf, const i32x4* itile) {
+    vec8<T> af[KSI];
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks)
+      af[ks] = lds_frag<T, SI::CPR>(itile, 32 * wave + l32, (16 * ks + 8 * h) / SI::EPC);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) mma(acc, af[ks], qit[ks]);
+    if (l32 < QT) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) zs[buf][l32 * ZST + 32 * wave + drow(e, h)] = acc[e] * zc2;
+    }
+  };
+
+  sk.store(kbuf[0], tid);
+  si.store(ibuf[0], tid);
+  if (kb_last >= 1) {
+    sk.load(kbase, kstride, 128, N, tid);
+    si.load(ibase, DI, 128, N, tid);
+  }
+  __syncthreads();
+  if (wave < 4) ztile(0, ibuf[0]);
+  if (kb_last >= 1) {
+    si.store(ibuf[1], tid);
+    if (kb_last >= 2) si.load(ibase, DI, 256, N, tid);
+  }
+  __syncthreads();  // table of block 0 and K_idx of block 1 in LDS
+
+  const float inv_g = 1.0f / (float)G;
+  float klacc[OWN], macc[OWN];
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) klacc[m] = macc[m] = 0.0f;
+
+  auto smma = [&](f32x16& s, const i32x4* ktile, int kt) {
+    vec8<T> bf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      bf[ks] = lds_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) mma(s, qf[ks], bf[ks]);
+  };
+  auto vtile = [&](auto masked, const f32x16& s, const float* zt, int kb, int kt) {
+    float part[NLQ];
+#pragma unroll
+    for (int lq = 0; lq < NLQ; ++lq) {
+      float p = 0.0f;
+#pragma unroll
+      for (int e = lq * RPQ; e < (lq + 1) * RPQ; ++e)
+        p += __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], sc2, -lm2[e]));
+      part[lq] = p;
+    }
+    const int kk = 32 * kt + l32;
+#pragma unroll
+    for (int m = 0; m < OWN; ++m) {
+      const float send = h ? part[2 * m] : part[2 * m + 1];
+      const float recv = shfl_xor_f(send, 32);
+      float P = ((h ? part[2 * m + 1] : part[2 * m]) + recv) * inv_g;
+      if constexpr (decltype(masked)::value) P = kb * 128 + kk > i_q[m] ? 0.0f : P;
+      const float lpi2 = zt[zrow[m] + kk] - li2[m];  // log2 P_idx
+      klacc[m] += P >= 1.17549435e-38f ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
+      macc[m] += P;
+    }
+  };
+  auto block = [&](auto masked, int kb) {
+    const int cur = kb & 1;
+    if (kb + 1 <= kb_last) {
+      sk.store(kbuf[cur ^ 1], tid);
+      if (kb + 2 <= kb_last) sk.load(kbase, kstride, (kb + 2) * 128, N, tid);
+      if (wave < 4) ztile(cur ^ 1, ibuf[cur ^ 1]);
+      if (kb + 2 <= kb_last) {
+        si.store(ibuf[cur], tid);  // block kb's K_idx was last read for its table
+        if (kb + 3 <= kb_last) si.load(ibase, DI, (kb + 3) * 128, N, tid);
+      }
+    }
+    const i32x4* kt_lds = kbuf[cur];
+    const float* zt = zs[cur];
+    f32x16 sa, sb;
+    smma(sa, kt_lds, 0);
+    smma(sb, kt_lds, 1);
+    vtile(masked, sa, zt, kb, 0);
+    smma(sa, kt_lds, 2);
+    vtile(masked, sb, zt, kb, 1);
+    smma(sb, kt_lds, 3);
+    vtile(masked, sa, zt, kb, 2);
+    vtile(masked, sb, zt, kb, 3);
+    if (mass) {
+#pragma unroll
+      for (int m = 0; m < OWN; ++m) {
+        float v = macc[m];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+        if (l32 == 0 && qv[m] && kb <= (i_q[m] >> 7)) mass[grow[m] * nb + kb] = v;
+        macc[m] = 0.0f;
+      }
+    }
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb < kb_mask; ++kb) block(std::false_type(), kb);
+  for (; kb <= kb_last; ++kb) block(std::true_type(), kb);
+
+#pragma unroll
+  for (int m = 0; m < OWN; ++m) {
+    float v = klacc[m] * kLn2;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
+    if (l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
+  }
+}
+
 // ============================================================== recall
 //
 // One wavefront per (b, t, r) row. T = the teacher's top min(k, L+1) blocks
@@ -498,9 +697,15 @@ static hipError_t kl_dense_run(const Dims& d, const void* q, const void* k, cons
   if (ntasks == 0) return hipSuccess;
   const float sc2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   const float zc2 = (float)(1.0 / std::sqrt((double)DI) * 1.4426950408889634);
-  kl_dense_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
-      (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass, d.N,
-      d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+  if constexpr (G >= 8 && sizeof(T) == 2) {  // fp32 tiles would not fit LDS with the table
+    kl_dense_zt_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
+        (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass,
+        d.N, d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+  } else {
+    kl_dense_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
+        (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass,
+        d.N, d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+  }
   return hipGetLastError();
 }
 
