@@ -86,7 +86,10 @@ typedef struct {
   int32_t dtype;        /* msa_dtype of every floating-point input and of `out` */
 } msa_shape;
 
-enum { MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_ATTN_BWD = 3, MSA_OP_IDX_BWD = 4 };
+enum {
+  MSA_OP_SELECT = 0, MSA_OP_ATTN = 1, MSA_OP_KL = 2, MSA_OP_ATTN_BWD = 3, MSA_OP_IDX_BWD = 4,
+  MSA_OP_KL_DENSE_BWD = 5
+};
 
 /*
  * Bytes of workspace the call `op` (MSA_OP_*) needs for `shape`; 0 for an
@@ -263,6 +266,35 @@ msa_status msa_kl_dense(const msa_shape* shape, const void* q, const void* k, co
                         float* kl_mean, float* block_mass, hipStream_t stream);
 
 /*
+ * msa_kl_dense_bwd — msa_kl_dense together with its gradient into the index
+ * projections (KL alignment note §3: the index logits receive P_idx - P; §6:
+ * the gradient is formed from the logits and the two LSEs, with no separate
+ * KL forward; MSA vs DSA indexer note §2.1: one k_idx head shared by every
+ * group). With dS = P_idx - P on every j <= i:
+ *   dq_idx[i, r] = coef / sqrt(idx_dim) * sum_j dS[i, r, j] k_idx[j]
+ *   dk_idx[j]    = coef / sqrt(idx_dim) * sum over (i, r), i >= j, of dS[i, r, j] q_idx[i, r]
+ *
+ *  in   q, k, q_idx, k_idx, lse_main  as for msa_kl_dense
+ *  in   coef                loss coefficient (e.g. lambda / (B * N * Hkv) for the mean KL)
+ *  out  lse_idx             device fp32 [batch, seqlen_q, num_kv_heads]
+ *  out  kl_rows, kl_mean, block_mass (opt)  as for msa_kl_dense
+ *  out  dq_idx              device [batch, seqlen_q, num_kv_heads, idx_dim], dtype
+ *  out  dk_idx              device [batch, seqlen_kv, idx_dim], dtype: the
+ *                           contributions of this call's query rows (overwritten)
+ *  ws   workspace of msa_workspace_size(shape, MSA_OP_KL_DENSE_BWD) bytes: dS of
+ *       a chunk of query rows in bf16 (at most ~2 GiB; the call loops over
+ *       chunks) and an fp32 dk_idx accumulator
+ * dS is rounded to bf16 and the two products run on bf16 matrix cores with
+ * fp32 accumulation (fp32 inputs are rounded to bf16 for them). fp32 inputs
+ * need head_dim 64.
+ */
+msa_status msa_kl_dense_bwd(const msa_shape* shape, const void* q, const void* k,
+                            const void* q_idx, const void* k_idx, const float* lse_main,
+                            float coef, float* lse_idx, float* kl_rows, float* kl_mean,
+                            float* block_mass, void* dq_idx, void* dk_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/*
  * msa_block_recall — block recall and score recall of a selection against the
  * full-history teacher (KL alignment note §8; selector supervision page
  * "4.1.1 · 监督与联合训练", eq. 2 set recall and eq. 3 coverage).
@@ -338,7 +370,7 @@ enum {
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
   MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_DENSE_LSE = 14, MSA_K_KL_DENSE = 15,
   MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_INDEX_FP8 = 18, MSA_K_QUANTIZE_FP8 = 19,
-  MSA_K_COUNT = 20
+  MSA_K_KL_DENSE_CHAIN = 20, MSA_K_COUNT = 21
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* total_ms, int* launches);

@@ -18,6 +18,8 @@ Functions (same names as the C entry points):
   msa_dense_lse(q, k, q_start=0, ...)                -> lse_main over the full causal context
   msa_kl_dense(q, k, q_idx, k_idx, lse_main, q_start=0, ...)
                                                      -> kl_rows, kl_mean, lse_idx, block_mass
+  msa_kl_dense_bwd(q, k, q_idx, k_idx, lse_main, coef, q_start=0, ...)
+                                                     -> the same + dq_idx, dk_idx
   msa_block_recall(block_mass, block_ids, q_start=0, ...)
                                                      -> block_recall, score_recall, means
   msa_index_quantize_fp8(q_idx, k_idx, ...)          -> q8, q_exp, k8, k_exp (OCP E4M3)
@@ -37,11 +39,12 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
 MSA_F32, MSA_BF16 = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2, 3, 4
+MSA_OP_KL_DENSE_BWD = 5
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8"]
+           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8", "kl_dense_chain"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
-           "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
+           "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
            "msa_index_quantize_fp8", "msa_select_fp8",
            "msa_status_string", "msa_prof_begin", "msa_prof_end"]
 
@@ -80,10 +83,12 @@ def lib() -> ctypes.CDLL:
         L.msa_dense_lse.argtypes = [S, P, P, P, P]
         L.msa_kl_dense.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
         L.msa_block_recall.argtypes = [S, P, P, P, P, P, P]
+        L.msa_kl_dense_bwd.argtypes = [S, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P,
+                                       ctypes.c_size_t, P]
         L.msa_index_quantize_fp8.argtypes = [S, P, P, P, P, P, P, P]
         L.msa_select_fp8.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
-                  "msa_dense_lse", "msa_kl_dense", "msa_block_recall",
+                  "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
                   "msa_index_quantize_fp8", "msa_select_fp8",
                   "msa_prof_begin", "msa_prof_end"):
             getattr(L, f).restype = ctypes.c_int
@@ -315,6 +320,39 @@ def msa_kl_dense(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: t
     out = {"kl_rows": kl_rows, "kl_mean": kl_mean, "lse_idx": lse_idx}
     if want_mass:
         out["block_mass"] = mass
+    return out
+
+
+def msa_kl_dense_bwd(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                     lse_main: torch.Tensor, coef: float = 1.0, q_start: int = 0,
+                     want_kl: bool = True, want_mass: bool = False,
+                     workspace: Optional[torch.Tensor] = None):
+    """The full-context KL with its gradient into the index projections: dict(dq_idx like
+    q_idx, dk_idx like k_idx, lse_idx, and kl_rows / kl_mean / block_mass when asked)."""
+    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx")):
+        _check(t, n, 4)
+    _check(k_idx, "k_idx", 3)
+    _check(lse_main, "lse_main", 3)
+    B, Nq, Hq, D = q.shape
+    N, Hkv = k.shape[1], k.shape[2]
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], 1, _dtype_code(q))
+    dev = q.device
+    nb = (N + 127) // 128
+    out = {"lse_idx": torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev),
+           "dq_idx": torch.empty_like(q_idx), "dk_idx": torch.empty_like(k_idx)}
+    if want_kl:
+        out["kl_rows"] = torch.empty((B, Nq, Hkv), dtype=torch.float32, device=dev)
+        out["kl_mean"] = torch.empty((1,), dtype=torch.float32, device=dev)
+    if want_mass:
+        out["block_mass"] = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev)
+    ws, nws = _workspace(sh, MSA_OP_KL_DENSE_BWD, dev, workspace)
+    st = lib().msa_kl_dense_bwd(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
+                                _ptr(lse_main), float(coef), _ptr(out["lse_idx"]),
+                                _ptr(out.get("kl_rows")), _ptr(out.get("kl_mean")),
+                                _ptr(out.get("block_mass")), _ptr(out["dq_idx"]),
+                                _ptr(out["dk_idx"]), _ptr(ws), nws, _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_kl_dense_bwd")
     return out
 
 

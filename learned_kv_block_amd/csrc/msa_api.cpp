@@ -9,6 +9,7 @@
 #include <mutex>
 #include <vector>
 
+#include "msa_dense.hpp"
 #include "msa_internal.hpp"
 
 using namespace msa;
@@ -103,6 +104,7 @@ struct Layout {
   size_t drow, dqpart, dk_acc, dv_acc;                               // attention backward
   size_t dqi_part, dki_acc;                                          // index chain
   size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
+  size_t dense_ds;                                                   // full-context KL gradient
   size_t total;
 };
 
@@ -117,6 +119,12 @@ Layout layout(const Dims& d, int op) {
   };
   if (op == MSA_OP_SELECT) {
     L.total = (size_t)d.rows * d.Hkv * d.nb * sizeof(float);
+    return L;
+  }
+  if (op == MSA_OP_KL_DENSE_BWD) {
+    L.dense_ds = take((size_t)dense_grad_ds_elems(d) * 2);
+    L.dki_acc = take((size_t)d.B * d.N * d.DI * 4);
+    L.total = o;
     return L;
   }
   L.counts = take(d.buckets * 4);
@@ -242,7 +250,7 @@ size_t msa_workspace_size(const msa_shape* shape, int op) {
   Dims d;
   if (make_dims(shape, &d) != MSA_OK) return 0;
   if (op != MSA_OP_SELECT && op != MSA_OP_ATTN && op != MSA_OP_KL && op != MSA_OP_ATTN_BWD &&
-      op != MSA_OP_IDX_BWD)
+      op != MSA_OP_IDX_BWD && op != MSA_OP_KL_DENSE_BWD)
     return 0;
   return layout(for_op(d, op), op).total;
 }
@@ -461,6 +469,50 @@ msa_status msa_kl_dense(const msa_shape* shape, const void* q, const void* k, co
   prof_after(MSA_K_KL_DENSE, stream);
   if (e != hipSuccess) return MSA_ERR_DEVICE;
   e = launch_mean(kl_rows, d.rows * d.Hkv, kl_mean, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
+msa_status msa_kl_dense_bwd(const msa_shape* shape, const void* q, const void* k,
+                            const void* q_idx, const void* k_idx, const float* lse_main,
+                            float coef, float* lse_idx, float* kl_rows, float* kl_mean,
+                            float* block_mass, void* dq_idx, void* dk_idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.dtype == MSA_F32 && d.D != 64) return MSA_ERR_UNSUPPORTED;
+  if (kl_mean && !kl_rows) return MSA_ERR_NULL;
+  const size_t dk_bytes = (size_t)d.B * d.N * d.DI * elem_size(d);
+  if (d.rows == 0) {  // no rows: dk_idx gets no contributions, the mean is 0
+    if (dk_bytes > 0 && !dk_idx) return MSA_ERR_NULL;
+    if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+    if (dk_bytes > 0 &&
+        launch_fill_i32(static_cast<int32_t*>(dk_idx), (int64_t)(dk_bytes / 4), 0, stream) !=
+            hipSuccess)
+      return MSA_ERR_DEVICE;
+    if (kl_mean && launch_fill_f32(kl_mean, 1, 0.0f, stream) != hipSuccess) return MSA_ERR_DEVICE;
+    return MSA_OK;
+  }
+  if (!q || !k || !q_idx || !k_idx || !lse_main || !lse_idx || !dq_idx || !dk_idx)
+    return MSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_idx) || !aligned16(k_idx))
+    return MSA_ERR_SHAPE;
+  const Layout L = layout(d, MSA_OP_KL_DENSE_BWD);
+  if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  if (block_mass &&
+      launch_fill_f32(block_mass, d.rows * d.Hkv * d.nb, 0.0f, stream) != hipSuccess)
+    return MSA_ERR_DEVICE;
+  prof_before(MSA_K_DENSE_LSE_IDX, stream);
+  hipError_t e = launch_dense_lse(d, true, q_idx, k_idx, lse_idx, stream);
+  prof_after(MSA_K_DENSE_LSE_IDX, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  e = launch_kl_dense_grad(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, block_mass, coef,
+                           reinterpret_cast<bf16*>(ws + L.dense_ds),
+                           reinterpret_cast<float*>(ws + L.dki_acc), dq_idx, dk_idx, stream);
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  if (kl_mean) e = launch_mean(kl_rows, d.rows * d.Hkv, kl_mean, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 

@@ -20,7 +20,7 @@
 //   mean_kernel       fixed-order mean of a vector (one workgroup).
 #include <type_traits>
 
-#include "msa_internal.hpp"
+#include "msa_dense.hpp"
 
 namespace msa {
 
@@ -37,6 +37,10 @@ namespace msa {
 struct Task {
   int b, y, tile;
 };
+
+// row stride (elements) of the bf16 dS rows of the gradient chain: N rounded
+// up to 8, so that every row starts 16-byte aligned
+__host__ __device__ __forceinline__ int ds_stride(int N) { return (N + 7) & ~7; }
 __device__ __forceinline__ bool task_of(int ntasks, int ntiles, int ngroups, Task* t) {
   const int g = blockIdx.x;
   if (g >= ntasks) return false;
@@ -211,8 +215,9 @@ __global__ void __launch_bounds__(64 * NW)
 kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx,
                 const T* __restrict__ k_idx, const float* __restrict__ lse_main,
                 const float* __restrict__ lse_idx, float* __restrict__ kl_rows,
-                float* __restrict__ mass, int N, int Nq, int q_start, int Hkv, int nb, int ntiles,
-                int ntasks, float sc2, float zc2) {
+                float* __restrict__ mass, bf16* __restrict__ ds, int N, int Nq, int q_start,
+                int t_begin, int t_end, int Hkv, int nb, int ntiles, int ntasks, float sc2,
+                float zc2) {
   constexpr int NT = 64 * NW, RT = 32 * NW, QT = RT / G, KS = D / 16, KSI = DI / 16;
   constexpr bool PARTNER = G >= 8;
   constexpr int RPQ = PARTNER ? G / 2 : G;  // rows of one query per lane
@@ -226,8 +231,8 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
   Task tk;
   if (!task_of(ntasks, ntiles, Hkv, &tk)) return;
-  const int b = tk.b, r = tk.y, t0 = tk.tile * QT;
-  const int t_last = min(Nq, t0 + QT) - 1;
+  const int b = tk.b, r = tk.y, t0 = t_begin + tk.tile * QT;
+  const int t_last = min(t_end, t0 + QT) - 1;
   const int kb_last = (q_start + t_last) >> 7;
   const int kb_mask = min((q_start + t0 + 1) >> 7, kb_last + 1);
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -245,7 +250,7 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   vec8<T> qf[KS], qif[KSI];
   {
     const int rho = 32 * wave + l32;
-    const int tc = min(t0 + rho / G, Nq - 1);
+    const int tc = min(t0 + rho / G, t_end - 1);
     const T* qp = q + (((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G) * D + 8 * h;
     const T* qip = q_idx + (((size_t)b * Nq + tc) * Hkv + r) * DI + 8 * h;
 #pragma unroll
@@ -258,23 +263,24 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int rho = 32 * wave + drow(e, h);
-    const int tc = min(t0 + rho / G, Nq - 1);
+    const int tc = min(t0 + rho / G, t_end - 1);
     lm2[e] = lse_main[((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G] * kLog2e;
   }
   // the lane's own queries
   int i_q[OWN];
   float li2[OWN];
-  size_t grow[OWN];
+  size_t grow[OWN], dsr[OWN];
   bool qv[OWN];
 #pragma unroll
   for (int m = 0; m < OWN; ++m) {
     const int wq = PARTNER ? 2 * m + h : drow(m * RPQ, h) / G;  // query within the wave
     const int tq = t0 + wave * QPW + wq;
-    const int tc = min(tq, Nq - 1);
-    qv[m] = tq < Nq;
+    const int tc = min(tq, t_end - 1);
+    qv[m] = tq < t_end;
     i_q[m] = q_start + tc;
     grow[m] = ((size_t)b * Nq + tc) * Hkv + r;
     li2[m] = lse_idx[grow[m]] * kLog2e;
+    dsr[m] = (((size_t)b * (t_end - t_begin) + (tc - t_begin)) * Hkv + r) * (size_t)ds_stride(N);
   }
   sk.store(kbuf[0], tid);
   si.store(ibuf[0], tid);
@@ -333,11 +339,14 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         zz = z[m * RPQ];
       }
       P *= inv_g;
-      if constexpr (decltype(masked)::value) P = key > i_q[m] ? 0.0f : P;
+      const bool vis = !decltype(masked)::value || key <= i_q[m];
+      P = vis ? P : 0.0f;
       const float lpi2 = __builtin_fmaf(zz, zc2, -li2[m]);  // log2 P_idx
       // P below the smallest normal float adds nothing (and v_log_f32 may read it as 0)
       klacc[m] += P >= 1.17549435e-38f ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
       macc[m] += P;
+      if (ds && qv[m] && key < N)
+        ds[dsr[m] + key] = (bf16)(vis ? __builtin_amdgcn_exp2f(lpi2) - P : 0.0f);
     }
   };
   auto block = [&](auto masked, int kb) {
@@ -373,7 +382,7 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     float v = klacc[m] * kLn2;
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
-    if (l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
+    if (kl_rows && l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
   }
 }
 
@@ -389,8 +398,9 @@ __global__ void __launch_bounds__(64 * NW)
 kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ q_idx,
                    const T* __restrict__ k_idx, const float* __restrict__ lse_main,
                    const float* __restrict__ lse_idx, float* __restrict__ kl_rows,
-                   float* __restrict__ mass, int N, int Nq, int q_start, int Hkv, int nb,
-                   int ntiles, int ntasks, float sc2, float zc2) {
+                   float* __restrict__ mass, bf16* __restrict__ ds, int N, int Nq,
+                   int q_start, int t_begin, int t_end, int Hkv, int nb, int ntiles, int ntasks,
+                   float sc2, float zc2) {
   constexpr int NT = 64 * NW, RT = 32 * NW, QT = RT / G, KS = D / 16, KSI = DI / 16;
   static_assert(G >= 8 && QT <= 32 && NW >= 4, "one table tile, four table waves");
   constexpr int RPQ = G / 2;    // rows of one query per lane
@@ -406,8 +416,8 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 
   Task tk;
   if (!task_of(ntasks, ntiles, Hkv, &tk)) return;
-  const int b = tk.b, r = tk.y, t0 = tk.tile * QT;
-  const int t_last = min(Nq, t0 + QT) - 1;
+  const int b = tk.b, r = tk.y, t0 = t_begin + tk.tile * QT;
+  const int t_last = min(t_end, t0 + QT) - 1;
   const int kb_last = (q_start + t_last) >> 7;
   const int kb_mask = min((q_start + t0 + 1) >> 7, kb_last + 1);
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -425,7 +435,7 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   vec8<T> qf[KS];
   {
     const int rho = 32 * wave + l32;
-    const int tc = min(t0 + rho / G, Nq - 1);
+    const int tc = min(t0 + rho / G, t_end - 1);
     const T* qp = q + (((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G) * D + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = ld8<T>(qp + 16 * ks);
@@ -434,7 +444,7 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
   // past the tile's queries repeat a valid row and are never stored
   vec8<T> qit[KSI];
   if (wave < 4) {
-    const int tc = min(t0 + min(l32, QT - 1), Nq - 1);
+    const int tc = min(t0 + min(l32, QT - 1), t_end - 1);
     const T* qip = q_idx + (((size_t)b * Nq + tc) * Hkv + r) * DI + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KSI; ++ks) qit[ks] = ld8<T>(qip + 16 * ks);
@@ -443,23 +453,24 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int rho = 32 * wave + drow(e, h);
-    const int tc = min(t0 + rho / G, Nq - 1);
+    const int tc = min(t0 + rho / G, t_end - 1);
     lm2[e] = lse_main[((size_t)b * Nq + tc) * Hq + (size_t)r * G + rho % G] * kLog2e;
   }
   int i_q[OWN], zrow[OWN];
   float li2[OWN];
-  size_t grow[OWN];
+  size_t grow[OWN], dsr[OWN];
   bool qv[OWN];
 #pragma unroll
   for (int m = 0; m < OWN; ++m) {
     const int wq = wave * QPW + 2 * m + h;  // query within the workgroup
     const int tq = t0 + wq;
-    const int tc = min(tq, Nq - 1);
+    const int tc = min(tq, t_end - 1);
     zrow[m] = wq * ZST;
-    qv[m] = tq < Nq;
+    qv[m] = tq < t_end;
     i_q[m] = q_start + tc;
     grow[m] = ((size_t)b * Nq + tc) * Hkv + r;
     li2[m] = lse_idx[grow[m]] * kLog2e;
+    dsr[m] = (((size_t)b * (t_end - t_begin) + (tc - t_begin)) * Hkv + r) * (size_t)ds_stride(N);
   }
 
   auto ztile = [&](int buf, const i32x4* itile) {
@@ -523,10 +534,13 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
       const float send = h ? part[2 * m] : part[2 * m + 1];
       const float recv = shfl_xor_f(send, 32);
       float P = ((h ? part[2 * m + 1] : part[2 * m]) + recv) * inv_g;
-      if constexpr (decltype(masked)::value) P = kb * 128 + kk > i_q[m] ? 0.0f : P;
+      const bool vis = !decltype(masked)::value || kb * 128 + kk <= i_q[m];
+      P = vis ? P : 0.0f;
       const float lpi2 = zt[zrow[m] + kk] - li2[m];  // log2 P_idx
       klacc[m] += P >= 1.17549435e-38f ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
       macc[m] += P;
+      if (ds && qv[m] && kb * 128 + kk < N)
+        ds[dsr[m] + kb * 128 + kk] = (bf16)(vis ? __builtin_amdgcn_exp2f(lpi2) - P : 0.0f);
     }
   };
   auto block = [&](auto masked, int kb) {
@@ -572,7 +586,257 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     float v = klacc[m] * kLn2;
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) v += shfl_xor_f(v, o);
-    if (l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
+    if (kl_rows && l32 == 0 && qv[m]) kl_rows[grow[m]] = v;
+  }
+}
+
+// ============================================================== KL gradient chain
+//
+// KL note §3: the index logits receive P_idx - P; through z = q_idx . k_idx /
+// sqrt(d_idx) with one shared k_idx head (indexer note §2.1),
+//   dq_idx[i, r] = coef / sqrt(d_idx) * sum_{j <= i} dS[i, r, j] k_idx[j]
+//   dk_idx[j]    = coef / sqrt(d_idx) * sum over (i, r), i >= j, of dS[i, r, j] q_idx[i, r].
+// The KL pass writes dS in bf16 for a chunk of query rows ([B, chunk, Hkv, N]);
+// the two products below run on bf16 matrix cores with fp32 accumulation.
+// Operands with the reduction index along rows of a row-major tile come from
+// the transposing LDS read (16-lane groups receive element j of 4 consecutive
+// rows); the other operand takes the same k-set {16c+4h+0..3, 16c+8+4h+0..3}
+// from a contiguous row.
+
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+// X^T fragment (32 columns x 16 rows) of a row-major bf16 LDS tile with row
+// stride LD: columns 32*ct.., rows 16c..16c+15, k-set as above
+template <int LD>
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int c, int ct, int lane) {
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int krow = 16 * c + 4 * (g16 >> 1) + (s16 >> 2);
+  const int col = ct * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + krow * LD + col));
+  const short4v hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(tile + (krow + 8) * LD + col));
+  const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = l4[e];
+    a[4 + e] = h4[e];
+  }
+  return a;
+}
+
+template <typename T>
+__device__ __forceinline__ bf16x8 to_bf16x8(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return ld8<bf16>(reinterpret_cast<const bf16*>(p));
+  } else {
+    const f32x8 v = ld8<float>(p);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+    return o;
+  }
+}
+
+// dq_idx rows of a chunk. Workgroup = 128 consecutive chunk rows (t, r) of one
+// batch; wave w takes rows 32w..32w+31 as the columns of D^T = K_idx^T . dS^T,
+// K_idx blocks staged through LDS. Keys after a row's query are masked here
+// (select, so unwritten parts of the dS rows are never used).
+template <typename T, int DI>
+__global__ void __launch_bounds__(256)
+dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
+                    T* __restrict__ dq, int N, int Nq, int q_start, int t_begin, int t_end,
+                    int Hkv, int tiles_b, float scale) {
+  constexpr int LK = DI + 8;
+  constexpr int DT = DI / 32;
+  __shared__ __attribute__((aligned(16))) bf16 kt[128 * LK];
+  const int rows_b = (t_end - t_begin) * Hkv;
+  const int b = blockIdx.x / tiles_b, rho0 = (blockIdx.x % tiles_b) * 128;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6;
+  const int rho = rho0 + 32 * wave + l32;
+  const int rc = min(rho, rows_b - 1);
+  const int t = t_begin + rc / Hkv, r = rc % Hkv;
+  const int i = q_start + t;
+  const bf16* dsrow = ds + ((size_t)b * rows_b + rc) * ds_stride(N);
+  const int rlast = min(rho0 + 127, rows_b - 1);
+  const int kb_last = (q_start + t_begin + rlast / Hkv) >> 7;
+  const T* kbase = k_idx + (size_t)b * N * DI;
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+  }
+  // next block's K_idx chunks (global -> registers) and this lane's dS runs
+  constexpr int KCH = 128 * DI / 8 / 256;
+  bf16x8 kraw[KCH];
+  bf16x4 dlo[8], dhi[8];
+  auto run = [&](const bf16* p, int key0) {  // 4 keys key0..key0+3 of the row (raw)
+    bf16x4 v;
+    if (key0 + 3 < N) {
+      v = ld4<bf16>(p + key0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = key0 + e < N ? p[key0 + e] : (bf16)0.0f;
+    }
+    return v;
+  };
+  auto prefetch = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int x = tid + 256 * u, row = x / (DI / 8), c = x % (DI / 8);
+      const int j = kb * 128 + row;
+      if (j < N) {
+        kraw[u] = to_bf16x8<T>(kbase + (size_t)j * DI + 8 * c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kraw[u][e] = (bf16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      dlo[c] = run(dsrow, kb * 128 + 16 * c + 4 * h);
+      dhi[c] = run(dsrow, kb * 128 + 16 * c + 8 + 4 * h);
+    }
+  };
+  prefetch(0);
+  for (int kb = 0; kb <= kb_last; ++kb) {
+    __syncthreads();  // the previous block's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      const int x = tid + 256 * u, row = x / (DI / 8), c = x % (DI / 8);
+      *reinterpret_cast<bf16x8*>(kt + row * LK + 8 * c) = kraw[u];
+    }
+    bf16x8 bfr[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int key0 = kb * 128 + 16 * c + 4 * h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // keys after the row's query are masked (select)
+        bfr[c][e] = key0 + e <= i ? dlo[c][e] : (bf16)0.0f;
+        bfr[c][4 + e] = key0 + 8 + e <= i ? dhi[c][e] : (bf16)0.0f;
+      }
+    }
+    __syncthreads();
+    if (kb + 1 <= kb_last) prefetch(kb + 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_tr<LK>(kt, c, dt, lane), bfr[c]);
+    }
+  }
+  if (rho < rows_b) {
+    T* out = dq + (((size_t)b * Nq + t) * Hkv + r) * DI;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) out[32 * dt + drow(e, h)] = (T)(acc[dt][e] * scale);
+    }
+  }
+}
+
+// dk_idx of one 128-key block over the chunk's rows whose query sees the
+// block (i >= 128 blk). D^T = Q_idx^T . dS: both operands by the transposing
+// read of 64-row LDS tiles (q_idx rows; the same rows' dS on the block's keys).
+// Wave w produces key tile w. The chunks of a call add up in an fp32
+// accumulator (one workgroup per block, so no atomics); the last chunk writes
+// dk_idx. dS of rows whose query is before a key is 0 (written by the KL pass).
+template <typename T, int DI>
+__global__ void __launch_bounds__(256)
+dense_dk_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ q_idx,
+                    float* __restrict__ dk_acc, T* __restrict__ dk, int N, int Nq, int q_start,
+                    int t_begin, int t_end, int Hkv, int nb, float scale, int first, int last) {
+  constexpr int RT = 64, LQ = DI + 8, LS = 128 + 8;
+  constexpr int DT = DI / 32;
+  __shared__ __attribute__((aligned(16))) bf16 qs[RT * LQ];
+  __shared__ __attribute__((aligned(16))) bf16 dss[RT * LS];
+  const int blk = blockIdx.x % nb, b = blockIdx.x / nb;
+  const int rows_b = (t_end - t_begin) * Hkv;
+  const int t_first = max(t_begin, 128 * blk - q_start);
+  const int rho_first = (t_first - t_begin) * Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = tid >> 6;
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
+  }
+  // next row tile (global -> registers): q_idx rows and the rows' dS on the block
+  constexpr int QCH = RT * DI / 8 / 256, SCH = RT * 16 / 256;
+  bf16x8 qraw[QCH], sraw[SCH];
+  auto prefetch = [&](int rho0) {
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) {
+      const int x = tid + 256 * u, rr = x / (DI / 8), c = x % (DI / 8), rho = rho0 + rr;
+      if (rho < rows_b) {
+        const size_t row = ((size_t)b * Nq + t_begin + rho / Hkv) * Hkv + rho % Hkv;
+        qraw[u] = to_bf16x8<T>(q_idx + row * DI + 8 * c);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qraw[u][e] = (bf16)0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int x = tid + 256 * u, rr = x / 16, c = x % 16, rho = rho0 + rr;
+      const int key0 = blk * 128 + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sraw[u][e] = (bf16)0.0f;
+      if (rho < rows_b) {
+        const bf16* p = ds + ((size_t)b * rows_b + rho) * ds_stride(N);
+        if (key0 + 7 < N) {
+          sraw[u] = ld8<bf16>(p + key0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e < N) sraw[u][e] = p[key0 + e];
+        }
+      }
+    }
+  };
+  if (rho_first < rows_b) prefetch(rho_first);
+  for (int rho0 = rho_first; rho0 < rows_b; rho0 += RT) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < QCH; ++u) {
+      const int x = tid + 256 * u, rr = x / (DI / 8), c = x % (DI / 8);
+      *reinterpret_cast<bf16x8*>(qs + rr * LQ + 8 * c) = qraw[u];
+    }
+#pragma unroll
+    for (int u = 0; u < SCH; ++u) {
+      const int x = tid + 256 * u, rr = x / 16, c = x % 16;
+      *reinterpret_cast<bf16x8*>(dss + rr * LS + 8 * c) = sraw[u];
+    }
+    __syncthreads();
+    if (rho0 + RT < rows_b) prefetch(rho0 + RT);
+#pragma unroll
+    for (int c = 0; c < RT / 16; ++c) {
+      const bf16x8 bfr = frag_tr<LS>(dss, c, wave, lane);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_tr<LQ>(qs, c, dt, lane), bfr);
+    }
+  }
+  const int j = blk * 128 + 32 * wave + l32;
+  if (j < N) {
+    const size_t base = ((size_t)b * N + j) * DI;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const size_t x = base + 32 * dt + drow(e, h);
+        float v = acc[dt][e];
+        if (!first) v += dk_acc[x];
+        if (last) {
+          dk[x] = (T)(v * scale);
+        } else {
+          dk_acc[x] = v;
+        }
+      }
+    }
   }
 }
 
@@ -687,63 +951,131 @@ hipError_t launch_dense_lse(const Dims& d, bool index_branch, const void* q, con
   return lse_by_dim<float>(d, dim, R, q, k, lse, qrows, kstride, ngroups, s);
 }
 
+struct DenseKlArgs {
+  const void *q, *k, *qi, *ki;
+  const float *lse_main, *lse_idx;
+  float *kl_rows, *mass;
+  bf16* ds;
+  int t_begin, t_end;
+};
+
 template <typename T, int D, int DI, int G>
-static hipError_t kl_dense_run(const Dims& d, const void* q, const void* k, const void* qi,
-                               const void* ki, const float* lse_main, const float* lse_idx,
-                               float* kl_rows, float* mass, hipStream_t s) {
+static hipError_t kl_dense_run(const Dims& d, const DenseKlArgs& a, hipStream_t s) {
   constexpr int QT = 32 * kDenseWaves / G;
-  const int ntiles = (d.Nq + QT - 1) / QT;
+  const int ntiles = (a.t_end - a.t_begin + QT - 1) / QT;
   const int ntasks = ntiles * d.B * d.Hkv;
   if (ntasks == 0) return hipSuccess;
   const float sc2 = (float)(1.0 / std::sqrt((double)D) * 1.4426950408889634);
   const float zc2 = (float)(1.0 / std::sqrt((double)DI) * 1.4426950408889634);
   if constexpr (G >= 8 && sizeof(T) == 2) {  // fp32 tiles would not fit LDS with the table
     kl_dense_zt_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
-        (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass,
-        d.N, d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+        (const T*)a.q, (const T*)a.k, (const T*)a.qi, (const T*)a.ki, a.lse_main, a.lse_idx,
+        a.kl_rows, a.mass, a.ds, d.N, d.Nq, d.q_start, a.t_begin, a.t_end, d.Hkv, d.nb, ntiles,
+        ntasks, sc2, zc2);
   } else {
     kl_dense_kernel<T, D, DI, G, kDenseWaves><<<task_grid(ntasks), 64 * kDenseWaves, 0, s>>>(
-        (const T*)q, (const T*)k, (const T*)qi, (const T*)ki, lse_main, lse_idx, kl_rows, mass,
-        d.N, d.Nq, d.q_start, d.Hkv, d.nb, ntiles, ntasks, sc2, zc2);
+        (const T*)a.q, (const T*)a.k, (const T*)a.qi, (const T*)a.ki, a.lse_main, a.lse_idx,
+        a.kl_rows, a.mass, a.ds, d.N, d.Nq, d.q_start, a.t_begin, a.t_end, d.Hkv, d.nb, ntiles,
+        ntasks, sc2, zc2);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D, int DI>
-static hipError_t kl_dense_by_g(const Dims& d, const void* q, const void* k, const void* qi,
-                                const void* ki, const float* lm, const float* li, float* kl,
-                                float* mass, hipStream_t s) {
+static hipError_t kl_dense_by_g(const Dims& d, const DenseKlArgs& a, hipStream_t s) {
   switch (d.G) {
-    case 1: return kl_dense_run<T, D, DI, 1>(d, q, k, qi, ki, lm, li, kl, mass, s);
-    case 2: return kl_dense_run<T, D, DI, 2>(d, q, k, qi, ki, lm, li, kl, mass, s);
-    case 4: return kl_dense_run<T, D, DI, 4>(d, q, k, qi, ki, lm, li, kl, mass, s);
-    case 8: return kl_dense_run<T, D, DI, 8>(d, q, k, qi, ki, lm, li, kl, mass, s);
-    case 16: return kl_dense_run<T, D, DI, 16>(d, q, k, qi, ki, lm, li, kl, mass, s);
+    case 1: return kl_dense_run<T, D, DI, 1>(d, a, s);
+    case 2: return kl_dense_run<T, D, DI, 2>(d, a, s);
+    case 4: return kl_dense_run<T, D, DI, 4>(d, a, s);
+    case 8: return kl_dense_run<T, D, DI, 8>(d, a, s);
+    case 16: return kl_dense_run<T, D, DI, 16>(d, a, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
-static hipError_t kl_dense_by_di(const Dims& d, const void* q, const void* k, const void* qi,
-                                 const void* ki, const float* lm, const float* li, float* kl,
-                                 float* mass, hipStream_t s) {
-  if (d.DI == 64) return kl_dense_by_g<T, D, 64>(d, q, k, qi, ki, lm, li, kl, mass, s);
-  if (d.DI == 32) return kl_dense_by_g<T, D, 32>(d, q, k, qi, ki, lm, li, kl, mass, s);
+static hipError_t kl_dense_by_di(const Dims& d, const DenseKlArgs& a, hipStream_t s) {
+  if (d.DI == 64) return kl_dense_by_g<T, D, 64>(d, a, s);
+  if (d.DI == 32) return kl_dense_by_g<T, D, 32>(d, a, s);
+  return hipErrorInvalidValue;
+}
+
+static hipError_t kl_dense_dispatch(const Dims& d, const DenseKlArgs& a, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.D == 128) return kl_dense_by_di<bf16, 128>(d, a, s);
+    if (d.D == 64) return kl_dense_by_di<bf16, 64>(d, a, s);
+  } else if (d.D == 64) {
+    return kl_dense_by_di<float, 64>(d, a, s);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_kl_dense(const Dims& d, const void* q, const void* k, const void* q_idx,
                            const void* k_idx, const float* lse_main, const float* lse_idx,
                            float* kl_rows, float* mass, hipStream_t s) {
-  if (d.dtype == MSA_BF16) {
-    if (d.D == 128)
-      return kl_dense_by_di<bf16, 128>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
-    if (d.D == 64)
-      return kl_dense_by_di<bf16, 64>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
-  } else if (d.D == 64) {
-    return kl_dense_by_di<float, 64>(d, q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, s);
+  const DenseKlArgs a{q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, nullptr, 0, d.Nq};
+  return kl_dense_dispatch(d, a, s);
+}
+
+// Rows per chunk of the gradient chain: a multiple of 256 query positions
+// (every KL tile lies in one chunk) with at most ~2 GiB of bf16 dS per chunk.
+int dense_grad_chunk(const Dims& d) {
+  const int64_t per_t = (int64_t)d.B * d.Hkv * ds_stride(d.N) * 2;
+  int64_t ch = per_t > 0 ? ((int64_t)1 << 31) / per_t : d.Nq;
+  ch = ch / 256 * 256;
+  if (ch < 256) ch = 256;
+  const int64_t all = ((int64_t)d.Nq + 255) / 256 * 256;
+  return (int)(ch < all ? ch : all);
+}
+
+template <typename T, int DI>
+static hipError_t chain_run(const Dims& d, const bf16* ds, const void* qi, const void* ki,
+                            float* dk_acc, void* dq, void* dk, int t_begin, int t_end, float scale,
+                            bool first, bool last, hipStream_t s) {
+  const int rows_b = (t_end - t_begin) * d.Hkv;
+  const int tiles_b = (rows_b + 127) / 128;
+  if (tiles_b > 0) {
+    dense_dq_idx_kernel<T, DI><<<(unsigned)(tiles_b * d.B), 256, 0, s>>>(
+        ds, (const T*)ki, (T*)dq, d.N, d.Nq, d.q_start, t_begin, t_end, d.Hkv, tiles_b, scale);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipErrorInvalidValue;
+  dense_dk_idx_kernel<T, DI><<<(unsigned)(d.nb * d.B), 256, 0, s>>>(
+      ds, (const T*)qi, dk_acc, (T*)dk, d.N, d.Nq, d.q_start, t_begin, t_end, d.Hkv, d.nb, scale,
+      first ? 1 : 0, last ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl_dense_grad(const Dims& d, const void* q, const void* k, const void* q_idx,
+                                const void* k_idx, const float* lse_main, const float* lse_idx,
+                                float* kl_rows, float* mass, float coef, bf16* ds,
+                                float* dk_acc, void* dq_idx, void* dk_idx, hipStream_t s) {
+  const int chunk = dense_grad_chunk(d);
+  const float scale = (float)((double)coef / std::sqrt((double)d.DI));
+  for (int t0 = 0; t0 < d.Nq; t0 += chunk) {
+    const int t1 = t0 + chunk < d.Nq ? t0 + chunk : d.Nq;
+    const DenseKlArgs a{q, k, q_idx, k_idx, lse_main, lse_idx, kl_rows, mass, ds, t0, t1};
+    prof_before(MSA_K_KL_DENSE, s);
+    hipError_t e = kl_dense_dispatch(d, a, s);
+    prof_after(MSA_K_KL_DENSE, s);
+    if (e != hipSuccess) return e;
+    const bool first = t0 == 0, last = t1 == d.Nq;
+    prof_before(MSA_K_KL_DENSE_CHAIN, s);
+    if (d.dtype == MSA_BF16) {
+      e = d.DI == 64 ? chain_run<bf16, 64>(d, ds, q_idx, k_idx, dk_acc, dq_idx, dk_idx, t0, t1,
+                                           scale, first, last, s)
+                     : chain_run<bf16, 32>(d, ds, q_idx, k_idx, dk_acc, dq_idx, dk_idx, t0, t1,
+                                           scale, first, last, s);
+    } else {
+      e = d.DI == 64 ? chain_run<float, 64>(d, ds, q_idx, k_idx, dk_acc, dq_idx, dk_idx, t0, t1,
+                                            scale, first, last, s)
+                     : chain_run<float, 32>(d, ds, q_idx, k_idx, dk_acc, dq_idx, dk_idx, t0, t1,
+                                            scale, first, last, s);
+    }
+    prof_after(MSA_K_KL_DENSE_CHAIN, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_recall(const Dims& d, const float* mass, const int32_t* ids, float* brec,

@@ -142,3 +142,19 @@ def test_fp8_calls_validate_on_host():
                             None) == msa.MSA_ERR_WORKSPACE
     assert L.msa_select_fp8(ctypes.byref(shape(topk=33)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
                             None, None, 0, None) == msa.MSA_ERR_UNSUPPORTED
+
+
+def test_dense_bwd_validates_on_host():
+    L = msa.lib()
+    sh = shape()
+    need = msa.workspace_size(sh, msa.MSA_OP_KL_DENSE_BWD)
+    assert need >= 1024 * 4 * 1024 * 2  # one chunk of bf16 dS rows
+    args = [ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0), FAKE, FAKE, FAKE,
+            None, FAKE, FAKE]
+    assert L.msa_kl_dense_bwd(*args, None, 0, None) == msa.MSA_ERR_WORKSPACE
+    bad = list(args)
+    bad[11] = None  # dq_idx
+    assert L.msa_kl_dense_bwd(*bad, FAKE, need, None) == msa.MSA_ERR_NULL
+    bad = list(args)
+    bad[8] = None  # kl_rows NULL with kl_mean given
+    assert L.msa_kl_dense_bwd(*bad, FAKE, need, None) == msa.MSA_ERR_NULL

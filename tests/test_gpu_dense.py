@@ -172,3 +172,92 @@ def test_dense_full_size_sampled():
     rep.update(block_recall_mean=float(rec["means"][0]), score_recall_mean=float(rec["means"][1]),
                kl_mean=float(kl["kl_mean"][0]))
     print(f"[dense] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
+GRAD_CASES = [
+    si.CONFIGS["tiny_f32_n1024"],
+    _cfg("bf16_g16_ragged", seqlen_kv=1000, seqlen_q=1000, num_q_heads=64, num_kv_heads=4),
+    _cfg("bf16_g8_chunk_d64", batch=2, seqlen_kv=1500, seqlen_q=300, q_start=1200,
+         num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
+    _cfg("bf16_g2_hkv8", seqlen_kv=600, seqlen_q=600, num_q_heads=16, num_kv_heads=8, topk=2),
+    _cfg("bf16_decode_b3", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
+         num_kv_heads=4, topk=6),
+]
+COEF = 0.37
+
+
+def _grad_close(name, got, ref, rep):
+    """bf16 chain (dS and operands rounded to bf16, fp32 sums): rel-L2 <= 1e-2 and max-abs
+    <= 3e-2 of the largest reference magnitude."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), name
+    rl = parity.rel_l2(got, ref)
+    mr = float(np.max(np.abs(got - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
+    rep[name] = dict(rel_l2=rl, max_rel=mr)
+    assert rl <= 1e-2 and mr <= 3e-2, (name, rl, mr)
+
+
+@pytest.mark.parametrize("cfg", GRAD_CASES, ids=[c.name for c in GRAD_CASES])
+def test_dense_grad_every_row(cfg):
+    """msa_kl_dense_bwd: dq_idx, dk_idx against the oracle's chain of its own full-context
+    dlogits ("KL alignment" §3, §5); KL rows bit-identical to msa_kl_dense."""
+    import learned_kv_block_amd as msa
+    print(f"[dense-grad] start {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg)
+    lse = msa.msa_dense_lse(x["q"], x["k"], q_start=cfg.q_start, idx_dim=cfg.idx_dim)
+    fwd = msa.msa_kl_dense(x["q"], x["k"], x["q_idx"], x["k_idx"], lse, q_start=cfg.q_start)
+    g = msa.msa_kl_dense_bwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse, COEF,
+                             q_start=cfg.q_start, want_mass=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g["kl_rows"], fwd["kl_rows"])
+    assert torch.equal(g["block_mass"], fwd["block_mass"])
+    n = cfg.batch * cfg.seqlen_q
+    rows = np.arange(n, dtype=np.int64)
+    shp = oracle.dense_shape(oracle.shape_of(cfg))
+    dids = oracle.dense_ids(shp)
+    q = si.host_query_rows(cfg, "q", rows)
+    q_idx = si.host_query_rows(cfg, "q_idx", rows)
+    k, k_idx = si.host_tensor(cfg, "k"), si.host_tensor(cfg, "k_idx")
+    kref = oracle.kl(shp, q, k, q_idx, k_idx, dids, want_dlogits=True)
+    rq, rk = oracle.idx_bwd(shp, q_idx, k_idx, dids, kref["dlogits"], coef=COEF)
+    rep = {}
+    _grad_close("dq_idx", g["dq_idx"].float().cpu().numpy().reshape(rq.shape), rq, rep)
+    _grad_close("dk_idx", g["dk_idx"].float().cpu().numpy(), rk, rep)
+    print(f"[dense-grad] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
+def test_dense_grad_full_size():
+    """2 x 32768 (the gradient runs in 8 chunks of 4096 query rows): dq_idx on sampled rows
+    against the oracle; dk_idx through identities over every row: <dk_idx, k_idx> equals
+    <dq_idx, q_idx> (both are coef * sum dS * z), and the keys' dk_idx sum to 0 (every
+    row's dS sums to 0)."""
+    import learned_kv_block_amd as msa
+    cfg = si.CONFIGS["train_b2_n32768"]
+    print(f"[dense-grad] start {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg)
+    lse = msa.msa_dense_lse(x["q"], x["k"], q_start=cfg.q_start, idx_dim=cfg.idx_dim)
+    g = msa.msa_kl_dense_bwd(x["q"], x["k"], x["q_idx"], x["k_idx"], lse, COEF,
+                             q_start=cfg.q_start, want_kl=False)
+    torch.cuda.synchronize()
+    rep = {}
+    dq, dk = g["dq_idx"].double(), g["dk_idx"].double()
+    lhs = float((dk * x["k_idx"].double()).sum())
+    rhs = float((dq * x["q_idx"].double()).sum())
+    rep["dk_k_vs_dq_q_rel"] = abs(lhs - rhs) / max(abs(rhs), 1e-30)
+    ksum = dk.sum(dim=1)
+    rep["dk_key_sum_rel"] = float(ksum.norm() / dk.abs().sum(dim=1).norm())
+    assert rep["dk_k_vs_dq_q_rel"] <= 1e-2, rep
+    assert rep["dk_key_sum_rel"] <= 1e-2, rep
+    rows = parity.sample_rows(cfg, n_random=6, seed=11)
+    sub, lrows, h = parity.host_inputs_for_rows(cfg, rows)
+    shp = oracle.dense_shape(oracle.shape_of(sub))
+    dids = oracle.dense_ids(shp, rows=lrows)
+    kref = oracle.kl(shp, h["q"], h["k"], h["q_idx"], h["k_idx"], dids, rows=lrows,
+                     want_dlogits=True)
+    rq, _ = oracle.idx_bwd(shp, h["q_idx"], h["k_idx"], dids, kref["dlogits"], coef=COEF,
+                           rows=lrows)
+    ridx = torch.from_numpy(rows).to(lse.device)
+    got = g["dq_idx"].reshape(-1, cfg.num_kv_heads, cfg.idx_dim)[ridx].float().cpu().numpy()
+    _grad_close("dq_idx_sampled", got, rq, rep)
+    print(f"[dense-grad] {cfg.name}: " + json.dumps(rep), flush=True)
