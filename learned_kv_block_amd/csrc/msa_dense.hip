@@ -56,11 +56,15 @@ static unsigned task_grid(int ntasks) { return (unsigned)ntasks; }
 // One 128-key tile of a key head ([128][DK], row j0 + r at base + (j0 + r) * stride)
 // moved global -> registers -> swizzled LDS by the NT threads of a workgroup.
 // Rows at or past N repeat row N - 1; such keys are after every query and masked.
+// Chunk c of row r sits at c ^ (idx_swz(r) & (CPR - 1)): with 16 chunks per row
+// (a row is one 256-byte bank row), the 16 rows one LDS cycle serves land in 16
+// distinct 4-bank groups (a 3-bit swizzle would pair them: 2-way conflicts).
 template <typename T, int DK, int NT>
 struct KeyStage {
   static constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int CPR = DK / EPC;        // chunks per row
-  static constexpr int SWM = (CPR < 8 ? CPR : 8) - 1;
+  static constexpr int SWM = CPR - 1;
+  static_assert(CPR <= 16, "swizzle of up to 16 chunks");
   static constexpr int CH = 128 * CPR / NT;   // chunks per thread
   static_assert((128 * CPR) % NT == 0, "tile shape");
   i32x4 raw[CH];
@@ -80,6 +84,26 @@ struct KeyStage {
     }
   }
 };
+
+// MFMA fragment (8 elements) of row r of a
+// KeyStage tile: chunk c0 (and c0 + 1 for fp32) of the row
+template <typename T, int CPR>
+__device__ __forceinline__ vec8<T> key_frag(const i32x4* tile, int r, int c0) {
+  const i32x4* row = tile + r * CPR;
+  const int s = idx_swz(r) & (CPR - 1);
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(vec8<T>, row[c0 ^ s]);
+  } else {
+    const i32x4 lo = row[c0 ^ s], hi = row[(c0 + 1) ^ s];
+    f32x8 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = __int_as_float(lo[e]);
+      v[4 + e] = __int_as_float(hi[e]);
+    }
+    return v;
+  }
+}
 
 // ============================================================== causal LSE
 //
@@ -140,7 +164,7 @@ dense_lse_kernel(const T* __restrict__ q, const T* __restrict__ k, float* __rest
   auto key_tile = [&](auto masked, const i32x4* tile, int kb, int kt) {
     vec8<T> af[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(tile, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
+    for (int ks = 0; ks < KS; ++ks) af[ks] = key_frag<T, CPR>(tile, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
     f32x16 acc[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -303,7 +327,7 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       vec8<T> bf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        bf[ks] = lds_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
+        bf[ks] = key_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) mma(s, qf[ks], bf[ks]);
     }
@@ -311,7 +335,7 @@ kl_dense_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       vec8<T> bi[KSI];
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks)
-        bi[ks] = lds_frag<T, SI::CPR>(itile, 32 * kt + l32, (16 * ks + 8 * h) / SI::EPC);
+        bi[ks] = key_frag<T, SI::CPR>(itile, 32 * kt + l32, (16 * ks + 8 * h) / SI::EPC);
 #pragma unroll
       for (int ks = 0; ks < KSI; ++ks) mma(z, qif[ks], bi[ks]);
     }
@@ -477,7 +501,7 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     vec8<T> af[KSI];
 #pragma unroll
     for (int ks = 0; ks < KSI; ++ks)
-      af[ks] = lds_frag<T, SI::CPR>(itile, 32 * wave + l32, (16 * ks + 8 * h) / SI::EPC);
+      af[ks] = key_frag<T, SI::CPR>(itile, 32 * wave + l32, (16 * ks + 8 * h) / SI::EPC);
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
@@ -512,7 +536,7 @@ kl_dense_zt_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     vec8<T> bf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      bf[ks] = lds_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
+      bf[ks] = key_frag<T, SK::CPR>(ktile, 32 * kt + l32, (16 * ks + 8 * h) / SK::EPC);
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.0f;
 #pragma unroll
