@@ -45,6 +45,12 @@ CASES = [
     _cfg("bf16_g2_hkv8", seqlen_kv=600, seqlen_q=600, num_q_heads=16, num_kv_heads=8, topk=2),
     _cfg("bf16_decode_b3", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
          num_kv_heads=4, topk=6),
+    # fp32 with G >= 8 takes the per-wave index logits with the lane-half split
+    _cfg("f32_g8", seqlen_kv=600, seqlen_q=600, num_q_heads=16, num_kv_heads=2, head_dim=64,
+         idx_dim=64, topk=3, dtype=si.F32, scale=1.0),
+    _cfg("f32_g16_hkv1_d32", seqlen_kv=520, seqlen_q=400, q_start=120, num_q_heads=16,
+         num_kv_heads=1, head_dim=64, idx_dim=32, topk=2, dtype=si.F32, scale=1.0),
+    _cfg("bf16_g4_hkv1", seqlen_kv=700, seqlen_q=700, num_q_heads=4, num_kv_heads=1, topk=3),
 ]
 
 
@@ -182,6 +188,9 @@ GRAD_CASES = [
     _cfg("bf16_g2_hkv8", seqlen_kv=600, seqlen_q=600, num_q_heads=16, num_kv_heads=8, topk=2),
     _cfg("bf16_decode_b3", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
          num_kv_heads=4, topk=6),
+    _cfg("f32_g8", seqlen_kv=600, seqlen_q=600, num_q_heads=16, num_kv_heads=2, head_dim=64,
+         idx_dim=64, topk=3, dtype=si.F32, scale=1.0),
+    _cfg("bf16_g4_hkv1", seqlen_kv=700, seqlen_q=700, num_q_heads=4, num_kv_heads=1, topk=3),
 ]
 COEF = 0.37
 
