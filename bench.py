@@ -59,6 +59,27 @@ def effective_flops(cfg, ids):
     return f_idx, f_attn, f_loc
 
 
+def tile_flops(cfg, ids):
+    """FLOPs the kernels execute on full 128-token tiles: the index GEMM over every causal
+    block 0..floor(i/128), the attention over every selected block."""
+    import torch
+    B, Nq, Hkv, G = cfg.batch, cfg.seqlen_q, cfg.num_kv_heads, cfg.group_size
+    i = torch.arange(Nq, device=ids.device, dtype=torch.int64) + cfg.q_start
+    f_idx = 2.0 * cfg.idx_dim * Hkv * B * 128.0 * float((i // 128 + 1).sum().item())
+    f_attn = 4.0 * cfg.head_dim * G * 128.0 * float((ids >= 0).sum().item())
+    return f_idx, f_attn
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def kv_outer_bytes(cfg, ids):
     """Algorithmic HBM bytes of one KV-outer attention launch (bf16), from the GPU's
     selection: per (query, group, non-local selected block) the group's G gathered Q rows
@@ -108,6 +129,7 @@ def cpu_baseline(cfg, seconds_target=15.0):
     rows = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=n))
     dt = run(rows)
     return {"value": n / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n} seeded uniformly random query rows of the same workload "
                       f"(rows are independent; fp64 select + attention in {dt:.1f} s)"}
 
@@ -373,12 +395,16 @@ def main():
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with msa.KernelTimer("sparse_attn", max_launches=args.steps) as kt:
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        ev[0].record()
+        for j in range(args.steps):
             step()
+            ev[j + 1].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+    step_ms = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(args.steps))
     ms_per_step = 1e3 * elapsed / max(1, args.steps)
     tokens = cfg.batch * cfg.seqlen_q
     value = tokens * args.steps / elapsed
@@ -433,7 +459,9 @@ def main():
                    "num_q_heads": cfg.num_q_heads, "num_kv_heads": cfg.num_kv_heads,
                    "head_dim": cfg.head_dim, "idx_dim": cfg.idx_dim,
                    "block_size": cfg.block_size, "topk": cfg.topk, "parallelism": "none"},
+        "ms_per_step_median": step_ms[len(step_ms) // 2] if step_ms else None,
         "effective_flops_per_step": f_idx + f_attn,
+        "tile_flops_per_step": sum(tile_flops(cfg, ids)),
         "index_flops_per_step": f_idx,
         "attn_flops_per_step": f_attn,
         "attn_local_flops_per_step": f_loc,
