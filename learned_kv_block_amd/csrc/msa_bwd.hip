@@ -81,8 +81,10 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) T QT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dOT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dSs[R * LT];
-  __shared__ float lse_s[R], d_s[R];
-  __shared__ int irow_s[R];
+  // per-row data of the item: LSE in the log2 domain, D = rowsum(dO o O), position i
+  __shared__ __attribute__((aligned(16))) float lse_s[R];
+  __shared__ __attribute__((aligned(16))) float d_s[R];
+  __shared__ __attribute__((aligned(16))) int irow_s[R];
 
   // contiguous item range of this workgroup inside its XCD's share
   const int total = totals[1];
@@ -234,7 +236,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       }
     }
     if (tid < R) {
-      lse_s[tid] = lr;
+      lse_s[tid] = lr * kLog2e;
       d_s[tid] = dr;
       irow_s[tid] = ir;
     }
@@ -260,14 +262,30 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         mma(sacc, ld8<T>(Qs + (32 * rt + l32) * LK + 16 * ks + 8 * h), kf);
         mma(pacc, ld8<T>(dOs + (32 * rt + l32) * LK + 16 * ks + 8 * h), vf);
       }
+      // the lane's 16 rows are 4 runs of 4 consecutive rows (8j + 4h + 0..3): their
+      // per-row data in 16-byte reads; the exponential is unconditional and selected
+      float lrow[16], drw[16];
+      int irw[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 32 * rt + 8 * j + 4 * h;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(lse_s + r0);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(d_s + r0);
+        const i32x4 g = *reinterpret_cast<const i32x4*>(irow_s + r0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          lrow[4 * j + x] = a[x];
+          drw[4 * j + x] = c[x];
+          irw[4 * j + x] = g[x];
+        }
+      }
       float p[16], ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = 32 * rt + drow(e, h);
-        const bool vis = key <= irow_s[row];
-        p[e] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lse_s[row] * kLog2e))
-                   : 0.0f;
-        ds[e] = p[e] * (pacc[e] - d_s[row]);
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lrow[e]));
+        p[e] = key <= irw[e] ? pe : 0.0f;
+        ds[e] = p[e] * (pacc[e] - drw[e]);
         dSs[row * LT + 32 * w + l32] = cvt<T>(ds[e]);
       }
 #pragma unroll
