@@ -432,7 +432,9 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
-        if rec.get("kernel_source_hash") == kernel_source_hash():
+        # The counters were taken on one workload: they apply to no other.
+        if (rec.get("kernel_source_hash") == kernel_source_hash()
+                and rec.get("workload") == cfg.name and not args.fp8):
             traffic = rec.get("bytes_per_launch")
     # The KV-outer kernel is bound by its side traffic (gathered Q rows and written
     # partials), not by its contraction: its MFMA share is reported beside it.

@@ -22,23 +22,25 @@
 
 namespace msa {
 
-// D[row, h] = dO . O (fp32), one thread per (row, head)
+// D[row, h] = dO . O (fp32). D/8 consecutive lanes share a (row, head), 8
+// elements each, so a wave reads whole rows; the partial sums meet by shuffles.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 bwd_rowdot_kernel(const T* __restrict__ out, const T* __restrict__ dout, int64_t n,
                   float* __restrict__ drow) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= n) return;
-  const T* o = out + x * D;
-  const T* g = dout + x * D;
+  constexpr int L = D / 8;
+  static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lanes per row");
+  const int64_t x = (int64_t)blockIdx.x * (256 / L) + threadIdx.x / L;
+  const int c = threadIdx.x % L;
   float acc = 0.0f;
-#pragma unroll 4
-  for (int c = 0; c < D; c += 8) {
-    const vec8<T> a = ld8<T>(o + c), b = ld8<T>(g + c);
+  if (x < n) {
+    const vec8<T> a = ld8<T>(out + x * D + 8 * c), b = ld8<T>(dout + x * D + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
   }
-  drow[x] = acc;
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) acc += shfl_xor_f(acc, m);
+  if (x < n && c == 0) drow[x] = acc;
 }
 
 // (query, head) rows per work item: 64 for bf16; 32 for fp32, whose tiles
@@ -355,11 +357,15 @@ dq_sum_kernel(const T* __restrict__ dqpart, const int32_t* __restrict__ ids, int
   const int hh = (int)((x / CH) % G);
   const int64_t rg = x / (CH * G);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // Every slot's partial is loaded (the buffer holds all of them) and an unused
+  // slot's, never written, is dropped by a select: no branch stands between the
+  // loads, so they are all in flight together.
+#pragma unroll 4
   for (int s = 0; s < topk; ++s) {
-    if (ids[rg * topk + s] < 0) continue;
+    const bool used = ids[rg * topk + s] >= 0;
     const vec8<T> a = ld8<T>(dqpart + ((rg * topk + s) * G + hh) * D + 8 * ch);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (float)a[e];
+    for (int e = 0; e < 8; ++e) acc[e] += used ? (float)a[e] : 0.0f;
   }
   vec8<T> res;
 #pragma unroll
@@ -530,19 +536,33 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   if (cur >= 0) flush(cur);
 }
 
-// dq_idx[row, r] = sum over the row's used slots of the slot partials
+// dq_idx[row, r] = sum over the row's used slots of the slot partials; a thread
+// sums 4 consecutive elements, loading every slot and dropping unused ones
+// (never written) by a select, so that the loads are all in flight together
 template <typename T, int DI>
 __global__ void __launch_bounds__(256)
 dqi_sum_kernel(const float* __restrict__ dqpart, const int32_t* __restrict__ ids, int64_t nrg,
                int topk, T* __restrict__ dq) {
-  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row*Hkv + r, d)
-  if (x >= nrg * DI) return;
-  const int64_t rg = x / DI;
-  const int dd = (int)(x % DI);
-  float acc = 0.0f;
-  for (int s = 0; s < topk; ++s)
-    if (ids[rg * topk + s] >= 0) acc += dqpart[(rg * topk + s) * DI + dd];
-  dq[x] = cvt<T>(acc);
+  constexpr int C4 = DI / 4;
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row*Hkv + r, 4-element chunk)
+  if (x >= nrg * C4) return;
+  const int64_t rg = x / C4;
+  const int cc = (int)(x % C4);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll 4
+  for (int s = 0; s < topk; ++s) {
+    const bool used = ids[rg * topk + s] >= 0;
+    const float4 a = *reinterpret_cast<const float4*>(dqpart + (rg * topk + s) * DI + 4 * cc);
+    acc.x += used ? a.x : 0.0f;
+    acc.y += used ? a.y : 0.0f;
+    acc.z += used ? a.z : 0.0f;
+    acc.w += used ? a.w : 0.0f;
+  }
+  T* o = dq + rg * DI + 4 * cc;
+  o[0] = cvt<T>(acc.x);
+  o[1] = cvt<T>(acc.y);
+  o[2] = cvt<T>(acc.z);
+  o[3] = cvt<T>(acc.w);
 }
 
 template <typename T, int DI>
@@ -561,8 +581,8 @@ static hipError_t idx_bwd_run(const Dims& d, const void* qi, const void* ki, con
   prof_after(MSA_K_IDX_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nrg = d.rows * d.Hkv;
-  dqi_sum_kernel<T, DI><<<(unsigned)((nrg * DI + 255) / 256), 256, 0, s>>>(dqpart, ids, nrg, d.K,
-                                                                           (T*)dq);
+  dqi_sum_kernel<T, DI><<<(unsigned)((nrg * (DI / 4) + 255) / 256), 256, 0, s>>>(
+      dqpart, ids, nrg, d.K, (T*)dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (nk > 0)
     f32_to_kernel<T><<<(unsigned)std::min<int64_t>((nk + 255) / 256, 4096), 256, 0, s>>>(
@@ -594,7 +614,7 @@ static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const voi
   if ((e = launch_fill_f32(dk_acc, nkv, 0.0f, s)) != hipSuccess) return e;
   if ((e = launch_fill_f32(dv_acc, nkv, 0.0f, s)) != hipSuccess) return e;
   const int64_t nrh = d.rows * d.Hq;
-  bwd_rowdot_kernel<T, D><<<(unsigned)((nrh + 255) / 256), 256, 0, s>>>(
+  bwd_rowdot_kernel<T, D><<<(unsigned)((nrh + 256 / (D / 8) - 1) / (256 / (D / 8))), 256, 0, s>>>(
       (const T*)out, (const T*)dout, nrh, drow);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
