@@ -143,7 +143,8 @@ Layout layout(const Dims& d, int op) {
   } else if (op == MSA_OP_ATTN_BWD) {
     const size_t nkv = (size_t)d.B * d.N * d.Hkv * d.D;
     L.drow = take((size_t)d.rows * d.Hq * 4);
-    L.dqpart = take((size_t)d.slots * d.G * d.D * elem_size(d));
+    // one extra slot: target of the backward kernel's unused rows
+    L.dqpart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
     L.dk_acc = take(nkv * 4);
     L.dv_acc = take(nkv * 4);
   } else if (op == MSA_OP_IDX_BWD) {

@@ -12,12 +12,12 @@
 //
 // Execution is KV-outer like the forward: the (query, slot) pairs are inverted
 // into per-(batch, group, block) buckets (the counting sort of msa_attn.hip,
-// local block included) and cut into items of 32 (query, head) rows. A
-// persistent workgroup (4 waves) walks a contiguous range of items; wave w owns
-// keys 32w..32w+31 of the current block and keeps their dK and dV in registers
-// across the consecutive items of a bucket, adding them to fp32 accumulators
-// (atomics) when the bucket changes. dQ gets one partial per (query, slot),
-// summed per row afterwards.
+// local block included) and cut into items of 64 (query, head) rows (32 in
+// fp32). A persistent workgroup walks a contiguous range of items; each wave
+// owns one (32-key quarter of the current block, 32-row tile of the item) pair
+// and keeps its keys' dK and dV in registers across the consecutive items of a
+// bucket, adding them to fp32 accumulators (atomics) when the bucket changes.
+// dQ gets one partial per (query, slot), summed per row afterwards.
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -55,17 +55,24 @@ template <typename T>
 constexpr int bwd_rows() {
   return sizeof(T) == 2 ? MSA_BWD_R16 : 32;
 }
+// one wave per (32-key quarter of the block, 32-row tile of the item)
+template <typename T>
+constexpr int bwd_threads() {
+  return 64 * 4 * (bwd_rows<T>() / 32);
+}
 
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(bwd_threads<T>(), 1)
 attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                 const T* __restrict__ dout, const float* __restrict__ lse,
                 const float* __restrict__ rowdot, const int4* __restrict__ items,
                 const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
                 T* __restrict__ dqpart, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
-                int N, int Nq, int q_start, int Hkv, int nb, int nbw, int topk, float scale) {
+                int N, int Nq, int q_start, int Hkv, int nb, int nbw, int topk, int nslots,
+                float scale) {
   constexpr int R = bwd_rows<T>();  // (query, head) rows per item
   constexpr int RT = R / 32;        // 32-row tiles per item
+  constexpr int NT = bwd_threads<T>();
   // bf16: the X^T operands (Q^T, dO^T, K^T) come from the row-major tiles
   // through the transposing LDS read; fp32 keeps transposed copies
   constexpr bool kTr = sizeof(T) == 2;
@@ -83,10 +90,14 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   __shared__ __attribute__((aligned(16))) T QT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dOT[kTr ? 8 : D * LR];
   __shared__ __attribute__((aligned(16))) T dSs[R * LT];
-  // per-row data of the item: LSE in the log2 domain, D = rowsum(dO o O), position i
-  __shared__ __attribute__((aligned(16))) float lse_s[R];
-  __shared__ __attribute__((aligned(16))) float d_s[R];
-  __shared__ __attribute__((aligned(16))) int irow_s[R];
+  // per-row data of the item, one array so that one address serves all four:
+  // [0, R) LSE in the log2 domain, [R, 2R) D = rowsum(dO o O) (both fp32 bits),
+  // [2R, 3R) position i, [3R, 4R) (query, slot) index of the row's dQ partial
+  __shared__ __attribute__((aligned(16))) int rowd_s[4 * R];
+  int* const lse_s = rowd_s;
+  int* const d_s = rowd_s + R;
+  int* const irow_s = rowd_s + 2 * R;
+  int* const slot_s = rowd_s + 3 * R;
 
   // contiguous item range of this workgroup inside its XCD's share
   const int total = totals[1];
@@ -100,11 +111,14 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = w & 3, rt = w >> 2;  // key quarter, row tile of phase 1
   const int Hq = Hkv * G;
   const size_t kvrow = (size_t)Hkv * D;
   const float sl2 = scale * kLog2e;
 
-  f32x16 dka[DT], dva[DT];  // dK^T, dV^T of keys 32w + l32: element e is d = 32dt + drow(e, h)
+  // dK^T, dV^T of keys 32kw + l32 from this wave's row tile: element e is
+  // d = 32dt + drow(e, h); the waves of the other row tiles hold the rest
+  f32x16 dka[DT], dva[DT];
   auto zero_acc = [&]() {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -116,7 +130,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   };
   auto flush = [&](int bkt) {
     const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
-    const int key = blk * 128 + 32 * w + l32;
+    const int key = blk * 128 + 32 * kw + l32;
     if (key >= N) return;
     const size_t base = ((size_t)b * N + key) * kvrow + (size_t)r * D;
 #pragma unroll
@@ -162,39 +176,54 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     return a;
   };
 
-  // rows of an item -> registers (issued one item ahead): chunk c = tid + 256u
+  // rows of an item -> registers (issued one item ahead): chunk c = tid + NT u
   // covers row c / CH, 8-element chunk c % CH
-  constexpr int RU = R * CH / 256;
-  static_assert(R * CH % 256 == 0 && R <= 256, "row chunks");
+  constexpr int RU = R * CH / NT;
+  static_assert(R * CH % NT == 0 && R <= NT, "row chunks");
   vec8<T> qr[RU], gr[RU];
   float lr = 0.0f, dr = 0.0f;
-  int ir = -1;
+  int ir = -1, sr = nslots;
+  // the entries of an item's rows, loaded one item ahead of the rows themselves:
+  // en[u] for chunk u's row, er for row tid % R (rows past cnt: a valid row)
+  int en[RU], er;
+  auto load_ents = [&](int it) {
+    const int4 itm = items[it];
+    const int start = itm.y, cnt = itm.z;
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+      en[u] = entries[start + min((tid + NT * u) / CH / G, cnt - 1)];
+    er = entries[start + min((tid % R) / G, cnt - 1)];
+  };
+  // Every lane loads (lanes past R repeat a row), so no load sits under a branch
+  // and the waits for them count a fixed number of later memory operations.
   auto load_rows = [&](int it) {
     const int4 itm = items[it];
-    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int bkt = itm.x, cnt = itm.z;
     const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-      const int c = tid + 256 * u;
+      const int c = tid + NT * u;
       const int rho = c / CH, dc = c % CH;
-      const int t = entries[start + min(rho / G, cnt - 1)] >> 6;  // rows past cnt: a valid row
+      const int t = en[u] >> 6;
       const size_t off = ((size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G) * D + 8 * dc;
       qr[u] = ld8<T>(q + off);
       gr[u] = ld8<T>(dout + off);
     }
-    if (tid < R) {
-      const int j = tid / G;
-      const int t = entries[start + min(j, cnt - 1)] >> 6;
-      const size_t rr = (size_t)(b * (size_t)Nq + t) * Hq + r * G + tid % G;
-      lr = lse[rr];
-      dr = rowdot[rr];
-      ir = j < cnt ? q_start + t : -1;  // an unused row masks every key: P = dS = 0
-    }
+    const int rho = tid % R, j = rho / G, t = er >> 6;
+    const size_t rr = (size_t)(b * (size_t)Nq + t) * Hq + r * G + rho % G;
+    lr = lse[rr];
+    dr = rowdot[rr];
+    ir = j < cnt ? q_start + t : -1;  // an unused row masks every key: P = dS = 0
+    // slot indices stay below 2^31 (checked by the caller); an unused row writes
+    // its (zero) dQ partial to the spare slot past the last
+    sr = j < cnt ? (int)((((size_t)b * Nq + t) * Hkv + r) * topk + (er & 63)) : nslots;
   };
 
   zero_acc();
   int cur = -1;
+  load_ents(i0);
   load_rows(i0);
+  load_ents(min(i0 + 1, i1 - 1));
   for (int it = i0; it < i1; ++it) {
     const int4 itm = items[it];
     const int bkt = itm.x, start = itm.y, cnt = itm.z;
@@ -205,7 +234,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       zero_acc();
       cur = bkt;
       // K and V of block blk (row-major; fp32 also K^T); rows past N are zero
-      for (int c = tid; c < 128 * CH; c += 256) {
+      for (int c = tid; c < 128 * CH; c += NT) {
         const int rho = c / CH, dc = c % CH;
         const int key = blk * 128 + rho;
         vec8<T> kk = zero8<T>(), vv = zero8<T>();
@@ -225,7 +254,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     // the item's rows (row rho = query rho / G of the item, head rho % G), prefetched
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-      const int c = tid + 256 * u;
+      const int c = tid + NT * u;
       const int rho = c / CH, dc = c % CH;
       st8<T>(Qs + rho * LK + 8 * dc, qr[u]);
       st8<T>(dOs + rho * LK + 8 * dc, gr[u]);
@@ -238,19 +267,20 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       }
     }
     if (tid < R) {
-      lse_s[tid] = lr * kLog2e;
-      d_s[tid] = dr;
+      lse_s[tid] = __float_as_int(lr * kLog2e);
+      d_s[tid] = __float_as_int(dr);
       irow_s[tid] = ir;
+      slot_s[tid] = sr;
     }
     load_rows(min(it + 1, i1 - 1));  // the next item's rows land during this item
+    load_ents(min(it + 2, i1 - 1));
     __syncthreads();
 
-    // ---- phase 1: wave w, keys 32w..32w+31, each 32-row tile of the item:
+    // ---- phase 1: keys 32kw..32kw+31 and rows 32rt..32rt+31 of the item:
     // S = Q K^T, dP = dO V^T (rows x keys), P = exp(S - LSE) on the support,
     // dS = P (dP - D); dV^T += dO^T P, dK^T += Q^T dS
-    const int key = blk * 128 + 32 * w + l32;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    const int key = blk * 128 + 32 * kw + l32;
+    {
       f32x16 sacc, pacc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -259,64 +289,54 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
       }
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks) {
-        const vec8<T> kf = ld8<T>(Ks + (32 * w + l32) * LK + 16 * ks + 8 * h);
-        const vec8<T> vf = ld8<T>(Vs + (32 * w + l32) * LK + 16 * ks + 8 * h);
+        const vec8<T> kf = ld8<T>(Ks + (32 * kw + l32) * LK + 16 * ks + 8 * h);
+        const vec8<T> vf = ld8<T>(Vs + (32 * kw + l32) * LK + 16 * ks + 8 * h);
         mma(sacc, ld8<T>(Qs + (32 * rt + l32) * LK + 16 * ks + 8 * h), kf);
         mma(pacc, ld8<T>(dOs + (32 * rt + l32) * LK + 16 * ks + 8 * h), vf);
       }
-      // the lane's 16 rows are 4 runs of 4 consecutive rows (8j + 4h + 0..3): their
-      // per-row data in 16-byte reads; the exponential is unconditional and selected
-      float lrow[16], drw[16];
-      int irw[16];
+      // the lane's 16 rows are 4 runs of 4 consecutive rows 8j + 4h + 0..3 (element
+      // e = 4j + x is row 8j + 4h + x): their per-row data in 16-byte reads, one run
+      // at a time; the exponential is unconditional and selected. P and dS go
+      // straight into the operands of the dV, dK products (elements 8c..8c+7).
+      vec8<T> pf[2], sf[2];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r0 = 32 * rt + 8 * j + 4 * h;
-        const f32x4 a = *reinterpret_cast<const f32x4*>(lse_s + r0);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(d_s + r0);
+        const f32x4 a = __builtin_bit_cast(f32x4, *reinterpret_cast<const i32x4*>(lse_s + r0));
+        const f32x4 c = __builtin_bit_cast(f32x4, *reinterpret_cast<const i32x4*>(d_s + r0));
         const i32x4 g = *reinterpret_cast<const i32x4*>(irow_s + r0);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          lrow[4 * j + x] = a[x];
-          drw[4 * j + x] = c[x];
-          irw[4 * j + x] = g[x];
+          const int e = 4 * j + x;
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -a[x]));
+          const float pv = key <= g[x] ? pe : 0.0f;
+          const float dv = pv * (pacc[e] - c[x]);
+          dSs[(r0 + x) * LT + 32 * kw + l32] = cvt<T>(dv);
+          pf[e >> 3][e & 7] = cvt<T>(pv);
+          sf[e >> 3][e & 7] = cvt<T>(dv);
         }
-      }
-      float p[16], ds[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = 32 * rt + drow(e, h);
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], sl2, -lrow[e]));
-        p[e] = key <= irw[e] ? pe : 0.0f;
-        ds[e] = p[e] * (pacc[e] - drw[e]);
-        dSs[row * LT + 32 * w + l32] = cvt<T>(ds[e]);
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        vec8<T> pf, sf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pf[e] = cvt<T>(p[8 * c + e]);
-          sf[e] = cvt<T>(ds[8 * c + e]);
-        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           if constexpr (kTr) {
-            mma(dva[dt], frag_tr(dOs, 2 * rt + c, dt), pf);
-            mma(dka[dt], frag_tr(Qs, 2 * rt + c, dt), sf);
+            mma(dva[dt], frag_tr(dOs, 2 * rt + c, dt), pf[c]);
+            mma(dka[dt], frag_tr(Qs, 2 * rt + c, dt), sf[c]);
           } else {
-            mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR + 32 * rt, c), pf);
-            mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR + 32 * rt, c), sf);
+            mma(dva[dt], frag_rows(dOT + (32 * dt + l32) * LR + 32 * rt, c), pf[c]);
+            mma(dka[dt], frag_rows(QT + (32 * dt + l32) * LR + 32 * rt, c), sf[c]);
           }
         }
       }
     }
     __syncthreads();  // dS of every wave's keys is in LDS
 
-    // ---- phase 2: dQ = dS K (rows x d); wave w takes d columns 32w..32w+31
-    if (32 * w < D) {  // uniform
-      const int dq_t = w;
-#pragma unroll
-      for (int rq = 0; rq < RT; ++rq) {
+    // ---- phase 2: dQ = dS K (rows x d); wave w takes row tile w / DT and
+    // d columns 32(w % DT)..+31
+    if (RT * DT * 64 >= NT || w < RT * DT) {  // uniform
+      const int dq_t = w % DT, rq = w / DT;
+      {
         f32x16 qacc;
 #pragma unroll
         for (int e = 0; e < 16; ++e) qacc[e] = 0.0f;
@@ -328,16 +348,15 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             mma(qacc, ld8<T>(dSs + (32 * rq + l32) * LT + 16 * kc + 8 * h),
                 ld8<T>(KT + (32 * dq_t + l32) * LT + 16 * kc + 8 * h));
         }
+        // the lane's rows 32rq + 8j + 4h + 0..3: their slots in 16-byte reads
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 32 * rq + drow(e, h);
-          const int j = row / G;
-          if (j < cnt) {
-            const int ent = entries[start + j];
-            const size_t slot =
-                ((size_t)(b * (size_t)Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
-            dqpart[(slot * G + row % G) * D + 32 * dq_t + l32] = cvt<T>(qacc[e] * scale);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = 32 * rq + 8 * j + 4 * h;
+          const i32x4 sl = *reinterpret_cast<const i32x4*>(slot_s + r0);
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            dqpart[((size_t)sl[x] * G + (r0 + x) % G) * D + 32 * dq_t + l32] =
+                cvt<T>(qacc[4 * j + x] * scale);
         }
       }
     }
@@ -625,10 +644,10 @@ static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const voi
 #define MSA_BWD_CASE(GG)                                                                        \
   case GG:                                                                                      \
     prof_before(MSA_K_ATTN_BWD, s);                                                             \
-    attn_bwd_kernel<T, D, GG><<<grid, 256, 0, s>>>(                                            \
+    attn_bwd_kernel<T, D, GG><<<grid, bwd_threads<T>(), 0, s>>>(                                            \
         (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, drow, w.items, w.entries,   \
         w.totals, (T*)dqpart, dk_acc, dv_acc, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, \
-        d.K, scale);                                                                            \
+        d.K, (int)d.slots, scale);                                                              \
     prof_after(MSA_K_ATTN_BWD, s);                                                              \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
     if (nrg > 0)                                                                                \
