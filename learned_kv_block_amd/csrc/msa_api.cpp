@@ -148,7 +148,8 @@ Layout layout(const Dims& d, int op) {
     L.dk_acc = take(nkv * 4);
     L.dv_acc = take(nkv * 4);
   } else if (op == MSA_OP_IDX_BWD) {
-    L.dqi_part = take((size_t)d.slots * d.DI * 4);
+    // one extra slot: target of the index backward kernel's unused queries
+    L.dqi_part = take((size_t)(d.slots + 1) * d.DI * 4);
     L.dki_acc = take((size_t)d.B * d.N * d.DI * 4);
   } else {
     L.slot_lse = take((size_t)d.slots * 4);

@@ -420,7 +420,7 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
                const int4* __restrict__ items, const int32_t* __restrict__ entries,
                const int32_t* __restrict__ totals, float* __restrict__ dqpart,
                float* __restrict__ dk_acc, int N, int Nq, int Hkv, int nb, int nbw, int topk,
-               float coef) {
+               int nslots, float coef) {
   constexpr int Q = 32;         // queries per item
   constexpr int LKT = 128 + 4;  // row stride of K_idx^T [DI][128] and of dl [Q][128]
   constexpr int LQ = Q + 4;     // row stride of dl^T [128][Q] and Q_idx^T [DI][Q]
@@ -429,6 +429,7 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   __shared__ __attribute__((aligned(16))) float DLs[Q * LKT];
   __shared__ __attribute__((aligned(16))) float DLT[128 * LQ];
   __shared__ __attribute__((aligned(16))) float QIT[DI * LQ];
+  __shared__ __attribute__((aligned(16))) int slot_s[Q];  // (query, slot) of each query's partial
 
   const int total = totals[1];
   const int nwg_x = gridDim.x / 8;
@@ -460,35 +461,51 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
     }
   };
 
-  // the item's dl rows (4 floats per chunk) and Q_idx rows, loaded one item ahead
+  // the item's dl rows (4 floats per chunk) and Q_idx rows, loaded one item
+  // ahead; the entries that address them one item earlier still. Every lane
+  // loads (rows past cnt repeat a valid row), so no load sits under a branch.
   constexpr int DU = Q * 128 / 4 / 256;  // dl chunks per thread
   constexpr int QU = (Q * DI + 255) / 256;  // Q_idx values per thread
   vec4<float> dlr[DU];
   float qir[QU];
+  int edl[DU], eqi[QU], es;
+  int sr = nslots;
+  auto load_ents = [&](int it) {
+    const int4 itm = items[it];
+    const int start = itm.y, cnt = itm.z;
+#pragma unroll
+    for (int u = 0; u < DU; ++u) edl[u] = entries[start + min((tid + 256 * u) / 32, cnt - 1)];
+#pragma unroll
+    for (int u = 0; u < QU; ++u)
+      eqi[u] = entries[start + min(min(tid + 256 * u, Q * DI - 1) / DI, cnt - 1)];
+    es = entries[start + min(tid % Q, cnt - 1)];
+  };
   auto load_rows = [&](int it) {
     const int4 itm = items[it];
-    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int bkt = itm.x, cnt = itm.z;
     const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
 #pragma unroll
     for (int u = 0; u < DU; ++u) {
-      const int c = tid + 256 * u;
-      const int j = c / 32, o4 = c % 32;
-      const int ent = entries[start + min(j, cnt - 1)];  // rows past cnt: zeroed when stored
+      const int o4 = (tid + 256 * u) % 32, ent = edl[u];  // rows past cnt: zeroed when stored
       dlr[u] = ld4<float>(dl + (((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk * 128 +
                           (ent & 63) * 128 + 4 * o4);
     }
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
-      const int c = min(tid + 256 * u, Q * DI - 1);
-      const int j = c / DI, dd = c % DI;
-      const int t = entries[start + min(j, cnt - 1)] >> 6;
-      qir[u] = (float)qi[(((size_t)b * Nq + t) * Hkv + r) * DI + dd];
+      const int dd = min(tid + 256 * u, Q * DI - 1) % DI;
+      qir[u] = (float)qi[(((size_t)b * Nq + (eqi[u] >> 6)) * Hkv + r) * DI + dd];
     }
+    // slot indices stay below 2^31 (checked by the caller); a query past cnt
+    // writes its (zero) partial to the spare slot past the last
+    sr = tid % Q < cnt ? (int)((((size_t)b * Nq + (es >> 6)) * Hkv + r) * topk + (es & 63))
+                       : nslots;
   };
 
   zero_acc();
   int cur = -1;
+  load_ents(i0);
   load_rows(i0);
+  load_ents(min(i0 + 1, i1 - 1));
   for (int it = i0; it < i1; ++it) {
     const int4 itm = items[it];
     const int bkt = itm.x, start = itm.y, cnt = itm.z;
@@ -517,12 +534,14 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
 #pragma unroll
     for (int u = 0; u < QU; ++u) {  // Q_idx^T of the item's queries (zero past cnt)
       const int c = tid + 256 * u;
-      if (c < Q * DI) {
+      if (Q * DI % 256 == 0 || c < Q * DI) {  // no branch when the chunks fill every thread
         const int j = c / DI, dd = c % DI;
         QIT[dd * LQ + j] = j < cnt ? qir[u] : 0.0f;
       }
     }
+    if (tid < Q) slot_s[tid] = sr;
     load_rows(min(it + 1, i1 - 1));  // the next item's rows land during this item
+    load_ents(min(it + 2, i1 - 1));
     __syncthreads();
     // dq_idx partial of the item's queries: dl (Q x 128) K_idx (128 x DI); wave w < DIT
     if (w < DIT) {  // uniform
@@ -533,14 +552,13 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
       for (int kc = 0; kc < 8; ++kc)
         mma(acc, ld8<float>(DLs + l32 * LKT + 16 * kc + 8 * h),
             ld8<float>(KIT + (32 * w + l32) * LKT + 16 * kc + 8 * h));
+      // the lane's queries 8jj + 4h + 0..3: their slots in 16-byte reads
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = drow(e, h);
-        if (j < cnt) {
-          const int ent = entries[start + j];
-          const size_t slot = (((size_t)b * Nq + (ent >> 6)) * Hkv + r) * topk + (ent & 63);
-          dqpart[slot * DI + 32 * w + l32] = acc[e] * coef;
-        }
+      for (int jj = 0; jj < 4; ++jj) {
+        const i32x4 sl = *reinterpret_cast<const i32x4*>(slot_s + 8 * jj + 4 * h);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          dqpart[(size_t)sl[x] * DI + 32 * w + l32] = acc[4 * jj + x] * coef;
       }
     }
     // dk_idx of keys 32w..: dl^T (keys x Q) Q_idx (Q x DI)
@@ -596,7 +614,7 @@ static hipError_t idx_bwd_run(const Dims& d, const void* qi, const void* ki, con
   prof_before(MSA_K_IDX_BWD, s);
   idx_bwd_kernel<T, DI><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, dl, w.items, w.entries,
                                              w.totals, dqpart, dk_acc, d.N, d.Nq, d.Hkv, d.nb,
-                                             d.nb * d.nwin, d.K, c);
+                                             d.nb * d.nwin, d.K, (int)d.slots, c);
   prof_after(MSA_K_IDX_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nrg = d.rows * d.Hkv;
