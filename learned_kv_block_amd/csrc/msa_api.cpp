@@ -154,7 +154,9 @@ Layout layout(const Dims& d, int op) {
   } else {
     L.slot_lse = take((size_t)d.slots * 4);
     L.lse_idx = take((size_t)d.rows * d.Hkv * 4);
-    L.kl_part = take((size_t)d.slots * 4);
+    // + one spare slot and one spare 128-float row: targets of the KL kernel's
+    // stores for queries past an item's count
+    L.kl_part = take((size_t)(d.slots + 1 + 128) * 4);
     L.block_sums = take((size_t)((d.rows * d.Hkv + 255) / 256 + 1) * 4);
   }
   L.total = o;

@@ -290,7 +290,7 @@ kl_main_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __rest
 //    student, KL and dS in the log2 domain; dS rows are streamed out.
 constexpr int kKlWaves = 8;
 
-template <int D, int DI, int G>
+template <int D, int DI, int G, bool DL>
 __global__ void __launch_bounds__(512, 1)
 kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const bf16* __restrict__ q_idx, const bf16* __restrict__ k_idx,
@@ -298,7 +298,7 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                     const int4* __restrict__ items, const int32_t* __restrict__ entries,
                     const int32_t* __restrict__ totals, float* __restrict__ kl_part,
                     float* __restrict__ dlogits, int N, int Nq, int q_start, int Hkv, int nb,
-                    int nbw, int topk, float scale_log2, float zscale_log2) {
+                    int nbw, int topk, int nslots, float scale_log2, float zscale_log2) {
   static_assert(G >= 8, "two lane halves per query");
   constexpr int QT = 256 / G;            // queries per item
   constexpr int KSD = D / 16, KSI = DI / 16;
@@ -362,6 +362,18 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
     for (int j = 0; j < QPW; ++j) es[j] = entries[min(itm.y + qw0 + j, ent_last)];
   };
+  // index-logit operand of an item: lane l32 < QT takes query l32 (others
+  // repeat query 0); every wave loads it, so no load sits under a branch
+  auto z_entry = [&](const int4& itm) {
+    const int qi = l32 < QT ? l32 : 0;
+    return entries[min(itm.y + min(qi, itm.z - 1), ent_last)];
+  };
+  auto load_qz = [&](const int4& itm, int ez, vec8<bf16>* qz) {
+    const int br = itm.x / nbw, r = br % Hkv, b = br / Hkv;
+    const bf16* qp = q_idx + (((size_t)b * Nq + (ez >> 6)) * Hkv + r) * DI + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qz[ks] = ld8<bf16>(qp + 16 * ks);
+  };
   // Q rows of the wave's queries (row-contiguous) and LSE_main of its rows
   auto load_rows = [&](int bkt, const int* es, vec8<bf16>* raw, float* lm2) {
     const int br = bkt / nbw, r = br % Hkv, b = br / Hkv;
@@ -406,6 +418,9 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   int4 nxt = items[min(i0 + 1, i1 - 1)];
   int es_n[QPW];
   wave_entries(nxt, es_n);
+  int ez_n = z_entry(nxt);
+  vec8<bf16> qz[KSI];
+  load_qz(cur, z_entry(cur), qz);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -416,29 +431,16 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int buf = (it - i0) & 1;
     const bool have_next = it + 1 < i1;
     const int4 nxt2 = items[min(it + 2, i1 - 1)];
+    // q_idx operand of the next item (its entry was loaded one item earlier)
+    vec8<bf16> qz_n[KSI];
+    load_qz(nxt, ez_n, qz_n);
     int es_n2[QPW];
     wave_entries(nxt2, es_n2);
+    const int ez_n2 = z_entry(nxt2);
     vec8<bf16> qraw[RCH];
     float lm2_n[16];
     load_rows(nxt.x, es_n, qraw, lm2_n);
 
-    // ---- index logits of the item's queries (waves 0-3: keys 32w..32w+31)
-    if (wave < 4) {
-      const int qi = l32 < QT ? l32 : 0;
-      const int e = entries[min(start + min(qi, cnt - 1), ent_last)];
-      const bf16* qp = q_idx + (((size_t)b * Nq + (e >> 6)) * Hkv + r) * DI + 8 * h;
-      f32x16 zacc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) zacc[i] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KSI; ++ks)
-        mma(zacc, ld8<bf16>(KIb + tile_off<DI, false>(32 * wave + l32, 16 * ks + 8 * h)),
-            ld8<bf16>(qp + 16 * ks));
-      if (l32 < QT) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) zs[buf][l32][32 * wave + drow(i, h)] = zacc[i] * zscale_log2;
-      }
-    }
     // ---- S = Q K^T
     f32x16 sacc[4];
 #pragma unroll
@@ -449,19 +451,37 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int ks = 0; ks < KSD; ++ks)
         mma(sacc[kt], qf[ks], ld8<bf16>(Kb + tile_off<D, false>(kt * 32 + l32, 16 * ks + 8 * h)));
     }
-    // per query of the lane: position, log2 LSE_idx, gradient row, ownership
+    // ---- index logits of the item's queries (waves 0-3: keys 32w..32w+31)
+    if (wave < 4) {
+      f32x16 zacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zacc[i] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KSI; ++ks)
+        mma(zacc, ld8<bf16>(KIb + tile_off<DI, false>(32 * wave + l32, 16 * ks + 8 * h)), qz[ks]);
+      if (l32 < QT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zs[buf][l32][32 * wave + drow(i, h)] = zacc[i] * zscale_log2;
+      }
+    }
+    // per query of the lane: position, log2 LSE_idx, KL slot and gradient row.
+    // Both lane halves hold the same values and store them to the same
+    // addresses; a query past cnt writes to the spare slot and row past the
+    // last slot. No store sits under a branch, so the waits for the loads
+    // issued before them can count them.
     int q_i[NLQ];
     float li2[NLQ];
-    size_t drow0[NLQ];
-    bool qown[NLQ];
+    int kslot[NLQ];
+    float* dptr[NLQ];
 #pragma unroll
     for (int lq = 0; lq < NLQ; ++lq) {
       const int t = es[lq] >> 6;
-      qown[lq] = qw0 + lq < cnt && h == 0;
+      const bool qv = qw0 + lq < cnt;
       q_i[lq] = q_start + t;
       const size_t rg = ((size_t)b * Nq + t) * Hkv + r;
       li2[lq] = lse_idx[rg] * kLog2e;
-      drow0[lq] = (rg * topk + (es[lq] & 63)) * 128;
+      kslot[lq] = qv ? (int)(rg * topk + (es[lq] & 63)) : nslots;
+      dptr[lq] = DL ? (qv ? dlogits + (size_t)kslot[lq] * 128 : kl_part + nslots + 1) : nullptr;
     }
     __syncthreads();  // the index-logit table of this item is complete
     float klacc[NLQ];
@@ -484,10 +504,8 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const float dS = vis ? __builtin_amdgcn_exp2f(lpi2) - P : 0.0f;
         const float term =
             (vis && P >= 1.17549435e-38f) ? P * (__builtin_amdgcn_logf(P) - lpi2) : 0.0f;
-        if (qown[lq]) {
-          klacc[lq] += term;
-          if (dlogits) __builtin_nontemporal_store(dS, dlogits + drow0[lq] + key);
-        }
+        klacc[lq] += term;
+        if constexpr (DL) __builtin_nontemporal_store(dS, dptr[lq] + key);
       }
     }
 #pragma unroll
@@ -495,7 +513,7 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       float v = klacc[lq] * kLn2;
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
-      if (l32 == 0 && qown[lq]) kl_part[drow0[lq] / 128] = v;
+      kl_part[kslot[lq]] = v;
     }
     // ---- next item's Q fragments
     rows_to_frags(qraw, qf);
@@ -507,6 +525,9 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     cur = nxt;
     nxt = nxt2;
+    ez_n = ez_n2;
+#pragma unroll
+    for (int ks = 0; ks < KSI; ++ks) qz[ks] = qz_n[ks];
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
       es[j] = es_n[j];
@@ -592,10 +613,18 @@ static hipError_t kl_run(const Dims& d, const void* q, const void* k, const void
       // one workgroup per CU, a multiple of 8 (one share per XCD)
       const unsigned pgrid = (unsigned)(((d.num_cus + 7) / 8) * 8);
       const float zscale_log2 = (float)(1.0 / sqrt((double)DI) * 1.4426950408889634);
-      kl_main_pipe_kernel<D, DI, G><<<pgrid, 64 * kKlWaves, 0, s>>>(
-          (const bf16*)q, (const bf16*)k, (const bf16*)q_idx, (const bf16*)k_idx, lse_main,
-          lse_idx, w.items, w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start, d.Hkv,
-          d.nb, d.nb * d.nwin, d.K, scale_log2, zscale_log2);
+      // kl_part holds one spare slot and one spare 128-float gradient row past
+      // the last slot (targets of the stores of queries past an item's count)
+      if (dlogits)
+        kl_main_pipe_kernel<D, DI, G, true><<<pgrid, 64 * kKlWaves, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)q_idx, (const bf16*)k_idx, lse_main,
+            lse_idx, w.items, w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start,
+            d.Hkv, d.nb, d.nb * d.nwin, d.K, (int)d.slots, scale_log2, zscale_log2);
+      else
+        kl_main_pipe_kernel<D, DI, G, false><<<pgrid, 64 * kKlWaves, 0, s>>>(
+            (const bf16*)q, (const bf16*)k, (const bf16*)q_idx, (const bf16*)k_idx, lse_main,
+            lse_idx, w.items, w.entries, w.totals, kl_part, dlogits, d.N, d.Nq, d.q_start,
+            d.Hkv, d.nb, d.nb * d.nwin, d.K, (int)d.slots, scale_log2, zscale_log2);
     } else {
       kl_main_kernel<T, D, DI, G><<<grid, 256, 0, s>>>(
           (const T*)q, (const T*)k, (const T*)q_idx, (const T*)k_idx, lse_main, lse_idx,
