@@ -379,10 +379,10 @@ dq_sum_kernel(const T* __restrict__ dqpart, const int32_t* __restrict__ ids, int
   // Every slot's partial is loaded (the buffer holds all of them) and an unused
   // slot's, never written, is dropped by a select: no branch stands between the
   // loads, so they are all in flight together.
-#pragma unroll 4
+#pragma unroll 16
   for (int s = 0; s < topk; ++s) {
     const bool used = ids[rg * topk + s] >= 0;
-    const vec8<T> a = ld8<T>(dqpart + ((rg * topk + s) * G + hh) * D + 8 * ch);
+    const vec8<T> a = ld8_nt<T>(dqpart + ((rg * topk + s) * G + hh) * D + 8 * ch);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += used ? (float)a[e] : 0.0f;
   }
