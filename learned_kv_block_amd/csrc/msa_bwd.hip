@@ -348,17 +348,21 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
             mma(qacc, ld8<T>(dSs + (32 * rq + l32) * LT + 16 * kc + 8 * h),
                 ld8<T>(KT + (32 * dq_t + l32) * LT + 16 * kc + 8 * h));
         }
-        // the lane's rows 32rq + 8j + 4h + 0..3: their slots in 16-byte reads
+        // into the Q tile, unused since the dK products (rows 32rq + drow(e, h))
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r0 = 32 * rq + 8 * j + 4 * h;
-          const i32x4 sl = *reinterpret_cast<const i32x4*>(slot_s + r0);
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            dqpart[((size_t)sl[x] * G + (r0 + x) % G) * D + 32 * dq_t + l32] =
-                cvt<T>(qacc[4 * j + x] * scale);
-        }
+        for (int e = 0; e < 16; ++e)
+          Qs[(32 * rq + drow(e, h)) * LK + 32 * dq_t + l32] = cvt<T>(qacc[e] * scale);
       }
+    }
+    __syncthreads();  // the item's dQ rows are complete
+    // each row's dQ goes out as the (query, slot) partial in whole-row chunks;
+    // an unused row writes the spare slot past the last
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int c = tid + NT * u;
+      const int rho = c / CH, dc = c % CH;
+      st8<T>(dqpart + ((size_t)slot_s[rho] * G + rho % G) * D + 8 * dc,
+             ld8<T>(Qs + rho * LK + 8 * dc));
     }
   }
   if (cur >= 0) flush(cur);
