@@ -697,27 +697,22 @@ dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
   constexpr int KCH = 128 * DI / 8 / 256;
   bf16x8 kraw[KCH];
   bf16x4 dlo[8], dhi[8];
+  // Loads without branches (a guarded load joins the unguarded path and the
+  // wait after the join drains every load in flight): a dS row holds
+  // ds_stride(N) >= N elements and key0 is a multiple of 4, so a run starting
+  // inside the row ends inside it; a run past the row reads the row's last run.
+  // Keys past N are after every query, so the select below zeroes their dS,
+  // and the K_idx row they meet (row N-1) is finite.
+  const int run_max = ds_stride(N) - 4;
   auto run = [&](const bf16* p, int key0) {  // 4 keys key0..key0+3 of the row (raw)
-    bf16x4 v;
-    if (key0 + 3 < N) {
-      v = ld4<bf16>(p + key0);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = key0 + e < N ? p[key0 + e] : (bf16)0.0f;
-    }
-    return v;
+    return ld4<bf16>(p + min(key0, run_max));
   };
   auto prefetch = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       const int x = tid + 256 * u, row = x / (DI / 8), c = x % (DI / 8);
-      const int j = kb * 128 + row;
-      if (j < N) {
-        kraw[u] = to_bf16x8<T>(kbase + (size_t)j * DI + 8 * c);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kraw[u][e] = (bf16)0.0f;
-      }
+      const int j = min(kb * 128 + row, N - 1);
+      kraw[u] = to_bf16x8<T>(kbase + (size_t)j * DI + 8 * c);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -792,34 +787,27 @@ dense_dk_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ q_idx,
   // next row tile (global -> registers): q_idx rows and the rows' dS on the block
   constexpr int QCH = RT * DI / 8 / 256, SCH = RT * 16 / 256;
   bf16x8 qraw[QCH], sraw[SCH];
+  // Loads without branches (a guarded load joins the unguarded path and the
+  // wait after the join drains every load in flight): rows past the chunk read
+  // its last row, and their q_idx rows are zeroed when the tile is stored, so
+  // they add nothing; dS runs past a row's ds_stride(N) elements read its last
+  // run (key0 is a multiple of 8): those keys are >= N, and their dk columns are
+  // never written.
+  const int srun_max = ds_stride(N) - 8;
   auto prefetch = [&](int rho0) {
 #pragma unroll
     for (int u = 0; u < QCH; ++u) {
-      const int x = tid + 256 * u, rr = x / (DI / 8), c = x % (DI / 8), rho = rho0 + rr;
-      if (rho < rows_b) {
-        const size_t row = ((size_t)b * Nq + t_begin + rho / Hkv) * Hkv + rho % Hkv;
-        qraw[u] = to_bf16x8<T>(q_idx + row * DI + 8 * c);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qraw[u][e] = (bf16)0.0f;
-      }
+      const int x = tid + 256 * u, rr = x / (DI / 8), c = x % (DI / 8);
+      const int rho = min(rho0 + rr, rows_b - 1);
+      const size_t row = ((size_t)b * Nq + t_begin + rho / Hkv) * Hkv + rho % Hkv;
+      qraw[u] = to_bf16x8<T>(q_idx + row * DI + 8 * c);
     }
 #pragma unroll
     for (int u = 0; u < SCH; ++u) {
-      const int x = tid + 256 * u, rr = x / 16, c = x % 16, rho = rho0 + rr;
-      const int key0 = blk * 128 + 8 * c;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sraw[u][e] = (bf16)0.0f;
-      if (rho < rows_b) {
-        const bf16* p = ds + ((size_t)b * rows_b + rho) * ds_stride(N);
-        if (key0 + 7 < N) {
-          sraw[u] = ld8<bf16>(p + key0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (key0 + e < N) sraw[u][e] = p[key0 + e];
-        }
-      }
+      const int x = tid + 256 * u, rr = x / 16, c = x % 16;
+      const int rho = min(rho0 + rr, rows_b - 1);
+      const bf16* p = ds + ((size_t)b * rows_b + rho) * ds_stride(N);
+      sraw[u] = ld8<bf16>(p + min(blk * 128 + 8 * c, srun_max));
     }
   };
   if (rho_first < rows_b) prefetch(rho_first);
@@ -828,7 +816,12 @@ dense_dk_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ q_idx,
 #pragma unroll
     for (int u = 0; u < QCH; ++u) {
       const int x = tid + 256 * u, rr = x / (DI / 8), c = x % (DI / 8);
-      *reinterpret_cast<bf16x8*>(qs + rr * LQ + 8 * c) = qraw[u];
+      bf16x8 v = qraw[u];
+      if (rho0 + rr >= rows_b) {  // a row past the chunk adds nothing
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f;
+      }
+      *reinterpret_cast<bf16x8*>(qs + rr * LQ + 8 * c) = v;
     }
 #pragma unroll
     for (int u = 0; u < SCH; ++u) {
