@@ -663,17 +663,21 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const T* p) {
 }
 
 // dq_idx rows of a chunk. Workgroup = 128 consecutive chunk rows (t, r) of one
-// batch; wave w takes rows 32w..32w+31 as the columns of D^T = K_idx^T . dS^T,
-// K_idx blocks staged through LDS. Keys after a row's query are masked here
-// (select, so unwritten parts of the dS rows are never used).
+// batch; wave w takes rows 32w..32w+31 as the columns of D^T = K_idx^T . dS^T.
+// Per 128-key block, the K_idx block and the rows' dS on it are loaded
+// row-contiguously (16 lanes per 256-byte dS row segment) one block ahead and
+// staged through LDS. Keys after a row's query are masked when the dS
+// fragments are read (select, so unwritten parts of the dS rows are never used).
 template <typename T, int DI>
 __global__ void __launch_bounds__(256)
 dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
                     T* __restrict__ dq, int N, int Nq, int q_start, int t_begin, int t_end,
                     int Hkv, int tiles_b, float scale) {
   constexpr int LK = DI + 8;
+  constexpr int LS = 128 + 8;  // row stride of the dS tile
   constexpr int DT = DI / 32;
   __shared__ __attribute__((aligned(16))) bf16 kt[128 * LK];
+  __shared__ __attribute__((aligned(16))) bf16 dst[128 * LS];
   const int rows_b = (t_end - t_begin) * Hkv;
   const int b = blockIdx.x / tiles_b, rho0 = (blockIdx.x % tiles_b) * 128;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -682,7 +686,6 @@ dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
   const int rc = min(rho, rows_b - 1);
   const int t = t_begin + rc / Hkv, r = rc % Hkv;
   const int i = q_start + t;
-  const bf16* dsrow = ds + ((size_t)b * rows_b + rc) * ds_stride(N);
   const int rlast = min(rho0 + 127, rows_b - 1);
   const int kb_last = (q_start + t_begin + rlast / Hkv) >> 7;
   const T* kbase = k_idx + (size_t)b * N * DI;
@@ -693,20 +696,17 @@ dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[dt][e] = 0.0f;
   }
-  // next block's K_idx chunks (global -> registers) and this lane's dS runs
+  // next block's K_idx chunks and dS row segments (global -> registers)
   constexpr int KCH = 128 * DI / 8 / 256;
-  bf16x8 kraw[KCH];
-  bf16x4 dlo[8], dhi[8];
+  constexpr int SCH = 128 * 16 / 256;
+  bf16x8 kraw[KCH], sraw[SCH];
   // Loads without branches (a guarded load joins the unguarded path and the
-  // wait after the join drains every load in flight): a dS row holds
-  // ds_stride(N) >= N elements and key0 is a multiple of 4, so a run starting
-  // inside the row ends inside it; a run past the row reads the row's last run.
-  // Keys past N are after every query, so the select below zeroes their dS,
-  // and the K_idx row they meet (row N-1) is finite.
-  const int run_max = ds_stride(N) - 4;
-  auto run = [&](const bf16* p, int key0) {  // 4 keys key0..key0+3 of the row (raw)
-    return ld4<bf16>(p + min(key0, run_max));
-  };
+  // wait after the join drains every load in flight): rows past the chunk read
+  // its last row (their dq_idx is never written); a dS row holds ds_stride(N)
+  // >= N elements and a segment starts at a multiple of 8, so a segment past
+  // the row reads the row's last one. Keys past N are after every query, so the
+  // select below zeroes their dS, and the K_idx row they meet (row N-1) is finite.
+  const int seg_max = ds_stride(N) - 8;
   auto prefetch = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
@@ -715,9 +715,10 @@ dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
       kraw[u] = to_bf16x8<T>(kbase + (size_t)j * DI + 8 * c);
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      dlo[c] = run(dsrow, kb * 128 + 16 * c + 4 * h);
-      dhi[c] = run(dsrow, kb * 128 + 16 * c + 8 + 4 * h);
+    for (int u = 0; u < SCH; ++u) {
+      const int x = tid + 256 * u, rr = x / 16, c = x % 16;
+      const bf16* p = ds + ((size_t)b * rows_b + min(rho0 + rr, rows_b - 1)) * ds_stride(N);
+      sraw[u] = ld8<bf16>(p + min(kb * 128 + 8 * c, seg_max));
     }
   };
   prefetch(0);
@@ -728,22 +729,29 @@ dense_dq_idx_kernel(const bf16* __restrict__ ds, const T* __restrict__ k_idx,
       const int x = tid + 256 * u, row = x / (DI / 8), c = x % (DI / 8);
       *reinterpret_cast<bf16x8*>(kt + row * LK + 8 * c) = kraw[u];
     }
-    bf16x8 bfr[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int key0 = kb * 128 + 16 * c + 4 * h;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {  // keys after the row's query are masked (select)
-        bfr[c][e] = key0 + e <= i ? dlo[c][e] : (bf16)0.0f;
-        bfr[c][4 + e] = key0 + 8 + e <= i ? dhi[c][e] : (bf16)0.0f;
-      }
+    for (int u = 0; u < SCH; ++u) {
+      const int x = tid + 256 * u, rr = x / 16, c = x % 16;
+      *reinterpret_cast<bf16x8*>(dst + rr * LS + 8 * c) = sraw[u];
     }
     __syncthreads();
     if (kb + 1 <= kb_last) prefetch(kb + 1);
+    // B fragments: the lane's row, keys {16c + 4h + 0..3, 16c + 8 + 4h + 0..3}
+    // (the k-set of the transposing read of K_idx); keys after the row's query
+    // are masked (select)
+    const bf16* srow = dst + (32 * wave + l32) * LS;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      const bf16x4 lo = ld4<bf16>(srow + 16 * c + 4 * h), hi = ld4<bf16>(srow + 16 * c + 8 + 4 * h);
+      const int key0 = kb * 128 + 16 * c + 4 * h;
+      bf16x8 bfr;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_tr<LK>(kt, c, dt, lane), bfr[c]);
+      for (int e = 0; e < 4; ++e) {
+        bfr[e] = key0 + e <= i ? lo[e] : (bf16)0.0f;
+        bfr[4 + e] = key0 + 8 + e <= i ? hi[e] : (bf16)0.0f;
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mma(acc[dt], frag_tr<LK>(kt, c, dt, lane), bfr);
     }
   }
   if (rho < rows_b) {
