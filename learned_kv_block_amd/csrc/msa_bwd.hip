@@ -225,8 +225,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   load_rows(i0);
   load_ents(min(i0 + 1, i1 - 1));
   for (int it = i0; it < i1; ++it) {
-    const int4 itm = items[it];
-    const int bkt = itm.x, start = itm.y, cnt = itm.z;
+    const int bkt = items[it].x;
     const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
     __syncthreads();  // every wave is done with the previous item's tiles
     if (bkt != cur) {  // uniform
@@ -512,8 +511,8 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   load_ents(min(i0 + 1, i1 - 1));
   for (int it = i0; it < i1; ++it) {
     const int4 itm = items[it];
-    const int bkt = itm.x, start = itm.y, cnt = itm.z;
-    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    const int bkt = itm.x, cnt = itm.z;
+    const int blk = bkt % nb, b = bkt / nbw / Hkv;
     __syncthreads();
     if (bkt != cur) {  // uniform
       if (cur >= 0) flush(cur);

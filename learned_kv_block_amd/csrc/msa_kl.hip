@@ -330,7 +330,6 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int Hq = Hkv * G;
   const size_t kvrow = (size_t)Hkv * D;
   bf16* const W = Wst[wave];
   const int qw0 = wave * QPW;  // first query of the wave in an item
@@ -426,7 +425,7 @@ kl_main_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const float inv_g = 1.0f / (float)G;
   for (int it = i0; it < i1; ++it) {
-    const int bkt = cur.x, start = cur.y, cnt = cur.z;
+    const int bkt = cur.x, cnt = cur.z;
     const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
     const int buf = (it - i0) & 1;
     const bool have_next = it + 1 < i1;
@@ -555,7 +554,7 @@ kl_reduce_kernel(const int32_t* __restrict__ ids, const float* __restrict__ kl_p
   red[threadIdx.x] = v;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
   if (threadIdx.x == 0) block_sums[blockIdx.x] = red[0];
@@ -570,7 +569,7 @@ kl_mean_kernel(const float* __restrict__ block_sums, int64_t nblocks, int64_t nr
   red[threadIdx.x] = v;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
     __syncthreads();
   }
   if (threadIdx.x == 0) *kl_mean = nrows > 0 ? (float)(red[0] / (double)nrows) : 0.0f;
