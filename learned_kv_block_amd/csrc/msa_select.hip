@@ -348,7 +348,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-constexpr int kTopkMax = 32;
 constexpr int kCandMax = 128;  // candidates ranked exactly (two passes of 64)
 
 // One (query, group) row with L candidate blocks, VV*64 >= L: lane l holds
