@@ -472,6 +472,10 @@ def main():
     }
     if kernels:
         line["kernel_ms"] = kernels
+    if decode:
+        line["metric"] = "MSA decode query-tokens/s (one query per sequence)"
+    elif cfg.name != "skewed_n131072":
+        line["metric"] = f"MSA-layer prefill query-tokens/s ({cfg.name}, 1 GPU)"
     if args.fp8:
         line["metric"] = ("MSA-layer prefill query-tokens/s with the FP8 (E4M3) index branch"
                           if not decode else "MSA decode query-tokens/s with the FP8 index branch")
