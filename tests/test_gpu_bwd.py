@@ -43,6 +43,11 @@ CASES = [
          num_kv_heads=4, topk=6),
     _cfg("f32_g2_short", seqlen_kv=300, seqlen_q=300, num_q_heads=4, num_kv_heads=2,
          head_dim=64, idx_dim=32, topk=2, dtype=si.F32, scale=1.0),
+    # bf16 G=2: d=64 with Hkv=8, and d=128 as a chunked prefill starting inside a block
+    _cfg("bf16_g2_d64_hkv8", seqlen_kv=700, seqlen_q=700, num_q_heads=16, num_kv_heads=8,
+         head_dim=64, topk=3),
+    _cfg("bf16_g2_chunk", seqlen_kv=1300, seqlen_q=500, q_start=800, num_q_heads=8,
+         num_kv_heads=4, topk=5),
 ]
 
 
@@ -138,6 +143,8 @@ IDX_CASES = [
          num_q_heads=16, num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
     _cfg("bf16_decode_idx", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, num_q_heads=64,
          num_kv_heads=4, topk=6),
+    # one group (Hkv = 1): every index row shares the one k_idx block accumulator
+    _cfg("bf16_hkv1_idx", seqlen_kv=900, seqlen_q=900, num_q_heads=16, num_kv_heads=1, topk=5),
 ]
 
 
