@@ -58,6 +58,11 @@ SMALL = [
     # two queries per sequence, G=8, d=64: one-wave attention on bucketed items
     _small("bf16_g8_q2", batch=2, seqlen_kv=2000, seqlen_q=2, q_start=1998, num_q_heads=16,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
+    # KL main pass (persistent kernel) at G=8 with d=128, and at G=16 with d_idx=32
+    _small("bf16_g8_d128_kl", seqlen_kv=1100, seqlen_q=1100, num_q_heads=32, num_kv_heads=4,
+           topk=5, with_kl=True),
+    _small("bf16_g16_di32_kl", seqlen_kv=800, seqlen_q=800, num_q_heads=32, num_kv_heads=2,
+           idx_dim=32, topk=4, with_kl=True),
     # fp32 decode, ragged last block
     _small("f32_decode_b2", batch=2, seqlen_kv=1500, seqlen_q=1, q_start=1499, num_q_heads=8,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=4, dtype=si.F32, scale=1.0,
@@ -148,7 +153,8 @@ def test_empty_inputs():
 # tests): the arithmetic is the same, but the two builds may fuse a multiply-add
 # differently (seen: a few ulps, <= 4e-7 on rows up to 0.4), so the bar is
 # relative 1e-5, far below any real divergence.
-KL_NO_DL = ["bf16_g16_ragged", "bf16_g8_chunk", "bf16_g4_kall", "bf16_decode_b3", "f32_g1_k1"]
+KL_NO_DL = ["bf16_g16_ragged", "bf16_g8_chunk", "bf16_g8_d128_kl", "bf16_g4_kall",
+            "bf16_decode_b3", "f32_g1_k1"]
 
 
 @pytest.mark.parametrize("name", KL_NO_DL)
