@@ -178,3 +178,24 @@ def test_idx_bwd_every_row(cfg):
     _check("dq_idx", dqi.float().cpu().numpy().reshape(rq.shape), rq, t, rep)
     _check("dk_idx", dki.float().cpu().numpy(), rk, t, rep)
     print(f"[idx_bwd] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
+def test_bwd_empty_rows():
+    """No query row: dq and dq_idx are empty; dk, dv and dk_idx (allocated uninitialised
+    by the binding) come back zero, since the calls overwrite them."""
+    import learned_kv_block_amd as msa
+    cfg = _cfg("bf16_empty_bwd", seqlen_kv=512, seqlen_q=0, topk=4)
+    x = parity.gpu_inputs(cfg, names=("q", "k", "v", "q_idx", "k_idx", "dout"))
+    sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, num_q_heads=cfg.num_q_heads,
+                         head_dim=cfg.head_dim)
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], idx_dim=cfg.idx_dim)
+    dq, dk, dv = msa.msa_attn_bwd(x["q"], x["k"], x["v"], sel["ids"], out, lse, x["dout"],
+                                  idx_dim=cfg.idx_dim)
+    dl = torch.zeros((cfg.batch, 0, cfg.num_kv_heads, cfg.topk, 128), dtype=torch.float32,
+                     device=x["q"].device)
+    dqi, dki = msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], dl,
+                               num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and dqi.numel() == 0
+    assert dk.shape == x["k"].shape and dv.shape == x["v"].shape and dki.shape == x["k_idx"].shape
+    assert bool((dk == 0).all()) and bool((dv == 0).all()) and bool((dki == 0).all())
