@@ -426,11 +426,10 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
                int nslots, float coef) {
   constexpr int Q = 32;         // queries per item
   constexpr int LKT = 128 + 4;  // row stride of K_idx^T [DI][128] and of dl [Q][128]
-  constexpr int LQ = Q + 4;     // row stride of dl^T [128][Q] and Q_idx^T [DI][Q]
+  constexpr int LQ = Q + 4;     // row stride of Q_idx^T [DI][Q]
   constexpr int DIT = DI / 32;
   __shared__ __attribute__((aligned(16))) float KIT[DI * LKT];
   __shared__ __attribute__((aligned(16))) float DLs[Q * LKT];
-  __shared__ __attribute__((aligned(16))) float DLT[128 * LQ];
   __shared__ __attribute__((aligned(16))) float QIT[DI * LQ];
   __shared__ __attribute__((aligned(16))) int slot_s[Q];  // (query, slot) of each query's partial
 
@@ -445,7 +444,7 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  f32x16 dka[DIT];  // dk_idx of keys 32w + drow(e, h), d columns 32dt + l32
+  f32x16 dka[DIT];  // dk_idx^T: d rows 32dt + drow(e, h), key column 32w + l32
   auto zero_acc = [&]() {
 #pragma unroll
     for (int dt = 0; dt < DIT; ++dt)
@@ -454,14 +453,13 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   };
   auto flush = [&](int bkt) {
     const int blk = bkt % nb, b = bkt / nbw / Hkv;
+    const int key = blk * 128 + 32 * w + l32;
+    if (key >= N) return;
+    float* const row = dk_acc + ((size_t)b * N + key) * DI;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = blk * 128 + 32 * w + drow(e, h);
-      if (key >= N) continue;
+    for (int dt = 0; dt < DIT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DIT; ++dt)
-        unsafeAtomicAdd(dk_acc + ((size_t)b * N + key) * DI + 32 * dt + l32, dka[dt][e] * coef);
-    }
+      for (int e = 0; e < 16; ++e) unsafeAtomicAdd(row + 32 * dt + drow(e, h), dka[dt][e] * coef);
   };
 
   // the item's dl rows (4 floats per chunk) and Q_idx rows, loaded one item
@@ -525,14 +523,12 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
       }
     }
 #pragma unroll
-    for (int u = 0; u < DU; ++u) {  // dl rows (zero past cnt) and dl^T
+    for (int u = 0; u < DU; ++u) {  // dl rows (zero past cnt)
       const int c = tid + 256 * u;
       const int j = c / 32, o4 = c % 32;
       vec4<float> val = dlr[u];
       if (j >= cnt) val = vec4<float>{0.0f, 0.0f, 0.0f, 0.0f};
       st4<float>(DLs + j * LKT + 4 * o4, val);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) DLT[(4 * o4 + e) * LQ + j] = val[e];
     }
 #pragma unroll
     for (int u = 0; u < QU; ++u) {  // Q_idx^T of the item's queries (zero past cnt)
@@ -564,13 +560,17 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
           dqpart[(size_t)sl[x] * DI + 32 * w + l32] = acc[4 * jj + x] * coef;
       }
     }
-    // dk_idx of keys 32w..: dl^T (keys x Q) Q_idx (Q x DI)
+    // dk_idx^T of keys 32w..: Q_idx^T (DI x Q) dl (Q x keys); the B fragment is 8
+    // queries of the lane's key column, read from the row-major dl tile (consecutive
+    // lanes, consecutive keys: no bank conflicts)
 #pragma unroll
     for (int kc = 0; kc < Q / 16; ++kc) {
-      const vec8<float> a = ld8<float>(DLT + (32 * w + l32) * LQ + 16 * kc + 8 * h);
+      vec8<float> bcol;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bcol[e] = DLs[(16 * kc + 8 * h + e) * LKT + 32 * w + l32];
 #pragma unroll
       for (int dt = 0; dt < DIT; ++dt)
-        mma(dka[dt], a, ld8<float>(QIT + (32 * dt + l32) * LQ + 16 * kc + 8 * h));
+        mma(dka[dt], ld8<float>(QIT + (32 * dt + l32) * LQ + 16 * kc + 8 * h), bcol);
     }
   }
   if (cur >= 0) flush(cur);
