@@ -27,15 +27,32 @@ sys.path.insert(0, ROOT)
 PEAK_BF16 = 2.5e15  # dense bf16 MFMA, MI355X
 PEAK_HBM = 8.0e12   # bytes/s
 PEAK_FP8 = 5.0e15   # dense fp8 MFMA, MI355X
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_skewed_n131072_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "learned_kv_block_amd", "csrc", f)
-                  for f in ("msa_attn.hip", "msa_internal.hpp")]
+CSRC = os.path.join(ROOT, "learned_kv_block_amd", "csrc")
+# Per-kernel HBM counter record (FETCH_SIZE / WRITE_SIZE per dispatch, calibrated on a copy),
+# written by `bench.py --ingest-counters`; an entry is used only while its kernel's source is
+# unchanged.
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.json")
 
 
-def kernel_source_hash() -> str:
+# rocprofv3 kernel-name fragment -> (timer name, source files whose hash ties the counters to
+# the code that was measured)
+KERNEL_FILES = {
+    "index_blockmax_kernel": ("index_blockmax", ["msa_select.hip"]),
+    "index_blockmax_fp8_kernel": ("index_fp8", ["msa_fp8.hip"]),
+    "topk_kernel": ("topk", ["msa_select.hip"]),
+    "bucket_hist_kernel": ("bucket_hist", ["msa_attn.hip"]),
+    "bucket_scatter_kernel": ("bucket_scatter", ["msa_attn.hip"]),
+    "work_items_kernel": ("work_items", ["msa_attn.hip"]),
+    "sparse_attn_pipe_kernel": ("sparse_attn", ["msa_attn.hip"]),
+    "combine_local_kernel": ("combine", ["msa_attn.hip"]),
+}
+
+
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+    for f in list(files) + ["msa_internal.hpp"]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -100,6 +117,15 @@ def kv_outer_bytes(cfg, ids):
     return n_trip * (2 * G * D * 2 + G * 4) + n_bkt * 2 * 128 * D * 2, n_trip, n_bkt
 
 
+def host_cpus():
+    """(CPUs this process may run on, CPUs the host reports)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return avail, os.cpu_count() or avail
+
+
 def cpu_baseline(cfg, seconds_target=15.0):
     """fp64 oracle (select + attention) on a seeded sample of query rows, timed on the host."""
     import numpy as np
@@ -108,6 +134,7 @@ def cpu_baseline(cfg, seconds_target=15.0):
     import seeded_inputs as si
 
     threads = oracle.threads()
+    avail, reported = host_cpus()
     k = si.host_tensor(cfg, "k")
     v = si.host_tensor(cfg, "v")
     k_idx = si.host_tensor(cfg, "k_idx")
@@ -129,9 +156,11 @@ def cpu_baseline(cfg, seconds_target=15.0):
     rows = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=n))
     dt = run(rows)
     return {"value": n / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "host_cpus_available": avail, "host_cpus_reported": reported,
             "cpu_model": cpu_model(),
             "sample": f"{n} seeded uniformly random query rows of the same workload "
-                      f"(rows are independent; fp64 select + attention in {dt:.1f} s)"}
+                      f"(rows are independent; fp64 select + attention in {dt:.1f} s, "
+                      f"OpenMP over rows on {threads} threads)"}
 
 
 def dense_flops(cfg):
@@ -277,6 +306,106 @@ def dense_main(args):
     print(json.dumps(line), flush=True)
 
 
+def step_work(cfg, ids):
+    """Algorithmic work of each kernel of one prefill / decode step (bf16), from the GPU's
+    own selection. Returns {timer name: dict(bound, flops | bytes, what)}."""
+    import torch
+    B, Nq, Hkv, G, D, K = (cfg.batch, cfg.seqlen_q, cfg.num_kv_heads, cfg.group_size,
+                           cfg.head_dim, cfg.topk)
+    Hq = Hkv * G
+    f_idx, f_attn, f_loc = effective_flops(cfg, ids)
+    kv_bytes, n_trip, n_bkt = kv_outer_bytes(cfg, ids)
+    i = torch.arange(Nq, device=ids.device, dtype=torch.int64) + cfg.q_start
+    L = i // 128
+    # Top-k reads the block scores of blocks 0..L-1 of rows with more than k visible blocks
+    # (the local block is forced) and writes k ids per (query, group)
+    m_read = 4 * B * Hkv * int(torch.where(L + 1 > K, L, torch.zeros_like(L)).sum().item())
+    rows = B * Nq * Hkv
+    n_sel = int((ids >= 0).sum().item())
+    rows_q = B * Nq
+    work = {
+        "index_blockmax": dict(bound="mfma", flops=f_idx,
+                               what="2*d_idx*Hkv flops per causally visible (query, key)"),
+        "topk": dict(bound="hbm", bytes=m_read + rows * K * 4,
+                     what="block scores of blocks 0..L-1 read, k int32 ids written per row"),
+        # histogram and scatter read the ids; the scatter writes one entry per selected
+        # non-local slot; work items are 16 B each (counted from the entries: 16 queries/item)
+        "bucketing": dict(bound="hbm", bytes=2 * rows * K * 4 + n_trip * 4 + (n_trip // 16) * 16,
+                          what="ids read twice, entries and work items written"),
+        "sparse_attn": dict(bound="mfma", flops=f_attn - f_loc,
+                            what="4*d flops per (query, head, key) of the non-local selected "
+                                 "blocks", side_bytes=kv_bytes, triples=n_trip, buckets=n_bkt,
+                            min_bytes=rows_q * Hq * D * 2 + n_bkt * 2 * 128 * D * 2,
+                            min_bytes_what="each query's Q rows once + each selected K/V block "
+                                           "once"),
+        "combine": dict(bound="hbm",
+                        bytes=n_trip * G * (D * 2 + 4) + rows_q * Hq * D * 2 * 2 + rows_q * Hq * 4
+                        + rows * K * 4,
+                        flops=f_loc,
+                        what="partials (bf16 O + fp32 LSE) read, Q read and O written once, "
+                             "LSE written; the local block's attention (flops) runs here"),
+    }
+    return work, f_idx, f_attn, f_loc, n_sel
+
+
+def load_traffic(cfg):
+    """{timer name: bytes per launch} from the counter record of this workload, for kernels
+    whose source is unchanged since the counters were taken."""
+    path = traffic_file(cfg.name)
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    out = {}
+    for frag, (name, files) in KERNEL_FILES.items():
+        e = rec.get("kernels", {}).get(frag)
+        if e and e.get("source_hash") == source_hash(files):
+            out[name] = e["bytes_per_launch"]
+    return out
+
+
+def ingest_counters(fetch_csv, write_csv, workload, commands):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs,
+    scaled by what the same counters read for the 1 GiB device copy of --copy-calibration,
+    written to profiles/hbm_counters_<workload>.json."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(lambda: [0.0, set()])
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            acc[r["Kernel_Name"]][0] += float(r["Counter_Value"])
+            acc[r["Kernel_Name"]][1].add(r["Dispatch_Id"])
+        return {k: (v[0], len(v[1])) for k, v in acc.items()}
+
+    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    copy = [k for k in fe if "copyBuffer" in k or "copy_kernel" in k]
+    gib_kib = float(1 << 20)
+    # the largest single copy dispatch is the 1 GiB calibration copy
+    fcopy = max(fe[k][0] / fe[k][1] for k in copy)
+    wcopy = max(wr[k][0] / wr[k][1] for k in copy if k in wr)
+    fs, ws = gib_kib / fcopy, gib_kib / wcopy
+    kernels = {}
+    for frag, (name, files) in KERNEL_FILES.items():
+        hits = [k for k in fe if frag in k]
+        if not hits:
+            continue
+        k = hits[0]
+        f, n = fe[k]
+        w, _ = wr.get(k, (0.0, n))
+        kernels[frag] = {"kernel": k[:120], "timer": name, "dispatches": n,
+                         "fetch_kib_raw": f / n, "write_kib_raw": w / n,
+                         "read_bytes": f / n * fs * 1024, "write_bytes": w / n * ws * 1024,
+                         "bytes_per_launch": (f / n * fs + w / n * ws) * 1024,
+                         "source_hash": source_hash(files)}
+    rec = {"workload": workload, "fetch_scale": fs, "write_scale": ws,
+           "calibration": "1 GiB device copy in the same process (bench.py --copy-calibration)",
+           "commands": commands, "kernels": kernels}
+    json.dump(rec, open(traffic_file(workload), "w"), indent=1)
+    print(json.dumps({k: round(v["bytes_per_launch"] / 1e9, 3) for k, v in kernels.items()}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,23 +427,32 @@ def main():
                     help="select with the FP8 (E4M3) index path: Q_idx quantized every step, "
                          "K_idx every step for prefill and once (as a cache holds it) for "
                          "decode; reports the churn against the bf16 selection")
-    ap.add_argument("--breakdown", action="store_true", help="also time every kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for HBM counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the per-kernel HBM counter record of --workload from two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--commands", nargs="*", default=[],
+                    help="the profiler commands recorded with --ingest-counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the MSA layer on a single "
               "MI355X; --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
-
-    if args.dense:
-        dense_main(args)
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, args.workload or "skewed_n131072", args.commands)
         return
 
     import torch
 
     import learned_kv_block_amd as msa
     import seeded_inputs as si
+
+    # the measurement build: the same kernels, with HIP events recorded around each launch
+    msa.use_timed_build()
+    if args.dense:
+        dense_main(args)
+        return
 
     cfg = si.CONFIGS[args.workload or "skewed_n131072"]
     torch.cuda.set_device(0)
@@ -388,15 +526,13 @@ def main():
     if ids is None:
         ids = step()
         torch.cuda.synchronize()
-    f_idx, f_attn, f_loc = effective_flops(cfg, ids)
-    kv_bytes, n_trip, n_bkt = kv_outer_bytes(cfg, ids)
-    # FLOPs of the KV-outer kernel: the local blocks run in the combine (bf16)
-    f_kv = f_attn - f_loc if cfg.dtype == si.BF16 else f_attn
+    work, f_idx, f_attn, f_loc, n_sel = step_work(cfg, ids)
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    with msa.KernelTimer("sparse_attn", max_launches=args.steps) as kt:
+    # every kernel of the step is timed by HIP events on its launch stream
+    with msa.KernelTimer(None, max_launches=max(64, args.steps * 64)) as kt:
         t0 = time.perf_counter()
         ev[0].record()
         for j in range(args.steps):
@@ -409,41 +545,63 @@ def main():
     tokens = cfg.batch * cfg.seqlen_q
     value = tokens * args.steps / elapsed
 
+    per = kt.per_kernel  # name -> (total ms, launches)
+    kernel_ms = {n: round(v[0] / args.steps, 4) for n, v in per.items()}  # per step
+    launches = {n: v[1] for n, v in per.items()}
+    bucket_names = ("bucket_hist", "bucket_scan", "bucket_scatter", "work_items")
+    traffic = {} if args.fp8 else load_traffic(cfg)
     kernels = {}
-    if args.breakdown:
-        names = (["quantize_fp8", "index_fp8"] if args.fp8 else ["index_blockmax"]) + [
-            "topk", "bucket_hist", "bucket_scan", "bucket_scatter", "work_items", "sparse_attn",
-            "combine"]
-        if args.kl:
-            names += ["kl_idx_stats", "kl_idx_lse", "kl_main", "kl_reduce"]
-        if args.bwd:
-            names += ["attn_bwd"] + (["idx_bwd"] if args.kl else [])
-        for name in names:
-            with msa.KernelTimer(name, max_launches=2) as t:
-                step()
-                step()
-                torch.cuda.synchronize()
-            kernels[name] = round(t.avg_ms, 4)
-        print(f"[bench] kernels {kernels}", file=sys.stderr, flush=True)
-
-    attn_ms = kt.avg_ms
-    achieved_flops = f_kv / (attn_ms * 1e-3)
-    achieved = kv_bytes / (attn_ms * 1e-3)
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
-        # The counters were taken on one workload: they apply to no other.
-        if (rec.get("kernel_source_hash") == kernel_source_hash()
-                and rec.get("workload") == cfg.name and not args.fp8):
-            traffic = rec.get("bytes_per_launch")
-    # The KV-outer kernel is bound by its side traffic (gathered Q rows and written
-    # partials), not by its contraction: its MFMA share is reported beside it.
-    roofline = {"bound": "hbm", "kernel": "sparse_attn", "achieved": achieved / 1e9,
-                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": achieved / PEAK_HBM,
-                "traffic": traffic, "avg_ms": attn_ms, "launches": kt.launches,
-                "bytes_per_launch": kv_bytes, "triples": n_trip, "buckets": n_bkt,
-                "flops_per_launch": f_kv, "mfma_tflops": achieved_flops / 1e12,
-                "mfma_frac": achieved_flops / PEAK_BF16}
+    for name, w in work.items():
+        if name == "bucketing":
+            ms = sum(kernel_ms.get(n, 0.0) for n in bucket_names)
+            nl = max([launches.get(n, 0) for n in bucket_names] + [0])
+            cbytes = (sum(traffic[n] for n in bucket_names if n in traffic)
+                      if all(n in traffic for n in ("bucket_hist", "bucket_scatter", "work_items"))
+                      else None)
+        else:
+            src = "index_fp8" if (name == "index_blockmax" and args.fp8) else name
+            ms = kernel_ms.get(src, 0.0)
+            nl = launches.get(src, 0)
+            cbytes = traffic.get(src)
+        if ms <= 0.0:
+            continue
+        e = {"ms": ms, "launches_per_step": nl / max(1, args.steps), "bound": w["bound"],
+             "what": w["what"]}
+        if w["bound"] == "mfma":
+            peak = PEAK_FP8 if (name == "index_blockmax" and args.fp8) else PEAK_BF16
+            e.update(flops=w["flops"], achieved_tflops=w["flops"] / (ms * 1e-3) / 1e12,
+                     peak_tflops=peak / 1e12, frac=w["flops"] / (ms * 1e-3) / peak)
+        else:
+            e.update(bytes=w["bytes"], achieved_gbs=w["bytes"] / (ms * 1e-3) / 1e9,
+                     peak_gbs=PEAK_HBM / 1e9, frac=w["bytes"] / (ms * 1e-3) / PEAK_HBM)
+            if "flops" in w:
+                e["flops"] = w["flops"]
+        for extra in ("side_bytes", "triples", "buckets", "min_bytes", "min_bytes_what"):
+            if extra in w:
+                e[extra] = w[extra]
+        e["counter_bytes"] = cbytes
+        if cbytes is not None and "min_bytes" in w:
+            e["counter_over_min_bytes"] = cbytes / w["min_bytes"]
+        kernels[name] = e
+    for n, ms in kernel_ms.items():  # training-side kernels and anything not tabled above
+        if n not in kernels and n not in bucket_names and not (n == "index_fp8" and args.fp8):
+            kernels[n] = {"ms": ms, "launches_per_step": launches[n] / max(1, args.steps)}
+    # the headline roofline is that of the step's dominant tabled kernel
+    dom = max((n for n in kernels if "bound" in kernels[n]), key=lambda n: kernels[n]["ms"])
+    d = kernels[dom]
+    if d["bound"] == "mfma":
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": d["achieved_tflops"],
+                    "peak": d["peak_tflops"], "unit": "TFLOP/s", "frac": d["frac"],
+                    "traffic": d["counter_bytes"], "avg_ms": d["ms"],
+                    "launches": launches.get(dom, 0), "flops_per_launch": d["flops"]}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": d["achieved_gbs"],
+                    "peak": d["peak_gbs"], "unit": "GB/s", "frac": d["frac"],
+                    "traffic": d["counter_bytes"], "avg_ms": d["ms"],
+                    "launches": launches.get(dom, 0), "bytes_per_launch": d["bytes"]}
+    for extra in ("side_bytes", "min_bytes", "counter_over_min_bytes"):
+        if extra in d:
+            roofline[extra] = d[extra]
     line = {
         "metric": "MSA-layer prefill query-tokens/s at N=128K (1 GPU) + % bf16 MFMA peak",
         "value": value,
@@ -468,10 +626,9 @@ def main():
         "attn_flops_per_step": f_attn,
         "attn_local_flops_per_step": f_loc,
         "mfma_frac_effective": (f_idx + f_attn) / (ms_per_step * 1e-3) / PEAK_BF16,
+        "kernels": kernels,
         "roofline": roofline,
     }
-    if kernels:
-        line["kernel_ms"] = kernels
     if decode:
         line["metric"] = "MSA decode query-tokens/s (one query per sequence)"
     elif cfg.name != "skewed_n131072":
@@ -480,9 +637,6 @@ def main():
         line["metric"] = ("MSA-layer prefill query-tokens/s with the FP8 (E4M3) index branch"
                           if not decode else "MSA decode query-tokens/s with the FP8 index branch")
         line["config"]["index_dtype"] = "fp8_e4m3"
-        if "index_fp8" in kernels:
-            line["index_fp8_tflops"] = f_idx / (kernels["index_fp8"] * 1e-3) / 1e12
-            line["index_fp8_frac"] = f_idx / (kernels["index_fp8"] * 1e-3) / PEAK_FP8
         # churn of the FP8 selection against the bf16 one on the same inputs
         s16 = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, q_start=cfg.q_start,
                              want_margin=True, num_q_heads=cfg.num_q_heads,
@@ -490,13 +644,14 @@ def main():
         ids8 = select()["ids"]
         changed = (s16["ids"] != ids8).any(dim=-1)
         small = torch.isfinite(s16["margin"]) & (s16["margin"] < 0.03)
+        big = torch.isfinite(s16["margin"]) & (s16["margin"] >= 0.1)
         line["fp8_churn"] = {
             "changed_share": float(changed.float().mean()),
-            "changed_share_margin_lt_0.03": float(changed[small].float().mean()) if bool(small.any()) else 0.0,
-            "changed_share_margin_ge_0.1": float(changed[torch.isfinite(s16["margin"]) &
-                                                         (s16["margin"] >= 0.1)].float().mean())
-            if bool((s16["margin"] >= 0.1).any()) else 0.0}
-        del s16, ids8, changed, small
+            "changed_share_margin_lt_0.03":
+                float(changed[small].float().mean()) if bool(small.any()) else 0.0,
+            "changed_share_margin_ge_0.1":
+                float(changed[big].float().mean()) if bool(big.any()) else 0.0}
+        del s16, ids8, changed, small, big
     if args.kl:
         line["metric"] = "MSA-layer training step (select + attention + KL align) query-tokens/s"
         line["config"]["kl"] = True
@@ -508,8 +663,9 @@ def main():
         # recomputed S and P, dP, dV, dK, dQ: five products of the forward's two,
         # on every selected (query, head, key) including the local blocks
         line["attn_bwd_flops_per_step"] = 2.5 * f_attn
-        if "attn_bwd" in kernels:
-            line["attn_bwd_mfma_frac"] = 2.5 * f_attn / (kernels["attn_bwd"] * 1e-3) / PEAK_BF16
+        if "attn_bwd" in kernel_ms:
+            line["attn_bwd_mfma_frac"] = 2.5 * f_attn / (kernel_ms["attn_bwd"] * 1e-3) / PEAK_BF16
+    print(f"[bench] kernels {kernel_ms}", file=sys.stderr, flush=True)
     del x, ws_sel, ws_attn, ws_kl, ws_bwd, ws_ibwd, out, lse, kz
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -357,24 +357,6 @@ msa_status msa_select_fp8(const msa_shape* shape, const uint8_t* q8, const int32
 /* Static, NUL-terminated description of a status code. */
 const char* msa_status_string(msa_status status);
 
-/*
- * Kernel timing for measurement tools. msa_prof_begin(kernel, n) makes the
- * library record a HIP event pair on the launch stream around each of the
- * next n launches of kernel `kernel` (MSA_K_*); msa_prof_end waits for them
- * and returns the summed duration in milliseconds and the number of launches
- * timed. The hook is process-wide and not meant for concurrent callers.
- */
-enum {
-  MSA_K_INDEX_BLOCKMAX = 0, MSA_K_TOPK = 1, MSA_K_BUCKET_HIST = 2, MSA_K_BUCKET_SCAN = 3,
-  MSA_K_BUCKET_SCATTER = 4, MSA_K_WORK_ITEMS = 5, MSA_K_SPARSE_ATTN = 6, MSA_K_COMBINE = 7,
-  MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
-  MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_DENSE_LSE = 14, MSA_K_KL_DENSE = 15,
-  MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_INDEX_FP8 = 18, MSA_K_QUANTIZE_FP8 = 19,
-  MSA_K_KL_DENSE_CHAIN = 20, MSA_K_COUNT = 21
-};
-msa_status msa_prof_begin(int kernel, int max_launches);
-msa_status msa_prof_end(float* total_ms, int* launches);
-
 #ifdef __cplusplus
 }
 #endif

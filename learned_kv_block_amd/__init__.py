@@ -35,6 +35,8 @@ import torch  # noqa: F401  (loads the HIP runtime that libmsa.so binds to)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsa.so")
+# the same kernel and API objects linked with the kernel-timing hook (include/msa_timing.h)
+TIMED_LIB_PATH = os.path.join(_HERE, "libmsa_timed.so")
 
 MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
 MSA_F32, MSA_BF16 = 0, 1
@@ -45,8 +47,8 @@ KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatt
            "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8", "kl_dense_chain"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
-           "msa_index_quantize_fp8", "msa_select_fp8",
-           "msa_status_string", "msa_prof_begin", "msa_prof_end"]
+           "msa_index_quantize_fp8", "msa_select_fp8", "msa_status_string"]
+TIMING_EXPORTS = ["msa_prof_begin", "msa_prof_end"]
 
 
 class MsaShape(ctypes.Structure):
@@ -62,16 +64,28 @@ class MsaError(RuntimeError):
 
 
 _lib = None
+_timed = False
+
+
+def use_timed_build() -> None:
+    """Route every call through libmsa_timed.so, the measurement build whose launches can be
+    timed with KernelTimer. Must be called before the first call into the library."""
+    global _timed
+    if _lib is not None and not _timed:
+        raise RuntimeError("the product library is already loaded")
+    _timed = True
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libmsa.so (raises if it has not been built)."""
+    """The loaded libmsa.so (libmsa_timed.so after use_timed_build()); raises if it has not
+    been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+        path = TIMED_LIB_PATH if _timed else LIB_PATH
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python learned_kv_block_amd/build.py` (or __graft_entry__.build())")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         P, S = ctypes.c_void_p, ctypes.POINTER(MsaShape)
         L.msa_workspace_size.argtypes = [S, ctypes.c_int]
         L.msa_workspace_size.restype = ctypes.c_size_t
@@ -89,13 +103,16 @@ def lib() -> ctypes.CDLL:
         L.msa_select_fp8.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
                   "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
-                  "msa_index_quantize_fp8", "msa_select_fp8",
-                  "msa_prof_begin", "msa_prof_end"):
+                  "msa_index_quantize_fp8", "msa_select_fp8"):
             getattr(L, f).restype = ctypes.c_int
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
-        L.msa_prof_begin.argtypes = [ctypes.c_int, ctypes.c_int]
-        L.msa_prof_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int)]
+        if _timed:
+            L.msa_prof_begin.argtypes = [ctypes.c_int, ctypes.c_int]
+            L.msa_prof_end.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_int)]
+            L.msa_prof_begin.restype = ctypes.c_int
+            L.msa_prof_end.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -127,10 +144,36 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _check(t: torch.Tensor, name: str, ndim: int):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
     if t.dim() != ndim or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor, got {tuple(t.shape)}")
+
+
+def _expect(t: torch.Tensor, name: str, shape, dtype=None):
+    """t must be a contiguous tensor of `shape` (None leaves a dimension free) and, when given,
+    of `dtype`. The library sees raw pointers only, so every size it derives from the shape
+    descriptor must match the buffers it is handed."""
+    _check(t, name, len(shape))
+    for ax, (got, want) in enumerate(zip(t.shape, shape)):
+        if want is not None and got != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}; dimension {ax} must be {want}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _on_device(*tensors):
+    """Every tensor must live on the same GPU (checked after the shapes and dtypes)."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("every tensor must be a device tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices: {dev} and {t.device}")
 
 
 def _stream(t: torch.Tensor):
@@ -142,6 +185,10 @@ def _workspace(shape: MsaShape, op: int, device, workspace: Optional[torch.Tenso
     if n == 0:
         return None, 0
     if workspace is not None:
+        if not workspace.is_cuda or workspace.device != torch.device(device):
+            raise ValueError(f"workspace must be a device tensor on {device}")
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
         if workspace.numel() * workspace.element_size() < n:
             raise ValueError(f"workspace of {workspace.numel()} bytes < {n} required")
         return workspace, workspace.numel() * workspace.element_size()
@@ -165,9 +212,10 @@ def msa_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_start: int
     Returns dict(ids [B, Nq, Hkv, topk] int32, block_scores [B, Nq, Hkv, nb] fp32 (opt),
     margin [B, Nq, Hkv] fp32 (opt)). num_q_heads / head_dim only enter the shape check."""
     _check(q_idx, "q_idx", 4)
-    _check(k_idx, "k_idx", 3)
+    B, Nq, Hkv, DI = q_idx.shape
+    _expect(k_idx, "k_idx", (B, None, DI), q_idx.dtype)
+    _on_device(q_idx, k_idx)
     sh = shape_for(q_idx, k_idx, topk, q_start, num_q_heads, head_dim)
-    B, Nq, Hkv, _ = q_idx.shape
     nb = (k_idx.shape[1] + 127) // 128
     dev = q_idx.device
     ids = torch.empty((B, Nq, Hkv, topk), dtype=torch.int32, device=dev)
@@ -191,10 +239,17 @@ def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: t
                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """Sparse attention over the selected blocks. q [B, Nq, Hq, d], k/v [B, N, Hkv, d],
     block_ids [B, Nq, Hkv, topk]. Returns (out [B, Nq, Hq, d], lse [B, Nq, Hq] fp32)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (block_ids, "block_ids")):
-        _check(t, n, 4)
+    _check(q, "q", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
     N, Hkv = k.shape[1], k.shape[2]
+    _expect(v, "v", tuple(k.shape), q.dtype)
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    if out is not None:
+        _expect(out, "out", tuple(q.shape), q.dtype)
+    if lse is not None:
+        _expect(lse, "lse", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, v, block_ids, out, lse)
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, block_ids.shape[3], _dtype_code(q))
     if out is None:
         out = torch.empty_like(q)
@@ -213,12 +268,15 @@ def msa_kl_align(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: t
                  want_dlogits: bool = True, workspace: Optional[torch.Tensor] = None):
     """KL alignment on the selected support. Returns dict(kl_rows [B, Nq, Hkv],
     kl_mean [1], dlogits [B, Nq, Hkv, topk, 128] (opt)), all fp32."""
-    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx"), (block_ids, "block_ids")):
-        _check(t, n, 4)
-    _check(k_idx, "k_idx", 3)
-    _check(lse_main, "lse_main", 3)
+    _check(q, "q", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
     N, Hkv = k.shape[1], k.shape[2]
+    _expect(q_idx, "q_idx", (B, Nq, Hkv, None), q.dtype)
+    _expect(k_idx, "k_idx", (B, N, q_idx.shape[3]), q.dtype)
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    _expect(lse_main, "lse_main", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, q_idx, k_idx, block_ids, lse_main)
     K = block_ids.shape[3]
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], K, _dtype_code(q))
     dev = q.device
@@ -241,12 +299,16 @@ def msa_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: t
                  out: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor, q_start: int = 0,
                  idx_dim: int = 64, workspace: Optional[torch.Tensor] = None):
     """Gradients of msa_attn_fwd with the selection fixed: (dq like q, dk like k, dv like v)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (block_ids, "block_ids"), (out, "out"),
-                 (dout, "dout")):
-        _check(t, n, 4)
-    _check(lse, "lse", 3)
+    _check(q, "q", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
     N, Hkv = k.shape[1], k.shape[2]
+    _expect(v, "v", tuple(k.shape), q.dtype)
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    _expect(out, "out", tuple(q.shape), q.dtype)
+    _expect(dout, "dout", tuple(q.shape), q.dtype)
+    _expect(lse, "lse", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, v, block_ids, out, dout, lse)
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, block_ids.shape[3], _dtype_code(q))
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
@@ -266,9 +328,11 @@ def msa_idx_bwd(q_idx: torch.Tensor, k_idx: torch.Tensor, block_ids: torch.Tenso
     """Index-logit gradient chained into the index projections: (dq_idx like q_idx,
     dk_idx like k_idx). dlogits [B, Nq, Hkv, topk, 128] fp32 as msa_kl_align returns it."""
     _check(q_idx, "q_idx", 4)
-    _check(k_idx, "k_idx", 3)
-    _check(block_ids, "block_ids", 4)
-    _check(dlogits, "dlogits", 5)
+    B, Nq, Hkv, DI = q_idx.shape
+    _expect(k_idx, "k_idx", (B, None, DI), q_idx.dtype)
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    _expect(dlogits, "dlogits", (B, Nq, Hkv, block_ids.shape[3], 128), torch.float32)
+    _on_device(q_idx, k_idx, block_ids, dlogits)
     sh = shape_for(q_idx, k_idx, block_ids.shape[3], q_start, num_q_heads, head_dim)
     dq = torch.empty_like(q_idx)
     dk = torch.empty_like(k_idx)
@@ -284,8 +348,9 @@ def msa_idx_bwd(q_idx: torch.Tensor, k_idx: torch.Tensor, block_ids: torch.Tenso
 def msa_dense_lse(q: torch.Tensor, k: torch.Tensor, q_start: int = 0, idx_dim: int = 64):
     """LSE of the main branch over the full causal context: fp32 [B, Nq, Hq]."""
     _check(q, "q", 4)
-    _check(k, "k", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
+    _on_device(q, k)
     N, Hkv = k.shape[1], k.shape[2]
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, 1, _dtype_code(q))
     lse = torch.empty((B, Nq, Hq), dtype=torch.float32, device=q.device)
@@ -299,12 +364,14 @@ def msa_kl_dense(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: t
                  lse_main: torch.Tensor, q_start: int = 0, want_mass: bool = True):
     """KL alignment on the full causal context (warm-up stage): dict(kl_rows [B, Nq, Hkv],
     kl_mean [1], lse_idx [B, Nq, Hkv], block_mass [B, Nq, Hkv, nb] (opt)), all fp32."""
-    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx")):
-        _check(t, n, 4)
-    _check(k_idx, "k_idx", 3)
-    _check(lse_main, "lse_main", 3)
+    _check(q, "q", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
     N, Hkv = k.shape[1], k.shape[2]
+    _expect(q_idx, "q_idx", (B, Nq, Hkv, None), q.dtype)
+    _expect(k_idx, "k_idx", (B, N, q_idx.shape[3]), q.dtype)
+    _expect(lse_main, "lse_main", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, q_idx, k_idx, lse_main)
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], 1, _dtype_code(q))
     dev = q.device
     nb = (N + 127) // 128
@@ -329,12 +396,14 @@ def msa_kl_dense_bwd(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_id
                      workspace: Optional[torch.Tensor] = None):
     """The full-context KL with its gradient into the index projections: dict(dq_idx like
     q_idx, dk_idx like k_idx, lse_idx, and kl_rows / kl_mean / block_mass when asked)."""
-    for t, n in ((q, "q"), (k, "k"), (q_idx, "q_idx")):
-        _check(t, n, 4)
-    _check(k_idx, "k_idx", 3)
-    _check(lse_main, "lse_main", 3)
+    _check(q, "q", 4)
     B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
     N, Hkv = k.shape[1], k.shape[2]
+    _expect(q_idx, "q_idx", (B, Nq, Hkv, None), q.dtype)
+    _expect(k_idx, "k_idx", (B, N, q_idx.shape[3]), q.dtype)
+    _expect(lse_main, "lse_main", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, q_idx, k_idx, lse_main)
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, q_idx.shape[3], 1, _dtype_code(q))
     dev = q.device
     nb = (N + 127) // 128
@@ -361,9 +430,10 @@ def msa_block_recall(block_mass: torch.Tensor, block_ids: torch.Tensor, q_start:
                      head_dim: int = 128, idx_dim: int = 64):
     """Block recall and score recall of block_ids [B, Nq, Hkv, topk] against the teacher's
     block masses [B, Nq, Hkv, nb]: dict(block_recall, score_recall [B, Nq, Hkv], means [2])."""
-    _check(block_mass, "block_mass", 4)
-    _check(block_ids, "block_ids", 4)
+    _expect(block_mass, "block_mass", (None, None, None, None), torch.float32)
     B, Nq, Hkv, nb = block_mass.shape
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    _on_device(block_mass, block_ids)
     N = seqlen_kv if seqlen_kv is not None else nb * 128
     if (N + 127) // 128 != nb:
         raise ValueError("seqlen_kv does not match the block count of block_mass")
@@ -393,10 +463,13 @@ def msa_index_quantize_fp8(q_idx: Optional[torch.Tensor], k_idx: Optional[torch.
         _check(q_idx, "q_idx", 4)
         B, Nq, Hkv, DI = q_idx.shape
     if k_idx is not None:
+        if q_idx is not None:
+            _expect(k_idx, "k_idx", (B, None, DI), q_idx.dtype)
         _check(k_idx, "k_idx", 3)
         B, N, DI = k_idx.shape
     else:
         N = seqlen_kv if seqlen_kv is not None else q_start + Nq
+    _on_device(q_idx, k_idx)
     if q_idx is None:
         Nq, Hkv = 1, 1
         q_start = N - 1
@@ -425,12 +498,13 @@ def msa_select_fp8(q8: torch.Tensor, q_exp: torch.Tensor, k8: torch.Tensor, k_ex
                    want_margin: bool = False, num_q_heads: Optional[int] = None,
                    head_dim: int = 128, workspace: Optional[torch.Tensor] = None):
     """msa_select on FP8 index inputs (as msa_index_quantize_fp8 returns them)."""
-    _check(q8, "q8", 4)
-    _check(k8, "k8", 3)
-    _check(q_exp, "q_exp", 3)
-    _check(k_exp, "k_exp", 2)
+    _expect(q8, "q8", (None, None, None, None), torch.uint8)
     B, Nq, Hkv, DI = q8.shape
+    _expect(k8, "k8", (B, None, DI), torch.uint8)
     N = k8.shape[1]
+    _expect(q_exp, "q_exp", (B, Nq, Hkv), torch.int32)
+    _expect(k_exp, "k_exp", (B, (N + 127) // 128), torch.int32)
+    _on_device(q8, k8, q_exp, k_exp)
     Hq = num_q_heads if num_q_heads is not None else Hkv
     sh = make_shape(B, N, Nq, q_start, Hq, Hkv, head_dim, DI, topk, MSA_BF16)
     nb = (N + 127) // 128
@@ -452,13 +526,21 @@ def msa_select_fp8(q8: torch.Tensor, q_exp: torch.Tensor, k8: torch.Tensor, k_ex
 
 
 class KernelTimer:
-    """Sum of the durations of one kernel's launches (HIP events recorded by the library)."""
+    """Durations of kernel launches, from HIP events the library records on the launch
+    stream: one kernel (by name) or every kernel (kernel=None). Needs the measurement build:
+    call use_timed_build() first.
 
-    def __init__(self, kernel: str, max_launches: int = 1000):
-        self.kid = KERNELS.index(kernel)
+    After the block: total_ms / launches for the named kernel (or all kernels), and
+    per_kernel = {name: (total_ms, launches)} for every kernel that ran."""
+
+    def __init__(self, kernel: Optional[str] = None, max_launches: int = 1000):
+        if not _timed:
+            raise RuntimeError("KernelTimer needs the measurement build (use_timed_build())")
+        self.kid = -1 if kernel is None else KERNELS.index(kernel)
         self.max = max_launches
         self.total_ms = 0.0
         self.launches = 0
+        self.per_kernel = {}
 
     def __enter__(self):
         st = lib().msa_prof_begin(self.kid, self.max)
@@ -467,13 +549,15 @@ class KernelTimer:
         return self
 
     def __exit__(self, *exc):
-        ms = ctypes.c_float(0.0)
-        n = ctypes.c_int(0)
-        st = lib().msa_prof_end(ctypes.byref(ms), ctypes.byref(n))
+        n = len(KERNELS)
+        ms = (ctypes.c_float * n)()
+        cnt = (ctypes.c_int * n)()
+        st = lib().msa_prof_end(ms, cnt)
         if st != MSA_OK:
             raise MsaError(st, "msa_prof_end")
-        self.total_ms = ms.value
-        self.launches = n.value
+        self.per_kernel = {KERNELS[x]: (ms[x], cnt[x]) for x in range(n) if cnt[x] > 0}
+        self.total_ms = sum(v[0] for v in self.per_kernel.values())
+        self.launches = sum(v[1] for v in self.per_kernel.values())
         return False
 
     @property

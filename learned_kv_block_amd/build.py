@@ -11,10 +11,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libmsa.so")
+OUT_TIMED = os.path.join(HERE, "libmsa_timed.so")
 BUILD = os.path.join(HERE, "_build")
 
+# kernels and the C ABI, linked into both libraries
 SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_kl.hip", "msa_bwd.hip",
            "msa_dense.hip", "msa_fp8.hip"]
+# the launch hooks: no-ops in the product library, HIP-event timing in the measurement build
+HOOK_PRODUCT = "msa_prof_off.cpp"
+HOOK_TIMED = "msa_timing.cpp"
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -43,14 +48,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    """Compile every source and link libmsa.so; always rebuilds."""
+def _link(out: str, objs) -> None:
+    tmp = out + ".tmp"
+    subprocess.check_call([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, out)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every source and link libmsa.so (the product) and libmsa_timed.so (the same
+    objects with the kernel-timing hook, for measurement tools); always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
-    subprocess.check_call([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, OUT)
+        objs = list(ex.map(_compile, SOURCES + [HOOK_PRODUCT, HOOK_TIMED]))
+    common, hook_off, hook_timed = objs[:-2], objs[-2], objs[-1]
+    _link(OUT, common + [hook_off])
+    _link(OUT_TIMED, common + [hook_timed])
     return OUT
 
 

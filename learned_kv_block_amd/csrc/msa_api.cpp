@@ -6,8 +6,6 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
-#include <mutex>
-#include <vector>
 
 #include "msa_dense.hpp"
 #include "msa_internal.hpp"
@@ -209,32 +207,7 @@ msa_status check_device(int* num_cus) {
 
 inline bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
-// ------------------------------------------------------------------ timing hook
-struct Prof {
-  std::mutex mu;
-  std::atomic<int> kernel{-1};
-  int max = 0;
-  int used = 0;
-  std::vector<hipEvent_t> ev;  // 2 per launch
-} g_prof;
-
 }  // namespace
-
-namespace msa {
-void prof_before(int kernel, hipStream_t s) {
-  if (g_prof.kernel != kernel) return;
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
-  (void)hipEventRecord(g_prof.ev[2 * g_prof.used], s);
-}
-void prof_after(int kernel, hipStream_t s) {
-  if (g_prof.kernel != kernel) return;
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (g_prof.kernel != kernel || g_prof.used >= g_prof.max) return;
-  (void)hipEventRecord(g_prof.ev[2 * g_prof.used + 1], s);
-  ++g_prof.used;
-}
-}  // namespace msa
 
 extern "C" {
 
@@ -586,45 +559,6 @@ msa_status msa_select_fp8(const msa_shape* shape, const uint8_t* q8, const int32
   e = launch_topk(d, M, block_ids, cutoff_margin, stream);
   prof_after(MSA_K_TOPK, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
-}
-
-msa_status msa_prof_begin(int kernel, int max_launches) {
-  if (kernel < 0 || kernel >= MSA_K_COUNT || max_launches < 1 || max_launches > 100000)
-    return MSA_ERR_SHAPE;
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
-  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
-  for (auto& e : g_prof.ev)
-    if (hipEventCreate(&e) != hipSuccess) {
-      g_prof.kernel = -1;
-      return MSA_ERR_DEVICE;
-    }
-  g_prof.max = max_launches;
-  g_prof.used = 0;
-  g_prof.kernel = kernel;
-  return MSA_OK;
-}
-
-msa_status msa_prof_end(float* total_ms, int* launches) {
-  std::lock_guard<std::mutex> lk(g_prof.mu);
-  float sum = 0.0f;
-  msa_status st = MSA_OK;
-  for (int x = 0; x < g_prof.used; ++x) {
-    if (hipEventSynchronize(g_prof.ev[2 * x + 1]) != hipSuccess) { st = MSA_ERR_DEVICE; break; }
-    float ms = 0.0f;
-    if (hipEventElapsedTime(&ms, g_prof.ev[2 * x], g_prof.ev[2 * x + 1]) != hipSuccess) {
-      st = MSA_ERR_DEVICE;
-      break;
-    }
-    sum += ms;
-  }
-  if (total_ms) *total_ms = sum;
-  if (launches) *launches = g_prof.used;
-  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
-  g_prof.ev.clear();
-  g_prof.kernel = -1;
-  g_prof.max = g_prof.used = 0;
-  return st;
 }
 
 }  // extern "C"

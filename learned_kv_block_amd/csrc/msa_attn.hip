@@ -246,7 +246,7 @@ direct_items_kernel(const int32_t* __restrict__ ids, int64_t nrows, int K, int n
   for (int64_t e0 = 0; e0 < n; e0 += 1024) {
     const int64_t e = e0 + tid;
     const int id = e < n ? ids[e] : -1;
-    const bool valid = id >= 0 && !(skip_local && id == L);
+    const bool valid = id >= 0 && id < nb && !(skip_local && id == L);
     const uint64_t bal = __ballot(valid);
     const int before = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));

@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include "msa.h"
+#include "msa_timing.h"
 
 namespace msa {
 
@@ -147,7 +148,10 @@ struct Dims {
 // Work items are ordered by (batch, group, query window, block): the rows of
 // one window of kQueryWindow queries are revisited by many consecutive items
 // and stay in L2 / Infinity Cache. Bucket id = ((b*Hkv + r)*nwin + w)*nb + blk.
-constexpr int kQueryWindow = 1 << 30;  // one window: plain (batch, group, block) order
+#ifndef MSA_QUERY_WINDOW
+#define MSA_QUERY_WINDOW (1 << 30)  // one window: plain (batch, group, block) order
+#endif
+constexpr int kQueryWindow = MSA_QUERY_WINDOW;
 
 // Workspace of the attention and KL calls (bucketing + partials).
 struct AttnWs {
@@ -162,7 +166,9 @@ struct AttnWs {
   int32_t* chunk_i;   // [buckets / 4096 + 1]: item count per scan chunk
 };
 
-// Process-wide kernel timing hook (msa_prof_begin / msa_prof_end).
+// Launch hooks around each kernel (kernel ids MSA_K_* of msa_timing.h). The
+// product library links no-ops (msa_prof_off.cpp); the measurement build links
+// the event-recording hook (msa_timing.cpp).
 void prof_before(int kernel, hipStream_t s);
 void prof_after(int kernel, hipStream_t s);
 

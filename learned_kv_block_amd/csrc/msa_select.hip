@@ -474,7 +474,10 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ M, int64_t ro
   if (lane == 0) {
     out[k - 1] = L;
     if (margin)
-      margin[row] = best_unsel ? key_score(worst_sel) - key_score(best_unsel) : INFINITY;
+      // +inf when nothing competes for a slot: k = 1 (no slot besides the local block) or
+      // no candidate left out
+      margin[row] = (k > 1 && best_unsel) ? key_score(worst_sel) - key_score(best_unsel)
+                                          : INFINITY;
   }
 }
 

@@ -75,7 +75,13 @@ def _L():
 
 
 def threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 16))
+    """OpenMP threads of the oracle: every CPU this process may run on, at most 16 (the host
+    share of one GPU on the measurement machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def _p(a: Optional[np.ndarray]):

@@ -152,6 +152,8 @@ def check_all(cfg, res, rows=None, want_kl=False, report=None):
     gm = res["margin"].reshape(-1, Hkv)[torch.from_numpy(rows).to(res["ids"].device)].cpu().numpy()
     fin = np.isfinite(ref["margin"])
     assert np.array_equal(np.isfinite(gm), fin)
+    # the oracle's non-finite margins are +inf (nothing competes for a slot); so must the GPU's be
+    assert np.all(np.isposinf(gm[~fin])), "non-finite GPU margins must be +inf"
     if fin.any():
         merr = float(np.max(np.abs(gm[fin] - ref["margin"][fin])))
         report["margin_max_abs"] = merr

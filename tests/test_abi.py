@@ -12,18 +12,27 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails before any launch
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+def declared_functions(header="msa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
+    """libmsa.so exports what msa.h declares and holds no timing hook; libmsa_timed.so (the
+    measurement build) exports that plus what msa_timing.h declares."""
     L = msa.lib()
     names = declared_functions()
     assert set(names) == set(msa.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
+    timing = declared_functions("msa_timing.h")
+    assert set(timing) == set(msa.TIMING_EXPORTS)
+    for n in timing:
+        assert not hasattr(L, n), f"the product library must not export {n}"
+    T = ctypes.CDLL(msa.TIMED_LIB_PATH)
+    for n in names + timing:
+        assert hasattr(T, n), n
 
 
 def shape(**kw):
@@ -158,3 +167,84 @@ def test_dense_bwd_validates_on_host():
     bad = list(args)
     bad[8] = None  # kl_rows NULL with kl_mean given
     assert L.msa_kl_dense_bwd(*bad, FAKE, need, None) == msa.MSA_ERR_NULL
+
+
+# ------------------------------------------------------------- binding: argument checks
+# The library sees raw pointers, so the binding must reject every shape, dtype or size
+# mismatch before a call: a wrong size would make the kernels read or write out of bounds.
+# These run on CPU tensors; the device check comes last, so a well-formed argument list
+# reaches it and fails with "device tensor" instead.
+
+import torch  # noqa: E402
+
+BF = torch.bfloat16
+
+
+def _attn_args(B=1, Nq=256, N=256, Hq=8, Hkv=2, D=64, K=4, dt=BF):
+    return dict(q=torch.zeros(B, Nq, Hq, D, dtype=dt), k=torch.zeros(B, N, Hkv, D, dtype=dt),
+                v=torch.zeros(B, N, Hkv, D, dtype=dt),
+                block_ids=torch.zeros(B, Nq, Hkv, K, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(block_ids=torch.zeros(1, 256, 2, 4, dtype=torch.int64)), "int32"),
+    (dict(k=torch.zeros(1, 256, 2, 64, dtype=torch.float32)), "bfloat16"),
+    (dict(v=torch.zeros(1, 128, 2, 64, dtype=BF)), "dimension 1"),
+    (dict(k=torch.zeros(1, 256, 2, 128, dtype=BF)), "dimension 3"),
+    (dict(block_ids=torch.zeros(1, 256, 4, 4, dtype=torch.int32)), "dimension 2"),
+    (dict(block_ids=torch.zeros(2, 256, 2, 4, dtype=torch.int32)), "dimension 0"),
+    (dict(q=torch.zeros(1, 256, 8, 64, dtype=BF).transpose(1, 2).contiguous().transpose(1, 2)),
+     "contiguous"),
+])
+def test_attn_fwd_rejects_mismatched_arguments(change, match):
+    a = _attn_args()
+    a.update(change)
+    with pytest.raises(ValueError, match=match):
+        msa.msa_attn_fwd(**a)
+
+
+def test_attn_fwd_rejects_bad_outputs_and_cpu_tensors():
+    a = _attn_args()
+    with pytest.raises(ValueError, match="float32"):
+        msa.msa_attn_fwd(**a, lse=torch.zeros(1, 256, 8, dtype=BF))
+    with pytest.raises(ValueError, match="dimension 2"):
+        msa.msa_attn_fwd(**a, out=torch.zeros(1, 256, 4, 64, dtype=BF))
+    with pytest.raises(ValueError, match="device tensor"):
+        msa.msa_attn_fwd(**a)
+
+
+def test_select_kl_bwd_recall_fp8_reject_mismatches():
+    qi = torch.zeros(1, 256, 2, 32, dtype=BF)
+    with pytest.raises(ValueError, match="dimension 2"):
+        msa.msa_select(qi, torch.zeros(1, 256, 64, dtype=BF), 4)
+    with pytest.raises(ValueError, match="bfloat16"):
+        msa.msa_select(qi, torch.zeros(1, 256, 32, dtype=torch.float32), 4)
+    a = _attn_args()
+    ki = torch.zeros(1, 256, 32, dtype=BF)
+    lse = torch.zeros(1, 256, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="dimension 1"):  # k_idx shorter than k
+        msa.msa_kl_align(a["q"], a["k"], qi, torch.zeros(1, 128, 32, dtype=BF), a["block_ids"],
+                         lse)
+    with pytest.raises(ValueError, match="dimension 2"):  # lse per group instead of per head
+        msa.msa_kl_align(a["q"], a["k"], qi, ki, a["block_ids"],
+                         torch.zeros(1, 256, 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="q_idx.*dimension 2"):  # q_idx per head, not per group
+        msa.msa_kl_align(a["q"], a["k"], torch.zeros(1, 256, 8, 32, dtype=BF), ki,
+                         a["block_ids"], lse)
+    with pytest.raises(ValueError, match="dout"):
+        msa.msa_attn_bwd(a["q"], a["k"], a["v"], a["block_ids"], a["q"], lse,
+                         torch.zeros(1, 256, 8, 32, dtype=BF))
+    with pytest.raises(ValueError, match="dimension 4"):
+        msa.msa_idx_bwd(qi, ki, a["block_ids"], torch.zeros(1, 256, 2, 4, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="float32"):
+        msa.msa_block_recall(torch.zeros(1, 256, 2, 2, dtype=BF), a["block_ids"])
+    with pytest.raises(ValueError, match="int32"):
+        msa.msa_select_fp8(torch.zeros(1, 256, 2, 32, dtype=torch.uint8),
+                           torch.zeros(1, 256, 2, dtype=torch.int64),
+                           torch.zeros(1, 256, 32, dtype=torch.uint8),
+                           torch.zeros(1, 2, dtype=torch.int32), 4)
+    with pytest.raises(ValueError, match="dimension 1"):  # one exponent per 128-token block
+        msa.msa_select_fp8(torch.zeros(1, 256, 2, 32, dtype=torch.uint8),
+                           torch.zeros(1, 256, 2, dtype=torch.int32),
+                           torch.zeros(1, 256, 32, dtype=torch.uint8),
+                           torch.zeros(1, 3, dtype=torch.int32), 4)
