@@ -8,10 +8,13 @@ dk and dv (sums over every query that selected a block), by the closed-form
 key sums: sum over keys of dv equals the sum of dout over the group's heads and
 rows, and dk sums to zero (the eq. (11) logit gradients of a row sum to zero).
 
-Tolerances: fp32 relative L2 <= 1e-5; bf16 relative L2 <= 1e-2 and max-abs
-<= 3e-2 of the largest reference magnitude. The bf16 kernel rounds P and dS to
-bf16 for the matrix cores and writes bf16 per-slot dq partials (each a relative
-2^-9 step); accumulation is fp32.
+Tolerances: fp32 relative L2 <= 1e-5; bf16 the forward's bar, relative L2 <= 5e-3
+and max-abs <= 1e-2, with the max-abs bar scaled by the largest reference magnitude
+where that exceeds 1 (dk and dv sum over every query that chose a block, so their
+entries grow with the bucket size, where an absolute 1e-2 would be finer than one
+bf16 step of the value). The bf16 kernel rounds P and dS to bf16 for the matrix
+cores and writes bf16 per-slot dq partials (each a relative 2^-9 step);
+accumulation is fp32.
 """
 import json
 
@@ -53,21 +56,23 @@ CASES = [
 
 def _tol(cfg):
     if cfg.dtype == si.F32:
-        return dict(rel_l2=1e-5, max_rel=1e-4)
-    return dict(rel_l2=1e-2, max_rel=3e-2)
+        return dict(rel_l2=1e-5, max_rel=1e-4, floor=0.0)
+    return dict(rel_l2=5e-3, max_rel=1e-2, floor=1.0)
 
 
 def _check(name, got, ref, t, rep):
+    """rel-L2 <= t.rel_l2 and max-abs <= t.max_rel * max(t.floor, max|ref|)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), name
-    scale = max(float(np.max(np.abs(ref))), 1e-30)
-    mr = float(np.max(np.abs(got - ref))) / scale
+    big = float(np.max(np.abs(ref))) if ref.size else 0.0
+    scale = max(big, t["floor"], 1e-30)
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     rl = parity.rel_l2(got, ref)
-    rep[name] = dict(rel_l2=rl, max_rel=mr)
+    rep[name] = dict(rel_l2=rl, max_abs=err, max_ref=big)
     assert rl <= t["rel_l2"], f"{name}: rel-L2 {rl:.3g}"
-    assert mr <= t["max_rel"], f"{name}: max-abs/max-ref {mr:.3g}"
+    assert err <= t["max_rel"] * scale, f"{name}: max-abs {err:.3g} (max |ref| {big:.3g})"
 
 
 def _run(cfg):

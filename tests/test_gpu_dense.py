@@ -196,15 +196,17 @@ COEF = 0.37
 
 
 def _grad_close(name, got, ref, rep):
-    """bf16 chain (dS and operands rounded to bf16, fp32 sums): rel-L2 <= 1e-2 and max-abs
-    <= 3e-2 of the largest reference magnitude."""
+    """bf16 chain (dS and operands rounded to bf16, fp32 sums): the forward's bf16 bar,
+    rel-L2 <= 5e-3 and max-abs <= 1e-2, the latter scaled by the largest reference
+    magnitude where it exceeds 1 (dk_idx sums over every query row that sees a key)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape and np.all(np.isfinite(got)), name
     rl = parity.rel_l2(got, ref)
-    mr = float(np.max(np.abs(got - ref))) / max(float(np.max(np.abs(ref))), 1e-30)
-    rep[name] = dict(rel_l2=rl, max_rel=mr)
-    assert rl <= 1e-2 and mr <= 3e-2, (name, rl, mr)
+    big = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got - ref)))
+    rep[name] = dict(rel_l2=rl, max_abs=err, max_ref=big)
+    assert rl <= 5e-3 and err <= 1e-2 * max(1.0, big), (name, rl, err, big)
 
 
 @pytest.mark.parametrize("cfg", GRAD_CASES, ids=[c.name for c in GRAD_CASES])
