@@ -67,7 +67,8 @@ typedef enum {
   MSA_ERR_SHAPE = 2,       /* inconsistent shape (e.g. Hq % Hkv != 0, q_start+seqlen_q > seqlen_kv) */
   MSA_ERR_UNSUPPORTED = 3, /* valid but not supported by this build (see list above) */
   MSA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than msa_workspace_size */
-  MSA_ERR_DEVICE = 5       /* HIP error at launch, or the current device is not gfx950 */
+  MSA_ERR_DEVICE = 5,      /* HIP error at launch, or the current device is not gfx950 */
+  MSA_ERR_SCRATCH = 6      /* msa_attn_fwd_noalloc: the call needs more than its fixed scratch */
 } msa_status;
 
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
@@ -146,6 +147,30 @@ msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_i
 msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                         const int32_t* block_ids, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_attn_fwd_noalloc — msa_attn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and kernels, with the workspace taken
+ * from a fixed device array of MSA_NOALLOC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends. The call
+ * allocates and frees nothing.
+ *
+ *  in/out  as for msa_attn_fwd (the caller passes every input and output).
+ *  Errors: as msa_attn_fwd; MSA_ERR_SCRATCH (nothing launched) when
+ *  msa_workspace_size(shape, MSA_OP_ATTN) exceeds MSA_NOALLOC_SCRATCH_BYTES
+ *  (e.g. a decode step of 64 sequences of 131072 tokens needs 20.3 MiB, a
+ *  prefill of 8192 tokens about 2 GiB); MSA_ERR_DEVICE if the scratch address
+ *  cannot be resolved on the current device.
+ *  Sharing: every call on one GPU uses that GPU's single scratch array and
+ *  leaves its contents behind (each call clears what it needs). Calls that
+ *  overlap on one GPU (other threads, or other streams whose work has not
+ *  finished) race on it: serialize them, e.g. on one stream.
+ */
+#define MSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+msa_status msa_attn_fwd_noalloc(const msa_shape* shape, const void* q, const void* k,
+                                const void* v, const int32_t* block_ids, void* out, float* lse,
+                                hipStream_t stream);
 
 /*
  * msa_kl_align — KL alignment of the index branch on the selected support

@@ -9,6 +9,8 @@ there is no fallback. If libmsa.so is missing the calls raise.
 Functions (same names as the C entry points):
   msa_select(q_idx, k_idx, topk, q_start=0, ...)     -> block ids (+ scores, margin)
   msa_attn_fwd(q, k, v, block_ids, q_start=0, ...)   -> (out, lse)
+  msa_attn_fwd_noalloc(q, k, v, block_ids, out, lse, ...)
+                                                     -> the same, on a fixed device scratch
   msa_kl_align(q, k, q_idx, k_idx, block_ids, lse_main, q_start=0, ...)
                                                      -> kl_rows, kl_mean, dlogits
   msa_attn_bwd(q, k, v, block_ids, out, lse, dout, q_start=0, ...)
@@ -38,7 +40,9 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 # the same kernel and API objects linked with the kernel-timing hook (include/msa_timing.h)
 TIMED_LIB_PATH = os.path.join(_HERE, "libmsa_timed.so")
 
-MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE = range(6)
+(MSA_OK, MSA_ERR_NULL, MSA_ERR_SHAPE, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_DEVICE,
+ MSA_ERR_SCRATCH) = range(7)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # fixed device scratch of msa_attn_fwd_noalloc
 MSA_F32, MSA_BF16 = 0, 1
 MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2, 3, 4
 MSA_OP_KL_DENSE_BWD = 5
@@ -47,7 +51,8 @@ KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatt
            "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8", "kl_dense_chain"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
-           "msa_index_quantize_fp8", "msa_select_fp8", "msa_status_string"]
+           "msa_index_quantize_fp8", "msa_select_fp8", "msa_status_string",
+           "msa_attn_fwd_noalloc"]
 TIMING_EXPORTS = ["msa_prof_begin", "msa_prof_end"]
 
 
@@ -91,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.msa_workspace_size.restype = ctypes.c_size_t
         L.msa_select.argtypes = [S, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_attn_fwd.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.msa_attn_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P]
         L.msa_kl_align.argtypes = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_attn_bwd.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.msa_idx_bwd.argtypes = [S, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
@@ -101,7 +107,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, P]
         L.msa_index_quantize_fp8.argtypes = [S, P, P, P, P, P, P, P]
         L.msa_select_fp8.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in ("msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd", "msa_idx_bwd",
+        for f in ("msa_select", "msa_attn_fwd", "msa_attn_fwd_noalloc", "msa_kl_align",
+                  "msa_attn_bwd", "msa_idx_bwd",
                   "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
                   "msa_index_quantize_fp8", "msa_select_fp8"):
             getattr(L, f).restype = ctypes.c_int
@@ -260,6 +267,29 @@ def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: t
                             _ptr(out), _ptr(lse), _ptr(ws), nws, _stream(q))
     if st != MSA_OK:
         raise MsaError(st, "msa_attn_fwd")
+    return out, lse
+
+
+def msa_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         block_ids: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                         q_start: int = 0, idx_dim: int = 64):
+    """msa_attn_fwd without a workspace: the library's fixed 64 MiB device scratch is used
+    (for callers that cannot allocate). The caller passes the outputs; calls that overlap
+    on one GPU race on the scratch. Raises MsaError(MSA_ERR_SCRATCH) for larger workloads."""
+    _check(q, "q", 4)
+    B, Nq, Hq, D = q.shape
+    _expect(k, "k", (B, None, None, D), q.dtype)
+    N, Hkv = k.shape[1], k.shape[2]
+    _expect(v, "v", tuple(k.shape), q.dtype)
+    _expect(block_ids, "block_ids", (B, Nq, Hkv, None), torch.int32)
+    _expect(out, "out", tuple(q.shape), q.dtype)
+    _expect(lse, "lse", (B, Nq, Hq), torch.float32)
+    _on_device(q, k, v, block_ids, out, lse)
+    sh = make_shape(B, N, Nq, q_start, Hq, Hkv, D, idx_dim, block_ids.shape[3], _dtype_code(q))
+    st = lib().msa_attn_fwd_noalloc(ctypes.byref(sh), _ptr(q), _ptr(k), _ptr(v), _ptr(block_ids),
+                                    _ptr(out), _ptr(lse), _stream(q))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_attn_fwd_noalloc")
     return out, lse
 
 

@@ -207,6 +207,32 @@ msa_status check_device(int* num_cus) {
 
 inline bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
+msa_status attn_fwd_launch(const Dims& d, const Layout& L, const void* q, const void* k,
+                           const void* v, const int32_t* block_ids, void* out, float* lse,
+                           void* workspace, hipStream_t stream);
+
+}  // namespace
+
+// ------------------------------------------------- fixed scratch of msa_attn_fwd_noalloc
+// A device array of MSA_NOALLOC_SCRATCH_BYTES, one copy per GPU. In host code its
+// name is only a stand-in: the device address is resolved once per device with
+// hipGetSymbolAddress (with that device current) and only that address is used.
+__device__ __align__(256) unsigned char scratch[MSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<void*> g_scratch_addr[64];  // device address of `scratch` per device (0: unresolved)
+
+msa_status scratch_address(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MSA_ERR_DEVICE;
+  void* p = g_scratch_addr[dev].load();
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_DEVICE;
+    g_scratch_addr[dev].store(p);  // concurrent first calls store the same address
+  }
+  *ptr = p;
+  return MSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -219,6 +245,8 @@ const char* msa_status_string(msa_status st) {
     case MSA_ERR_UNSUPPORTED: return "shape or type not supported by this build";
     case MSA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case MSA_ERR_DEVICE: return "HIP launch error or device is not gfx950";
+    case MSA_ERR_SCRATCH:
+      return "workload needs more than the fixed scratch of msa_attn_fwd_noalloc (64 MiB)";
   }
   return "unknown status";
 }
@@ -271,6 +299,34 @@ msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, co
   const Layout L = layout(d, MSA_OP_ATTN);
   if ((st = check_ws(L, workspace, workspace_bytes)) != MSA_OK) return st;
   if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  return attn_fwd_launch(d, L, q, k, v, block_ids, out, lse, workspace, stream);
+}
+
+msa_status msa_attn_fwd_noalloc(const msa_shape* shape, const void* q, const void* k,
+                                const void* v, const int32_t* block_ids, void* out, float* lse,
+                                hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  d = for_op(d, MSA_OP_ATTN);
+  if (d.rows == 0) return MSA_OK;
+  if (!q || !k || !v || !block_ids || !out || !lse) return MSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return MSA_ERR_SHAPE;
+  const Layout L = layout(d, MSA_OP_ATTN);
+  if (L.total > MSA_NOALLOC_SCRATCH_BYTES) return MSA_ERR_SCRATCH;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MSA_OK) return st;
+  return attn_fwd_launch(d, L, q, k, v, block_ids, out, lse, ws, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// the launch sequence of msa_attn_fwd on a validated shape and a workspace of L.total bytes
+msa_status attn_fwd_launch(const Dims& d, const Layout& L, const void* q, const void* k,
+                           const void* v, const int32_t* block_ids, void* out, float* lse,
+                           void* workspace, hipStream_t stream) {
   char* ws = static_cast<char*>(workspace);
   const AttnWs w = carve(L, workspace);
   // bf16: each row's local block is attended query-outer inside the combine,
@@ -291,6 +347,9 @@ msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, co
   prof_after(MSA_K_COMBINE, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
+}  // namespace
+
+extern "C" {
 
 msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                         const int32_t* block_ids, const void* out, const float* lse,

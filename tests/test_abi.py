@@ -47,8 +47,23 @@ def select(sh, ws=None, nws=0, ids=FAKE, qi=FAKE, ki=FAKE):
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         assert msa.status_string(s)
+
+
+def test_noalloc_rejects_on_host():
+    """msa_attn_fwd_noalloc: NULL pointers, and workloads whose workspace exceeds the fixed
+    64 MiB scratch, are rejected before anything is launched."""
+    L = msa.lib()
+    small = shape(batch=16, seqlen_kv=8192, seqlen_q=1, q_start=8191)
+    assert msa.workspace_size(small, msa.MSA_OP_ATTN) <= msa.NOALLOC_SCRATCH_BYTES
+    assert L.msa_attn_fwd_noalloc(ctypes.byref(small), FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                  None) == msa.MSA_ERR_NULL
+    big = shape(seqlen_kv=8192, seqlen_q=8192)
+    assert msa.workspace_size(big, msa.MSA_OP_ATTN) > msa.NOALLOC_SCRATCH_BYTES
+    assert L.msa_attn_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == msa.MSA_ERR_SCRATCH
+    assert "scratch" in msa.status_string(msa.MSA_ERR_SCRATCH)
 
 
 @pytest.mark.parametrize("kw,status", [
