@@ -15,8 +15,8 @@ OUT_TIMED = os.path.join(HERE, "libmsa_timed.so")
 BUILD = os.path.join(HERE, "_build")
 
 # kernels and the C ABI, linked into both libraries
-SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_kl.hip", "msa_bwd.hip",
-           "msa_dense.hip", "msa_fp8.hip"]
+SOURCES = ["msa_api.cpp", "msa_select.hip", "msa_attn.hip", "msa_decode.hip", "msa_kl.hip",
+           "msa_bwd.hip", "msa_dense.hip", "msa_fp8.hip"]
 # the launch hooks: no-ops in the product library, HIP-event timing in the measurement build
 HOOK_PRODUCT = "msa_prof_off.cpp"
 HOOK_TIMED = "msa_timing.cpp"

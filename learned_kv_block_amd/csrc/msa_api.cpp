@@ -327,6 +327,13 @@ namespace {
 msa_status attn_fwd_launch(const Dims& d, const Layout& L, const void* q, const void* k,
                            const void* v, const int32_t* block_ids, void* out, float* lse,
                            void* workspace, hipStream_t stream) {
+  if (decode_attn_supported(d)) {
+    // one query per sequence: query-outer over the selected blocks, no workspace used
+    prof_before(MSA_K_SPARSE_ATTN, stream);
+    const hipError_t e = launch_decode_attn(d, q, k, v, block_ids, out, lse, stream);
+    prof_after(MSA_K_SPARSE_ATTN, stream);
+    return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+  }
   char* ws = static_cast<char*>(workspace);
   const AttnWs w = carve(L, workspace);
   // bf16: each row's local block is attended query-outer inside the combine,

@@ -179,6 +179,11 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
                                  hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s);
+// bf16 with one query per sequence: a register-streamed scan of K_idx whose block
+// scores are bit-identical to those of the tiled index kernel
+bool decode_index_supported(const Dims& d);
+hipError_t launch_decode_index(const Dims& d, const void* q_idx, const void* k_idx, float* M,
+                               hipStream_t s);
 
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
                             hipStream_t s);
@@ -186,6 +191,11 @@ hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const
                               const AttnWs& w, void* opart, float* lpart, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const void* opart, const float* lpart,
                           const int32_t* ids, void* out, float* lse, hipStream_t s);
+// bf16 with one query per sequence (a decode step): query-outer attention of each
+// (sequence, group) over its selected blocks, written straight to out / lse
+bool decode_attn_supported(const Dims& d);
+hipError_t launch_decode_attn(const Dims& d, const void* q, const void* k, const void* v,
+                              const int32_t* ids, void* out, float* lse, hipStream_t s);
 // bf16: attention of each row's local block (query-outer) fused with the combine
 hipError_t launch_combine_local(const Dims& d, const void* q, const void* k, const void* v,
                                 const void* opart, const float* lpart, const int32_t* ids,

@@ -288,6 +288,7 @@ static hipError_t index_dispatch_hkv(const Dims& d, const void* qi, const void* 
 
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
                                  hipStream_t s) {
+  if (decode_index_supported(d)) return launch_decode_index(d, q_idx, k_idx, M, s);
   if (d.dtype == MSA_BF16) {
     if (d.DI == 64) return index_dispatch_hkv<bf16, 64>(d, q_idx, k_idx, M, s);
     if (d.DI == 32) return index_dispatch_hkv<bf16, 32>(d, q_idx, k_idx, M, s);
