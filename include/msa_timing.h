@@ -34,7 +34,8 @@ enum {
   MSA_K_KL_IDX_STATS = 8, MSA_K_KL_IDX_LSE = 9, MSA_K_KL_MAIN = 10, MSA_K_KL_REDUCE = 11,
   MSA_K_ATTN_BWD = 12, MSA_K_IDX_BWD = 13, MSA_K_DENSE_LSE = 14, MSA_K_KL_DENSE = 15,
   MSA_K_RECALL = 16, MSA_K_DENSE_LSE_IDX = 17, MSA_K_INDEX_FP8 = 18, MSA_K_QUANTIZE_FP8 = 19,
-  MSA_K_KL_DENSE_CHAIN = 20, MSA_K_COUNT = 21, MSA_K_ALL = -1
+  MSA_K_KL_DENSE_CHAIN = 20, MSA_K_BUCKET_SORT = 21, MSA_K_BWD_FINALIZE = 22,
+  MSA_K_COUNT = 23, MSA_K_ALL = -1
 };
 msa_status msa_prof_begin(int kernel, int max_launches);
 msa_status msa_prof_end(float* ms, int* launches);

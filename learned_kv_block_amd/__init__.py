@@ -48,7 +48,8 @@ MSA_OP_SELECT, MSA_OP_ATTN, MSA_OP_KL, MSA_OP_ATTN_BWD, MSA_OP_IDX_BWD = 0, 1, 2
 MSA_OP_KL_DENSE_BWD = 5
 KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatter",
            "work_items", "sparse_attn", "combine", "kl_idx_stats", "kl_idx_lse", "kl_main",
-           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8", "kl_dense_chain"]
+           "kl_reduce", "attn_bwd", "idx_bwd", "dense_lse", "kl_dense", "recall", "dense_lse_idx", "index_fp8", "quantize_fp8", "kl_dense_chain",
+           "bucket_sort", "bwd_finalize"]
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
            "msa_index_quantize_fp8", "msa_select_fp8", "msa_status_string",

@@ -99,7 +99,8 @@ struct Layout {
   size_t counts, offsets, cursor, item_off, totals, items, entries, chunks;  // bucketing
   size_t nchunks;  // scan chunks of 4096 buckets (+1)
   size_t opart, lpart;                                               // attention
-  size_t drow, dqpart, dk_acc, dv_acc;                               // attention backward
+  size_t sorted;                                                     // backward: canonical entries
+  size_t drow, dqpart, slabs;                                        // attention backward
   size_t dqi_part, dki_acc;                                          // index chain
   size_t slot_lse, lse_idx, kl_part, block_sums;                     // KL
   size_t dense_ds;                                                   // full-context KL gradient
@@ -139,16 +140,19 @@ Layout layout(const Dims& d, int op) {
     L.opart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
     L.lpart = take((size_t)(d.slots + 1) * d.G * 4);
   } else if (op == MSA_OP_ATTN_BWD) {
-    const size_t nkv = (size_t)d.B * d.N * d.Hkv * d.D;
+    L.sorted = take(d.entries_max * 4);
     L.drow = take((size_t)d.rows * d.Hq * 4);
     // one extra slot: target of the backward kernel's unused rows
     L.dqpart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
-    L.dk_acc = take(nkv * 4);
-    L.dv_acc = take(nkv * 4);
+    // [bucket or workgroup run][32-row tile][dK, dV][128 keys][D] fp32
+    const size_t row_tiles = (d.dtype == MSA_BF16 ? MSA_BWD_R16 : 32) / 32;
+    L.slabs = take(((size_t)d.buckets + 2 * kBwdMaxGrid) * row_tiles * 2 * 128 * d.D * 4);
   } else if (op == MSA_OP_IDX_BWD) {
+    L.sorted = take(d.entries_max * 4);
     // one extra slot: target of the index backward kernel's unused queries
     L.dqi_part = take((size_t)(d.slots + 1) * d.DI * 4);
-    L.dki_acc = take((size_t)d.B * d.N * d.DI * 4);
+    // [bucket or workgroup run][128 keys][d_idx] fp32
+    L.slabs = take(((size_t)d.buckets + 2 * kBwdMaxGrid) * 128 * d.DI * 4);
   } else {
     L.slot_lse = take((size_t)d.slots * 4);
     L.lse_idx = take((size_t)d.rows * d.Hkv * 4);
@@ -173,6 +177,7 @@ AttnWs carve(const Layout& L, void* ws) {
   w.entries = reinterpret_cast<int32_t*>(p + L.entries);
   w.chunk_e = reinterpret_cast<int32_t*>(p + L.chunks);
   w.chunk_i = w.chunk_e + L.nchunks;
+  w.sorted = L.sorted ? reinterpret_cast<int32_t*>(p + L.sorted) : nullptr;
   return w;
 }
 
@@ -393,8 +398,7 @@ msa_status msa_attn_bwd(const msa_shape* shape, const void* q, const void* k, co
   if (launch_bucketing(d, block_ids, w, false, stream) != hipSuccess) return MSA_ERR_DEVICE;
   const hipError_t e = launch_attn_bwd(
       d, q, k, v, block_ids, out, lse, dout, w, reinterpret_cast<float*>(ws + L.drow),
-      ws + L.dqpart, reinterpret_cast<float*>(ws + L.dk_acc),
-      reinterpret_cast<float*>(ws + L.dv_acc), dq, dk, dv, stream);
+      ws + L.dqpart, reinterpret_cast<float*>(ws + L.slabs), dq, dk, dv, stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 
@@ -431,7 +435,7 @@ msa_status msa_idx_bwd(const msa_shape* shape, const void* q_idx, const void* k_
   if (launch_bucketing(d, block_ids, w, false, stream) != hipSuccess) return MSA_ERR_DEVICE;
   const hipError_t e = launch_idx_bwd(d, q_idx, k_idx, block_ids, dlogits_idx, coef, w,
                                       reinterpret_cast<float*>(ws + L.dqi_part),
-                                      reinterpret_cast<float*>(ws + L.dki_acc), dq_idx, dk_idx,
+                                      reinterpret_cast<float*>(ws + L.slabs), dq_idx, dk_idx,
                                       stream);
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }

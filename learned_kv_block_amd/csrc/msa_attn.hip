@@ -276,6 +276,83 @@ direct_items_kernel(const int32_t* __restrict__ ids, int64_t nrows, int K, int n
   }
 }
 
+// Canonical order inside each bucket, for the backward's fixed summation order.
+// A bucket's entries come from distinct rows t (the valid ids of a row are
+// distinct), so row order is a total order: one workgroup per bucket marks the
+// rows present in an LDS bitmap (kSortWords words, 32 * kSortWords rows per
+// pass) and writes each entry at its rank, the number of present rows below
+// its own (prefix popcounts). If the ranks do not account for every entry (two
+// entries of one row: ids repeated in a row, which msa_select never produces)
+// the bucket is copied in scatter order, so the output is always a
+// permutation of the input.
+constexpr int kSortWords = 4096;
+
+__global__ void __launch_bounds__(256)
+bucket_sort_kernel(const int32_t* __restrict__ offsets, int64_t nbk, int Nq, int entries_max,
+                   const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
+  __shared__ uint32_t bits[kSortWords];
+  __shared__ int32_t pref[kSortWords];
+  __shared__ int32_t wsum[4];
+  constexpr int WPT = kSortWords / 256;  // words per thread in the scan
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int64_t bkt = blockIdx.x; bkt < nbk; bkt += gridDim.x) {
+    const int lo = min(offsets[bkt], entries_max), hi = min(offsets[bkt + 1], entries_max);
+    if (hi - lo <= 1) {
+      if (hi - lo == 1 && tid == 0) dst[lo] = src[lo];
+      continue;  // uniform
+    }
+    int placed = 0;
+    for (int tb = 0; tb < Nq; tb += 32 * kSortWords) {
+      const int nw = min(kSortWords, (Nq - tb + 31) / 32);  // words used in this pass
+      for (int x = tid; x < nw; x += 256) bits[x] = 0u;
+      __syncthreads();
+      for (int e = lo + tid; e < hi; e += 256) {
+        const int t = (src[e] >> 6) - tb;
+        if (t >= 0 && t < 32 * nw) atomicOr(&bits[t >> 5], 1u << (t & 31));
+      }
+      __syncthreads();
+      int c[WPT], sum = 0;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        const int x = tid * WPT + j;
+        c[j] = x < nw ? __popc(bits[x]) : 0;
+        sum += c[j];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (lane == 63) wsum[wave] = incl;
+      __syncthreads();
+      int run = incl - sum;
+      for (int v = 0; v < wave; ++v) run += wsum[v];
+      const int pass_total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        const int x = tid * WPT + j;
+        if (x < nw) pref[x] = run;
+        run += c[j];
+      }
+      __syncthreads();
+      for (int e = lo + tid; e < hi; e += 256) {
+        const int v = src[e];
+        const int t = (v >> 6) - tb;
+        if (t >= 0 && t < 32 * nw) {
+          const int rank = placed + pref[t >> 5] + __popc(bits[t >> 5] & ((1u << (t & 31)) - 1u));
+          if (rank < hi - lo) dst[lo + rank] = v;
+        }
+      }
+      placed += pass_total;
+      __syncthreads();  // bitmap, prefix and wsum are rewritten by the next pass
+    }
+    if (placed != hi - lo) {  // uniform: not a set of distinct rows
+      for (int e = lo + tid; e < hi; e += 256) dst[e] = src[e];
+    }
+  }
+}
+
 static size_t bucket_lds_bytes(const Dims& d, int arrays) {
   return (size_t)arrays * d.Hkv * d.nb * sizeof(int32_t);
 }
@@ -284,7 +361,8 @@ static bool bucket_use_lds(const Dims& d) { return bucket_lds_bytes(d, 2) <= 64 
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
                             hipStream_t s) {
   hipError_t e;
-  if (d.Nq == 1 && d.rows > 0 && d.items_max >= d.entries_max &&
+  // the direct path records no per-bucket offsets, which the canonical order needs
+  if (!w.sorted && d.Nq == 1 && d.rows > 0 && d.items_max >= d.entries_max &&
       d.rows * d.Hkv * d.K <= kDirectMax) {
     prof_before(MSA_K_BUCKET_HIST, s);
     direct_items_kernel<<<1, 1024, 0, s>>>(ids, d.rows * d.Hkv, d.K, d.nb, d.nwin, d.q_start,
@@ -331,6 +409,13 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
                                                      (int)d.entries_max);
   prof_after(MSA_K_BUCKET_SCATTER, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (w.sorted && d.buckets > 0) {
+    prof_before(MSA_K_BUCKET_SORT, s);
+    bucket_sort_kernel<<<(unsigned)std::min<int64_t>(d.buckets, 4096), 256, 0, s>>>(
+        w.offsets, d.buckets, d.Nq, (int)d.entries_max, w.entries, w.sorted);
+    prof_after(MSA_K_BUCKET_SORT, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (d.items_max > 0) {
     prof_before(MSA_K_WORK_ITEMS, s);
     work_items_kernel<<<(unsigned)((d.items_max + 255) / 256), 256, 0, s>>>(

@@ -16,8 +16,15 @@
 // fp32). A persistent workgroup walks a contiguous range of items; each wave
 // owns one (32-key quarter of the current block, 32-row tile of the item) pair
 // and keeps its keys' dK and dV in registers across the consecutive items of a
-// bucket, adding them to fp32 accumulators (atomics) when the bucket changes.
-// dQ gets one partial per (query, slot), summed per row afterwards.
+// bucket. dQ gets one partial per (query, slot), summed per row afterwards.
+//
+// Every sum has a fixed order, so the backward is bitwise repeatable: the
+// entries of a bucket are in row order (bucket_sort_kernel), hence so are its
+// items; a workgroup's run of items of one bucket writes its fp32 dK, dV sums
+// (one slab per 32-row tile) to the bucket's slab when the run is the whole
+// bucket, else to one of the workgroup's two slabs (its first and last run;
+// only those can be shared with a neighbour); the finalize kernel adds a
+// bucket's slabs in item order and writes dK, dV (zero for unselected keys).
 #include "msa_internal.hpp"
 
 namespace msa {
@@ -41,6 +48,13 @@ bwd_rowdot_kernel(const T* __restrict__ out, const T* __restrict__ dout, int64_t
 #pragma unroll
   for (int m = L / 2; m >= 1; m >>= 1) acc += shfl_xor_f(acc, m);
   if (x < n && c == 0) drow[x] = acc;
+}
+
+// persistent grid of the backward kernels: one workgroup per CU, at most
+// kBwdMaxGrid (the workspace holds two slabs per workgroup)
+static int bwd_grid(const Dims& d) {
+  const int g = ((d.num_cus + 7) / 8) * 8;
+  return g < kBwdMaxGrid ? g : kBwdMaxGrid;
 }
 
 // (query, head) rows per work item: 64 for bf16; 32 for fp32, whose tiles
@@ -67,9 +81,8 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
                 const T* __restrict__ dout, const float* __restrict__ lse,
                 const float* __restrict__ rowdot, const int4* __restrict__ items,
                 const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
-                T* __restrict__ dqpart, float* __restrict__ dk_acc, float* __restrict__ dv_acc,
-                int N, int Nq, int q_start, int Hkv, int nb, int nbw, int topk, int nslots,
-                float scale) {
+                T* __restrict__ dqpart, float* __restrict__ slabs, int nbk, int N, int Nq,
+                int q_start, int Hkv, int nb, int nbw, int topk, int nslots, float scale) {
   constexpr int R = bwd_rows<T>();  // (query, head) rows per item
   constexpr int RT = R / 32;        // 32-row tiles per item
   constexpr int NT = bwd_threads<T>();
@@ -101,12 +114,9 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
 
   // contiguous item range of this workgroup inside its XCD's share
   const int total = totals[1];
-  const int nwg_x = gridDim.x / 8;
-  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
-  const int per_x = (total + 7) / 8;
-  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
-  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
-  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  const ItemSplit split(total, gridDim.x);
+  int i0, i1;
+  split.range(blockIdx.x, &i0, &i1);
   if (i0 >= i1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -128,19 +138,30 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
         dva[dt][e] = 0.0f;
       }
   };
-  auto flush = [&](int bkt) {
-    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
-    const int key = blk * 128 + 32 * kw + l32;
-    if (key >= N) return;
-    const size_t base = ((size_t)b * N + key) * kvrow + (size_t)r * D;
+  // the run [ra, rb) of bucket bkt ends: its sums go to the bucket's slab, or
+  // to this workgroup's first- or last-run slab when a neighbour holds items
+  // of the same bucket; slab layout [row tile][dK, dV][128 keys][D] fp32
+  // (the buckets a neighbour may share: that of the item before the range and
+  // that of the item after it)
+  const int bkt_prev = __builtin_amdgcn_readfirstlane(i0 > 0 ? items[i0 - 1].x : -1);
+  const int bkt_next = __builtin_amdgcn_readfirstlane(i1 < total ? items[i1].x : -1);
+  auto flush = [&](int bkt, int ra, int rb) {
+    const bool shared = (ra == i0 && bkt_prev == bkt) || (rb == i1 && bkt_next == bkt);
+    const size_t slab = shared ? (size_t)nbk + 2 * blockIdx.x + (ra == i0 ? 0 : 1) : (size_t)bkt;
+    float* const pk = slabs + ((slab * RT + rt) * 2) * 128 * D + (size_t)(32 * kw + l32) * D;
+    float* const pv = pk + 128 * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      dka[dt] *= scale;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int dd = 32 * dt + drow(e, h);
-        unsafeAtomicAdd(dk_acc + base + dd, dka[dt][e] * scale);
-        unsafeAtomicAdd(dv_acc + base + dd, dva[dt][e]);
+      for (int j = 0; j < 4; ++j) {  // elements 4j..4j+3: d = 32dt + 8j + 4h + 0..3
+        const int dd = 32 * dt + 8 * j + 4 * h;
+        *reinterpret_cast<f32x4*>(pk + dd) =
+            f32x4{dka[dt][4 * j], dka[dt][4 * j + 1], dka[dt][4 * j + 2], dka[dt][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(pv + dd) =
+            f32x4{dva[dt][4 * j], dva[dt][4 * j + 1], dva[dt][4 * j + 2], dva[dt][4 * j + 3]};
       }
+    }
   };
   // two 4-element runs of a contiguous row: k-indices {16c+4h+0..3, 16c+8+4h+0..3},
   // the rows (or keys) an accumulator's elements 8c..8c+7 hold
@@ -220,7 +241,7 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
   };
 
   zero_acc();
-  int cur = -1;
+  int cur = -1, run0 = i0;
   load_ents(i0);
   load_rows(i0);
   load_ents(min(i0 + 1, i1 - 1));
@@ -229,9 +250,10 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
     const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
     __syncthreads();  // every wave is done with the previous item's tiles
     if (bkt != cur) {  // uniform
-      if (cur >= 0) flush(cur);
+      if (cur >= 0) flush(cur, run0, it);
       zero_acc();
       cur = bkt;
+      run0 = it;
       // K and V of block blk (row-major; fp32 also K^T); rows past N are zero
       for (int c = tid; c < 128 * CH; c += NT) {
         const int rho = c / CH, dc = c % CH;
@@ -364,7 +386,65 @@ attn_bwd_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __res
              ld8<T>(Qs + rho * LK + 8 * dc));
     }
   }
-  if (cur >= 0) flush(cur);
+  if (cur >= 0) flush(cur, run0, i1);
+}
+
+// dK, dV of one bucket's 128 keys (one workgroup per bucket, grid-stride): the
+// sum of its slabs in item order (workgroup by workgroup, row tile by row
+// tile), zero when no row selected the block. Keys past N are not written.
+template <typename T, int D, int RT>
+__global__ void __launch_bounds__(256)
+attn_bwd_finalize_kernel(const float* __restrict__ slabs, const int32_t* __restrict__ item_off,
+                         const int32_t* __restrict__ totals,
+                         int nbk, int grid, int N, int Hkv, int nb, int nbw, T* __restrict__ dk,
+                         T* __restrict__ dv) {
+  constexpr int C4 = 128 * D / 4;  // 4-element chunks of a [128][D] slab
+  const int total = totals[1];
+  const ItemSplit split(total, grid);
+  for (int bkt = blockIdx.x; bkt < nbk; bkt += gridDim.x) {
+    const int blk = bkt % nb, br = bkt / nbw, r = br % Hkv, b = br / Hkv;
+    const int ia = min(item_off[bkt], total), ib = min(item_off[bkt + 1], total);
+    for (int c = threadIdx.x; c < C4; c += 256) {
+      const int kl = c / (D / 4), dd = 4 * (c % (D / 4));
+      const int key = blk * 128 + kl;
+      if (key >= N) continue;
+      f32x4 sk = {0.0f, 0.0f, 0.0f, 0.0f}, sv = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (ia < ib) {
+        const int wa = split.owner(ia);
+        int wa0, wa1;
+        split.range(wa, &wa0, &wa1);
+        if (ib <= wa1) {  // the whole bucket is one workgroup's run: the bucket's slab
+          for (int rt = 0; rt < RT; ++rt) {
+            const float* p = slabs + (((size_t)bkt * RT + rt) * 2) * 128 * D + (size_t)kl * D + dd;
+            sk += *reinterpret_cast<const f32x4*>(p);
+            sv += *reinterpret_cast<const f32x4*>(p + 128 * D);
+          }
+        } else {  // runs of consecutive workgroups, in item order
+          for (int it = ia; it < ib;) {
+            const int wg = split.owner(it);
+            int w0, w1;
+            split.range(wg, &w0, &w1);
+            const size_t slab = (size_t)nbk + 2 * wg + (it == w0 ? 0 : 1);
+            for (int rt = 0; rt < RT; ++rt) {
+              const float* p = slabs + ((slab * RT + rt) * 2) * 128 * D + (size_t)kl * D + dd;
+              sk += *reinterpret_cast<const f32x4*>(p);
+              sv += *reinterpret_cast<const f32x4*>(p + 128 * D);
+            }
+            it = w1;
+          }
+        }
+      }
+      const size_t o = (((size_t)b * N + key) * Hkv + r) * D + dd;
+      vec4<T> ok, ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok[e] = cvt<T>(sk[e]);
+        ov[e] = cvt<T>(sv[e]);
+      }
+      st4<T>(dk + o, ok);
+      st4<T>(dv + o, ov);
+    }
+  }
 }
 
 // dq[row, r*G + hh] = sum over the row's used slots of the slot partials
@@ -412,18 +492,20 @@ f32_to_kernel(const float* __restrict__ src, int64_t n, T* __restrict__ dst) {
 //   dq_idx[i, r] = c/sqrt(d_idx) sum_j dl[i, r, j] k_idx[j],
 //   dk_idx[j]    = c/sqrt(d_idx) sum over (i, r) that selected j of dl[i, r, j] q_idx[i, r],
 // c = the caller's loss coefficient. Same buckets as the attention (items of up
-// to 32 queries of one (batch, group, block)); a persistent workgroup (4
-// waves) keeps the block's dk_idx in registers across the bucket's items (wave
-// w: keys 32w..32w+31) and adds it to an fp32 accumulator at bucket changes;
-// dq_idx gets one fp32 partial per (query, slot), summed per row afterwards.
-// Products use fp32 matrix cores (dlogits are fp32).
+// to 32 queries of one (batch, group, block), entries in row order); a
+// persistent workgroup (4 waves) keeps the block's dk_idx in registers across
+// the bucket's items (wave w: keys 32w..32w+31) and writes it to a slab at the
+// end of each run, as the attention backward does; the finalize kernel adds,
+// per key, the buckets of every group in group order (each bucket's slabs in
+// item order). dq_idx gets one fp32 partial per (query, slot), summed per row
+// afterwards. Products use fp32 matrix cores (dlogits are fp32).
 template <typename T, int DI>
 __global__ void __launch_bounds__(256, 1)
 idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* __restrict__ dl,
                const int4* __restrict__ items, const int32_t* __restrict__ entries,
                const int32_t* __restrict__ totals, float* __restrict__ dqpart,
-               float* __restrict__ dk_acc, int N, int Nq, int Hkv, int nb, int nbw, int topk,
-               int nslots, float coef) {
+               float* __restrict__ slabs, int nbk, int N, int Nq, int Hkv, int nb, int nbw,
+               int topk, int nslots, float coef) {
   constexpr int Q = 32;         // queries per item
   constexpr int LKT = 128 + 4;  // row stride of K_idx^T [DI][128] and of dl [Q][128]
   constexpr int LQ = Q + 4;     // row stride of Q_idx^T [DI][Q]
@@ -434,12 +516,9 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   __shared__ __attribute__((aligned(16))) int slot_s[Q];  // (query, slot) of each query's partial
 
   const int total = totals[1];
-  const int nwg_x = gridDim.x / 8;
-  const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
-  const int per_x = (total + 7) / 8;
-  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
-  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
-  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  const ItemSplit split(total, gridDim.x);
+  int i0, i1;
+  split.range(blockIdx.x, &i0, &i1);
   if (i0 >= i1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -451,15 +530,20 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) dka[dt][e] = 0.0f;
   };
-  auto flush = [&](int bkt) {
-    const int blk = bkt % nb, b = bkt / nbw / Hkv;
-    const int key = blk * 128 + 32 * w + l32;
-    if (key >= N) return;
-    float* const row = dk_acc + ((size_t)b * N + key) * DI;
+  // the run [ra, rb) of bucket bkt ends: [128 keys][DI] fp32 slab, chosen as in
+  // the attention backward
+  auto flush = [&](int bkt, int ra, int rb) {
+    const bool shared = (ra == i0 && i0 > 0 && items[i0 - 1].x == bkt) ||
+                        (rb == i1 && i1 < total && items[i1].x == bkt);
+    const size_t slab = shared ? (size_t)nbk + 2 * blockIdx.x + (ra == i0 ? 0 : 1) : (size_t)bkt;
+    float* const row = slabs + (slab * 128 + 32 * w + l32) * DI;
 #pragma unroll
     for (int dt = 0; dt < DIT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) unsafeAtomicAdd(row + 32 * dt + drow(e, h), dka[dt][e] * coef);
+      for (int j = 0; j < 4; ++j)  // elements 4j..4j+3: d = 32dt + 8j + 4h + 0..3
+        *reinterpret_cast<f32x4*>(row + 32 * dt + 8 * j + 4 * h) =
+            f32x4{dka[dt][4 * j] * coef, dka[dt][4 * j + 1] * coef, dka[dt][4 * j + 2] * coef,
+                  dka[dt][4 * j + 3] * coef};
   };
 
   // the item's dl rows (4 floats per chunk) and Q_idx rows, loaded one item
@@ -503,7 +587,7 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
   };
 
   zero_acc();
-  int cur = -1;
+  int cur = -1, run0 = i0;
   load_ents(i0);
   load_rows(i0);
   load_ents(min(i0 + 1, i1 - 1));
@@ -513,9 +597,10 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
     const int blk = bkt % nb, b = bkt / nbw / Hkv;
     __syncthreads();
     if (bkt != cur) {  // uniform
-      if (cur >= 0) flush(cur);
+      if (cur >= 0) flush(cur, run0, it);
       zero_acc();
       cur = bkt;
+      run0 = it;
       for (int c = tid; c < 128 * DI; c += 256) {  // K_idx^T of the block, keys past N zero
         const int key = c / DI, dd = c % DI;
         const int kk = blk * 128 + key;
@@ -573,7 +658,55 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
         mma(dka[dt], ld8<float>(QIT + (32 * dt + l32) * LQ + 16 * kc + 8 * h), bcol);
     }
   }
-  if (cur >= 0) flush(cur);
+  if (cur >= 0) flush(cur, run0, i1);
+}
+
+// dk_idx of one (batch, block)'s 128 keys (one workgroup each, grid-stride):
+// the groups' buckets in group order, each the sum of its slabs in item order;
+// zero when no row of any group selected the block. Keys past N are not written.
+template <typename T, int DI>
+__global__ void __launch_bounds__(256)
+idx_bwd_finalize_kernel(const float* __restrict__ slabs, const int32_t* __restrict__ item_off,
+                        const int32_t* __restrict__ totals, int nbk, int grid, int B, int N,
+                        int Hkv, int nb, int nbw, T* __restrict__ dk) {
+  constexpr int C4 = 128 * DI / 4;
+  const int total = totals[1];
+  const ItemSplit split(total, grid);
+  for (int bb = blockIdx.x; bb < B * nb; bb += gridDim.x) {
+    const int b = bb / nb, blk = bb % nb;
+    for (int c = threadIdx.x; c < C4; c += 256) {
+      const int kl = c / (DI / 4), dd = 4 * (c % (DI / 4));
+      const int key = blk * 128 + kl;
+      if (key >= N) continue;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int r = 0; r < Hkv; ++r) {
+        const int bkt = (b * Hkv + r) * nbw + blk;
+        const int ia = min(item_off[bkt], total), ib = min(item_off[bkt + 1], total);
+        if (ia >= ib) continue;
+        const int wa = split.owner(ia);
+        int wa0, wa1;
+        split.range(wa, &wa0, &wa1);
+        f32x4 sb = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ib <= wa1) {
+          sb = *reinterpret_cast<const f32x4*>(slabs + ((size_t)bkt * 128 + kl) * DI + dd);
+        } else {
+          for (int it = ia; it < ib;) {
+            const int wg = split.owner(it);
+            int w0, w1;
+            split.range(wg, &w0, &w1);
+            const size_t slab = (size_t)nbk + 2 * wg + (it == w0 ? 0 : 1);
+            sb += *reinterpret_cast<const f32x4*>(slabs + (slab * 128 + kl) * DI + dd);
+            it = w1;
+          }
+        }
+        acc += sb;
+      }
+      vec4<T> o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = cvt<T>(acc[e]);
+      st4<T>(dk + ((size_t)b * N + key) * DI + dd, o);
+    }
+  }
 }
 
 // dq_idx[row, r] = sum over the row's used slots of the slot partials; a thread
@@ -608,37 +741,41 @@ dqi_sum_kernel(const float* __restrict__ dqpart, const int32_t* __restrict__ ids
 template <typename T, int DI>
 static hipError_t idx_bwd_run(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
                               const float* dl, float coef, const AttnWs& w, float* dqpart,
-                              float* dk_acc, void* dq, void* dk, hipStream_t s) {
-  const int64_t nk = (int64_t)d.B * d.N * DI;
+                              float* slabs, void* dq, void* dk, hipStream_t s) {
   hipError_t e;
-  if ((e = launch_fill_f32(dk_acc, nk, 0.0f, s)) != hipSuccess) return e;
-  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  const int grid = bwd_grid(d);
   const float c = coef / sqrtf((float)DI);
+  const int nbk = (int)d.buckets, nbw = d.nb * d.nwin;
   prof_before(MSA_K_IDX_BWD, s);
-  idx_bwd_kernel<T, DI><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, dl, w.items, w.entries,
-                                             w.totals, dqpart, dk_acc, d.N, d.Nq, d.Hkv, d.nb,
-                                             d.nb * d.nwin, d.K, (int)d.slots, c);
+  idx_bwd_kernel<T, DI><<<grid, 256, 0, s>>>((const T*)qi, (const T*)ki, dl, w.items, w.sorted,
+                                             w.totals, dqpart, slabs, nbk, d.N, d.Nq, d.Hkv,
+                                             d.nb, nbw, d.K, (int)d.slots, c);
   prof_after(MSA_K_IDX_BWD, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t nrg = d.rows * d.Hkv;
   dqi_sum_kernel<T, DI><<<(unsigned)((nrg * (DI / 4) + 255) / 256), 256, 0, s>>>(
       dqpart, ids, nrg, d.K, (T*)dq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (nk > 0)
-    f32_to_kernel<T><<<(unsigned)std::min<int64_t>((nk + 255) / 256, 4096), 256, 0, s>>>(
-        dk_acc, nk, (T*)dk);
+  const int64_t nbb = (int64_t)d.B * d.nb;
+  if (nbb > 0) {
+    prof_before(MSA_K_BWD_FINALIZE, s);
+    idx_bwd_finalize_kernel<T, DI><<<(unsigned)std::min<int64_t>(nbb, 4096), 256, 0, s>>>(
+        slabs, w.item_off, w.totals, nbk, grid, d.B, d.N, d.Hkv, d.nb, nbw, (T*)dk);
+    prof_after(MSA_K_BWD_FINALIZE, s);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_idx_bwd(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
                           const float* dl, float coef, const AttnWs& w, float* dqpart,
-                          float* dk_acc, void* dq, void* dk, hipStream_t s) {
+                          float* slabs, void* dq, void* dk, hipStream_t s) {
+  if (d.nwin != 1 || !w.sorted) return hipErrorInvalidValue;  // one bucket per (b, group, block)
   if (d.dtype == MSA_BF16) {
-    if (d.DI == 64) return idx_bwd_run<bf16, 64>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
-    if (d.DI == 32) return idx_bwd_run<bf16, 32>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+    if (d.DI == 64) return idx_bwd_run<bf16, 64>(d, qi, ki, ids, dl, coef, w, dqpart, slabs, dq, dk, s);
+    if (d.DI == 32) return idx_bwd_run<bf16, 32>(d, qi, ki, ids, dl, coef, w, dqpart, slabs, dq, dk, s);
   } else {
-    if (d.DI == 64) return idx_bwd_run<float, 64>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
-    if (d.DI == 32) return idx_bwd_run<float, 32>(d, qi, ki, ids, dl, coef, w, dqpart, dk_acc, dq, dk, s);
+    if (d.DI == 64) return idx_bwd_run<float, 64>(d, qi, ki, ids, dl, coef, w, dqpart, slabs, dq, dk, s);
+    if (d.DI == 32) return idx_bwd_run<float, 32>(d, qi, ki, ids, dl, coef, w, dqpart, slabs, dq, dk, s);
   }
   return hipErrorInvalidValue;
 }
@@ -647,28 +784,25 @@ template <typename T, int D>
 static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const void* v,
                           const int32_t* ids, const void* out, const float* lse,
                           const void* dout, const AttnWs& w,
-                          float* drow, void* dqpart, float* dk_acc, float* dv_acc, void* dq,
+                          float* drow, void* dqpart, float* slabs, void* dq,
                           void* dk, void* dv, hipStream_t s) {
-  const int64_t nkv = (int64_t)d.B * d.N * d.Hkv * D;
   hipError_t e;
-  if ((e = launch_fill_f32(dk_acc, nkv, 0.0f, s)) != hipSuccess) return e;
-  if ((e = launch_fill_f32(dv_acc, nkv, 0.0f, s)) != hipSuccess) return e;
   const int64_t nrh = d.rows * d.Hq;
   bwd_rowdot_kernel<T, D><<<(unsigned)((nrh + 256 / (D / 8) - 1) / (256 / (D / 8))), 256, 0, s>>>(
       (const T*)out, (const T*)dout, nrh, drow);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const unsigned grid = (unsigned)(((d.num_cus + 7) / 8) * 8);
+  const int grid = bwd_grid(d);
   const float scale = (float)(1.0 / sqrt((double)D));
   const int64_t nrg = d.rows * d.Hkv;
   const unsigned sgrid = (unsigned)((nrg * d.G * (D / 8) + 255) / 256);
-  const unsigned cgrid = (unsigned)std::min<int64_t>((nkv + 255) / 256, 4096);
+  const int nbk = (int)d.buckets, nbw = d.nb * d.nwin;
 #define MSA_BWD_CASE(GG)                                                                        \
   case GG:                                                                                      \
     prof_before(MSA_K_ATTN_BWD, s);                                                             \
-    attn_bwd_kernel<T, D, GG><<<grid, bwd_threads<T>(), 0, s>>>(                                            \
-        (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, drow, w.items, w.entries,   \
-        w.totals, (T*)dqpart, dk_acc, dv_acc, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, \
-        d.K, (int)d.slots, scale);                                                              \
+    attn_bwd_kernel<T, D, GG><<<grid, bwd_threads<T>(), 0, s>>>(                                \
+        (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, drow, w.items, w.sorted,    \
+        w.totals, (T*)dqpart, slabs, nbk, d.N, d.Nq, d.q_start, d.Hkv, d.nb, nbw, d.K,          \
+        (int)d.slots, scale);                                                                   \
     prof_after(MSA_K_ATTN_BWD, s);                                                              \
     if ((e = hipGetLastError()) != hipSuccess) return e;                                        \
     if (nrg > 0)                                                                                \
@@ -685,9 +819,13 @@ static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const voi
   }
 #undef MSA_BWD_CASE
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (nkv > 0) {
-    f32_to_kernel<T><<<cgrid, 256, 0, s>>>(dk_acc, nkv, (T*)dk);
-    f32_to_kernel<T><<<cgrid, 256, 0, s>>>(dv_acc, nkv, (T*)dv);
+  if (nbk > 0) {
+    prof_before(MSA_K_BWD_FINALIZE, s);
+    attn_bwd_finalize_kernel<T, D, bwd_rows<T>() / 32>
+        <<<(unsigned)std::min(nbk, 4096), 256, 0, s>>>(slabs, w.item_off, w.totals,
+                                                       nbk, grid, d.N, d.Hkv, d.nb, nbw,
+                                                       (T*)dk, (T*)dv);
+    prof_after(MSA_K_BWD_FINALIZE, s);
   }
   return hipGetLastError();
 }
@@ -695,17 +833,18 @@ static hipError_t bwd_run(const Dims& d, const void* q, const void* k, const voi
 hipError_t launch_attn_bwd(const Dims& d, const void* q, const void* k, const void* v,
                            const int32_t* ids, const void* out, const float* lse,
                            const void* dout, const AttnWs& w,
-                           float* drow, void* dqpart, float* dk_acc, float* dv_acc, void* dq,
+                           float* drow, void* dqpart, float* slabs, void* dq,
                            void* dk, void* dv, hipStream_t s) {
+  if (d.nwin != 1 || !w.sorted) return hipErrorInvalidValue;  // one bucket per (b, group, block)
   if (d.dtype == MSA_BF16) {
     if (d.D == 128)
-      return bwd_run<bf16, 128>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq,
-                                dk, dv, s);
+      return bwd_run<bf16, 128>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, slabs, dq, dk,
+                                dv, s);
     if (d.D == 64)
-      return bwd_run<bf16, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq,
-                               dk, dv, s);
+      return bwd_run<bf16, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, slabs, dq, dk,
+                               dv, s);
   } else if (d.D == 64) {
-    return bwd_run<float, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, dk_acc, dv_acc, dq, dk,
+    return bwd_run<float, 64>(d, q, k, v, ids, out, lse, dout, w, drow, dqpart, slabs, dq, dk,
                               dv, s);
   }
   return hipErrorInvalidValue;

@@ -128,6 +128,27 @@ __device__ __forceinline__ vec8<T> lds_frag(const i32x4* tile, int r, int c0) {
   }
 }
 
+// The persistent kernels' split of the work items over a grid of workgroups
+// (a multiple of 8; workgroup w runs on XCD w % 8): each XCD gets an equal
+// contiguous share, cut into equal contiguous ranges of its workgroups in
+// order. owner(it) is the workgroup whose range holds item it (total > 0).
+struct ItemSplit {
+  int total, nwg_x, per_x, per_wg;
+  __device__ ItemSplit(int total_items, int grid)
+      : total(total_items), nwg_x(grid / 8), per_x((total_items + 7) / 8),
+        per_wg((per_x + nwg_x - 1) / nwg_x) {}
+  __device__ void range(int wg, int* i0, int* i1) const {
+    const int x = wg & 7, gx = wg >> 3;
+    const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+    *i0 = x0 + gx * per_wg;
+    *i1 = min(x1, *i0 + per_wg);
+  }
+  __device__ int owner(int it) const {
+    const int x = it / per_x;
+    return ((it - x * per_x) / per_wg) * 8 + x;
+  }
+};
+
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -153,6 +174,12 @@ struct Dims {
 #endif
 constexpr int kQueryWindow = MSA_QUERY_WINDOW;
 
+// Backward: at most this many persistent workgroups (a multiple of 8). The
+// dK/dV (and dk_idx) sums of a run of items of one bucket go to fp32 slabs of
+// 128 keys: one per bucket, plus two per workgroup for the runs it shares with
+// a neighbour.
+constexpr int kBwdMaxGrid = 256;
+
 // Workspace of the attention and KL calls (bucketing + partials).
 struct AttnWs {
   int32_t* counts;    // [buckets]
@@ -164,6 +191,9 @@ struct AttnWs {
   int32_t* entries;   // [entries_max]: (t << 6) | slot
   int32_t* chunk_e;   // [buckets / 4096 + 1]: entry count per scan chunk
   int32_t* chunk_i;   // [buckets / 4096 + 1]: item count per scan chunk
+  // [entries_max] or null: when set, bucketing also writes the entries here in
+  // row order inside each bucket (the order the backward sums in)
+  int32_t* sorted;
 };
 
 // Launch hooks around each kernel (kernel ids MSA_K_* of msa_timing.h). The
@@ -204,11 +234,10 @@ hipError_t launch_combine_local(const Dims& d, const void* q, const void* k, con
 hipError_t launch_attn_bwd(const Dims& d, const void* q, const void* k, const void* v,
                            const int32_t* ids, const void* out, const float* lse,
                            const void* dout, const AttnWs& w, float* drow, void* dqpart,
-                           float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
-                           hipStream_t s);
+                           float* slabs, void* dq, void* dk, void* dv, hipStream_t s);
 hipError_t launch_idx_bwd(const Dims& d, const void* qi, const void* ki, const int32_t* ids,
                           const float* dl, float coef, const AttnWs& w, float* dqpart,
-                          float* dk_acc, void* dq, void* dk, hipStream_t s);
+                          float* slabs, void* dq, void* dk, hipStream_t s);
 hipError_t launch_kl(const Dims& d, const void* q, const void* k, const void* q_idx,
                      const void* k_idx, const int32_t* ids, const float* lse_main,
                      const AttnWs& w, float* idx_stats, float* lse_idx, float* kl_part,

@@ -141,6 +141,37 @@ def test_bwd_full_size_sampled():
     assert ek <= 1e-3, ek
 
 
+def test_bwd_bitwise_repeatable():
+    """Training workload (2 x 32768 tokens): two calls of msa_attn_bwd and of msa_idx_bwd on
+    the same inputs give the same bits. Every sum has a fixed order: entries in row order
+    inside each bucket, dk / dv / dk_idx slabs of a bucket added in item order (its hot
+    buckets span many workgroups), dq and dq_idx partials in slot order."""
+    import learned_kv_block_amd as msa
+    cfg = si.CONFIGS["train_b2_n32768"]
+    print(f"[bwd] start repeatability {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg, names=("q", "k", "v", "q_idx", "k_idx", "dout"))
+    sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, num_q_heads=cfg.num_q_heads,
+                         head_dim=cfg.head_dim)
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], idx_dim=cfg.idx_dim)
+    first = msa.msa_attn_bwd(x["q"], x["k"], x["v"], sel["ids"], out, lse, x["dout"],
+                             idx_dim=cfg.idx_dim)
+    second = msa.msa_attn_bwd(x["q"], x["k"], x["v"], sel["ids"], out, lse, x["dout"],
+                              idx_dim=cfg.idx_dim)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), first, second):
+        assert torch.equal(a, b), name
+    del first, second
+    kl = msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse)
+    ia = msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], kl["dlogits"], 1.0,
+                         num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    ib = msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], kl["dlogits"], 1.0,
+                         num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    torch.cuda.synchronize()
+    assert torch.equal(ia[0], ib[0]), "dq_idx"
+    assert torch.equal(ia[1], ib[1]), "dk_idx"
+    print(f"[bwd] repeatability {cfg.name}: ok", flush=True)
+
+
 IDX_CASES = [
     si.CONFIGS["tiny_f32_n1024"],
     _cfg("bf16_g16_idx", seqlen_kv=1000, seqlen_q=1000, num_q_heads=64, num_kv_heads=4, topk=4),
