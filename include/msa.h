@@ -128,6 +128,23 @@ msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_i
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * msa_index_block_lse — the index forward with per-block log-sum-exp (KL
+ * alignment note §6: the index forward keeps one LSE per block, and the
+ * student's LSE_idx is their log-sum-exp over the selected blocks).
+ *
+ *  in   q_idx, k_idx        device, layouts above
+ *  out  block_scores        device fp32 [batch, seqlen_q, num_kv_heads, nb]:
+ *                           M[i,b], the same values msa_select computes
+ *  out  block_lse           device fp32, same layout: log sum over the keys j
+ *                           of block b with j <= i of exp(S_idx[i,j]),
+ *                           S_idx = q_idx.k_idx / sqrt(d_idx)
+ *  Both outputs are -inf for blocks past the row's local block. The buffers
+ *  belong to the caller; no workspace. Errors as msa_select.
+ */
+msa_status msa_index_block_lse(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                               float* block_scores, float* block_lse, hipStream_t stream);
+
+/*
  * msa_attn_fwd — exact softmax attention over the selected blocks ("2.4"
  * eq. 2 restricted to the support; MSA vs DSA indexer note §2.3: the group's
  * heads share the block list and their KV head, each keeps its own query;

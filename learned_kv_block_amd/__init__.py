@@ -53,7 +53,7 @@ KERNELS = ["index_blockmax", "topk", "bucket_hist", "bucket_scan", "bucket_scatt
 EXPORTS = ["msa_workspace_size", "msa_select", "msa_attn_fwd", "msa_kl_align", "msa_attn_bwd",
            "msa_idx_bwd", "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
            "msa_index_quantize_fp8", "msa_select_fp8", "msa_status_string",
-           "msa_attn_fwd_noalloc"]
+           "msa_attn_fwd_noalloc", "msa_index_block_lse"]
 TIMING_EXPORTS = ["msa_prof_begin", "msa_prof_end"]
 
 
@@ -108,7 +108,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.c_size_t, P]
         L.msa_index_quantize_fp8.argtypes = [S, P, P, P, P, P, P, P]
         L.msa_select_fp8.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
-        for f in ("msa_select", "msa_attn_fwd", "msa_attn_fwd_noalloc", "msa_kl_align",
+        L.msa_index_block_lse.argtypes = [S, P, P, P, P, P]
+        for f in ("msa_select", "msa_index_block_lse", "msa_attn_fwd", "msa_attn_fwd_noalloc",
+                  "msa_kl_align",
                   "msa_attn_bwd", "msa_idx_bwd",
                   "msa_dense_lse", "msa_kl_dense", "msa_kl_dense_bwd", "msa_block_recall",
                   "msa_index_quantize_fp8", "msa_select_fp8"):
@@ -240,6 +242,28 @@ def msa_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_start: int
     if want_margin:
         out["margin"] = margin
     return out
+
+
+def msa_index_block_lse(q_idx: torch.Tensor, k_idx: torch.Tensor, q_start: int = 0,
+                        num_q_heads: Optional[int] = None, head_dim: int = 128):
+    """Index forward with per-block LSE. q_idx [B, Nq, Hkv, d_idx], k_idx [B, N, d_idx].
+
+    Returns dict(block_scores, block_lse), both [B, Nq, Hkv, nb] fp32, -inf past each row's
+    local block. num_q_heads / head_dim only enter the shape check."""
+    _check(q_idx, "q_idx", 4)
+    B, Nq, Hkv, DI = q_idx.shape
+    _expect(k_idx, "k_idx", (B, None, DI), q_idx.dtype)
+    _on_device(q_idx, k_idx)
+    sh = shape_for(q_idx, k_idx, 1, q_start, num_q_heads, head_dim)
+    nb = (k_idx.shape[1] + 127) // 128
+    dev = q_idx.device
+    scores = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev)
+    blse = torch.empty((B, Nq, Hkv, nb), dtype=torch.float32, device=dev)
+    st = lib().msa_index_block_lse(ctypes.byref(sh), _ptr(q_idx), _ptr(k_idx), _ptr(scores),
+                                   _ptr(blse), _stream(q_idx))
+    if st != MSA_OK:
+        raise MsaError(st, "msa_index_block_lse")
+    return {"block_scores": scores, "block_lse": blse}
 
 
 def msa_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_ids: torch.Tensor,

@@ -291,6 +291,25 @@ msa_status msa_select(const msa_shape* shape, const void* q_idx, const void* k_i
   return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
 }
 
+msa_status msa_index_block_lse(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                               float* block_scores, float* block_lse, hipStream_t stream) {
+  Dims d;
+  msa_status st = make_dims(shape, &d);
+  if (st != MSA_OK) return st;
+  if (d.rows == 0) return MSA_OK;
+  if (!q_idx || !k_idx || !block_scores || !block_lse) return MSA_ERR_NULL;
+  if (!aligned16(q_idx) || !aligned16(k_idx)) return MSA_ERR_SHAPE;
+  if ((st = check_device(&d.num_cus)) != MSA_OK) return st;
+  const int64_t n = d.rows * d.Hkv * d.nb;
+  if (launch_fill_f32(block_scores, n, -INFINITY, stream) != hipSuccess ||
+      launch_fill_f32(block_lse, n, -INFINITY, stream) != hipSuccess)
+    return MSA_ERR_DEVICE;
+  prof_before(MSA_K_INDEX_BLOCKMAX, stream);
+  const hipError_t e = launch_index_block_lse(d, q_idx, k_idx, block_scores, block_lse, stream);
+  prof_after(MSA_K_INDEX_BLOCKMAX, stream);
+  return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+}
+
 msa_status msa_attn_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                         const int32_t* block_ids, void* out, float* lse, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {

@@ -209,6 +209,9 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
                                  hipStream_t s);
 hipError_t launch_topk(const Dims& d, const float* M, int32_t* ids, float* margin, hipStream_t s);
+// the tiled index kernel that also writes each causal block's log-sum-exp to BL
+hipError_t launch_index_block_lse(const Dims& d, const void* q_idx, const void* k_idx, float* M,
+                                  float* BL, hipStream_t s);
 // bf16 with one query per sequence: a register-streamed scan of K_idx whose block
 // scores are bit-identical to those of the tiled index kernel
 bool decode_index_supported(const Dims& d);

@@ -58,10 +58,14 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // c ^ swz(r) inside the row, so that the 32 rows a fragment read touches (and
 // the rows a store touches) spread over all banks.
 
-template <typename T, int DI, int HKV, int NW, int CB>
+// LSE: also the per-block log-sum-exp of the index logits over the block's
+// keys j <= i (a running max and sum per key tile, the two lane halves merged
+// at the block's end), written to BL beside the block maxima.
+template <typename T, int DI, int HKV, int NW, int CB, bool LSE>
 __global__ void __launch_bounds__(64 * NW, sizeof(T) == 2 ? 8 / NW : 1)
 index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
-                      float* __restrict__ M, int N, int Nq, int q_start, int nb, float scale) {
+                      float* __restrict__ M, float* __restrict__ BL, int N, int Nq, int q_start,
+                      int nb, float scale) {
   constexpr int NT = 64 * NW;
   constexpr int RT = 64 * NW;              // GEMM rows per tile
   constexpr int QT = RT / HKV;             // queries per tile
@@ -73,7 +77,7 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   constexpr int QCH = 32 * CPR / 64;       // Q_idx chunks per lane per 32-row half
   constexpr int MST = CB + 1;              // block-max row stride (floats): empty column + CB
   constexpr int QBYTES = NW * 32 * CPR * 16;
-  constexpr int MBYTES = RT * MST * 4;
+  constexpr int MBYTES = RT * MST * 4 * (LSE ? 2 : 1);  // block maxima (then block LSEs)
   constexpr int UBYTES = QBYTES > MBYTES ? QBYTES : MBYTES;
   static_assert((128 * CPR) % NT == 0 && (32 * CPR) % 64 == 0, "tile shape");
   __shared__ __attribute__((aligned(16))) char ubuf[UBYTES];  // Q_idx staging, then block maxima
@@ -143,6 +147,8 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   __syncthreads();  // block kb0 is in LDS; every wave has its Q fragments
 
   float* mbuf = reinterpret_cast<float*>(ubuf);
+  float* lbuf = mbuf + RT * MST;  // LSE only
+  const float c2 = scale * kLog2e;  // exp(scale * s) = exp2(c2 * s)
   const int row0 = wave * 64;  // first GEMM row of the wave
   int i_row[2];
 #pragma unroll
@@ -164,7 +170,9 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
       for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
     }
   };
-  // causal mask (MASK) and running in-lane block max of one key tile
+  // causal mask (MASK) and running in-lane block max (LSE: and the sum of
+  // exp(scale (s - max))) of one key tile
+  float l[2] = {0.0f, 0.0f};
   auto reduce_tile = [&](auto masked, f32x16* acc, float* m, int kb, int kt) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -176,6 +184,13 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
       float x = m[ct];
 #pragma unroll
       for (int e = 0; e < 16; e += 2) x = vmax(vmax(x, acc[ct][e]), acc[ct][e + 1]);
+      if constexpr (LSE) {
+        const float mu = x == -INFINITY ? 0.0f : x;  // all masked so far: every term is 0
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f((acc[ct][e] - mu) * c2);
+        l[ct] = l[ct] * __builtin_amdgcn_exp2f((m[ct] - mu) * c2) + sum;
+      }
       m[ct] = x;
     }
   };
@@ -184,8 +199,19 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   auto finish_block = [&](float* m, int kb) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float x = vmax(m[ct], shfl_xor_f(m[ct], 32));
+      const float mo = shfl_xor_f(m[ct], 32);
+      const float x = vmax(m[ct], mo);
       mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0 + 1)] = x;
+      if constexpr (LSE) {
+        const float lo = shfl_xor_f(l[ct], 32);
+        const float mu = x == -INFINITY ? 0.0f : x;
+        const float z = l[ct] * __builtin_amdgcn_exp2f((m[ct] - mu) * c2) +
+                        lo * __builtin_amdgcn_exp2f((mo - mu) * c2);
+        // ln sum exp(scale s) = scale max + ln z
+        lbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0 + 1)] =
+            x == -INFINITY ? -INFINITY : (x * c2 + __builtin_amdgcn_logf(z)) * kLn2;
+        l[ct] = 0.0f;
+      }
     }
   };
 
@@ -236,6 +262,7 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     const int tq = t0 + row / HKV;
     if (tq >= Nq || kb0 + kk > ((q_start + tq) >> 7)) continue;
     M[(grow0 + row) * nb + kb0 + kk] = mbuf[row * MST + kk + 1] * scale;  // scale > 0 commutes with max
+    if constexpr (LSE) BL[(grow0 + row) * nb + kb0 + kk] = lbuf[row * MST + kk + 1];
   }
 }
 
@@ -246,42 +273,56 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
 #define MSA_IDX_CB 32
 #endif
 
-template <typename T, int DI, int HKV, int NW>
-static hipError_t index_launch(const Dims& d, const void* qi, const void* ki, float* M,
+template <typename T, int DI, int HKV, int NW, bool LSE>
+static hipError_t index_launch(const Dims& d, const void* qi, const void* ki, float* M, float* BL,
                                hipStream_t s) {
-  constexpr int CB = MSA_IDX_CB;
+  constexpr int CB = LSE ? 16 : MSA_IDX_CB;  // LSE: two LDS staging arrays
   constexpr int QT = 64 * NW / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
   const int nchunks = (d.nb + CB - 1) / CB;
   if (ntiles == 0 || d.B == 0) return hipSuccess;
   dim3 grid(ntiles, nchunks, d.B);
   const float scale = 1.0f / sqrtf((float)DI);
-  index_blockmax_kernel<T, DI, HKV, NW, CB><<<grid, 64 * NW, 0, s>>>(
-      (const T*)qi, (const T*)ki, M, d.N, d.Nq, d.q_start, d.nb, scale);
+  index_blockmax_kernel<T, DI, HKV, NW, CB, LSE><<<grid, 64 * NW, 0, s>>>(
+      (const T*)qi, (const T*)ki, M, BL, d.N, d.Nq, d.q_start, d.nb, scale);
   return hipGetLastError();
 }
 
-template <typename T, int DI, int HKV>
+template <typename T, int DI, int HKV, bool LSE>
 static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, float* M,
-                                 hipStream_t s) {
+                                 float* BL, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
-    return index_launch<T, DI, HKV, 4>(d, qi, ki, M, s);  // fp32 tiles: LDS and register limits
+    // fp32 tiles: LDS and register limits
+    return index_launch<T, DI, HKV, 4, LSE>(d, qi, ki, M, BL, s);
   } else {
     // a decode step has a few rows per sequence: one-wave tiles (64 rows)
     // instead of 512-row tiles keep the MFMA work near the rows that exist
-    if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1>(d, qi, ki, M, s);
-    return index_launch<T, DI, HKV, MSA_IDX_NW>(d, qi, ki, M, s);
+    if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1, LSE>(d, qi, ki, M, BL, s);
+    return index_launch<T, DI, HKV, MSA_IDX_NW, LSE>(d, qi, ki, M, BL, s);
   }
 }
 
-template <typename T, int DI>
+template <typename T, int DI, bool LSE>
 static hipError_t index_dispatch_hkv(const Dims& d, const void* qi, const void* ki, float* M,
-                                     hipStream_t s) {
+                                     float* BL, hipStream_t s) {
   switch (d.Hkv) {
-    case 1: return index_dispatch<T, DI, 1>(d, qi, ki, M, s);
-    case 2: return index_dispatch<T, DI, 2>(d, qi, ki, M, s);
-    case 4: return index_dispatch<T, DI, 4>(d, qi, ki, M, s);
-    case 8: return index_dispatch<T, DI, 8>(d, qi, ki, M, s);
+    case 1: return index_dispatch<T, DI, 1, LSE>(d, qi, ki, M, BL, s);
+    case 2: return index_dispatch<T, DI, 2, LSE>(d, qi, ki, M, BL, s);
+    case 4: return index_dispatch<T, DI, 4, LSE>(d, qi, ki, M, BL, s);
+    case 8: return index_dispatch<T, DI, 8, LSE>(d, qi, ki, M, BL, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool LSE>
+static hipError_t index_dispatch_all(const Dims& d, const void* q_idx, const void* k_idx,
+                                     float* M, float* BL, hipStream_t s) {
+  if (d.dtype == MSA_BF16) {
+    if (d.DI == 64) return index_dispatch_hkv<bf16, 64, LSE>(d, q_idx, k_idx, M, BL, s);
+    if (d.DI == 32) return index_dispatch_hkv<bf16, 32, LSE>(d, q_idx, k_idx, M, BL, s);
+  } else {
+    if (d.DI == 64) return index_dispatch_hkv<float, 64, LSE>(d, q_idx, k_idx, M, BL, s);
+    if (d.DI == 32) return index_dispatch_hkv<float, 32, LSE>(d, q_idx, k_idx, M, BL, s);
   }
   return hipErrorInvalidValue;
 }
@@ -289,14 +330,12 @@ static hipError_t index_dispatch_hkv(const Dims& d, const void* qi, const void* 
 hipError_t launch_index_blockmax(const Dims& d, const void* q_idx, const void* k_idx, float* M,
                                  hipStream_t s) {
   if (decode_index_supported(d)) return launch_decode_index(d, q_idx, k_idx, M, s);
-  if (d.dtype == MSA_BF16) {
-    if (d.DI == 64) return index_dispatch_hkv<bf16, 64>(d, q_idx, k_idx, M, s);
-    if (d.DI == 32) return index_dispatch_hkv<bf16, 32>(d, q_idx, k_idx, M, s);
-  } else {
-    if (d.DI == 64) return index_dispatch_hkv<float, 64>(d, q_idx, k_idx, M, s);
-    if (d.DI == 32) return index_dispatch_hkv<float, 32>(d, q_idx, k_idx, M, s);
-  }
-  return hipErrorInvalidValue;
+  return index_dispatch_all<false>(d, q_idx, k_idx, M, nullptr, s);
+}
+
+hipError_t launch_index_block_lse(const Dims& d, const void* q_idx, const void* k_idx, float* M,
+                                  float* BL, hipStream_t s) {
+  return index_dispatch_all<true>(d, q_idx, k_idx, M, BL, s);
 }
 
 // ============================================================== block Top-k
