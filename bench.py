@@ -46,6 +46,14 @@ KERNEL_FILES = {
     "work_items_kernel": ("work_items", ["msa_attn.hip"]),
     "sparse_attn_pipe_kernel": ("sparse_attn", ["msa_attn.hip"]),
     "combine_local_kernel": ("combine", ["msa_attn.hip"]),
+    "decode_index_kernel": ("index_blockmax", ["msa_decode.hip"]),
+    "decode_attn_kernel": ("sparse_attn", ["msa_decode.hip"]),
+    "kl_main_pipe_kernel": ("kl_main", ["msa_kl.hip"]),
+    "attn_bwd_kernel": ("attn_bwd", ["msa_bwd.hip"]),
+    "dq_sum_kernel": ("dq_sum", ["msa_bwd.hip"]),
+    "idx_bwd_kernel": ("idx_bwd", ["msa_bwd.hip"]),
+    "bucket_sort_kernel": ("bucket_sort", ["msa_attn.hip"]),
+    "attn_bwd_finalize_kernel": ("bwd_finalize", ["msa_bwd.hip"]),
 }
 
 
@@ -370,21 +378,23 @@ def ingest_counters(fetch_csv, write_csv, workload, commands):
     import csv
     import collections
 
-    def per_kernel(path, counter):
-        acc = collections.defaultdict(lambda: [0.0, set()])
+    def per_dispatch(path, counter):
+        """{kernel: {dispatch id: KiB}} (rows of one dispatch summed)."""
+        acc = collections.defaultdict(lambda: collections.defaultdict(float))
         for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != counter:
-                continue
-            acc[r["Kernel_Name"]][0] += float(r["Counter_Value"])
-            acc[r["Kernel_Name"]][1].add(r["Dispatch_Id"])
-        return {k: (v[0], len(v[1])) for k, v in acc.items()}
+            if r["Counter_Name"] == counter:
+                acc[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return acc
 
-    fe, wr = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    copy = [k for k in fe if "copyBuffer" in k or "copy_kernel" in k]
+    fd, wd = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    fe = {k: (sum(v.values()), len(v)) for k, v in fd.items()}
+    wr = {k: (sum(v.values()), len(v)) for k, v in wd.items()}
+    copy = [k for k in fd if "copyBuffer" in k or "copy_kernel" in k]
     gib_kib = float(1 << 20)
-    # the largest single copy dispatch is the 1 GiB calibration copy
-    fcopy = max(fe[k][0] / fe[k][1] for k in copy)
-    wcopy = max(wr[k][0] / wr[k][1] for k in copy if k in wr)
+    # the largest single copy dispatch is the 1 GiB calibration copy (other copies of
+    # the process are small): it reads and writes 1 GiB
+    fcopy = max(max(fd[k].values()) for k in copy)
+    wcopy = max(max(wd[k].values()) for k in copy if k in wd)
     fs, ws = gib_kib / fcopy, gib_kib / wcopy
     kernels = {}
     for frag, (name, files) in KERNEL_FILES.items():
