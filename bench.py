@@ -7,10 +7,12 @@ Hkv = 4, d = 128, d_idx = 64, 128-token blocks, k = 16, bf16 inputs with
 seeded synthetic values (inputs resident in HBM before timing).
 
 Prints one JSON line: query-tokens/s, ms per step, the effective-FLOP MFMA
-fraction of the whole layer, the roofline of the dominant kernel (the KV-outer
-sparse attention, timed live with HIP events over the timed steps; bound by
-its gathered-Q and partial-output traffic, with its MFMA share alongside) and
-the fp64 oracle timed on the host on a bounded row sample.
+fraction of the whole layer, every kernel of the step against its own roofline
+(MFMA for the index GEMM and the attention, HBM for the Top-k, the bucketing
+and the combine), the roofline of the dominant kernel (the KV-outer sparse
+attention, timed live with HIP events over the timed steps in the measurement
+build; its gathered-Q and partial-output bytes and the counter bytes alongside)
+and the fp64 oracle timed on the host on a bounded row sample.
 """
 from __future__ import annotations
 
@@ -160,7 +162,7 @@ def cpu_baseline(cfg, seconds_target=15.0):
     # calibrate on a small sample, then size the sample to ~seconds_target
     probe = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=2 * threads))
     dt = run(probe)
-    n = int(max(2 * threads, min(4096, len(probe) * seconds_target / max(dt, 1e-3))))
+    n = int(max(2 * threads, min(16384, len(probe) * seconds_target / max(dt, 1e-3))))
     rows = np.sort(rng.integers(0, cfg.batch * cfg.seqlen_q, size=n))
     dt = run(rows)
     return {"value": n / dt, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
@@ -318,6 +320,8 @@ def step_work(cfg, ids):
     """Algorithmic work of each kernel of one prefill / decode step (bf16), from the GPU's
     own selection. Returns {timer name: dict(bound, flops | bytes, what)}."""
     import torch
+
+    import seeded_inputs as si
     B, Nq, Hkv, G, D, K = (cfg.batch, cfg.seqlen_q, cfg.num_kv_heads, cfg.group_size,
                            cfg.head_dim, cfg.topk)
     Hq = Hkv * G
@@ -353,6 +357,20 @@ def step_work(cfg, ids):
                         what="partials (bf16 O + fp32 LSE) read, Q read and O written once, "
                              "LSE written; the local block's attention (flops) runs here"),
     }
+    if Nq == 1 and cfg.dtype == si.BF16:
+        # decode: the K_idx scan and the query-outer attention stream their operands once
+        # (no bucketing, partials or combine), so both are bound by HBM
+        DI = cfg.idx_dim
+        keys = B * int(torch.clamp((L + 1) * 128, max=cfg.seqlen_kv).sum().item())
+        work["index_blockmax"] = dict(
+            bound="hbm", bytes=keys * DI * 2 + rows * DI * 2 + 4 * rows * int((L + 1).max()),
+            flops=f_idx, what="K_idx rows of blocks 0..L read once per sequence, Q_idx read, "
+                              "block scores written")
+        work["sparse_attn"] = dict(
+            bound="hbm", bytes=n_sel * 2 * 128 * D * 2 + rows_q * Hq * (2 * D * 2 + 4),
+            flops=f_attn, what="K and V of each selected block read once per (sequence, "
+                               "group), q read, out and LSE written")
+        del work["bucketing"], work["combine"]
     return work, f_idx, f_attn, f_loc, n_sel
 
 
