@@ -1524,14 +1524,33 @@ combine_local_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         issue(j, dn, e + W - NE);
     }
     const int t = apos(qi) - q_start;
-    bf16* dst = out + ((size_t)(b * (size_t)Nq + t) * Hq + r * G) * D;
+    // the query's output replaces its local O rows in Ob (read for the last time
+    // above); the wave writes its finished queries of the tile together (8 KB
+    // bursts instead of 4 KB between the partial reads: HBM loses less to
+    // turning between reads and writes), before the next tile's phase A
+    // overwrites Ob
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       if (!ok[c]) continue;
+      const int u = lane + 64 * c, orow = orow0 + hd[c];
       vec8<bf16> res;
 #pragma unroll
       for (int x = 0; x < 8; ++x) res[x] = cvt<bf16>(acc[c][x]);
-      st8_nt<bf16>(dst + 8 * (lane + 64 * c), res);  // read back only by the caller
+      st8<bf16>(Ob + orow * D + 8 * ((u % UPH) ^ (orow % CPR)), res);
+    }
+    if (i == QPW - 1 || qi == qi_hi) {  // uniform
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the rows are in LDS
+      __builtin_amdgcn_wave_barrier();
+      for (int qq = max(qi_lo, qi - i); qq <= qi; ++qq) {
+        const int orq = (wave * QPW + qq % QPW) * G;
+        bf16* dq = out + ((size_t)(b * (size_t)Nq + (apos(qq) - q_start)) * Hq + r * G) * D;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (!ok[c]) continue;
+          const int u = lane + 64 * c, orow = orq + hd[c];
+          st8_nt<bf16>(dq + 8 * u, ld8<bf16>(Ob + orow * D + 8 * ((u % UPH) ^ (orow % CPR))));
+        }
+      }
     }
     if constexpr (kPack) {  // lanes of slot 0 hold every head once
       if (4 * lane < G) {
