@@ -316,9 +316,10 @@ def dense_main(args):
     print(json.dumps(line), flush=True)
 
 
-def step_work(cfg, ids):
-    """Algorithmic work of each kernel of one prefill / decode step (bf16), from the GPU's
-    own selection. Returns {timer name: dict(bound, flops | bytes, what)}."""
+def step_work(cfg, ids, fp8=False):
+    """Algorithmic work of each kernel of one prefill / decode step (bf16, or with the FP8
+    index: 1-byte index operands), from the GPU's own selection. Returns
+    {timer name: dict(bound, flops | bytes, what)}."""
     import torch
 
     import seeded_inputs as si
@@ -360,12 +361,15 @@ def step_work(cfg, ids):
     if Nq == 1 and cfg.dtype == si.BF16:
         # decode: the K_idx scan and the query-outer attention stream their operands once
         # (no bucketing, partials or combine), so both are bound by HBM
-        DI = cfg.idx_dim
+        DI, eb = cfg.idx_dim, (1 if fp8 else 2)
         keys = B * int(torch.clamp((L + 1) * 128, max=cfg.seqlen_kv).sum().item())
+        nbl = int((L + 1).max())
         work["index_blockmax"] = dict(
-            bound="hbm", bytes=keys * DI * 2 + rows * DI * 2 + 4 * rows * int((L + 1).max()),
+            bound="hbm", bytes=keys * DI * eb + rows * DI * eb + 4 * rows * nbl
+            + (4 * B * nbl + 4 * rows if fp8 else 0),
             flops=f_idx, what="K_idx rows of blocks 0..L read once per sequence, Q_idx read, "
-                              "block scores written")
+                              "block scores written" + (" (E4M3 bytes and their block and row "
+                                                         "exponents)" if fp8 else ""))
         work["sparse_attn"] = dict(
             bound="hbm", bytes=n_sel * 2 * 128 * D * 2 + rows_q * Hq * (2 * D * 2 + 4),
             flops=f_attn, what="K and V of each selected block read once per (sequence, "
@@ -554,7 +558,7 @@ def main():
     if ids is None:
         ids = step()
         torch.cuda.synchronize()
-    work, f_idx, f_attn, f_loc, n_sel = step_work(cfg, ids)
+    work, f_idx, f_attn, f_loc, n_sel = step_work(cfg, ids, fp8=args.fp8)
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -595,6 +599,7 @@ def main():
             continue
         e = {"ms": ms, "launches_per_step": nl / max(1, args.steps), "bound": w["bound"],
              "what": w["what"]}
+        e["timer"] = src if name != "bucketing" else "bucket_*"
         if w["bound"] == "mfma":
             peak = PEAK_FP8 if (name == "index_blockmax" and args.fp8) else PEAK_BF16
             e.update(flops=w["flops"], achieved_tflops=w["flops"] / (ms * 1e-3) / 1e12,
@@ -621,12 +626,12 @@ def main():
         roofline = {"bound": "mfma", "kernel": dom, "achieved": d["achieved_tflops"],
                     "peak": d["peak_tflops"], "unit": "TFLOP/s", "frac": d["frac"],
                     "traffic": d["counter_bytes"], "avg_ms": d["ms"],
-                    "launches": launches.get(dom, 0), "flops_per_launch": d["flops"]}
+                    "launches": launches.get(d["timer"], 0), "flops_per_launch": d["flops"]}
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d["achieved_gbs"],
                     "peak": d["peak_gbs"], "unit": "GB/s", "frac": d["frac"],
                     "traffic": d["counter_bytes"], "avg_ms": d["ms"],
-                    "launches": launches.get(dom, 0), "bytes_per_launch": d["bytes"]}
+                    "launches": launches.get(d["timer"], 0), "bytes_per_launch": d["bytes"]}
     for extra in ("side_bytes", "min_bytes", "counter_over_min_bytes"):
         if extra in d:
             roofline[extra] = d[extra]

@@ -388,9 +388,122 @@ static hipError_t fp8_index_hkv(const Dims& d, const uint8_t* q8, const int32_t*
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------- decode scan
+//
+// One query per sequence: the register-streamed scan of the bf16 decode step
+// (each wave takes 8 consecutive blocks of one sequence and loads a block's
+// fragments straight from HBM, one block ahead of its products; no LDS, no
+// barrier) on the FP8 operands. Each key tile is the tiled kernel's single
+// 32x32x64 instruction on the same bytes (lane l: K8 row 32kt + l%32, bytes
+// 32h .. 32h+31, h = l/32; the Hkv index-query rows as B columns, zero past
+// Hkv), and the maxima are scaled the same way, so the block scores equal the
+// tiled kernel's bit for bit.
+template <int DI>
+__global__ void __launch_bounds__(256, 2)
+decode_index_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restrict__ q_exp,
+                        const uint8_t* __restrict__ k8, const int32_t* __restrict__ k_exp,
+                        float* __restrict__ M, int N, int q_start, int Hkv, int nb, int chunks,
+                        int total_waves, float inv_sqrt_di) {
+  constexpr int CB = 8;  // blocks per wave
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int gw = blockIdx.x * 4 + wave;
+  if (gw >= total_waves) return;  // the last workgroup may have spare waves
+  const int b = gw / chunks, ch = gw % chunks;
+  const int i = q_start, L = i / 128;
+  const int kb0 = ch * CB;
+  if (kb0 > L) return;
+  const int kb1 = min(kb0 + CB - 1, L);
+  const bool on = DI == 64 || h == 0;  // d_idx = 32: the upper lane half holds zeros
+  i32x8 qf;
+  {
+    i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+    if (on && l32 < Hkv) {
+      const i32x4* p = reinterpret_cast<const i32x4*>(q8 + ((size_t)b * Hkv + l32) * DI + 32 * h);
+      lo = p[0];
+      hi = p[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[e] = lo[e];
+      qf[4 + e] = hi[e];
+    }
+  }
+  const uint8_t* kbase = k8 + (size_t)b * N * DI;
+  auto load = [&](int blk, i32x4* f) {  // f[2kt], f[2kt + 1]: the lane's 32 bytes of tile kt
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = min(blk * 128 + 32 * kt + l32, N - 1);  // keys past N are masked
+      if (on) {
+        const i32x4* p = reinterpret_cast<const i32x4*>(kbase + (size_t)key * DI + 32 * h);
+        f[2 * kt] = p[0];
+        f[2 * kt + 1] = p[1];
+      } else {
+        f[2 * kt] = i32x4{0, 0, 0, 0};
+        f[2 * kt + 1] = i32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  float* mrow = M + (size_t)b * Hkv * nb;  // row r of sequence b: mrow + r * nb
+  auto block = [&](int blk, const i32x4* f) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      i32x8 af;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        af[e] = f[2 * kt][e];
+        af[4 + e] = f[2 * kt + 1][e];
+      }
+      f32x16 z;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+      f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, qf, z, 0, 0, 0, 127, 0, 127);
+      if (blk == L) {  // the local block: keys after the query are masked
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (blk * 128 + 32 * kt + drow(e, h) > i) acc[e] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = vmax(vmax(m, acc[e]), acc[e + 1]);
+    }
+    m = vmax(m, shfl_xor_f(m, 32));
+    if (h == 0 && l32 < Hkv) {
+      const int ex = q_exp[(size_t)b * Hkv + l32] + k_exp[(size_t)b * nb + blk];
+      mrow[(size_t)l32 * nb + blk] = m * ldexpf(inv_sqrt_di, ex);
+    }
+  };
+  i32x4 fa[8], fb[8];
+  load(kb0, fa);
+  for (int blk = kb0; blk <= kb1; blk += 2) {
+    if (blk + 1 <= kb1) load(blk + 1, fb);
+    block(blk, fa);
+    if (blk + 1 > kb1) break;
+    if (blk + 2 <= kb1) load(blk + 2, fa);
+    block(blk + 1, fb);
+  }
+}
+
+template <int DI>
+static hipError_t fp8_decode_launch(const Dims& d, const uint8_t* q8, const int32_t* qe,
+                                    const uint8_t* k8, const int32_t* ke, float* M,
+                                    hipStream_t s) {
+  const int L = d.q_start / 128;
+  const int chunks = (L + 8) / 8;  // 8 blocks per wave
+  const int total = d.B * chunks;
+  decode_index_fp8_kernel<DI><<<(unsigned)((total + 3) / 4), 256, 0, s>>>(
+      q8, qe, k8, ke, M, d.N, d.q_start, d.Hkv, d.nb, chunks, total,
+      (float)(1.0 / std::sqrt((double)DI)));  // the tiled kernel's constant
+  return hipGetLastError();
+}
+
 hipError_t launch_index_blockmax_fp8(const Dims& d, const uint8_t* q8, const int32_t* q_exp,
                                      const uint8_t* k8, const int32_t* k_exp, float* M,
                                      hipStream_t s) {
+  if (d.Nq == 1 && d.rows > 0 && d.Hkv <= 32) {  // one query per sequence: the decode scan
+    if (d.DI == 64) return fp8_decode_launch<64>(d, q8, q_exp, k8, k_exp, M, s);
+    if (d.DI == 32) return fp8_decode_launch<32>(d, q8, q_exp, k8, k_exp, M, s);
+  }
   if (d.DI == 64) return fp8_index_hkv<64>(d, q8, q_exp, k8, k_exp, M, s);
   if (d.DI == 32) return fp8_index_hkv<32>(d, q8, q_exp, k8, k_exp, M, s);
   return hipErrorInvalidValue;

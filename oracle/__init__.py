@@ -64,7 +64,7 @@ def _L():
         lib.msa_ref_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.msa_ref_e4m3_decode.restype = ctypes.c_double
         lib.msa_ref_fp8_scale_exp.argtypes = [ctypes.c_double]
-        lib.msa_ref_quantize_fp8.argtypes = [sp, P, P, I64, P, P, P, P]
+        lib.msa_ref_quantize_fp8.argtypes = [sp, P, P, I64, P, P, P, P, ctypes.c_int]
         lib.msa_ref_select_fp8.argtypes = [sp, P, P, P, P, P, I64, P, P, P, ctypes.c_int]
         for f in ("msa_ref_topk_row", "msa_ref_select", "msa_ref_attn", "msa_ref_kl_row",
                   "msa_ref_kl", "msa_ref_attn_bwd", "msa_ref_idx_bwd", "msa_ref_fp8_scale_exp",
@@ -301,7 +301,7 @@ def quantize_fp8(shape: RefShape, q_idx, k_idx=None):
         k8 = np.zeros((shape.batch, shape.seqlen_kv, di), dtype=np.uint8)
         ke = np.empty((shape.batch, nb), dtype=np.int32)
     rc = _L().msa_ref_quantize_fp8(ctypes.byref(shape), _p(q_idx), _p(k_idx), n, _p(q8), _p(qe),
-                                   _p(k8), _p(ke))
+                                   _p(k8), _p(ke), threads())
     assert rc == 0, rc
     out = {"q8": q8, "q_exp": qe}
     if k_idx is not None:

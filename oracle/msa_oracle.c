@@ -670,12 +670,15 @@ int msa_ref_fp8_scale_exp(double amax) {
  */
 int msa_ref_quantize_fp8(const msa_ref_shape* s, const void* q_idx, const void* k_idx,
                          int64_t nrows, uint8_t* q8, int32_t* q_exp, uint8_t* k8,
-                         int32_t* k_exp) {
+                         int32_t* k_exp, int nthreads) {
   if (!shape_ok(s) || nrows < 0 || (nrows > 0 && (!q_idx || !q8 || !q_exp)) ||
       (k8 && (!k_idx || !k_exp)))
     return REF_ERR_ARG;
+  if (nthreads < 1) nthreads = 1;
   const int Hkv = s->num_kv_heads, di = s->idx_dim, Bk = s->block_size, nb = num_blocks(s);
   const int64_t N = s->seqlen_kv;
+  /* rows and blocks are independent: threads split them, each writes its own outputs */
+#pragma omp parallel for schedule(static) num_threads(nthreads)
   for (int64_t x = 0; x < nrows * Hkv; ++x) {
     double amax = 0.0;
     for (int c = 0; c < di; ++c) amax = fmax(amax, fabs(ld(q_idx, s->dtype, x * di + c)));
@@ -685,20 +688,22 @@ int msa_ref_quantize_fp8(const msa_ref_shape* s, const void* q_idx, const void* 
       q8[x * di + c] = msa_ref_e4m3_encode(ldexp(ld(q_idx, s->dtype, x * di + c), -e));
   }
   if (k8) {
-    for (int64_t b = 0; b < s->batch; ++b)
-      for (int blk = 0; blk < nb; ++blk) {
-        const int64_t j0 = (int64_t)blk * Bk, j1 = j0 + Bk < N ? j0 + Bk : N;
-        double amax = 0.0;
-        for (int64_t j = j0; j < j1; ++j)
-          for (int c = 0; c < di; ++c)
-            amax = fmax(amax, fabs(ld(k_idx, s->dtype, (b * N + j) * di + c)));
-        const int e = msa_ref_fp8_scale_exp(amax);
-        k_exp[b * nb + blk] = e;
-        for (int64_t j = j0; j < j1; ++j)
-          for (int c = 0; c < di; ++c)
-            k8[(b * N + j) * di + c] =
-                msa_ref_e4m3_encode(ldexp(ld(k_idx, s->dtype, (b * N + j) * di + c), -e));
-      }
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t bb = 0; bb < (int64_t)s->batch * nb; ++bb) {
+      const int64_t b = bb / nb;
+      const int blk = (int)(bb % nb);
+      const int64_t j0 = (int64_t)blk * Bk, j1 = j0 + Bk < N ? j0 + Bk : N;
+      double amax = 0.0;
+      for (int64_t j = j0; j < j1; ++j)
+        for (int c = 0; c < di; ++c)
+          amax = fmax(amax, fabs(ld(k_idx, s->dtype, (b * N + j) * di + c)));
+      const int e = msa_ref_fp8_scale_exp(amax);
+      k_exp[b * nb + blk] = e;
+      for (int64_t j = j0; j < j1; ++j)
+        for (int c = 0; c < di; ++c)
+          k8[(b * N + j) * di + c] =
+              msa_ref_e4m3_encode(ldexp(ld(k_idx, s->dtype, (b * N + j) * di + c), -e));
+    }
   }
   return REF_OK;
 }

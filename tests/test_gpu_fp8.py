@@ -123,6 +123,60 @@ def test_fp8_full_size_sampled():
     print(f"[fp8] {cfg.name}: " + json.dumps(rep), flush=True)
 
 
+@pytest.mark.parametrize("di", [64, 32])
+def test_fp8_decode_matches_prefill(di):
+    """One query per sequence runs the register-streamed FP8 scan; it issues the tiled
+    kernel's instruction on the same bytes, so one decode step at the last position gives
+    the last prefill row's FP8 block scores and ids bit for bit."""
+    import learned_kv_block_amd as msa
+    cfg = _cfg(f"fp8_dec_vs_pre_di{di}", batch=2, seqlen_kv=2100, seqlen_q=2100, idx_dim=di,
+               num_kv_heads=4 if di == 64 else 8, num_q_heads=64, topk=6)
+    x = parity.gpu_inputs(cfg, names=("q_idx", "k_idx"))
+    _, pre = _gpu_fp8(cfg, x)
+    dcfg = cfg.replace(seqlen_q=1, q_start=cfg.seqlen_kv - 1)
+    xd = {"q_idx": x["q_idx"][:, -1:].contiguous(), "k_idx": x["k_idx"]}
+    _, dec = _gpu_fp8(dcfg, xd)
+    nbl = (cfg.seqlen_kv - 1) // 128 + 1
+    H = cfg.num_kv_heads
+    sd = dec["block_scores"].reshape(cfg.batch, H, -1)[..., :nbl]
+    sp = pre["block_scores"].reshape(cfg.batch, cfg.seqlen_q, H, -1)[:, -1, :, :nbl]
+    assert torch.equal(sd, sp)
+    assert torch.equal(dec["ids"][:, 0], pre["ids"][:, -1])
+    assert torch.equal(dec["margin"][:, 0], pre["margin"][:, -1])
+
+
+def test_fp8_decode_full_size():
+    """64 x 131072 decode with the FP8 index: every K_idx byte and exponent, and every
+    sequence's selection against the oracle (K_idx generated 8 sequences at a time)."""
+    cfg = si.CONFIGS["decode_b64_n131072"]
+    print(f"[fp8] start {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg, names=("q_idx", "k_idx"))
+    qz, sel = _gpu_fp8(cfg, x)
+    rep = {"rows_checked": 0}
+    H, DI = cfg.num_kv_heads, cfg.idx_dim
+    for b0 in range(0, cfg.batch, 8):
+        rows = np.arange(b0, min(cfg.batch, b0 + 8), dtype=np.int64)  # row = sequence
+        lrows = np.arange(len(rows), dtype=np.int64)
+        shp = oracle.shape_of(cfg.replace(batch=len(rows)))
+        refq = oracle.quantize_fp8(shp, si.host_query_rows(cfg, "q_idx", rows),
+                                   si.host_batch_rows(cfg, "k_idx", rows))
+        ridx = torch.from_numpy(rows).to(qz["q8"].device)
+        np.testing.assert_array_equal(qz["q8"].reshape(-1, H, DI)[ridx].cpu().numpy(), refq["q8"])
+        np.testing.assert_array_equal(qz["q_exp"].reshape(-1, H)[ridx].cpu().numpy(),
+                                      refq["q_exp"])
+        np.testing.assert_array_equal(qz["k8"][b0:b0 + len(rows)].cpu().numpy(), refq["k8"])
+        np.testing.assert_array_equal(qz["k_exp"][b0:b0 + len(rows)].cpu().numpy(),
+                                      refq["k_exp"])
+        part = {}
+        _check_select(cfg, sel, rows, refq, lrows, shp, part)
+        rep["rows_checked"] += len(rows) * H
+        rep["block_scores_max_abs"] = max(rep.get("block_scores_max_abs", 0.0),
+                                          part["block_scores_max_abs"])
+        print(f"[fp8] {cfg.name} sequences {b0}..{rows[-1]} ok", flush=True)
+    assert rep["rows_checked"] == cfg.batch * H
+    print(f"[fp8] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
 def churn_report(cfg, x):
     """FP8 vs bf16 selection on every row (GPU values): changed-row share overall and per
     bf16 cutoff-margin bin, set overlap, and the eq.-(9) bound check."""
