@@ -58,6 +58,12 @@ SMALL = [
     # decode with d=64 and G=4 (heads padded to the 16-row tile), k above the block count
     _small("bf16_decode_g4_d64", batch=5, seqlen_kv=700, seqlen_q=1, q_start=699, num_q_heads=8,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=8),
+    # decode with Hkv=8 (G=2) and a ragged last block; decode with one group (Hkv=1, G=16,
+    # d_idx=32) at a position inside the cache (keys past the query are never scanned)
+    _small("bf16_decode_hkv8", batch=2, seqlen_kv=1500, seqlen_q=1, q_start=1499,
+           num_q_heads=16, num_kv_heads=8, topk=5, with_kl=True),
+    _small("bf16_decode_hkv1_mid", batch=2, seqlen_kv=2000, seqlen_q=1, q_start=1234,
+           num_q_heads=16, num_kv_heads=1, idx_dim=32, topk=4),
     # two queries per sequence, G=8, d=64: one-wave attention on bucketed items
     _small("bf16_g8_q2", batch=2, seqlen_kv=2000, seqlen_q=2, q_start=1998, num_q_heads=16,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=5),
