@@ -172,6 +172,36 @@ def test_bwd_bitwise_repeatable():
     print(f"[bwd] repeatability {cfg.name}: ok", flush=True)
 
 
+def test_bwd_bucket_sort_two_passes():
+    """140000 query rows: the row-order sort of each bucket takes two passes of its
+    131072-row bitmap. Small heads (Hq=2, Hkv=1, d=64, k=2) keep the oracle cheap: dq, dk,
+    dv on every row and key, and two calls give the same bits."""
+    import learned_kv_block_amd as msa
+    cfg = _cfg("bf16_sort_2pass", seqlen_kv=140000, seqlen_q=140000, num_q_heads=2,
+               num_kv_heads=1, head_dim=64, idx_dim=32, topk=2)
+    print(f"[bwd] start {cfg.name}", flush=True)
+    x, ids, dq, dk, dv = _run(cfg)
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], ids, idx_dim=cfg.idx_dim)
+    again = msa.msa_attn_bwd(x["q"], x["k"], x["v"], ids, out, lse, x["dout"],
+                             idx_dim=cfg.idx_dim)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), again):
+        assert torch.equal(a, b), name
+    n = cfg.batch * cfg.seqlen_q
+    rows = np.arange(n, dtype=np.int64)
+    q = si.host_query_rows(cfg, "q", rows)
+    dout = si.host_query_rows(cfg, "dout", rows)
+    gids = ids.reshape(n, cfg.num_kv_heads, cfg.topk).cpu().numpy()
+    rq, rk, rv = oracle.attn_bwd(oracle.shape_of(cfg), q, si.host_tensor(cfg, "k"),
+                                 si.host_tensor(cfg, "v"), gids, dout)
+    t = _tol(cfg)
+    rep = {}
+    _check("dq", dq.float().cpu().numpy().reshape(rq.shape), rq, t, rep)
+    _check("dk", dk.float().cpu().numpy(), rk, t, rep)
+    _check("dv", dv.float().cpu().numpy(), rv, t, rep)
+    print(f"[bwd] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
 IDX_CASES = [
     si.CONFIGS["tiny_f32_n1024"],
     _cfg("bf16_g16_idx", seqlen_kv=1000, seqlen_q=1000, num_q_heads=64, num_kv_heads=4, topk=4),
