@@ -1160,8 +1160,11 @@ combine_kernel(const T* __restrict__ opart, const float* __restrict__ lpart,
 // every later LDS read until all vector loads land.)
 // Only the K/V copy needs a workgroup barrier.
 
+// partial entries in flight per wave, in units of 4 loads per lane: one 4 KB
+// entry at G = 16, d = 128 (two measured 0.5 ms slower at the skewed 131072
+// shape: more reads in flight leave the output writes waiting longer)
 #ifndef MSA_CL_W4
-#define MSA_CL_W4 2
+#define MSA_CL_W4 1
 #endif
 
 template <int D, int G, int SMAX>
