@@ -174,11 +174,11 @@ struct Dims {
 #endif
 constexpr int kQueryWindow = MSA_QUERY_WINDOW;
 
-// Backward: at most this many persistent workgroups (a multiple of 8). The
-// dK/dV (and dk_idx) sums of a run of items of one bucket go to fp32 slabs of
-// 128 keys: one per bucket, plus two per workgroup for the runs it shares with
-// a neighbour.
-constexpr int kBwdMaxGrid = 256;
+// Backward: at most this many persistent workgroups (a multiple of 8; two per
+// CU on 256 CUs). The dK/dV (and dk_idx) sums of a run of items of one bucket
+// go to fp32 slabs of 128 keys: one per bucket, plus two per workgroup for the
+// runs it shares with a neighbour.
+constexpr int kBwdMaxGrid = 512;
 
 // Workspace of the attention and KL calls (bucketing + partials).
 struct AttnWs {
