@@ -468,8 +468,8 @@ def main():
                     help="the profiler commands recorded with --ingest-counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the MSA layer on a single "
-              "MI355X; --gpus must be 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the MSA layer on a single "
+              "MI355X (sharding is a design, not code); --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, args.workload or "skewed_n131072", args.commands)

@@ -65,7 +65,7 @@ typedef enum {
   MSA_OK = 0,
   MSA_ERR_NULL = 1,        /* a required pointer is NULL */
   MSA_ERR_SHAPE = 2,       /* inconsistent shape (e.g. Hq % Hkv != 0, q_start+seqlen_q > seqlen_kv) */
-  MSA_ERR_UNSUPPORTED = 3, /* valid but not supported by this build (see list above) */
+  MSA_ERR_UNSUPPORTED = 3, /* valid but not supported by the library (see list above) */
   MSA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than msa_workspace_size */
   MSA_ERR_DEVICE = 5,      /* HIP error at launch, or the current device is not gfx950 */
   MSA_ERR_SCRATCH = 6      /* msa_attn_fwd_noalloc: the call needs more than its fixed scratch */

@@ -247,7 +247,7 @@ const char* msa_status_string(msa_status st) {
     case MSA_OK: return "ok";
     case MSA_ERR_NULL: return "a required pointer is NULL";
     case MSA_ERR_SHAPE: return "inconsistent shape";
-    case MSA_ERR_UNSUPPORTED: return "shape or type not supported by this build";
+    case MSA_ERR_UNSUPPORTED: return "shape or type not supported by the library";
     case MSA_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case MSA_ERR_DEVICE: return "HIP launch error or device is not gfx950";
     case MSA_ERR_SCRATCH:
