@@ -136,21 +136,21 @@ quantize_blocks_kernel(const T* __restrict__ x, uint8_t* __restrict__ k8,
 
 // ---------------------------------------------------------------- index GEMM + block max
 //
-// The bf16 kernel's structure with FP8 operands: a workgroup owns RT = 64*NW
+// The bf16 kernel's structure with FP8 operands: a workgroup owns RT = 32*CT*NW
 // consecutive GEMM rows (QT = RT/HKV queries x all HKV groups) and a chunk of CB
-// key blocks; wave w keeps the Q8 rows 64w..64w+63 as two 32-column B operands
+// key blocks; wave w keeps its 32*CT Q8 rows as CT 32-column B operands
 // (32 bytes per lane: lane half h holds bytes 32h..32h+31 of its row; zero for
 // d_idx = 32, h = 1). Each 128-key K8 block goes global -> registers -> swizzled
 // LDS, double-buffered, one barrier per block. D^T = K8_tile (32 keys) x Q8^T,
 // so a lane holds 16 keys of one row; the block max is in-lane plus one
 // lane-half exchange. Maxima are collected in LDS and scaled on the way out.
-template <int DI, int HKV, int NW, int CB>
+template <int DI, int HKV, int NW, int CT, int CB>
 __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 8 / NW)
 index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restrict__ q_exp,
                           const uint8_t* __restrict__ k8, const int32_t* __restrict__ k_exp,
                           float* __restrict__ M, int N, int Nq, int q_start, int nb,
                           float inv_sqrt_di) {
-  constexpr int NT = 64 * NW, RT = 64 * NW, QT = RT / HKV;
+  constexpr int NT = 64 * NW, RT = 32 * CT * NW, QT = RT / HKV;
   constexpr int CPR = DI / 16;  // 16-byte chunks per row
   constexpr int SWM = CPR - 1;
   constexpr int NCH = 128 * CPR;
@@ -196,13 +196,13 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
   };
   load_raw(kb0);
 
-  i32x8 qf[2];
+  i32x8 qf[CT];
   {
     const size_t rbase = (size_t)b * Nq * HKV;
     const size_t rmax = rbase + (size_t)Nq * HKV - 1;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const size_t grow = min(rbase + (size_t)t0 * HKV + 64 * wave + 32 * ct + l32, rmax);
+    for (int ct = 0; ct < CT; ++ct) {
+      const size_t grow = min(rbase + (size_t)t0 * HKV + 32 * CT * wave + 32 * ct + l32, rmax);
       i32x4 lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
       if (DI == 64 || h == 0) {
         const i32x4* p = reinterpret_cast<const i32x4*>(q8 + grow * DI + 32 * h);
@@ -220,10 +220,10 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
   if (kb0 + 1 <= kb1) load_raw(kb0 + 1);
   __syncthreads();
 
-  const int row0 = wave * 64;
-  int i_row[2];
+  const int row0 = wave * 32 * CT;
+  int i_row[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
+  for (int ct = 0; ct < CT; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
 
   auto mma_tile = [&](const i32x4* ktile, int kt, f32x16* acc) {
     i32x8 af;
@@ -242,7 +242,7 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
       for (int e = 0; e < 8; ++e) af[e] = 0;
     }
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       f32x16 z;
 #pragma unroll
       for (int e = 0; e < 16; ++e) z[e] = 0.0f;
@@ -251,7 +251,7 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
   };
   auto reduce_tile = [&](auto masked, f32x16* acc, float* m, int kb, int kt) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if constexpr (decltype(masked)::value) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
@@ -265,20 +265,21 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
   };
   auto finish_block = [&](float* m, int kb) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const float x = vmax(m[ct], shfl_xor_f(m[ct], 32));
       mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0 + 1)] = x;
     }
   };
 
   // MFMAs of key tile kt+1 are issued before the max of tile kt (as in bf16)
-  f32x16 accA[2], accB[2];
+  f32x16 accA[CT], accB[CT];
+  float m[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) accB[ct][e] = -INFINITY;
+    m[ct] = -INFINITY;
   }
-  float m[2] = {-INFINITY, -INFINITY};
   auto block_body = [&](auto masked, int kb) {
     const int cur = (kb - kb0) & 1;
     if (kb + 1 <= kb1) {
@@ -289,7 +290,8 @@ index_blockmax_fp8_kernel(const uint8_t* __restrict__ q8, const int32_t* __restr
     mma_tile(kt_lds, 0, accA);
     reduce_tile(masked, accB, m, kb - 1, 3);
     finish_block(m, kb - 1);
-    m[0] = m[1] = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) m[ct] = -INFINITY;
     mma_tile(kt_lds, 1, accB);
     reduce_tile(masked, accA, m, kb, 0);
     mma_tile(kt_lds, 2, accA);
@@ -354,16 +356,22 @@ hipError_t launch_quantize_fp8(const Dims& d, const void* q_idx, const void* k_i
 #ifndef MSA_FP8_NW
 #define MSA_FP8_NW 4
 #endif
+// 96 GEMM rows per wave (three 32-row B operands per K8 fragment read from
+// LDS): 2.31 -> 2.14 ms at the skewed 131072 shape against 64 rows; two
+// 384-row workgroups per CU beat one of 768 rows (2.33 ms)
+#ifndef MSA_FP8_CT
+#define MSA_FP8_CT 3
+#endif
 constexpr int kFp8Cb = MSA_FP8_CB;
 
-template <int DI, int HKV, int NW>
+template <int DI, int HKV, int NW, int CT>
 static hipError_t fp8_index_launch(const Dims& d, const uint8_t* q8, const int32_t* qe,
                                    const uint8_t* k8, const int32_t* ke, float* M, hipStream_t s) {
-  constexpr int QT = 64 * NW / HKV;
+  constexpr int QT = 32 * CT * NW / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
   const int nchunks = (d.nb + kFp8Cb - 1) / kFp8Cb;
   if (ntiles == 0 || d.B == 0) return hipSuccess;
-  index_blockmax_fp8_kernel<DI, HKV, NW, kFp8Cb><<<dim3(ntiles, nchunks, d.B), 64 * NW, 0, s>>>(
+  index_blockmax_fp8_kernel<DI, HKV, NW, CT, kFp8Cb><<<dim3(ntiles, nchunks, d.B), 64 * NW, 0, s>>>(
       q8, qe, k8, ke, M, d.N, d.Nq, d.q_start, d.nb, (float)(1.0 / std::sqrt((double)DI)));
   return hipGetLastError();
 }
@@ -372,8 +380,8 @@ template <int DI, int HKV>
 static hipError_t fp8_index_nw(const Dims& d, const uint8_t* q8, const int32_t* qe,
                                const uint8_t* k8, const int32_t* ke, float* M, hipStream_t s) {
   // one-wave tiles when a sequence has at most 64 GEMM rows (decode)
-  if ((int64_t)d.Nq * HKV <= 64) return fp8_index_launch<DI, HKV, 1>(d, q8, qe, k8, ke, M, s);
-  return fp8_index_launch<DI, HKV, MSA_FP8_NW>(d, q8, qe, k8, ke, M, s);
+  if ((int64_t)d.Nq * HKV <= 64) return fp8_index_launch<DI, HKV, 1, 2>(d, q8, qe, k8, ke, M, s);
+  return fp8_index_launch<DI, HKV, MSA_FP8_NW, MSA_FP8_CT>(d, q8, qe, k8, ke, M, s);
 }
 
 template <int DI>

@@ -41,10 +41,11 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 
 // ============================================================== index GEMM + block max
 //
-// Workgroup = one tile of RT = 64*NW consecutive GEMM rows (QT = RT/HKV
+// Workgroup = one tile of RT = 32*CT*NW consecutive GEMM rows (QT = RT/HKV
 // queries x all HKV groups; the rows are contiguous in Q_idx) x a chunk of CB
-// key blocks. Wave w owns GEMM rows [64w, 64w+64): its Q_idx rows stay in
-// registers as MFMA B fragments for the whole chunk. Each 128-key block of
+// key blocks. Wave w owns CT row tiles of 32 GEMM rows, [32CTw, 32CT(w+1)):
+// its Q_idx rows stay in registers as MFMA B fragments for the whole chunk,
+// and every K_idx fragment read from LDS feeds CT MFMAs. Each 128-key block of
 // K_idx is read from HBM/L2 once per workgroup, row-contiguously, and shared by
 // all NW waves through a double-buffered LDS tile (one barrier per block).
 // The product is formed transposed, D = K_idx_tile (32 keys as rows) x
@@ -61,13 +62,15 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 // LSE: also the per-block log-sum-exp of the index logits over the block's
 // keys j <= i (a running max and sum per key tile, the two lane halves merged
 // at the block's end), written to BL beside the block maxima.
-template <typename T, int DI, int HKV, int NW, int CB, bool LSE>
-__global__ void __launch_bounds__(64 * NW, sizeof(T) == 2 ? 8 / NW : 1)
+// bf16 with CT <= 3 runs two waves per SIMD (256 registers each), CT = 4 one
+// wave per SIMD with the 512 registers of a lone wave.
+template <typename T, int DI, int HKV, int NW, int CT, int CB, bool LSE>
+__global__ void __launch_bounds__(64 * NW, sizeof(T) != 2 ? 1 : CT == 2 ? 8 / NW : CT == 3 ? 2 : 1)
 index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
                       float* __restrict__ M, float* __restrict__ BL, int N, int Nq, int q_start,
                       int nb, float scale) {
   constexpr int NT = 64 * NW;
-  constexpr int RT = 64 * NW;              // GEMM rows per tile
+  constexpr int RT = 32 * CT * NW;         // GEMM rows per tile
   constexpr int QT = RT / HKV;             // queries per tile
   constexpr int KS = DI / 16;
   constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
@@ -117,20 +120,20 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   };
   load_raw(kb0);
 
-  // Q_idx: the wave's 64 rows, in two halves of 32 rows staged through LDS.
+  // Q_idx: the wave's 32*CT rows, in CT tiles of 32 rows staged through LDS.
   // Rows past the last query read a valid row and are never stored.
-  vec8<T> qf[2][KS];
+  vec8<T> qf[CT][KS];
   {
     i32x4* qs = reinterpret_cast<i32x4*>(ubuf) + wave * 32 * CPR;
     const char* qbase = reinterpret_cast<const char*>(q_idx);
     const size_t rbase = (size_t)b * Nq * HKV;
     const size_t rmax = rbase + (size_t)Nq * HKV - 1;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
       for (int u = 0; u < QCH; ++u) {
         const int q = lane + 64 * u, r = q / CPR, c = q % CPR;
-        const size_t grow = min(rbase + (size_t)t0 * HKV + wave * 64 + 32 * ct + r, rmax);
+        const size_t grow = min(rbase + (size_t)t0 * HKV + wave * 32 * CT + 32 * ct + r, rmax);
         qs[r * CPR + (c ^ (idx_swz(r) & SWM))] =
             *reinterpret_cast<const i32x4*>(qbase + (grow * CPR + c) * 16);
       }
@@ -149,33 +152,33 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   float* mbuf = reinterpret_cast<float*>(ubuf);
   float* lbuf = mbuf + RT * MST;  // LSE only
   const float c2 = scale * kLog2e;  // exp(scale * s) = exp2(c2 * s)
-  const int row0 = wave * 64;  // first GEMM row of the wave
-  int i_row[2];
+  const int row0 = wave * 32 * CT;  // first GEMM row of the wave
+  int i_row[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
+  for (int ct = 0; ct < CT; ++ct) i_row[ct] = q_start + t0 + (row0 + 32 * ct + l32) / HKV;
 
-  // One key tile (32 keys) of the block: D^T tiles for the wave's two row tiles.
+  // One key tile (32 keys) of the block: D^T tiles for the wave's CT row tiles.
   auto mma_tile = [&](const i32x4* tile, int kt, f32x16* acc) {
     vec8<T> af[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) af[ks] = lds_frag<T, CPR>(tile, 32 * kt + l32, (16 * ks + 8 * h) / EPC);
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[ct][e] = 0.0f;
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
+      for (int ct = 0; ct < CT; ++ct) mma(acc[ct], af[ks], qf[ct][ks]);
     }
   };
   // causal mask (MASK) and running in-lane block max (LSE: and the sum of
   // exp(scale (s - max))) of one key tile
-  float l[2] = {0.0f, 0.0f};
+  float l[CT] = {};
   auto reduce_tile = [&](auto masked, f32x16* acc, float* m, int kb, int kt) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       if constexpr (decltype(masked)::value) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
@@ -198,7 +201,7 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   // block before kb0); both lane halves hold the value and store it
   auto finish_block = [&](float* m, int kb) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
+    for (int ct = 0; ct < CT; ++ct) {
       const float mo = shfl_xor_f(m[ct], 32);
       const float x = vmax(m[ct], mo);
       mbuf[(row0 + 32 * ct + l32) * MST + (kb - kb0 + 1)] = x;
@@ -219,13 +222,14 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   // reduces tile kt; tile 3 of a block is reduced under tile 0 of the next.
   // The body is branch-free so that the two streams can interleave; blocks
   // that need the causal mask (the tile's last one or two) run in a second loop.
-  f32x16 accA[2], accB[2];
+  f32x16 accA[CT], accB[CT];
+  float m[CT];
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
+  for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) accB[ct][e] = -INFINITY;
+    m[ct] = -INFINITY;
   }
-  float m[2] = {-INFINITY, -INFINITY};
   auto block_body = [&](auto masked, int kb) {
     const int cur = (kb - kb0) & 1;
     if (kb + 1 <= kb1) {
@@ -236,7 +240,8 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
     mma_tile(kt_lds, 0, accA);
     reduce_tile(masked, accB, m, kb - 1, 3);
     finish_block(m, kb - 1);
-    m[0] = m[1] = -INFINITY;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) m[ct] = -INFINITY;
     mma_tile(kt_lds, 1, accB);
     reduce_tile(masked, accA, m, kb, 0);
     mma_tile(kt_lds, 2, accA);
@@ -266,6 +271,13 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
   }
 }
 
+// bf16 tiles: 8 waves of 96 GEMM rows (768 rows per workgroup). Against 64
+// rows per wave this cuts the LDS fragment reads per MFMA by a third
+// (3.80 -> 3.70 ms at the skewed 131072 shape); 128 rows per wave spill at two
+// waves per SIMD and lose latency hiding at one.
+#ifndef MSA_IDX_CT
+#define MSA_IDX_CT 3
+#endif
 #ifndef MSA_IDX_NW
 #define MSA_IDX_NW 8
 #endif
@@ -273,17 +285,17 @@ index_blockmax_kernel(const T* __restrict__ q_idx, const T* __restrict__ k_idx,
 #define MSA_IDX_CB 32
 #endif
 
-template <typename T, int DI, int HKV, int NW, bool LSE>
+template <typename T, int DI, int HKV, int NW, int CT, bool LSE>
 static hipError_t index_launch(const Dims& d, const void* qi, const void* ki, float* M, float* BL,
                                hipStream_t s) {
   constexpr int CB = LSE ? 16 : MSA_IDX_CB;  // LSE: two LDS staging arrays
-  constexpr int QT = 64 * NW / HKV;
+  constexpr int QT = 32 * CT * NW / HKV;
   const int ntiles = (d.Nq + QT - 1) / QT;
   const int nchunks = (d.nb + CB - 1) / CB;
   if (ntiles == 0 || d.B == 0) return hipSuccess;
   dim3 grid(ntiles, nchunks, d.B);
   const float scale = 1.0f / sqrtf((float)DI);
-  index_blockmax_kernel<T, DI, HKV, NW, CB, LSE><<<grid, 64 * NW, 0, s>>>(
+  index_blockmax_kernel<T, DI, HKV, NW, CT, CB, LSE><<<grid, 64 * NW, 0, s>>>(
       (const T*)qi, (const T*)ki, M, BL, d.N, d.Nq, d.q_start, d.nb, scale);
   return hipGetLastError();
 }
@@ -293,12 +305,15 @@ static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, 
                                  float* BL, hipStream_t s) {
   if constexpr (sizeof(T) == 4) {
     // fp32 tiles: LDS and register limits
-    return index_launch<T, DI, HKV, 4, LSE>(d, qi, ki, M, BL, s);
+    return index_launch<T, DI, HKV, 4, 2, LSE>(d, qi, ki, M, BL, s);
   } else {
     // a decode step has a few rows per sequence: one-wave tiles (64 rows)
     // instead of 512-row tiles keep the MFMA work near the rows that exist
-    if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1, LSE>(d, qi, ki, M, BL, s);
-    return index_launch<T, DI, HKV, MSA_IDX_NW, LSE>(d, qi, ki, M, BL, s);
+    if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1, 2, LSE>(d, qi, ki, M, BL, s);
+    // the block-LSE pass keeps 64 rows per wave: its running sums do not fit
+    // the registers of more
+    constexpr int CT = LSE ? 2 : MSA_IDX_CT;
+    return index_launch<T, DI, HKV, LSE ? 8 : MSA_IDX_NW, CT, LSE>(d, qi, ki, M, BL, s);
   }
 }
 
