@@ -72,6 +72,13 @@ SMALL = [
            topk=5, with_kl=True),
     _small("bf16_g16_di32_kl", seqlen_kv=800, seqlen_q=800, num_q_heads=32, num_kv_heads=2,
            idx_dim=32, topk=4, with_kl=True),
+    # prefill at the group counts whose index tiles differ most in queries per tile:
+    # Hkv=8 (96 queries per 768-row tile, ragged N=1000, two sequences) and Hkv=1
+    # (768 queries per tile, three tiles with a ragged last one, d_idx=32)
+    _small("bf16_hkv8_prefill", batch=2, seqlen_kv=1000, seqlen_q=1000, num_q_heads=16,
+           num_kv_heads=8, topk=5, with_kl=True),
+    _small("bf16_hkv1_prefill", seqlen_kv=1900, seqlen_q=1900, num_q_heads=8, num_kv_heads=1,
+           idx_dim=32, topk=6),
     # fp32 decode, ragged last block
     _small("f32_decode_b2", batch=2, seqlen_kv=1500, seqlen_q=1, q_start=1499, num_q_heads=8,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=4, dtype=si.F32, scale=1.0,
