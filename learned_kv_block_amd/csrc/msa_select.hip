@@ -308,7 +308,7 @@ static hipError_t index_dispatch(const Dims& d, const void* qi, const void* ki, 
     return index_launch<T, DI, HKV, 4, 2, LSE>(d, qi, ki, M, BL, s);
   } else {
     // a decode step has a few rows per sequence: one-wave tiles (64 rows)
-    // instead of 512-row tiles keep the MFMA work near the rows that exist
+    // instead of 768-row tiles keep the MFMA work near the rows that exist
     if ((int64_t)d.Nq * HKV <= 64) return index_launch<T, DI, HKV, 1, 2, LSE>(d, qi, ki, M, BL, s);
     // the block-LSE pass keeps 64 rows per wave: its running sums do not fit
     // the registers of more
