@@ -407,7 +407,9 @@ constexpr int kCandMax = 128;  // candidates ranked exactly (two passes of 64)
 
 // One (query, group) row with L candidate blocks, VV*64 >= L: lane l holds
 // blocks v*64 + l, v < VV.
-template <int VV>
+// NF: the first NF groups v are known to lie below L (64*NF < L), so only the
+// others need the -inf select.
+template <int VV, int NF>
 __device__ __forceinline__ void topk_row(const float* __restrict__ M, int64_t row, int L, int nb,
                                          int k, int32_t* __restrict__ out,
                                          float* __restrict__ margin, uint64_t* __restrict__ candw,
@@ -421,9 +423,11 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ M, int64_t ro
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const float raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (v * 64 + lane) * 4, 0, 0));
-    x[v] = v * 64 + lane < L ? raw : -INFINITY;
-    lm = vmax(lm, x[v]);
+    x[v] = (v < NF || v * 64 + lane < L) ? raw : -INFINITY;
   }
+#pragma unroll
+  for (int v = 0; v + 1 < V; v += 2) lm = vmax(vmax(lm, x[v]), x[v + 1]);
+  if constexpr (V % 2) lm = vmax(lm, x[V - 1]);
   // 1. threshold: bisection on the order-preserving bits of the lane maxima
   const uint32_t om = ord_f32(lm);
   uint32_t T = 0;
@@ -439,24 +443,22 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ M, int64_t ro
   // which the exact ranking below handles
   const float Tf = f32_of_ord(T);
 
-  // 2. count and compact the candidates
+  // 2. compact the candidates (positions past kCandMax go to the sink; C
+  // counts them all, and a list that overflowed is not used)
   int C = 0;
 #pragma unroll
-  for (int v = 0; v < V; ++v) C += __popcll(__ballot(x[v] >= Tf));
+  for (int v = 0; v < V; ++v) {
+    const bool c = x[v] >= Tf;
+    const uint64_t bal = __ballot(c);
+    if (bal) {  // uniform
+      const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      candw[(c && pos < kCandMax) ? pos : kCandMax] = make_key(x[v] + 0.0f, v * 64 + lane);  // -0 -> +0
+      C += __popcll(bal);
+    }
+  }
   uint64_t worst_sel = 0, best_unsel = 0;
   if (C <= kCandMax) {
-    int base = 0;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const bool c = x[v] >= Tf;
-      const uint64_t bal = __ballot(c);
-      if (bal) {  // uniform
-        const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-        candw[c ? pos : kCandMax] = make_key(x[v] + 0.0f, v * 64 + lane);  // -0 -> +0
-        base += __popcll(bal);
-      }
-    }
     if (margin && lane < 2) mselw[lane] = 0;
     wave_sync();
     // 3. exact ranks among candidates
@@ -541,11 +543,13 @@ __device__ __forceinline__ void topk_row_fit(const float* __restrict__ M, int64_
                                              int k, int32_t* __restrict__ out,
                                              float* __restrict__ margin, uint64_t* __restrict__ candw,
                                              uint64_t* __restrict__ mselw, int lane) {
+  // here L > (VV - STEP) * 64: the first VV - STEP groups are whole
+  constexpr int NF = VV > STEP ? VV - STEP : 0;
   if constexpr (VV >= V) {
-    topk_row<V>(M, row, L, nb, k, out, margin, candw, mselw, lane);
+    topk_row<V, NF>(M, row, L, nb, k, out, margin, candw, mselw, lane);
   } else {
     if (L <= VV * 64)  // uniform
-      topk_row<VV>(M, row, L, nb, k, out, margin, candw, mselw, lane);
+      topk_row<VV, NF>(M, row, L, nb, k, out, margin, candw, mselw, lane);
     else
       topk_row_fit<VV + STEP, STEP, V>(M, row, L, nb, k, out, margin, candw, mselw, lane);
   }
