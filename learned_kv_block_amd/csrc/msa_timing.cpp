@@ -55,8 +55,11 @@ msa_status msa_prof_begin(int kernel, int max_launches) {
   for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
   g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
   g_prof.id.assign((size_t)max_launches, -1);
+  // timing-only events: no system-scope fence (cache writeback and invalidate)
+  // when a record completes, so the records do not slow the kernels they time
   for (auto& e : g_prof.ev)
-    if (hipEventCreate(&e) != hipSuccess) return MSA_ERR_DEVICE;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
+      return MSA_ERR_DEVICE;
   g_prof.max = max_launches;
   g_prof.used = 0;
   g_prof.kernel = kernel;
