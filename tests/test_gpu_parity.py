@@ -79,6 +79,10 @@ SMALL = [
            num_kv_heads=8, topk=5, with_kl=True),
     _small("bf16_hkv1_prefill", seqlen_kv=1900, seqlen_q=1900, num_q_heads=8, num_kv_heads=1,
            idx_dim=32, topk=6),
+    # decode at the largest supported cache (2048 blocks = 262144 tokens): the
+    # 32-group Top-k over up to 2047 candidate blocks, Hkv=8
+    _small("bf16_decode_max", batch=2, seqlen_kv=262144, seqlen_q=1, q_start=262143,
+           num_q_heads=16, num_kv_heads=8, topk=16),
     # fp32 decode, ragged last block
     _small("f32_decode_b2", batch=2, seqlen_kv=1500, seqlen_q=1, q_start=1499, num_q_heads=8,
            num_kv_heads=2, head_dim=64, idx_dim=32, topk=4, dtype=si.F32, scale=1.0,
@@ -207,7 +211,19 @@ FULL = ["main_n8192", "train_b2_n32768", "skewed_n131072", "decode_b64_n131072"]
 
 @pytest.mark.parametrize("name", FULL)
 def test_parity_full_size_sampled(name):
-    cfg = si.CONFIGS[name]
+    _check_sampled(si.CONFIGS[name])
+
+
+def test_parity_max_blocks_sampled():
+    # the largest supported sequence, 2048 blocks, at Hkv=8: the index GEMM over
+    # 2048 blocks, the 32-group Top-k, bucketing with global bin counters (16384
+    # bins do not fit the LDS histogram) and a block-score array of 4.3e9 floats
+    _check_sampled(_small("bf16_prefill_max", seqlen_kv=262144, seqlen_q=262144,
+                          num_q_heads=16, num_kv_heads=8, topk=16, seed=5))
+
+
+def _check_sampled(cfg):
+    name = cfg.name
     print(f"[parity] start {name}", flush=True)
     x = parity.gpu_inputs(cfg)
     res = parity.run_gpu(cfg, x, want_kl=cfg.with_kl)
