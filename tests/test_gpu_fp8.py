@@ -45,6 +45,9 @@ CASES = [
     _cfg("bf16_decode_b3", batch=3, seqlen_kv=3000, seqlen_q=1, q_start=2999, topk=6),
     _cfg("bf16_decode_hkv8_d32", batch=2, seqlen_kv=2000, seqlen_q=1, q_start=1999,
          num_q_heads=16, num_kv_heads=8, idx_dim=32, topk=4),
+    # prefill at Hkv=8: 48 queries per 384-row FP8 index tile, ragged N=1000, two sequences
+    _cfg("bf16_hkv8_prefill", batch=2, seqlen_kv=1000, seqlen_q=1000, num_q_heads=16,
+         num_kv_heads=8, topk=5),
 ]
 
 
@@ -100,10 +103,16 @@ def test_fp8_every_row(cfg):
     print(f"[fp8] {cfg.name}: " + json.dumps(rep), flush=True)
 
 
-def test_fp8_full_size_sampled():
-    """Skewed N=131072 workload: every K_idx byte and exponent, Q_idx bytes and the
-    selection on sampled rows against the oracle."""
-    cfg = si.CONFIGS["skewed_n131072"]
+# the skewed 131072 workload, and the largest supported sequence (2048 blocks) at Hkv=8
+FP8_FULL = [si.CONFIGS["skewed_n131072"],
+            _cfg("fp8_prefill_max", seqlen_kv=262144, seqlen_q=262144, num_q_heads=16,
+                 num_kv_heads=8, topk=16)]
+
+
+@pytest.mark.parametrize("cfg", FP8_FULL, ids=[c.name for c in FP8_FULL])
+def test_fp8_full_size_sampled(cfg):
+    """Every K_idx byte and exponent, Q_idx bytes and the selection on sampled rows
+    against the oracle."""
     print(f"[fp8] start {cfg.name}", flush=True)
     x = parity.gpu_inputs(cfg, names=("q_idx", "k_idx"))
     qz, sel = _gpu_fp8(cfg, x)
@@ -145,10 +154,16 @@ def test_fp8_decode_matches_prefill(di):
     assert torch.equal(dec["margin"][:, 0], pre["margin"][:, -1])
 
 
-def test_fp8_decode_full_size():
-    """64 x 131072 decode with the FP8 index: every K_idx byte and exponent, and every
-    sequence's selection against the oracle (K_idx generated 8 sequences at a time)."""
-    cfg = si.CONFIGS["decode_b64_n131072"]
+# 64 x 131072, and two sequences at the largest supported cache (2048 blocks, Hkv=8)
+FP8_DECODE_FULL = [si.CONFIGS["decode_b64_n131072"],
+                   _cfg("fp8_decode_max", batch=2, seqlen_kv=262144, seqlen_q=1,
+                        q_start=262143, num_q_heads=16, num_kv_heads=8, topk=16)]
+
+
+@pytest.mark.parametrize("cfg", FP8_DECODE_FULL, ids=[c.name for c in FP8_DECODE_FULL])
+def test_fp8_decode_full_size(cfg):
+    """Decode with the FP8 index: every K_idx byte and exponent, and every sequence's
+    selection against the oracle (K_idx generated 8 sequences at a time)."""
     print(f"[fp8] start {cfg.name}", flush=True)
     x = parity.gpu_inputs(cfg, names=("q_idx", "k_idx"))
     qz, sel = _gpu_fp8(cfg, x)
