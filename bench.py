@@ -11,8 +11,11 @@ fraction of the whole layer, every kernel of the step against its own roofline
 (MFMA for the index GEMM and the attention, HBM for the Top-k, the bucketing
 and the combine), the roofline of the dominant kernel (the KV-outer sparse
 attention, timed live with HIP events over the timed steps in the measurement
-build; its gathered-Q and partial-output bytes and the counter bytes alongside)
-and the fp64 oracle timed on the host on a bounded row sample.
+build; its gathered-Q and partial-output bytes and the counter bytes alongside,
+all per launch: a prefill of more than 32768 queries per sequence runs the
+attention once per 32768-query window) and the fp64 oracle timed on the host on a
+bounded row sample. In `kernels` the work, bytes and times are per step and
+`counter_bytes` per launch.
 """
 from __future__ import annotations
 
@@ -60,8 +63,10 @@ KERNEL_FILES = {
 
 
 def source_hash(files) -> str:
+    # the entry points decide how a step splits into launches (e.g. attention windows),
+    # so a counter record also goes stale when msa_api.cpp changes
     h = hashlib.sha256()
-    for f in list(files) + ["msa_internal.hpp"]:
+    for f in list(files) + ["msa_internal.hpp", "msa_api.cpp"]:
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -612,9 +617,10 @@ def main():
         for extra in ("side_bytes", "triples", "buckets", "min_bytes", "min_bytes_what"):
             if extra in w:
                 e[extra] = w[extra]
+        # counter bytes are per launch; the work fields above are per step
         e["counter_bytes"] = cbytes
         if cbytes is not None and "min_bytes" in w:
-            e["counter_over_min_bytes"] = cbytes / w["min_bytes"]
+            e["counter_over_min_bytes"] = cbytes * e["launches_per_step"] / w["min_bytes"]
         kernels[name] = e
     for n, ms in kernel_ms.items():  # training-side kernels and anything not tabled above
         if n not in kernels and n not in bucket_names and not (n == "index_fp8" and args.fp8):
@@ -622,19 +628,24 @@ def main():
     # the headline roofline is that of the step's dominant tabled kernel
     dom = max((n for n in kernels if "bound" in kernels[n]), key=lambda n: kernels[n]["ms"])
     d = kernels[dom]
+    # the roofline is per launch: a kernel that runs several times a step (the
+    # attention of a windowed prefill) reports its work and time per launch
+    lps = max(1e-9, d["launches_per_step"])
     if d["bound"] == "mfma":
         roofline = {"bound": "mfma", "kernel": dom, "achieved": d["achieved_tflops"],
                     "peak": d["peak_tflops"], "unit": "TFLOP/s", "frac": d["frac"],
-                    "traffic": d["counter_bytes"], "avg_ms": d["ms"],
-                    "launches": launches.get(d["timer"], 0), "flops_per_launch": d["flops"]}
+                    "traffic": d["counter_bytes"], "avg_ms": d["ms"] / lps,
+                    "launches": launches.get(d["timer"], 0), "flops_per_launch": d["flops"] / lps}
     else:
         roofline = {"bound": "hbm", "kernel": dom, "achieved": d["achieved_gbs"],
                     "peak": d["peak_gbs"], "unit": "GB/s", "frac": d["frac"],
-                    "traffic": d["counter_bytes"], "avg_ms": d["ms"],
-                    "launches": launches.get(d["timer"], 0), "bytes_per_launch": d["bytes"]}
-    for extra in ("side_bytes", "min_bytes", "counter_over_min_bytes"):
+                    "traffic": d["counter_bytes"], "avg_ms": d["ms"] / lps,
+                    "launches": launches.get(d["timer"], 0), "bytes_per_launch": d["bytes"] / lps}
+    for extra in ("side_bytes", "min_bytes"):
         if extra in d:
-            roofline[extra] = d[extra]
+            roofline[extra] = d[extra] / lps
+    if "counter_over_min_bytes" in d:
+        roofline["counter_over_min_bytes"] = d["counter_over_min_bytes"]
     line = {
         "metric": "MSA-layer prefill query-tokens/s at N=128K (1 GPU) + % bf16 MFMA peak",
         "value": value,

@@ -123,9 +123,15 @@ def test_empty_workloads_are_noops():
 def test_workspace_sizes_scale_with_the_workload():
     small = shape(seqlen_kv=8192, seqlen_q=8192)
     big = shape(seqlen_kv=131072, seqlen_q=131072)
-    # partial outputs: slots * G * d * 2 bytes (bf16) dominate the attention workspace
-    assert msa.workspace_size(big, msa.MSA_OP_ATTN) >= 131072 * 4 * 16 * 16 * 128 * 2
+    # partial outputs: slots * G * d * 2 bytes (bf16) dominate the attention workspace;
+    # a sequence of more than 32768 queries runs the attention in 32768-query windows
+    # that share one window's workspace, the same as a 32768-query call's
+    window = shape(seqlen_kv=131072, seqlen_q=32768)
+    assert msa.workspace_size(big, msa.MSA_OP_ATTN) >= 32768 * 4 * 16 * 16 * 128 * 2
+    assert msa.workspace_size(big, msa.MSA_OP_ATTN) == msa.workspace_size(window, msa.MSA_OP_ATTN)
     assert msa.workspace_size(small, msa.MSA_OP_ATTN) < msa.workspace_size(big, msa.MSA_OP_ATTN)
+    # the other calls still scale with the whole workload
+    assert msa.workspace_size(big, msa.MSA_OP_SELECT) == 131072 * 4 * 1024 * 4
     assert msa.workspace_size(big, 7) == 0
 
 

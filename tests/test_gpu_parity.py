@@ -222,7 +222,19 @@ def test_parity_max_blocks_sampled():
                           num_q_heads=16, num_kv_heads=8, topk=16, seed=5))
 
 
-def _check_sampled(cfg):
+def test_parity_windowed_prefill():
+    # more than 32768 queries per sequence: the attention runs in 32768-query windows
+    # (one full and one ragged per sequence here), with batch 2 and a chunked-prefill
+    # offset; the rows on both sides of each window boundary are in the sample
+    cfg = _small("bf16_windows", batch=2, seqlen_kv=50000, seqlen_q=40000, q_start=10000,
+                 num_q_heads=16, num_kv_heads=4, topk=8, seed=7)
+    edge = [b * cfg.seqlen_q + t for b in range(cfg.batch) for t in (32766, 32767, 32768, 32769)]
+    rows = np.unique(np.concatenate([parity.sample_rows(cfg, n_random=24, seed=3),
+                                     np.array(edge, dtype=np.int64)]))
+    _check_sampled(cfg, rows=rows)
+
+
+def _check_sampled(cfg, rows=None):
     name = cfg.name
     print(f"[parity] start {name}", flush=True)
     x = parity.gpu_inputs(cfg)
@@ -242,7 +254,8 @@ def _check_sampled(cfg):
             print(f"[parity] {name} sequences {b0}..{rows[-1]} ok", flush=True)
         assert rep["rows_checked"] == cfg.batch * cfg.num_kv_heads
     else:
-        rows = parity.sample_rows(cfg, n_random=24, seed=cfg.seed)
+        if rows is None:
+            rows = parity.sample_rows(cfg, n_random=24, seed=cfg.seed)
         rep = parity.check_all(cfg, res, rows=rows, want_kl=cfg.with_kl)
     # whole-workload invariants: every row keeps its local block, ids ascending
     ids = res["ids"]
