@@ -51,6 +51,10 @@ CASES = [
          head_dim=64, topk=3),
     _cfg("bf16_g2_chunk", seqlen_kv=1300, seqlen_q=500, q_start=800, num_q_heads=8,
          num_kv_heads=4, topk=5),
+    # two sequences of at least 4096 queries: the forward attention runs one window per
+    # sequence, the backward over both at once (ragged last block)
+    _cfg("bf16_b2_windows", batch=2, seqlen_kv=4500, seqlen_q=4500, num_q_heads=16,
+         num_kv_heads=4, topk=6),
 ]
 
 
