@@ -97,6 +97,7 @@ size_t elem_size(const Dims& d) { return d.dtype == MSA_BF16 ? 2 : 4; }
 
 struct Layout {
   size_t counts, offsets, cursor, item_off, totals, items, entries, chunks;  // bucketing
+  size_t cost_off, wg_start;                                            // balanced split
   size_t nchunks;  // scan chunks of 4096 buckets (+1)
   size_t opart, lpart;                                               // attention
   size_t sorted;                                                     // backward: canonical entries
@@ -134,7 +135,9 @@ Layout layout(const Dims& d, int op) {
   L.items = take(d.items_max * 16);
   L.entries = take(d.entries_max * 4);
   L.nchunks = (size_t)(d.buckets / 4096 + 1);
-  L.chunks = take(L.nchunks * 2 * 4);  // per-chunk scan sums (entries, items)
+  L.chunks = take(L.nchunks * 3 * 4);  // per-chunk scan sums (entries, items, cost)
+  L.cost_off = take((d.buckets + 1) * 4);
+  L.wg_start = take((kMaxSplit + 1) * 4);
   if (op == MSA_OP_ATTN) {
     // one extra slot: scratch target of the attention kernel's unused rows
     L.opart = take((size_t)(d.slots + 1) * d.G * d.D * elem_size(d));
@@ -177,6 +180,9 @@ AttnWs carve(const Layout& L, void* ws) {
   w.entries = reinterpret_cast<int32_t*>(p + L.entries);
   w.chunk_e = reinterpret_cast<int32_t*>(p + L.chunks);
   w.chunk_i = w.chunk_e + L.nchunks;
+  w.chunk_c = w.chunk_i + L.nchunks;
+  w.cost_off = reinterpret_cast<int32_t*>(p + L.cost_off);
+  w.wg_start = reinterpret_cast<int32_t*>(p + L.wg_start);
   w.sorted = L.sorted ? reinterpret_cast<int32_t*>(p + L.sorted) : nullptr;
   return w;
 }
@@ -439,7 +445,9 @@ msa_status attn_fwd_launch(const Dims& d, const Layout& L, const void* q, const 
   // bf16: each row's local block is attended query-outer inside the combine,
   // so the KV-outer work lists leave it out
   const bool local_in_combine = d.dtype == MSA_BF16;
-  if (launch_bucketing(d, block_ids, w, local_in_combine, stream) != hipSuccess)
+  // the persistent bf16 kernel takes cost-balanced item ranges
+  const int split = d.dtype == MSA_BF16 ? (int)attn_pipe_grid(d) : 0;
+  if (launch_bucketing(d, block_ids, w, local_in_combine, stream, split) != hipSuccess)
     return MSA_ERR_DEVICE;
   prof_before(MSA_K_SPARSE_ATTN, stream);
   hipError_t e = launch_sparse_attn(d, q, k, v, w, ws + L.opart,

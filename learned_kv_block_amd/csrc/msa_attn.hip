@@ -76,94 +76,116 @@ constexpr int kScanChunk = 4096;  // buckets per workgroup (1024 threads x 4)
 
 __global__ void __launch_bounds__(1024)
 bucket_chunk_sum_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
-                        int32_t* __restrict__ chunk_e, int32_t* __restrict__ chunk_i) {
-  __shared__ int32_t se[32], si[32];
+                        int32_t* __restrict__ chunk_e, int32_t* __restrict__ chunk_i,
+                        int32_t* __restrict__ chunk_c) {
+  __shared__ int32_t se[32], si[32], sc[32];
   const int tid = threadIdx.x;
   const int64_t lo = (int64_t)blockIdx.x * kScanChunk;
-  int32_t ce = 0, ci = 0;
+  int32_t ce = 0, ci = 0, cc = 0;
   for (int j = 0; j < kScanChunk / 1024; ++j) {
     const int64_t x = lo + j * 1024 + tid;
     if (x < nbk) {
       const int32_t c = counts[x];
+      const int32_t ni = (c + qt - 1) / qt;
       ce += c;
-      ci += (c + qt - 1) / qt;
+      ci += ni;
+      cc += ni * kItemCost + (ni > 0 ? kItemStartCost : 0);
     }
   }
   for (int m = 32; m >= 1; m >>= 1) {
     ce += __shfl_xor(ce, m, 64);
     ci += __shfl_xor(ci, m, 64);
+    cc += __shfl_xor(cc, m, 64);
   }
   if ((tid & 63) == 0) {
     se[tid >> 6] = ce;
     si[tid >> 6] = ci;
+    sc[tid >> 6] = cc;
   }
   __syncthreads();
   if (tid == 0) {
-    int32_t te = 0, ti = 0;
+    int32_t te = 0, ti = 0, tc = 0;
     for (int w = 0; w < 16; ++w) {
       te += se[w];
       ti += si[w];
+      tc += sc[w];
     }
     chunk_e[blockIdx.x] = te;
     chunk_i[blockIdx.x] = ti;
+    chunk_c[blockIdx.x] = tc;
   }
 }
 
 __global__ void __launch_bounds__(1024)
 bucket_scan_kernel(const int32_t* __restrict__ counts, int64_t nbk, int qt,
                    const int32_t* __restrict__ chunk_e, const int32_t* __restrict__ chunk_i,
-                   int32_t* __restrict__ offsets, int32_t* __restrict__ cursor,
-                   int32_t* __restrict__ item_off, int32_t* __restrict__ totals,
+                   const int32_t* __restrict__ chunk_c, int32_t* __restrict__ offsets,
+                   int32_t* __restrict__ cursor, int32_t* __restrict__ item_off,
+                   int32_t* __restrict__ cost_off, int32_t* __restrict__ totals,
                    int entries_max, int items_max) {
-  __shared__ int32_t se[1024], si[1024];
-  __shared__ int32_t base_e, base_i;
+  __shared__ int32_t se[1024], si[1024], sc[1024];
+  __shared__ int32_t base_e, base_i, base_c;
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
   if (tid == 0) {
-    int32_t be = 0, bi = 0;
+    int32_t be = 0, bi = 0, bc = 0;
     for (int c = 0; c < chunk; ++c) {
       be += chunk_e[c];
       bi += chunk_i[c];
+      bc += chunk_c[c];
     }
     base_e = be;
     base_i = bi;
+    base_c = bc;
   }
   const int64_t lo = (int64_t)chunk * kScanChunk + (int64_t)tid * (kScanChunk / 1024);
   const int64_t hi = min(nbk, lo + kScanChunk / 1024);
-  int32_t ce = 0, ci = 0;
+  int32_t ce = 0, ci = 0, cc = 0;
   for (int64_t x = lo; x < hi; ++x) {
     const int32_t c = counts[x];
+    const int32_t ni = (c + qt - 1) / qt;
     ce += c;
-    ci += (c + qt - 1) / qt;
+    ci += ni;
+    cc += ni * kItemCost + (ni > 0 ? kItemStartCost : 0);
   }
   se[tid] = ce;
   si[tid] = ci;
+  sc[tid] = cc;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
     const int32_t ae = tid >= off ? se[tid - off] : 0;
     const int32_t ai = tid >= off ? si[tid - off] : 0;
+    const int32_t ac = tid >= off ? sc[tid - off] : 0;
     __syncthreads();
     se[tid] += ae;
     si[tid] += ai;
+    sc[tid] += ac;
     __syncthreads();
   }
-  int32_t re = base_e + se[tid] - ce, ri = base_i + si[tid] - ci;  // exclusive
+  // exclusive
+  int32_t re = base_e + se[tid] - ce, ri = base_i + si[tid] - ci, rc = base_c + sc[tid] - cc;
   for (int64_t x = lo; x < hi; ++x) {
     const int32_t c = counts[x];
+    const int32_t ni = (c + qt - 1) / qt;
     offsets[x] = re;
     cursor[x] = re;
     item_off[x] = ri;
+    cost_off[x] = rc;
     re += c;
-    ri += (c + qt - 1) / qt;
+    ri += ni;
+    rc += ni * kItemCost + (ni > 0 ? kItemStartCost : 0);
   }
   if (chunk == (int)gridDim.x - 1 && tid == 1023) {
-    const int32_t te = base_e + se[1023], ti = base_i + si[1023];
+    const int32_t te = base_e + se[1023], ti = base_i + si[1023], tc = base_c + sc[1023];
     offsets[nbk] = te;
     item_off[nbk] = ti;
+    cost_off[nbk] = tc;
     // both bounds hold for valid ids; clamping keeps malformed ids from
     // indexing past the work arrays
     totals[0] = min(te, entries_max);
     totals[1] = min(ti, items_max);
+    totals[2] = tc;
+    totals[3] = 0;  // no balanced split until wg_split_kernel writes one
   }
 }
 
@@ -216,8 +238,8 @@ bucket_scatter_kernel(const int32_t* __restrict__ ids, int Nq, int q_start, int 
 // One thread per work item: item = (bucket, first entry, count <= qt).
 __global__ void __launch_bounds__(256)
 work_items_kernel(const int32_t* __restrict__ item_off, const int32_t* __restrict__ offsets,
-                  const int32_t* __restrict__ totals, int64_t nbk, int qt,
-                  int4* __restrict__ items) {
+                  const int32_t* __restrict__ cost_off, const int32_t* __restrict__ totals,
+                  int64_t nbk, int qt, int4* __restrict__ items) {
   const int it = blockIdx.x * 256 + threadIdx.x;
   if (it >= totals[1]) return;
   int64_t lo = 0, hi = nbk - 1;  // largest bkt with item_off[bkt] <= it
@@ -230,7 +252,27 @@ work_items_kernel(const int32_t* __restrict__ item_off, const int32_t* __restric
   const int local = it - item_off[bkt];
   const int start = offsets[bkt] + local * qt;
   const int cnt = max(0, min(min(qt, offsets[bkt + 1] - start), totals[0] - start));
-  items[it] = make_int4((int)bkt, start, cnt, 0);
+  // work cost before the item: a bucket's first item costs kItemCost + kItemStartCost
+  const int cost = cost_off[bkt] + (local == 0 ? 0 : kItemStartCost + local * kItemCost);
+  items[it] = make_int4((int)bkt, start, cnt, cost);
+}
+
+// Balanced ranges of a persistent kernel of R workgroups: range r holds the items
+// whose work cost before them lies in [r C / R, (r+1) C / R), C the total cost
+// (costs increase along the item list, so the ranges are contiguous and partition
+// it). Item i writes wg_start[r] = i for every r in (range(i-1), range(i)]; the
+// end sentinel i = total closes the last ranges. Every entry 0..R has one writer.
+__global__ void __launch_bounds__(256)
+wg_split_kernel(const int4* __restrict__ items, int32_t* __restrict__ totals, int R,
+                int32_t* __restrict__ wg_start) {
+  const int total = totals[1];
+  const int64_t C = totals[2];
+  for (int i = blockIdx.x * 256 + threadIdx.x; i <= total; i += gridDim.x * 256) {
+    const int ri = i < total ? (int)((int64_t)items[i].w * R / C) : R;
+    const int rp = i > 0 ? (int)((int64_t)items[i - 1].w * R / C) : -1;
+    for (int r = rp + 1; r <= ri; ++r) wg_start[r] = i;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) totals[3] = R;
 }
 
 // One query per sequence (decode): a row's valid ids are distinct, so every
@@ -279,6 +321,8 @@ direct_items_kernel(const int32_t* __restrict__ ids, int64_t nrows, int K, int n
   if (tid == 0) {
     totals[0] = base;
     totals[1] = base;
+    totals[2] = base;
+    totals[3] = 0;  // no balanced split: one-entry items are split by count
   }
 }
 
@@ -365,7 +409,7 @@ static size_t bucket_lds_bytes(const Dims& d, int arrays) {
 static bool bucket_use_lds(const Dims& d) { return bucket_lds_bytes(d, 2) <= 64 * 1024; }
 
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
-                            hipStream_t s) {
+                            hipStream_t s, int split_grid) {
   hipError_t e;
   // the direct path records no per-bucket offsets, which the canonical order needs
   if (!w.sorted && d.Nq == 1 && d.rows > 0 && d.items_max >= d.entries_max &&
@@ -380,10 +424,11 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   const unsigned nchunks = (unsigned)((d.buckets + kScanChunk - 1) / kScanChunk);
   auto scan = [&](int entries_max, int items_max) {
     bucket_chunk_sum_kernel<<<nchunks, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.chunk_e,
-                                                     w.chunk_i);
+                                                     w.chunk_i, w.chunk_c);
     bucket_scan_kernel<<<nchunks, 1024, 0, s>>>(w.counts, d.buckets, d.qt, w.chunk_e,
-                                                w.chunk_i, w.offsets, w.cursor, w.item_off,
-                                                w.totals, entries_max, items_max);
+                                                w.chunk_i, w.chunk_c, w.offsets, w.cursor,
+                                                w.item_off, w.cost_off, w.totals, entries_max,
+                                                items_max);
   };
   if (d.rows == 0) {
     scan(0, 0);
@@ -425,7 +470,10 @@ hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, 
   if (d.items_max > 0) {
     prof_before(MSA_K_WORK_ITEMS, s);
     work_items_kernel<<<(unsigned)((d.items_max + 255) / 256), 256, 0, s>>>(
-        w.item_off, w.offsets, w.totals, d.buckets, d.qt, w.items);
+        w.item_off, w.offsets, w.cost_off, w.totals, d.buckets, d.qt, w.items);
+    if (split_grid > 0 && split_grid <= kMaxSplit)
+      wg_split_kernel<<<(unsigned)std::min<int64_t>((d.items_max + 256) / 256, 1024), 256, 0,
+                        s>>>(w.items, w.totals, split_grid, w.wg_start);
     prof_after(MSA_K_WORK_ITEMS, s);
   }
   return hipGetLastError();
@@ -660,6 +708,7 @@ __global__ void __launch_bounds__(64 * NWV, 1)
 sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                         const bf16* __restrict__ v, const int4* __restrict__ items,
                         const int32_t* __restrict__ entries, const int32_t* __restrict__ totals,
+                        const int32_t* __restrict__ wg_start,
                         bf16* __restrict__ opart, float* __restrict__ lpart, int N, int Nq,
                         int q_start, int Hkv, int nb, int nbw, int topk, float scale_log2,
                         size_t dummy_entry) {
@@ -675,13 +724,25 @@ sparse_attn_pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   __shared__ bf16 Wst[NWV][32 * LDW];
   typedef __attribute__((address_space(3))) void lds_void;
 
+  // Workgroup g runs on XCD g % 8. XCD x takes the x-th eighth of the item list and
+  // its workgroups contiguous ranges of it, so consecutive items (one block) share an
+  // XCD's L2: range r = x * (gridDim.x / 8) + g / 8, cut by work cost when the
+  // bucketing wrote a split for this grid (balances the K/V reloads), else by count.
   const int total = totals[1];
   const int nwg_x = gridDim.x / 8;  // workgroups per XCD (gridDim.x is a multiple of 8)
   const int x = blockIdx.x & 7, gx = blockIdx.x >> 3;
-  const int per_x = (total + 7) / 8;
-  const int x0 = x * per_x, x1 = min(total, x0 + per_x);
-  const int per_wg = (per_x + nwg_x - 1) / nwg_x;
-  const int i0 = x0 + gx * per_wg, i1 = min(x1, i0 + per_wg);
+  int i0, i1;
+  if (totals[3] == (int)gridDim.x) {
+    const int rg = x * nwg_x + gx;
+    i0 = wg_start[rg];
+    i1 = wg_start[rg + 1];
+  } else {
+    const int per_x = (total + 7) / 8;
+    const int x0 = x * per_x, x1 = min(total, x0 + per_x);
+    const int per_wg = (per_x + nwg_x - 1) / nwg_x;
+    i0 = x0 + gx * per_wg;
+    i1 = min(x1, i0 + per_wg);
+  }
   if (i0 >= i1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -979,18 +1040,24 @@ static hipError_t attn_dispatch_g(const Dims& d, const void* q, const void* k, c
   return hipGetLastError();
 }
 
+unsigned attn_pipe_grid(const Dims& d) {
+  const bool one_wave = d.qt * d.G <= 32;
+  return (unsigned)((((one_wave ? 2 : 1) * d.num_cus + 7) / 8) * 8);
+}
+
 template <int D>
 static hipError_t attn_pipe_dispatch_g(const Dims& d, const void* q, const void* k, const void* v,
                                        const AttnWs& w, void* opart, float* lpart, hipStream_t s) {
   // persistent grid, a multiple of 8 (one share per XCD): one 8-wave workgroup
   // per CU, or two 1-wave workgroups per CU for items of at most 32/G queries
   const bool one_wave = d.qt * d.G <= 32;
-  const unsigned grid = (unsigned)((((one_wave ? 2 : 1) * d.num_cus + 7) / 8) * 8);
+  const unsigned grid = attn_pipe_grid(d);
   const float scale_log2 = (float)(1.0 / sqrt((double)D) * 1.4426950408889634);
 #define MSA_PIPE_LAUNCH(GG, NW)                                                                 \
   sparse_attn_pipe_kernel<D, GG, NW><<<grid, 64 * NW, 0, s>>>(                                 \
       (const bf16*)q, (const bf16*)k, (const bf16*)v, w.items, w.entries, w.totals,            \
-      (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K, scale_log2,   \
+      w.wg_start, (bf16*)opart, lpart, d.N, d.Nq, d.q_start, d.Hkv, d.nb, d.nb * d.nwin, d.K,  \
+      scale_log2,                                                                              \
       (size_t)d.slots)
 #define MSA_PIPE_CASE(GG)                                                                       \
   case GG:                                                                                      \

@@ -173,6 +173,23 @@ struct Dims {
 #define MSA_QUERY_WINDOW (1 << 30)  // one window: plain (batch, group, block) order
 #endif
 constexpr int kQueryWindow = MSA_QUERY_WINDOW;
+// Work cost of the persistent attention's items for the range split: kItemCost
+// units per item and kItemStartCost more for the first item of a bucket, whose K/V
+// tiles a workgroup must load behind a barrier and a full drain of its memory
+// operations. Per-workgroup timings under a split by item count showed the late
+// blocks of each group (small buckets, up to 20x more K/V reloads per workgroup)
+// finishing last; at the skewed 131072-token step, start/item cost ratios of
+// 0 (count split), 0.25, 0.5, 1, 1.5, 2, 4, 8, 16 gave attention times of
+// 11.66, 11.58, 11.31, 11.12, 11.17, 11.51, 11.74, 12.29, 12.99 ms.
+#ifndef MSA_ITEM_START_COST
+#define MSA_ITEM_START_COST 1
+#endif
+#ifndef MSA_ITEM_COST
+#define MSA_ITEM_COST 1
+#endif
+constexpr int kItemStartCost = MSA_ITEM_START_COST;
+constexpr int kItemCost = MSA_ITEM_COST;
+constexpr int kMaxSplit = 2048;  // workgroup ranges the balanced split can describe
 
 // Backward: at most this many persistent workgroups (a multiple of 8; two per
 // CU on 256 CUs). The dK/dV (and dk_idx) sums of a run of items of one bucket
@@ -186,11 +203,14 @@ struct AttnWs {
   int32_t* offsets;   // [buckets + 1]
   int32_t* cursor;    // [buckets]
   int32_t* item_off;  // [buckets + 1]
-  int32_t* totals;    // [4]: entries, items
-  int4* items;        // [items_max]: bucket, first entry, count, 0
+  int32_t* totals;    // [4]: entries, items, work cost, grid of the balanced split (0: none)
+  int4* items;        // [items_max]: bucket, first entry, count, work cost before it
   int32_t* entries;   // [entries_max]: (t << 6) | slot
   int32_t* chunk_e;   // [buckets / 4096 + 1]: entry count per scan chunk
   int32_t* chunk_i;   // [buckets / 4096 + 1]: item count per scan chunk
+  int32_t* chunk_c;   // [buckets / 4096 + 1]: work cost per scan chunk
+  int32_t* cost_off;  // [buckets + 1]: exclusive prefix of the work cost of each bucket
+  int32_t* wg_start;  // [kMaxSplit + 1]: first item of each balanced workgroup range
   // [entries_max] or null: when set, bucketing also writes the entries here in
   // row order inside each bucket (the order the backward sums in)
   int32_t* sorted;
@@ -218,8 +238,12 @@ bool decode_index_supported(const Dims& d);
 hipError_t launch_decode_index(const Dims& d, const void* q_idx, const void* k_idx, float* M,
                                hipStream_t s);
 
+// split_grid > 0: also cut the items into split_grid cost-balanced contiguous
+// ranges (wg_start, totals[3] = split_grid) for a persistent kernel of that grid
 hipError_t launch_bucketing(const Dims& d, const int32_t* ids, const AttnWs& w, bool skip_local,
-                            hipStream_t s);
+                            hipStream_t s, int split_grid = 0);
+// grid of the persistent bf16 attention kernel for d
+unsigned attn_pipe_grid(const Dims& d);
 hipError_t launch_sparse_attn(const Dims& d, const void* q, const void* k, const void* v,
                               const AttnWs& w, void* opart, float* lpart, hipStream_t s);
 hipError_t launch_combine(const Dims& d, const void* opart, const float* lpart,
