@@ -536,10 +536,15 @@ idx_bwd_kernel(const T* __restrict__ qi, const T* __restrict__ ki, const float* 
       for (int e = 0; e < 16; ++e) dka[dt][e] = 0.0f;
   };
   // the run [ra, rb) of bucket bkt ends: [128 keys][DI] fp32 slab, chosen as in
-  // the attention backward
+  // the attention backward. The buckets a neighbour may share (those of the items
+  // just outside the range) are read once here: with the test written inline in
+  // the item loop, the compiled flush inside the loop dropped the comparison of
+  // the previous item's bucket and sent the first run of a range that opens a
+  // bucket to the shared slab, leaving the bucket's own slab unwritten.
+  const int bkt_prev = __builtin_amdgcn_readfirstlane(i0 > 0 ? items[i0 - 1].x : -1);
+  const int bkt_next = __builtin_amdgcn_readfirstlane(i1 < total ? items[i1].x : -1);
   auto flush = [&](int bkt, int ra, int rb) {
-    const bool shared = (ra == i0 && i0 > 0 && items[i0 - 1].x == bkt) ||
-                        (rb == i1 && i1 < total && items[i1].x == bkt);
+    const bool shared = (ra == i0 && bkt_prev == bkt) || (rb == i1 && bkt_next == bkt);
     const size_t slab = shared ? (size_t)nbk + 2 * blockIdx.x + (ra == i0 ? 0 : 1) : (size_t)bkt;
     float* const row = slabs + (slab * 128 + 32 * w + l32) * DI;
 #pragma unroll

@@ -250,6 +250,50 @@ def test_idx_bwd_every_row(cfg):
     print(f"[idx_bwd] {cfg.name}: " + json.dumps(rep), flush=True)
 
 
+def test_idx_bwd_full_size_block_sums():
+    """Training workload (2 x 32768 tokens): dk_idx by closed-form block sums. The chain is
+    linear in the dlogits, so for every (batch, block) the sum of dk_idx over the block's keys
+    equals coef/sqrt(d_idx) times the sum, over the (query, group, slot) that selected the
+    block, of that slot's dlogits row sum times the query's q_idx row. Every bucket's slab
+    enters these sums: at this size a few buckets start exactly where a workgroup's item
+    range starts, whose sums must reach the bucket's own slab."""
+    import scipy.sparse
+    import learned_kv_block_amd as msa
+    cfg = si.CONFIGS["train_b2_n32768"]
+    print(f"[idx_bwd] start block sums {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg, names=("q", "k", "v", "q_idx", "k_idx"))
+    sel = msa.msa_select(x["q_idx"], x["k_idx"], cfg.topk, num_q_heads=cfg.num_q_heads,
+                         head_dim=cfg.head_dim)
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], sel["ids"], idx_dim=cfg.idx_dim)
+    kl = msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], sel["ids"], lse)
+    del out, lse
+    coef = 0.37
+    _, dki = msa.msa_idx_bwd(x["q_idx"], x["k_idx"], sel["ids"], kl["dlogits"], coef,
+                             num_q_heads=cfg.num_q_heads, head_dim=cfg.head_dim)
+    torch.cuda.synchronize()
+    B, Nq, Hkv, K, DI = cfg.batch, cfg.seqlen_q, cfg.num_kv_heads, cfg.topk, cfg.idx_dim
+    N, nb = cfg.seqlen_kv, cfg.num_blocks
+    n = B * Nq
+    ids = sel["ids"].reshape(n * Hkv * K).cpu().numpy()
+    # dlogits row sums, one batch at a time on the host
+    rs = np.concatenate([kl["dlogits"][b].cpu().numpy().astype(np.float64).sum(axis=-1).ravel()
+                         for b in range(B)])
+    del kl
+    q_idx = si.host_query_rows(cfg, "q_idx", np.arange(n, dtype=np.int64))  # bf16 bits
+    qrows = si.bf16_bits_to_f32(q_idx).astype(np.float64).reshape(n * Hkv, DI)
+    e = np.nonzero(ids >= 0)[0]
+    col = e // K                                     # (b*Nq + t)*Hkv + r
+    row = (col // (Nq * Hkv)) * nb + ids[e]          # b*nb + block
+    A = scipy.sparse.csr_matrix((rs[e], (row, col)), shape=(B * nb, n * Hkv))
+    want = (A @ qrows) * (coef / np.sqrt(DI))
+    got = np.zeros((B, nb * 128, DI), np.float64)
+    got[:, :N] = dki.float().cpu().numpy()
+    got = got.reshape(B, nb, 128, DI).sum(axis=2).reshape(B * nb, DI)
+    rep = {}
+    _check("dk_idx_block_sums", got, want, _tol(cfg), rep)
+    print(f"[idx_bwd] {cfg.name}: " + json.dumps(rep), flush=True)
+
+
 def test_bwd_empty_rows():
     """No query row: dq and dq_idx are empty; dk, dv and dk_idx (allocated uninitialised
     by the binding) come back zero, since the calls overwrite them."""
