@@ -1,0 +1,67 @@
+"""Results must not depend on what the caller's workspace held before the call.
+
+Each call runs once on a zeroed workspace and then twice on the same workspace with a float
+region filled with 0xFF bytes (NaN in fp32 and bf16), and the outputs must be bit-identical
+and free of NaN. Only regions that hold float data are filled (the selection's block-score
+matrix, the backward kernels' fp32 dK/dV and dk_idx slabs, which are the last region of
+their workspaces), so an index or count is never poisoned: a read of memory that the call did
+not write shows up as a NaN or a changed bit, never as an access out of range.
+The slab sizes follow the library's layout: one 128-key slab per (batch, group, block) bucket
+plus two per persistent workgroup (at most 512 workgroups); the attention backward keeps two
+32-row tiles of (dK, dV) per slab, the index backward one [128][d_idx] tile.
+"""
+import pytest
+import torch
+
+import seeded_inputs as si
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(tag, ref, got):
+    for i, (a, b) in enumerate(zip(ref, got)):
+        assert not bool(torch.isnan(b.float()).any()), f"{tag}[{i}]: NaN"
+        assert torch.equal(a, b), f"{tag}[{i}]: bits differ"
+
+
+def _poisoned(tag, op, tail_bytes, shape, call):
+    import learned_kv_block_amd as msa
+    n = msa.workspace_size(shape, op)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ref = [t.clone() for t in call(ws)]
+    pb = min(tail_bytes, n)
+    for _ in range(2):
+        ws.zero_()
+        ws[n - pb:].fill_(255)
+        got = call(ws)
+        torch.cuda.synchronize()
+        _same(tag, ref, got)
+    print(f"[workspace] {tag}: {pb} of {n} bytes poisoned, outputs identical", flush=True)
+
+
+def test_outputs_independent_of_workspace_contents():
+    """Training workload (2 x 32768 tokens): selection, attention backward and index
+    backward."""
+    import learned_kv_block_amd as msa
+    cfg = si.CONFIGS["train_b2_n32768"]
+    print(f"[workspace] start {cfg.name}", flush=True)
+    x = parity.gpu_inputs(cfg, names=("q", "k", "v", "q_idx", "k_idx", "dout"))
+    B, Hkv, K, D, DI = cfg.batch, cfg.num_kv_heads, cfg.topk, cfg.head_dim, cfg.idx_dim
+    sh = msa.make_shape(B, cfg.seqlen_kv, cfg.seqlen_q, 0, cfg.num_q_heads, Hkv, D, DI, K,
+                        msa.MSA_BF16)
+    _poisoned("select", msa.MSA_OP_SELECT, 1 << 40, sh,
+              lambda ws: (lambda r: (r["ids"], r["margin"]))(
+                  msa.msa_select(x["q_idx"], x["k_idx"], K, want_margin=True,
+                                 num_q_heads=cfg.num_q_heads, head_dim=D, workspace=ws)))
+    ids = msa.msa_select(x["q_idx"], x["k_idx"], K, num_q_heads=cfg.num_q_heads,
+                         head_dim=D)["ids"]
+    out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], ids, idx_dim=DI)
+    slabs = B * Hkv * cfg.num_blocks + 2 * 512
+    _poisoned("attn_bwd", msa.MSA_OP_ATTN_BWD, slabs * 2 * 2 * 128 * D * 4, sh,
+              lambda ws: msa.msa_attn_bwd(x["q"], x["k"], x["v"], ids, out, lse, x["dout"],
+                                          idx_dim=DI, workspace=ws))
+    kl = msa.msa_kl_align(x["q"], x["k"], x["q_idx"], x["k_idx"], ids, lse)
+    _poisoned("idx_bwd", msa.MSA_OP_IDX_BWD, slabs * 128 * DI * 4, sh,
+              lambda ws: msa.msa_idx_bwd(x["q_idx"], x["k_idx"], ids, kl["dlogits"], 1.0,
+                                         num_q_heads=cfg.num_q_heads, head_dim=D, workspace=ws))
