@@ -42,8 +42,8 @@ def _poisoned(tag, op, tail_bytes, shape, call):
 
 
 def test_outputs_independent_of_workspace_contents():
-    """Training workload (2 x 32768 tokens): selection, attention backward and index
-    backward."""
+    """Training workload (2 x 32768 tokens): selection (bf16 and FP8 index), attention
+    backward and index backward."""
     import learned_kv_block_amd as msa
     cfg = si.CONFIGS["train_b2_n32768"]
     print(f"[workspace] start {cfg.name}", flush=True)
@@ -55,6 +55,14 @@ def test_outputs_independent_of_workspace_contents():
               lambda ws: (lambda r: (r["ids"], r["margin"]))(
                   msa.msa_select(x["q_idx"], x["k_idx"], K, want_margin=True,
                                  num_q_heads=cfg.num_q_heads, head_dim=D, workspace=ws)))
+    qz = msa.msa_index_quantize_fp8(x["q_idx"], x["k_idx"], num_q_heads=cfg.num_q_heads,
+                                    head_dim=D)
+    _poisoned("select_fp8", msa.MSA_OP_SELECT, 1 << 40, sh,
+              lambda ws: (lambda r: (r["ids"], r["margin"]))(
+                  msa.msa_select_fp8(qz["q8"], qz["q_exp"], qz["k8"], qz["k_exp"], K,
+                                     want_margin=True, num_q_heads=cfg.num_q_heads, head_dim=D,
+                                     workspace=ws)))
+    del qz
     ids = msa.msa_select(x["q_idx"], x["k_idx"], K, num_q_heads=cfg.num_q_heads,
                          head_dim=D)["ids"]
     out, lse = msa.msa_attn_fwd(x["q"], x["k"], x["v"], ids, idx_dim=DI)
