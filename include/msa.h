@@ -40,7 +40,9 @@
  *    msa_workspace_size). The library allocates no memory, keeps no pointer
  *    past a call and does not synchronise: all work is enqueued on `stream`,
  *    and buffers must stay valid until that work has run. Calls on different
- *    streams with different workspaces may run concurrently.
+ *    streams with different workspaces may run concurrently. The workspace needs
+ *    no initialisation: every call writes what it reads there, so its results
+ *    do not depend on the workspace's earlier contents.
  *  - Every argument is validated on the host before anything is launched; a
  *    call that returns an error has enqueued nothing. Faults inside kernels
  *    surface asynchronously on the stream.
